@@ -1,0 +1,147 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check that the pins
+in test_oracle_pins.py catch each one.  Nothing here touches the GPU path."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import decode as O
+from persistent_moe_amd import workloads as W
+from tests import test_oracle_pins as P
+
+_orig = {n: getattr(O, n) for n in ("rms_norm", "rope", "attention_decode", "route", "swiglu",
+                                    "moe", "bf16_round", "attention_combine")}
+
+
+def _rms_sum(x, g, eps):
+    return x / np.sqrt(np.sum(x * x) + eps) * g
+
+
+def _rms_eps_outside(x, g, eps):
+    return x / (np.sqrt(np.mean(x * x)) + eps) * g
+
+
+def _rope_adjacent(x, pos, theta):
+    hd = x.shape[-1]
+    i = np.arange(hd // 2, dtype=np.float64)
+    ang = pos * theta ** (-2.0 * i / hd)
+    a, b = x[..., 0::2], x[..., 1::2]
+    out = np.empty_like(x)
+    out[..., 0::2] = a * np.cos(ang) - b * np.sin(ang)
+    out[..., 1::2] = b * np.cos(ang) + a * np.sin(ang)
+    return out
+
+
+def _rope_sign(x, pos, theta):
+    return _orig["rope"](x, -pos, theta)
+
+
+def _rope_freq(x, pos, theta):
+    hd = x.shape[-1]
+    half = hd // 2
+    i = np.arange(half, dtype=np.float64)
+    ang = pos * theta ** (-1.0 * i / hd)
+    a, b = x[..., :half], x[..., half:]
+    return np.concatenate([a * np.cos(ang) - b * np.sin(ang), b * np.cos(ang) + a * np.sin(ang)], -1)
+
+
+def _attn_scale(q, K, V):
+    return _orig["attention_decode"](q * math.sqrt(q.shape[1]) / q.shape[1], K, V)
+
+
+def _attn_mapping(q, K, V):
+    Hq, hd = q.shape
+    out = np.empty((Hq, hd))
+    for i in range(Hq):
+        g = i % K.shape[1]
+        p = O.softmax(K[:, g, :] @ q[i] / math.sqrt(hd))
+        out[i] = p @ V[:, g, :]
+    return out
+
+
+def _route_ties_high(logits, k):
+    E = logits.shape[0]
+    order = sorted(range(E), key=lambda e: (-logits[e], -e))
+    r = _orig["route"](logits, k)
+    r.ids = np.array(order[:k])
+    r.weights = r.probs[r.ids] / r.probs[r.ids].sum()
+    return r
+
+
+def _route_no_renorm(logits, k):
+    r = _orig["route"](logits, k)
+    r.weights = r.probs[r.ids]
+    return r
+
+
+def _swiglu_swapped(h, w_ug, w_d):
+    inter = w_ug.shape[0] // 2
+    return w_d @ (O.silu(w_ug[inter:] @ h) * (w_ug[:inter] @ h))
+
+
+def _moe_unweighted(h, r, expert):
+    return sum(O.swiglu(h, *expert(int(e))) for e in r.ids)
+
+
+def _bf16_truncate(x):
+    m, e = np.frexp(np.asarray(x, dtype=np.float64))
+    return np.ldexp(np.trunc(m * 256.0) / 256.0, e)
+
+
+def _combine_no_rescale(parts):
+    num = sum(p[2] for p in parts)
+    den = sum(p[1] for p in parts)
+    return num / den[:, None]
+
+
+MUTATIONS = [
+    ("rms_norm", _rms_sum, [P.test_rmsnorm_constant_vector_closed_form]),
+    ("rms_norm", _rms_eps_outside, [P.test_rmsnorm_constant_vector_closed_form]),
+    ("rope", _rope_adjacent, [P.test_rope_pairs_frequencies_and_direction]),
+    ("rope", _rope_sign, [P.test_rope_pairs_frequencies_and_direction]),
+    ("rope", _rope_freq, [P.test_rope_pairs_frequencies_and_direction]),
+    ("attention_decode", _attn_scale, [P.test_attention_two_keys_closed_form_scale]),
+    ("attention_decode", _attn_mapping, [P.test_attention_gqa_head_mapping]),
+    ("route", _route_ties_high, [P.test_route_ties_go_to_lower_expert_id]),
+    ("route", _route_no_renorm, [P.test_route_weights_and_probs_sum_to_one]),
+    ("swiglu", _swiglu_swapped, [P.test_swiglu_worked_example_gate_then_up]),
+    ("moe", _moe_unweighted, [P.test_moe_two_experts_weighted_by_renormalised_softmax]),
+    ("bf16_round", _bf16_truncate, [P.test_bf16_round_matches_torch_conversion]),
+]
+
+
+@pytest.mark.parametrize("name,fn,pins", MUTATIONS, ids=[f"{m[0]}:{m[1].__name__}" for m in MUTATIONS])
+def test_pin_catches_planted_mistake(monkeypatch, name, fn, pins):
+    monkeypatch.setattr(O, name, fn)
+    caught = 0
+    for pin in pins:
+        try:
+            pin()
+        except AssertionError:
+            caught += 1
+    assert caught > 0, f"no pin caught the mutation {fn.__name__} of {name}"
+
+
+def test_split_combine_pin_catches_missing_rescale(monkeypatch):
+    monkeypatch.setattr(O, "attention_combine", _combine_no_rescale)
+    with pytest.raises(AssertionError):
+        P.test_split_combine_equals_monolithic([0, 7, 16, 33])
+
+
+def test_window_off_by_one_is_caught(monkeypatch):
+    orig = W.ModelConfig.layer_window
+    monkeypatch.setattr(W.ModelConfig, "layer_window", lambda self, l: orig(self, l) + 1 if orig(self, l) else 0)
+    with pytest.raises(AssertionError):
+        P.test_sliding_window_boundary()
+
+
+def test_oracle_reproduces_golden_greedy_decode():
+    path = os.path.join(os.path.dirname(__file__), "golden", "tiny_greedy.json")
+    gold = json.load(open(path))
+    fed, res = O.greedy_decode(W.WORKLOADS["tiny"], 4)
+    for g, f, r in zip(gold["steps"], fed, res):
+        assert g["fed_token"] == f[0] and g["argmax"] == r[0].token
+        assert g["experts"] == [t.route.ids.tolist() for t in r[0].layers]
+        assert np.allclose(g["logits_head"], r[0].logits[:8], rtol=0, atol=1e-12)

@@ -1,0 +1,45 @@
+"""Speed-of-light accounting, pinned to the pages' own arithmetic.
+
+The persistent decode megakernel pages (page 1, "Why decode leaves the GPU
+idle"; page 3, "Where the bandwidth actually goes") put the bs=1 bound of the
+30B / 3.3B-active model at about 470 tok/s: 6.6 GB of active bf16 weights plus
+about 0.5 GB of KV at 8K context, over 3.35 TB/s.  292 tok/s is 62% of it and
+185 tok/s is 39%.
+"""
+import math
+
+from persistent_moe_amd import sol
+from persistent_moe_amd import workloads as W
+
+
+def test_pages_speed_of_light_arithmetic():
+    tok_s = sol.sol_tok_s(6.6e9 + 0.5e9, 1, bw=3.35e12)
+    assert 465 < tok_s < 475
+    assert abs(1e3 / tok_s - 2.1) < 0.05            # ~2.1 ms per step
+    assert round(292 / 470, 2) == 0.62 and round(185 / 470, 2) == 0.39
+
+
+def test_active_and_total_parameters_of_the_30b_model():
+    cfg = W.MOE_30B
+    active_bytes = sol.weight_bytes(cfg, 1, [cfg.top_k] * cfg.n_layers)
+    active = active_bytes / 2
+    assert abs(active / 3.3e9 - 1) < 0.02          # "3.3B active"
+    total = sol.weight_bytes(cfg, 1, [cfg.n_experts] * cfg.n_layers) / 2 + cfg.vocab * cfg.d_model
+    assert abs(total / 30.96e9 - 1) < 0.005        # ~30B total with an untied LM head
+
+
+def test_step_bytes_of_the_bs1_8k_workload():
+    cfg = W.MOE_30B
+    nbytes = sol.step_bytes(cfg, [8192], [8] * 48)
+    kv = 48 * 8193 * 2 * 4 * 128 * 2
+    assert nbytes - sol.weight_bytes(cfg, 1, [8] * 48) == kv
+    assert abs(nbytes / 7.33e9 - 1) < 0.01
+    assert abs(sol.sol_tok_s(nbytes, 1) - 1092) < 10
+
+
+def test_sliding_window_limits_kv():
+    cfg = W.MOE_30B_SWA
+    assert sol.visible_keys(cfg, 0, 262144) == 4096
+    assert sol.visible_keys(cfg, 3, 262144) == 262145
+    kv = sol.kv_bytes(cfg, [262144])
+    assert kv == (12 * 262145 + 36 * 4096) * 2048
