@@ -1,0 +1,793 @@
+// mk_host.cpp - C ABI of libmk.so: validation, workspace layout, the host
+// schedule builder, a discrete-event deadlock check of a schedule, and the
+// step launch.
+//
+// The schedule follows the persistent decode megakernel pages (page 1
+// "Scheduling: mostly static, selectively dynamic"; page 3 on the tuned
+// per-layer wave order QKV, router, attention, MoE projections, O-proj and
+// RMSNorm): the host emits named waves per layer in a topological order and
+// deals task k to workgroup k mod N.  Attention splits and MoE expert tiles,
+// whose counts depend on live lengths and routing, are claimer tasks: claimer
+// c of a wave owns item c of its queue and pulls any items beyond the number
+// of claimers from an atomic queue head.
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "mk_internal.h"
+
+namespace {
+
+constexpr int kMaxWorkgroups = 1024;
+constexpr int kYsFloats = 8192;    // LDS capacity for scores / tile outputs (mk_kernel.hip)
+constexpr int kXsFloats = 16384;   // LDS capacity for staged activations
+
+struct Layout {
+  size_t off_tasks, off_ctr, off_err, off_layers, off_invf;
+  size_t off_x, off_xn, off_xmid, off_xn2, off_qkv, off_attn, off_opart, off_rlog, off_topi, off_topw;
+  size_t off_moe, off_H, off_Y, off_fh, off_fo, off_oout, off_pml, off_po;
+  size_t total;
+  int32_t max_tasks, n_ctr, max_splits, bk, moe_stride;
+  mk_ctr_layout cl;
+};
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+int validate_config(const mk_config* c) {
+  if (!c) return MK_E_INVAL;
+  if (c->n_layers <= 0 || c->d_model <= 0 || c->n_q_heads <= 0 || c->n_kv_heads <= 0 || c->vocab <= 0)
+    return MK_E_INVAL;
+  if (c->n_q_heads % c->n_kv_heads != 0) return MK_E_INVAL;
+  if (c->d_model % 8 != 0 || c->page_size <= 0) return MK_E_INVAL;
+  if (c->max_batch < 1 || c->max_batch > 8) return MK_E_UNSUPPORTED;
+  if (c->head_dim != 64 && c->head_dim != 128) return MK_E_UNSUPPORTED;
+  if (c->n_q_heads / c->n_kv_heads > 8) return MK_E_UNSUPPORTED;
+  if (c->rms_eps < 0.f || !(c->rope_theta > 0.f)) return MK_E_INVAL;
+  const bool moe = c->n_experts > 0;
+  if (moe) {
+    if (c->top_k < 1 || c->top_k > c->n_experts || c->n_experts > 256 || c->expert_inter <= 0)
+      return MK_E_INVAL;
+    if (c->expert_inter % 8 != 0) return MK_E_INVAL;
+    if (c->max_batch * c->top_k > 64) return MK_E_UNSUPPORTED;
+    if (!c->parallel_block) return MK_E_UNSUPPORTED;
+  } else {
+    if (c->ffn_inter <= 0 || c->ffn_inter % 8 != 0) return MK_E_INVAL;
+    if (c->parallel_block) return MK_E_UNSUPPORTED;
+    if ((size_t)c->max_batch * c->ffn_inter > (size_t)kXsFloats) return MK_E_UNSUPPORTED;
+  }
+  if ((size_t)c->max_batch * c->d_model > (size_t)kXsFloats) return MK_E_UNSUPPORTED;
+  const int gd = c->n_q_heads / c->n_kv_heads * c->head_dim;
+  if ((size_t)c->max_batch * gd > (size_t)kXsFloats) return MK_E_UNSUPPORTED;
+  if (c->swa_window < 0 || c->swa_period < 0) return MK_E_INVAL;
+  return MK_OK;
+}
+
+int max_tasks_bound(const mk_config* c) {
+  const int per_layer = 8 * kMaxWorkgroups + 2 * c->max_batch * c->n_kv_heads + 64;
+  return (c->n_layers + 1) * per_layer + kMaxWorkgroups;
+}
+
+Layout make_layout(const mk_config* c, int32_t max_blocks) {
+  Layout L{};
+  const int Lr = c->n_layers, B = c->max_batch, d = c->d_model, hd = c->head_dim;
+  const int rows = (c->n_q_heads + 2 * c->n_kv_heads) * hd;
+  const int adim = c->n_q_heads * hd;
+  const int E = c->n_experts, K = c->top_k;
+  L.bk = E > 0 ? B * K : 1;
+  L.moe_stride = mk_moe_stride(L.bk);
+  L.cl = mk_make_ctr_layout(Lr, c->n_kv_heads, B, E > 0 ? K : 0);
+  L.n_ctr = L.cl.total;
+  L.max_tasks = max_tasks_bound(c);
+  const long max_ctx = (long)max_blocks * c->page_size;
+  L.max_splits = (int)std::max<long>(1, (max_ctx + MK_MIN_SPLIT - 1) / MK_MIN_SPLIT);
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t r = o; o = align_up(o + bytes, 256); return r; };
+  L.off_tasks = take((size_t)L.max_tasks * sizeof(mk_task));
+  L.off_ctr = take((size_t)L.n_ctr * 4);
+  L.off_err = take(MK_ERR_WORDS * 4);
+  L.off_layers = take((size_t)Lr * sizeof(mk_layer_dev));
+  L.off_invf = take((size_t)(hd / 2) * 8);
+  L.off_x = take((size_t)(Lr + 1) * B * d * 4);
+  L.off_xn = take((size_t)(Lr + 1) * B * d * 4);
+  L.off_xmid = take(c->parallel_block ? 4 : (size_t)Lr * B * d * 4);
+  L.off_xn2 = take(c->parallel_block ? 4 : (size_t)Lr * B * d * 4);
+  L.off_qkv = take((size_t)Lr * B * rows * 4);
+  L.off_attn = take((size_t)Lr * B * adim * 4);
+  L.off_opart = take((size_t)Lr * c->n_kv_heads * B * d * 4);
+  L.off_rlog = take(E > 0 ? (size_t)Lr * B * E * 4 : 4);
+  L.off_topi = take(E > 0 ? (size_t)Lr * B * K * 4 : 4);
+  L.off_topw = take(E > 0 ? (size_t)Lr * B * K * 4 : 4);
+  L.off_moe = take(E > 0 ? (size_t)Lr * L.moe_stride * 4 : 4);
+  L.off_H = take(E > 0 ? (size_t)Lr * L.bk * c->expert_inter * 4 : 4);
+  L.off_Y = take(E > 0 ? (size_t)Lr * L.bk * d * 4 : 4);
+  L.off_fh = take(E > 0 ? 4 : (size_t)Lr * B * c->ffn_inter * 4);
+  L.off_fo = take((size_t)Lr * B * d * 4);
+  L.off_oout = take((size_t)Lr * B * d * 4);
+  L.off_pml = take((size_t)2 * B * c->n_q_heads * L.max_splits * 2 * 4);
+  L.off_po = take((size_t)2 * B * c->n_q_heads * L.max_splits * hd * 4);
+  L.total = o;
+  return L;
+}
+
+int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
+
+// ------------------------------------------------------------ plan builder
+struct Plan {
+  std::vector<mk_task> tasks;
+  std::vector<int32_t> wave_bounds;   // starts of each named wave, then the end
+  int n_ctr = 0;
+  int attn_split = 0, max_splits = 0;
+  int ug_tiles = 0, ug_pairs = 0, dn_tiles = 0, dn_rows = 0;
+  int n_qkv = 0;
+  mk_ctr_layout cl{};
+};
+
+mk_task blank(int op, int layer) {
+  mk_task t;
+  std::memset(&t, 0, sizeof t);
+  t.op = op;
+  t.layer = layer;
+  t.wait_ctr = -1;
+  t.wait_target = 0;
+  t.signal_ctr = -1;
+  t.queue = -1;
+  return t;
+}
+
+int ctr_of(const mk_ctr_layout& cl, int layer, int off) { return MK_CG_COUNT + layer * cl.stride + off; }
+
+int build_plan(const mk_config* c, int B, int32_t max_blocks, const mk_sched_opts* opt, int NW, Plan* P) {
+  if (B < 1 || B > c->max_batch || NW < 1 || NW > kMaxWorkgroups || max_blocks < 1) return MK_E_INVAL;
+  mk_sched_opts o{};
+  if (opt) o = *opt;
+  if (o.wave_order < 0 || o.wave_order > 2 || o.launch_mode < 0 || o.launch_mode > 1) return MK_E_INVAL;
+  const int Lr = c->n_layers, d = c->d_model, hd = c->head_dim, Hkv = c->n_kv_heads;
+  const int G = c->n_q_heads / Hkv;
+  const bool moe = c->n_experts > 0;
+  const long max_ctx = (long)max_blocks * c->page_size;
+  Plan& p = *P;
+  p.cl = mk_make_ctr_layout(Lr, Hkv, c->max_batch, moe ? c->top_k : 0);
+  p.n_ctr = p.cl.total;
+  // attention split length: about NW items per layer at the longest context
+  int S = o.attn_split;
+  const int smax = std::min(kYsFloats / G, 1024);
+  if (S > 0) {
+    if (S % c->page_size != 0 || S < MK_MIN_SPLIT || S > smax) return MK_E_INVAL;
+  } else {
+    long want = (max_ctx * B * Hkv + NW - 1) / NW;
+    want = std::max<long>(want, MK_MIN_SPLIT);
+    want = (want + c->page_size - 1) / c->page_size * c->page_size;
+    S = (int)std::min<long>(want, smax);
+    S = std::max(S, MK_MIN_SPLIT);
+  }
+  p.attn_split = S;
+  p.max_splits = ceil_div(max_ctx, S);
+  if (p.max_splits > 1024) return MK_E_UNSUPPORTED;
+  // tilings
+  const int pairs_tot = (c->n_q_heads + 2 * Hkv) * hd / 2;
+  const int qkv_pp = std::max(1, ceil_div(pairs_tot, NW));
+  const int n_qkv = ceil_div(pairs_tot, qkv_pp);
+  if (2 * qkv_pp > kYsFloats / 8) return MK_E_UNSUPPORTED;
+  p.n_qkv = n_qkv;
+  const int o_tiles_g = std::max(1, NW / Hkv);
+  const int o_rows = ceil_div(d, o_tiles_g);
+  const int n_o_g = ceil_div(d, o_rows);
+  const int lm_rows = ceil_div(c->vocab, NW);
+  const int n_lm = ceil_div(c->vocab, lm_rows);
+  int r_rows = 0, n_r = 0;
+  if (moe) {
+    const int E = c->n_experts, K = c->top_k, I = c->expert_inter;
+    r_rows = std::max(8, ceil_div(E, 8));
+    n_r = ceil_div(E, r_rows);
+    p.ug_pairs = std::max(1, ceil_div((long)K * I, NW));
+    p.ug_pairs = std::min(p.ug_pairs, kYsFloats / 8 / 2);
+    p.ug_tiles = ceil_div(I, p.ug_pairs);
+    p.dn_rows = std::max(1, ceil_div((long)K * d, NW));
+    p.dn_tiles = ceil_div(d, p.dn_rows);
+  }
+  int ffn_pp = 0, n_fug = 0, ffn_rows = 0, n_fdn = 0;
+  if (!moe) {
+    ffn_pp = std::max(1, ceil_div(c->ffn_inter, NW));
+    ffn_pp = std::min(ffn_pp, kYsFloats / 8 / 2);
+    n_fug = ceil_div(c->ffn_inter, ffn_pp);
+    ffn_rows = std::max(1, ceil_div(d, NW));
+    n_fdn = ceil_div(d, ffn_rows);
+  }
+  const int n_claim = NW;
+  std::vector<mk_task>& T = p.tasks;
+  T.clear();
+  p.wave_bounds.clear();
+  auto wave = [&]() { p.wave_bounds.push_back((int32_t)T.size()); };
+  if (o.flags & MK_SCHED_UNREACHABLE_WAIT) {
+    // waits on a global counter slot that nothing signals
+    wave();
+    mk_task t = blank(MK_OP_LM_HEAD, Lr);
+    t.n0 = 0;
+    t.n1 = std::min(c->vocab, 8);
+    t.wait_ctr = MK_CG_COUNT - 1;
+    t.wait_target = 1;
+    T.push_back(t);
+  }
+
+  int layer_target_prev = 0;
+  for (int l = 0; l <= Lr; ++l) {
+    // ADD_RMSNORM entering layer l (l == Lr: the final norm)
+    wave();
+    {
+      mk_task t = blank(MK_OP_ADD_RMSNORM, l);
+      if (l == 0) {
+        t.flags |= MK_F_EMBED;
+      } else {
+        t.wait_ctr = ctr_of(p.cl, l - 1, MK_CTR_LAYER);
+        t.wait_target = layer_target_prev;
+      }
+      if (l == Lr) t.flags |= MK_F_FINAL;
+      t.signal_ctr = ctr_of(p.cl, l, MK_CTR_NORM);
+      T.push_back(t);
+    }
+    if (l == Lr) break;
+    const int cNORM = ctr_of(p.cl, l, MK_CTR_NORM);
+    auto emit_qkv = [&]() {
+      wave();
+      for (int i = 0; i < n_qkv; ++i) {
+        mk_task t = blank(MK_OP_QKV_PROJ, l);
+        t.n0 = i * qkv_pp;
+        t.n1 = std::min(pairs_tot, t.n0 + qkv_pp);
+        t.wait_ctr = cNORM;
+        t.wait_target = 1;
+        t.signal_ctr = ctr_of(p.cl, l, MK_CTR_QKV);
+        T.push_back(t);
+      }
+    };
+    auto emit_attn = [&]() {
+      wave();
+      for (int i = 0; i < n_claim; ++i) {
+        mk_task t = blank(MK_OP_ATTN_DRAIN, l);
+        t.n0 = i;
+        t.n1 = n_claim;
+        t.wait_ctr = ctr_of(p.cl, l, MK_CTR_QKV);
+        t.wait_target = n_qkv;
+        t.queue = ctr_of(p.cl, l, MK_CTR_QATTN);
+        T.push_back(t);
+      }
+    };
+    auto emit_combine = [&]() {
+      wave();
+      for (int b = 0; b < B; ++b)
+        for (int g = 0; g < Hkv; ++g) {
+          mk_task t = blank(MK_OP_ATTN_COMBINE, l);
+          t.batch = b;
+          t.group = g;
+          t.wait_ctr = ctr_of(p.cl, l, p.cl.attn + b * Hkv + g);
+          t.wait_target = MK_WAIT_SPLITS;
+          t.signal_ctr = ctr_of(p.cl, l, p.cl.comb + g);
+          T.push_back(t);
+        }
+    };
+    auto emit_oproj = [&](int signal) {
+      wave();
+      for (int g = 0; g < Hkv; ++g)
+        for (int i = 0; i < n_o_g; ++i) {
+          mk_task t = blank(MK_OP_O_PROJ, l);
+          t.group = g;
+          t.n0 = i * o_rows;
+          t.n1 = std::min(d, t.n0 + o_rows);
+          t.k0 = g * G * hd;
+          t.k1 = t.k0 + G * hd;
+          t.wait_ctr = ctr_of(p.cl, l, p.cl.comb + g);
+          t.wait_target = B;
+          t.signal_ctr = signal;
+          T.push_back(t);
+        }
+    };
+    if (moe) {
+      const int cROUTE = ctr_of(p.cl, l, MK_CTR_ROUTE);
+      const int cLAYER = ctr_of(p.cl, l, MK_CTR_LAYER);
+      auto emit_router = [&]() {
+        wave();
+        for (int i = 0; i < n_r; ++i) {
+          mk_task t = blank(MK_OP_ROUTER_GEMM, l);
+          t.n0 = i * r_rows;
+          t.n1 = std::min(c->n_experts, t.n0 + r_rows);
+          t.wait_ctr = cNORM;
+          t.wait_target = 1;
+          t.signal_ctr = ctr_of(p.cl, l, MK_CTR_ROUTER);
+          T.push_back(t);
+        }
+        wave();
+        mk_task t = blank(MK_OP_ROUTER_TOPK, l);
+        t.flags |= MK_F_FUSE_FINALIZE;
+        t.wait_ctr = ctr_of(p.cl, l, MK_CTR_ROUTER);
+        t.wait_target = n_r;
+        t.signal_ctr = cROUTE;
+        T.push_back(t);
+      };
+      auto emit_ug = [&]() {
+        wave();
+        for (int i = 0; i < n_claim; ++i) {
+          mk_task t = blank(MK_OP_MOE_UPGATE_ACT_DRAIN, l);
+          t.n0 = i;
+          t.n1 = n_claim;
+          t.wait_ctr = cROUTE;
+          t.wait_target = 1;
+          t.queue = ctr_of(p.cl, l, MK_CTR_QUG);
+          T.push_back(t);
+        }
+      };
+      auto emit_dn = [&]() {
+        wave();
+        for (int i = 0; i < n_claim; ++i) {
+          mk_task t = blank(MK_OP_MOE_DOWN_DRAIN, l);
+          t.n0 = i;
+          t.n1 = n_claim;
+          t.wait_ctr = cROUTE;
+          t.wait_target = 1;
+          t.queue = ctr_of(p.cl, l, MK_CTR_QDN);
+          t.signal_ctr = cLAYER;
+          T.push_back(t);
+        }
+      };
+      switch (o.wave_order) {
+        case MK_ORDER_ATTENTION_FIRST:
+          emit_qkv(); emit_attn(); emit_combine(); emit_oproj(cLAYER);
+          emit_router(); emit_ug(); emit_dn();
+          break;
+        case MK_ORDER_INTERLEAVED:
+          emit_qkv(); emit_router(); emit_ug(); emit_attn(); emit_dn(); emit_combine(); emit_oproj(cLAYER);
+          break;
+        default:  // tuned: QKV, router, attention, MoE projections, O-proj, norm
+          emit_qkv(); emit_router(); emit_attn(); emit_ug(); emit_combine(); emit_dn(); emit_oproj(cLAYER);
+          break;
+      }
+      layer_target_prev = n_claim + Hkv * n_o_g;
+    } else {
+      const int cO = ctr_of(p.cl, l, MK_CTR_OPROJ);
+      const int cN2 = ctr_of(p.cl, l, MK_CTR_NORM2);
+      const int cFUG = ctr_of(p.cl, l, MK_CTR_FFNUG);
+      emit_qkv(); emit_attn(); emit_combine(); emit_oproj(cO);
+      wave();
+      {
+        mk_task t = blank(MK_OP_ADD_RMSNORM, l);
+        t.flags |= MK_F_MID;
+        t.wait_ctr = cO;
+        t.wait_target = Hkv * n_o_g;
+        t.signal_ctr = cN2;
+        T.push_back(t);
+      }
+      wave();
+      for (int i = 0; i < n_fug; ++i) {
+        mk_task t = blank(MK_OP_FFN_UPGATE_ACT, l);
+        t.n0 = i * ffn_pp;
+        t.n1 = std::min(c->ffn_inter, t.n0 + ffn_pp);
+        t.wait_ctr = cN2;
+        t.wait_target = 1;
+        t.signal_ctr = cFUG;
+        T.push_back(t);
+      }
+      wave();
+      for (int i = 0; i < n_fdn; ++i) {
+        mk_task t = blank(MK_OP_FFN_DOWN, l);
+        t.n0 = i * ffn_rows;
+        t.n1 = std::min(d, t.n0 + ffn_rows);
+        t.wait_ctr = cFUG;
+        t.wait_target = n_fug;
+        t.signal_ctr = ctr_of(p.cl, l, MK_CTR_LAYER);
+        T.push_back(t);
+      }
+      layer_target_prev = n_fdn;
+    }
+  }
+  wave();
+  for (int i = 0; i < n_lm; ++i) {
+    mk_task t = blank(MK_OP_LM_HEAD, Lr);
+    t.n0 = i * lm_rows;
+    t.n1 = std::min(c->vocab, t.n0 + lm_rows);
+    t.wait_ctr = ctr_of(p.cl, Lr, MK_CTR_NORM);
+    t.wait_target = 1;
+    T.push_back(t);
+  }
+  p.wave_bounds.push_back((int32_t)T.size());
+  if ((int)T.size() > max_tasks_bound(c)) return MK_E_NOMEM;
+  return MK_OK;
+}
+
+// ------------------------------------------------------- deadlock checker
+// Discrete-event model of the persistent kernel: NW in-order workers, task k
+// on worker k mod NW; a task runs when its counter reaches its target; a
+// claimer owns item c of its queue and then pulls items past the number of
+// claimers one at a time.  Items of a down queue wait on their expert's
+// up-gate counter.  Any state in which no worker can advance and some task is
+// unfinished is a deadlock.
+struct SimQueue {
+  int n_items = 0, head = 0;
+};
+
+int simulate(const mk_config* c, int B, const Plan& p, int NW, const int32_t* seq_lens,
+             const int32_t* n_active, int32_t* stuck) {
+  const int Hkv = c->n_kv_heads, Lr = c->n_layers;
+  std::vector<long> ctr(p.n_ctr, 0);
+  auto vis = [&](int l, int sl) {
+    if (c->swa_window > 0 && c->swa_period > 0 && l % c->swa_period != c->swa_period - 1)
+      return std::min(sl, c->swa_window);
+    return sl;
+  };
+  auto nspl = [&](int l, int b) {
+    int sl = seq_lens[b];
+    return sl <= 0 ? 0 : ceil_div(vis(l, sl), p.attn_split);
+  };
+  std::vector<int> cursor(NW);
+  for (int w = 0; w < NW; ++w) cursor[w] = w;
+  // per-claimer state: -1 before the static item, then dynamic claiming
+  std::vector<int> phase(NW, 0);
+  std::vector<int> cur_item(NW, -1);
+  std::vector<SimQueue> qa(Lr), qu(Lr), qd(Lr);
+  for (int l = 0; l < Lr; ++l) {
+    int na = 0;
+    for (int b = 0; b < B; ++b) na += Hkv * nspl(l, b);
+    qa[l].n_items = na;
+    if (c->n_experts > 0) {
+      qu[l].n_items = n_active[l] * p.ug_tiles;
+      qd[l].n_items = n_active[l] * p.dn_tiles;
+    }
+  }
+  const int n_tasks = (int)p.tasks.size();
+  // attention item -> (b, g)
+  auto attn_bg = [&](int l, int item, int* b_out, int* g_out) {
+    for (int b = 0; b < B; ++b) {
+      int ns = nspl(l, b), cnt = ns * Hkv;
+      if (item < cnt) { *b_out = b; *g_out = item / ns; return; }
+      item -= cnt;
+    }
+    *b_out = *g_out = 0;
+  };
+  for (long iter = 0;; ++iter) {
+    bool progress = false, all_done = true;
+    for (int w = 0; w < NW; ++w) {
+      while (cursor[w] < n_tasks) {
+        all_done = false;
+        const mk_task& t = p.tasks[cursor[w]];
+        int target = t.wait_target;
+        if (target == MK_WAIT_SPLITS) target = nspl(t.layer, t.batch);
+        if (t.wait_ctr >= 0 && target > 0 && ctr[t.wait_ctr] < target) break;
+        const bool claimer = t.op == MK_OP_ATTN_DRAIN || t.op == MK_OP_MOE_UPGATE_ACT_DRAIN ||
+                             t.op == MK_OP_MOE_DOWN_DRAIN;
+        if (claimer) {
+          SimQueue& q = (t.op == MK_OP_ATTN_DRAIN) ? qa[t.layer]
+                        : (t.op == MK_OP_MOE_UPGATE_ACT_DRAIN) ? qu[t.layer] : qd[t.layer];
+          // pick the next item of this claimer
+          if (cur_item[w] < 0) {
+            if (phase[w] == 0) {
+              phase[w] = 1;
+              if (t.n0 < q.n_items) cur_item[w] = t.n0;
+            }
+            if (cur_item[w] < 0) {
+              const int item = t.n1 + q.head;
+              if (item < q.n_items) { q.head++; cur_item[w] = item; }
+            }
+          }
+          if (cur_item[w] >= 0) {
+            const int item = cur_item[w];
+            if (t.op == MK_OP_MOE_DOWN_DRAIN) {
+              const int ae = item / p.dn_tiles;
+              if (ctr[ctr_of(p.cl, t.layer, p.cl.ug + ae)] < p.ug_tiles) break;
+            }
+            if (t.op == MK_OP_ATTN_DRAIN) {
+              int b, g;
+              attn_bg(t.layer, item, &b, &g);
+              ctr[ctr_of(p.cl, t.layer, p.cl.attn + b * Hkv + g)]++;
+            } else if (t.op == MK_OP_MOE_UPGATE_ACT_DRAIN) {
+              ctr[ctr_of(p.cl, t.layer, p.cl.ug + item / p.ug_tiles)]++;
+            }
+            cur_item[w] = -1;
+            progress = true;
+            continue;   // look for another item
+          }
+          phase[w] = 0;
+        }
+        if (t.signal_ctr >= 0) ctr[t.signal_ctr]++;
+        cursor[w] += NW;
+        progress = true;
+      }
+    }
+    if (all_done) return MK_OK;
+    if (!progress) {
+      int first = n_tasks;
+      for (int w = 0; w < NW; ++w) first = std::min(first, cursor[w]);
+      if (stuck) *stuck = first;
+      return MK_E_STATE;
+    }
+    if (iter > 100000000L) return MK_E_STATE;
+  }
+}
+
+int device_cu_count(int* out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MK_E_HIP;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return MK_E_HIP;
+  *out = cus;
+  return MK_OK;
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------ handle
+struct mk_handle {
+  mk_config cfg;
+  Layout lay;
+  char* ws;
+  size_t ws_bytes;
+  int32_t max_blocks;
+  int32_t num_pages;
+  std::vector<mk_layer_dev> layers;
+  const uint16_t* embed;
+  const uint16_t* lm_head;
+  const uint16_t* final_norm;
+  Plan plan;
+  bool have_plan;
+  int batch;
+  int n_wg;
+  mk_sched_opts opts;
+  hipStream_t last_stream;
+  int device;
+};
+
+extern "C" {
+
+size_t mk_workspace_size(const mk_config* cfg, int32_t max_blocks_per_seq) {
+  if (validate_config(cfg) != MK_OK || max_blocks_per_seq < 1) return 0;
+  return make_layout(cfg, max_blocks_per_seq).total;
+}
+
+int mk_init(const mk_config* cfg, const mk_weights* w, const mk_kv_pool* kv, void* workspace,
+            size_t ws_bytes, int32_t max_blocks_per_seq, mk_handle** out) {
+  if (!out) return MK_E_INVAL;
+  *out = nullptr;
+  int rc = validate_config(cfg);
+  if (rc != MK_OK) return rc;
+  if (!w || !kv || !workspace || max_blocks_per_seq < 1) return MK_E_INVAL;
+  if (!w->embed || !w->lm_head || !w->final_norm || !w->layers || !kv->k || !kv->v || kv->num_pages < 1)
+    return MK_E_INVAL;
+  const bool moe = cfg->n_experts > 0;
+  for (int l = 0; l < cfg->n_layers; ++l) {
+    const mk_layer_weights& lw = w->layers[l];
+    if (!lw.attn_norm || !lw.w_qkv || !lw.w_o || !lw.w_upgate || !lw.w_down || !kv->k[l] || !kv->v[l])
+      return MK_E_INVAL;
+    if (moe && !lw.w_router) return MK_E_INVAL;
+    if (!moe && !lw.ffn_norm) return MK_E_INVAL;
+  }
+  Layout lay = make_layout(cfg, max_blocks_per_seq);
+  if (ws_bytes < lay.total) return MK_E_NOMEM;
+  if (((uintptr_t)workspace) % 256 != 0) return MK_E_INVAL;
+  mk_handle* h = new (std::nothrow) mk_handle();
+  if (!h) return MK_E_INVAL;
+  h->cfg = *cfg;
+  h->lay = lay;
+  h->ws = static_cast<char*>(workspace);
+  h->ws_bytes = ws_bytes;
+  h->max_blocks = max_blocks_per_seq;
+  h->num_pages = kv->num_pages;
+  h->embed = static_cast<const uint16_t*>(w->embed);
+  h->lm_head = static_cast<const uint16_t*>(w->lm_head);
+  h->final_norm = static_cast<const uint16_t*>(w->final_norm);
+  h->layers.resize(cfg->n_layers);
+  for (int l = 0; l < cfg->n_layers; ++l) {
+    const mk_layer_weights& lw = w->layers[l];
+    mk_layer_dev& ld = h->layers[l];
+    ld.attn_norm = static_cast<const uint16_t*>(lw.attn_norm);
+    ld.ffn_norm = static_cast<const uint16_t*>(lw.ffn_norm);
+    ld.w_qkv = static_cast<const uint16_t*>(lw.w_qkv);
+    ld.w_o = static_cast<const uint16_t*>(lw.w_o);
+    ld.w_router = static_cast<const uint16_t*>(lw.w_router);
+    ld.w_upgate = static_cast<const uint16_t*>(lw.w_upgate);
+    ld.w_down = static_cast<const uint16_t*>(lw.w_down);
+    ld.k = static_cast<uint16_t*>(kv->k[l]);
+    ld.v = static_cast<uint16_t*>(kv->v[l]);
+  }
+  h->have_plan = false;
+  h->batch = 0;
+  h->last_stream = nullptr;
+  if (hipGetDevice(&h->device) != hipSuccess) { delete h; return MK_E_HIP; }
+  std::vector<double> invf(cfg->head_dim / 2);
+  for (int i = 0; i < cfg->head_dim / 2; ++i)
+    invf[i] = std::pow((double)cfg->rope_theta, -2.0 * i / (double)cfg->head_dim);
+  if (hipMemset(h->ws, 0, lay.total) != hipSuccess ||
+      hipMemcpy(h->ws + lay.off_layers, h->layers.data(), h->layers.size() * sizeof(mk_layer_dev),
+                hipMemcpyHostToDevice) != hipSuccess ||
+      hipMemcpy(h->ws + lay.off_invf, invf.data(), invf.size() * 8, hipMemcpyHostToDevice) != hipSuccess) {
+    delete h;
+    return MK_E_HIP;
+  }
+  *out = h;
+  return MK_OK;
+}
+
+int mk_build_schedule(mk_handle* h, int32_t batch_size, const mk_sched_opts* opt) {
+  if (!h) return MK_E_INVAL;
+  mk_sched_opts o{};
+  if (opt) o = *opt;
+  int nw = o.n_workgroups;
+  if (nw <= 0) {
+    int rc = device_cu_count(&nw);
+    if (rc != MK_OK) return rc;
+  }
+  if (nw > kMaxWorkgroups) return MK_E_UNSUPPORTED;
+  Plan p;
+  int rc = build_plan(&h->cfg, batch_size, h->max_blocks, &o, nw, &p);
+  if (rc != MK_OK) return rc;
+  if ((int)p.tasks.size() > h->lay.max_tasks) return MK_E_NOMEM;
+  if (p.max_splits > h->lay.max_splits) return MK_E_UNSUPPORTED;
+  if (hipMemcpy(h->ws + h->lay.off_tasks, p.tasks.data(), p.tasks.size() * sizeof(mk_task),
+                hipMemcpyHostToDevice) != hipSuccess ||
+      hipMemset(h->ws + h->lay.off_ctr, 0, (size_t)h->lay.n_ctr * 4) != hipSuccess ||
+      hipDeviceSynchronize() != hipSuccess)
+    return MK_E_HIP;
+  h->plan = std::move(p);
+  h->have_plan = true;
+  h->batch = batch_size;
+  h->n_wg = nw;
+  h->opts = o;
+  return MK_OK;
+}
+
+int mk_decode_step(mk_handle* h, const int32_t* token_ids, const int32_t* positions,
+                   const int32_t* block_tables, const int32_t* seq_lens, float* logits, void* stream) {
+  if (!h) return MK_E_INVAL;
+  if (!h->have_plan) return MK_E_STATE;
+  if (!token_ids || !positions || !block_tables || !seq_lens || !logits) return MK_E_INVAL;
+  const mk_config& c = h->cfg;
+  const Layout& L = h->lay;
+  mk_kargs a;
+  std::memset(&a, 0, sizeof a);
+  char* ws = h->ws;
+  a.tasks = reinterpret_cast<const mk_task*>(ws + L.off_tasks);
+  a.n_tasks = (int32_t)h->plan.tasks.size();
+  a.n_wg = h->n_wg;
+  a.ctr = reinterpret_cast<int32_t*>(ws + L.off_ctr);
+  a.n_ctr = L.n_ctr;
+  a.err = reinterpret_cast<int32_t*>(ws + L.off_err);
+  a.layers = reinterpret_cast<const mk_layer_dev*>(ws + L.off_layers);
+  a.embed = h->embed;
+  a.lm_head = h->lm_head;
+  a.final_norm = h->final_norm;
+  a.inv_freq = reinterpret_cast<const double*>(ws + L.off_invf);
+  a.tokens = token_ids;
+  a.positions = positions;
+  a.block_tables = block_tables;
+  a.seq_lens = seq_lens;
+  a.logits = logits;
+  a.L = c.n_layers; a.d = c.d_model; a.Hq = c.n_q_heads; a.Hkv = c.n_kv_heads; a.hd = c.head_dim;
+  a.G = c.n_q_heads / c.n_kv_heads; a.E = c.n_experts; a.topk = c.top_k; a.I = c.expert_inter;
+  a.F = c.ffn_inter; a.V = c.vocab; a.parallel = c.parallel_block; a.page = c.page_size;
+  a.swa_window = c.swa_window; a.swa_period = c.swa_period;
+  a.B = h->batch; a.max_blocks = h->max_blocks; a.num_pages = h->num_pages;
+  a.eps = c.rms_eps;
+  a.attn_scale = (float)(1.0 / std::sqrt((double)c.head_dim));
+  a.attn_split = h->plan.attn_split;
+  a.max_splits = h->plan.max_splits;
+  a.ug_tiles = h->plan.ug_tiles; a.ug_pairs = h->plan.ug_pairs;
+  a.dn_tiles = h->plan.dn_tiles; a.dn_rows = h->plan.dn_rows;
+  a.n_qkv_tiles = h->plan.n_qkv;
+  a.bk = L.bk;
+  a.moe_stride = L.moe_stride;
+  a.cl = h->plan.cl;
+  const int tmo = h->opts.timeout_ms > 0 ? h->opts.timeout_ms : 2000;
+  a.timeout_ticks = (uint64_t)tmo * 100000ull;   // 100 MHz constant clock
+  a.x = reinterpret_cast<float*>(ws + L.off_x);
+  a.xn = reinterpret_cast<float*>(ws + L.off_xn);
+  a.xmid = reinterpret_cast<float*>(ws + L.off_xmid);
+  a.xn2 = reinterpret_cast<float*>(ws + L.off_xn2);
+  a.qkv = reinterpret_cast<float*>(ws + L.off_qkv);
+  a.attn = reinterpret_cast<float*>(ws + L.off_attn);
+  a.opart = reinterpret_cast<float*>(ws + L.off_opart);
+  a.rlog = reinterpret_cast<float*>(ws + L.off_rlog);
+  a.topi = reinterpret_cast<int32_t*>(ws + L.off_topi);
+  a.topw = reinterpret_cast<float*>(ws + L.off_topw);
+  a.moe = reinterpret_cast<int32_t*>(ws + L.off_moe);
+  a.H = reinterpret_cast<float*>(ws + L.off_H);
+  a.Y = reinterpret_cast<float*>(ws + L.off_Y);
+  a.fh = reinterpret_cast<float*>(ws + L.off_fh);
+  a.fo = reinterpret_cast<float*>(ws + L.off_fo);
+  a.oout = reinterpret_cast<float*>(ws + L.off_oout);
+  a.part_ml = reinterpret_cast<float*>(ws + L.off_pml);
+  a.part_o = reinterpret_cast<float*>(ws + L.off_po);
+  h->last_stream = reinterpret_cast<hipStream_t>(stream);
+  const std::vector<int32_t>& wb = h->plan.wave_bounds;
+  return mk_launch(&a, h->opts.launch_mode, wb.data(), (int)wb.size() - 1, stream);
+}
+
+int mk_get_status(mk_handle* h, mk_status* st) {
+  if (!h) return MK_E_INVAL;
+  if (hipStreamSynchronize(h->last_stream) != hipSuccess) return MK_E_HIP;
+  int32_t e[MK_ERR_WORDS];
+  if (hipMemcpy(e, h->ws + h->lay.off_err, sizeof e, hipMemcpyDeviceToHost) != hipSuccess) return MK_E_HIP;
+  if (e[0] != 0) {
+    if (hipMemset(h->ws + h->lay.off_err, 0, sizeof e) != hipSuccess) return MK_E_HIP;
+    // a timed-out step may leave counters behind; clear them for the next step
+    if (e[0] == MK_E_TIMEOUT && hipMemset(h->ws + h->lay.off_ctr, 0, (size_t)h->lay.n_ctr * 4) != hipSuccess)
+      return MK_E_HIP;
+    if (hipDeviceSynchronize() != hipSuccess) return MK_E_HIP;
+  }
+  if (st) {
+    st->code = e[0];
+    st->task = e[1];
+    st->counter = e[2];
+    st->value = e[3];
+    st->target = e[4];
+    st->workgroup = e[5];
+  }
+  return e[0];
+}
+
+int mk_tap_offset(const mk_handle* h, int32_t tap, size_t* offset, size_t* bytes) {
+  if (!h || !offset || !bytes) return MK_E_INVAL;
+  const Layout& L = h->lay;
+  const mk_config& c = h->cfg;
+  const size_t Lr = c.n_layers, B = c.max_batch, d = c.d_model;
+  switch (tap) {
+    case MK_TAP_X: *offset = L.off_x; *bytes = (Lr + 1) * B * d * 4; break;
+    case MK_TAP_XN: *offset = L.off_xn; *bytes = (Lr + 1) * B * d * 4; break;
+    case MK_TAP_QKV: *offset = L.off_qkv; *bytes = Lr * B * (c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim * 4; break;
+    case MK_TAP_ATTN: *offset = L.off_attn; *bytes = Lr * B * c.n_q_heads * c.head_dim * 4; break;
+    case MK_TAP_ROUTER_LOGITS: *offset = L.off_rlog; *bytes = c.n_experts > 0 ? Lr * B * c.n_experts * 4 : 0; break;
+    case MK_TAP_TOPK_IDS: *offset = L.off_topi; *bytes = c.n_experts > 0 ? Lr * B * c.top_k * 4 : 0; break;
+    case MK_TAP_TOPK_WEIGHTS: *offset = L.off_topw; *bytes = c.n_experts > 0 ? Lr * B * c.top_k * 4 : 0; break;
+    case MK_TAP_FFN_OUT: *offset = L.off_fo; *bytes = Lr * B * d * 4; break;
+    case MK_TAP_ATTN_OUT: *offset = L.off_oout; *bytes = Lr * B * d * 4; break;
+    default: return MK_E_INVAL;
+  }
+  return MK_OK;
+}
+
+int mk_plan_schedule(const mk_config* cfg, int32_t batch_size, int32_t max_blocks_per_seq,
+                     const mk_sched_opts* opt, int32_t n_workgroups, mk_task* out, int32_t cap,
+                     int32_t* n_tasks, int32_t* n_counters) {
+  int rc = validate_config(cfg);
+  if (rc != MK_OK) return rc;
+  Plan p;
+  rc = build_plan(cfg, batch_size, max_blocks_per_seq, opt, n_workgroups, &p);
+  if (rc != MK_OK) return rc;
+  if (n_tasks) *n_tasks = (int32_t)p.tasks.size();
+  if (n_counters) *n_counters = p.n_ctr;
+  if (out) {
+    if (cap < (int32_t)p.tasks.size()) return MK_E_NOMEM;
+    std::memcpy(out, p.tasks.data(), p.tasks.size() * sizeof(mk_task));
+  }
+  return MK_OK;
+}
+
+int mk_plan_simulate(const mk_config* cfg, int32_t batch_size, int32_t max_blocks_per_seq,
+                     const mk_sched_opts* opt, int32_t n_workgroups, const int32_t* seq_lens,
+                     const int32_t* n_active_experts, int32_t* stuck_task) {
+  int rc = validate_config(cfg);
+  if (rc != MK_OK) return rc;
+  if (!seq_lens || (cfg->n_experts > 0 && !n_active_experts)) return MK_E_INVAL;
+  Plan p;
+  rc = build_plan(cfg, batch_size, max_blocks_per_seq, opt, n_workgroups, &p);
+  if (rc != MK_OK) return rc;
+  return simulate(cfg, batch_size, p, n_workgroups, seq_lens, n_active_experts, stuck_task);
+}
+
+void mk_destroy(mk_handle* h) { delete h; }
+
+const char* mk_strerror(int code) {
+  switch (code) {
+    case MK_OK: return "ok";
+    case MK_E_INVAL: return "invalid argument";
+    case MK_E_UNSUPPORTED: return "unsupported shape";
+    case MK_E_NOMEM: return "workspace too small";
+    case MK_E_HIP: return "HIP runtime error";
+    case MK_E_TIMEOUT: return "device watchdog: counter wait timed out";
+    case MK_E_DEVICE: return "device-detected bad input";
+    case MK_E_STATE: return "bad call order or blocked schedule";
+    default: return "unknown error";
+  }
+}
+
+}  // extern "C"

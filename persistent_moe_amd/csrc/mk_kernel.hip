@@ -1,0 +1,1019 @@
+// mk_kernel.hip - the persistent decode megakernel for gfx950 (MI355X).
+//
+// One launch runs one decode step.  The grid holds one workgroup per CU
+// (512 threads = 8 wave64s, ~130 KB of LDS so no second workgroup fits);
+// workgroup w walks tasks w, w+N, w+2N, ... of the host-built list (task k on
+// workgroup k mod N).  A task waits on one counter in global memory, runs one
+// tile, and bumps one counter (persistent decode megakernel pages: page 1
+// "One kernel for the full decode step", "The calling convention that makes
+// it hand-writable", "Scheduling: mostly static, selectively dynamic"; page 2
+// "Overview"; page 3 on counters that tasks bump and spin on).
+//
+// Memory ordering across the 8 XCDs (each with its own L2): a producer's
+// waves each issue an agent-scope release fence (L2 write-back, wait for
+// their stores), meet at a workgroup barrier, then one lane bumps the counter
+// with an agent-scope atomic.  A consumer spins on agent-scope relaxed loads
+// of the counter with s_sleep between polls and, once the target is reached,
+// issues one agent-scope acquire fence (L1/L2 invalidate) before the
+// workgroup barrier that releases its other waves.
+//
+// Weights are immutable during a step, so every GEMV tile issues the loads of
+// its first row group into registers *before* it waits on its activation
+// dependency (page 1, third gain of the megakernel: weight prefetch across
+// task boundaries).  Attention splits and MoE expert tiles are pulled from
+// claim queues whose head is an atomic counter (page 1, "Scheduling").
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mk_internal.h"
+
+#define MK_THREADS 512
+#define MK_WAVES 8
+#define XS_FLOATS 16384   // staged activations, 64 KB
+#define YS_FLOATS 8192    // tile outputs / attention scores, 32 KB
+#define RED_FLOATS 8192   // attention cross-wave reduction, 32 KB
+#define NBMAX 8
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+struct __attribute__((aligned(16))) Smem {
+  float xs[XS_FLOATS];
+  float ys[YS_FLOATS];
+  float red[RED_FLOATS];
+  int misc[192];
+};
+
+// ------------------------------------------------------------------ helpers
+__device__ __forceinline__ float bf_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_to_f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+__device__ __forceinline__ uint16_t f_to_bf16(float f) {
+  uint32_t b = __float_as_uint(f);
+  return (uint16_t)((b + 0x7FFFu + ((b >> 16) & 1u)) >> 16);
+}
+__device__ __forceinline__ u32x4 ldg_nt(const uint16_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
+  return v;
+}
+__device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
+
+__device__ __forceinline__ int ld_agent(const int32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ void report(const mk_kargs& a, int code, int task, int ctr, int val, int target) {
+  if (atomicCAS(&a.err[0], 0, code) == 0) {
+    a.err[1] = task;
+    a.err[2] = ctr;
+    a.err[3] = val;
+    a.err[4] = target;
+    a.err[5] = (int)blockIdx.x;
+  }
+}
+
+// One lane spins until ctr[idx] >= target.  false if the watchdog fired or
+// another workgroup aborted the step.
+__device__ bool spin_until(const mk_kargs& a, int idx, int target, int task) {
+  const int32_t* p = a.ctr + idx;
+  if (ld_agent(p) < target) {
+    const uint64_t t0 = wall_clock64();
+    for (;;) {
+      __builtin_amdgcn_s_sleep(2);
+      if (ld_agent(p) >= target) break;
+      if (ld_agent(a.ctr + MK_CG_ABORT)) return false;
+      if (wall_clock64() - t0 > a.timeout_ticks) {
+        report(a, MK_E_TIMEOUT, task, idx, ld_agent(p), target);
+        __hip_atomic_store(a.ctr + MK_CG_ABORT, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return false;
+      }
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  return true;
+}
+
+// Workgroup-wide wait; every thread must call it.  Uses misc[0].
+__device__ bool wg_wait(const mk_kargs& a, Smem& sm, int idx, int target, int task) {
+  if (threadIdx.x == 0) sm.misc[0] = (idx < 0 || target <= 0) ? 1 : (int)spin_until(a, idx, target, task);
+  __syncthreads();
+  const bool ok = sm.misc[0] != 0;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  return ok;
+}
+
+// Workgroup-wide signal: every wave makes its stores visible at agent scope,
+// then one lane bumps the counter.
+__device__ void wg_signal(const mk_kargs& a, int idx, int inc) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  __syncthreads();
+  if (threadIdx.x == 0 && idx >= 0)
+    __hip_atomic_fetch_add(a.ctr + idx, inc, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Claim the next item of a queue; every thread must call it.  Uses misc[1].
+__device__ int wg_claim(const mk_kargs& a, Smem& sm, int qidx) {
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    sm.misc[1] = ld_agent(a.ctr + MK_CG_ABORT)
+                     ? 0x3FFFFFFF
+                     : __hip_atomic_fetch_add(a.ctr + qidx, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  return sm.misc[1];
+}
+
+// Claimer item order: claimer c of a wave owns item c of the queue; items
+// past the number of claimers are pulled one at a time from the atomic queue
+// head.  Returns -1 when the queue is exhausted.  Every thread must call it.
+__device__ int next_item(const mk_kargs& a, Smem& sm, const mk_task& t, int n_items, int qidx, bool& first) {
+  if (first) {
+    first = false;
+    if (t.n0 < n_items) return t.n0;
+  }
+  if (n_items <= t.n1) return -1;
+  const int it = t.n1 + wg_claim(a, sm, qidx);
+  return it < n_items ? it : -1;
+}
+
+__device__ __forceinline__ int layer_ctr(const mk_kargs& a, int layer, int off) {
+  return MK_CG_COUNT + layer * a.cl.stride + off;
+}
+
+__device__ __forceinline__ int visible_keys(const mk_kargs& a, int layer, int seq_len) {
+  if (a.swa_window > 0 && a.swa_period > 0 && (layer % a.swa_period) != a.swa_period - 1)
+    return seq_len < a.swa_window ? seq_len : a.swa_window;
+  return seq_len;
+}
+// Live length of slot b, clamped to what its block table can hold (a longer
+// length is reported by the layer-0 norm task).
+__device__ __forceinline__ int live_len(const mk_kargs& a, int b) {
+  const int sl = a.seq_lens[b];
+  const int cap = a.max_blocks * a.page;
+  return sl < cap ? sl : cap;
+}
+__device__ __forceinline__ int n_splits(const mk_kargs& a, int layer, int b) {
+  const int sl = live_len(a, b);
+  if (sl <= 0) return 0;
+  return (visible_keys(a, layer, sl) + a.attn_split - 1) / a.attn_split;
+}
+
+// --------------------------------------------------------- the GEMV pipeline
+// y[b][r] = sum_k W[row(r)][k] * x[b][k] for the rows of one tile.  Every
+// GEMV opcode runs through this one routine; they differ in the row mapping,
+// where x comes from, and the epilogue (page 1: all GEMM opcodes share one
+// pipeline).  Each wave owns RPW consecutive tile rows per row group; lane l
+// reads 16-byte segments l, l+64, ... of each row (KCH of them), so one wave
+// load moves 1 KB of contiguous weights.  The register tile of the next row
+// group is loaded while the current one is reduced (double buffering).
+enum { ROW_PLAIN = 0, ROW_ROPE_PAIRS = 1, ROW_GATE_UP = 2 };
+
+struct GemvArgs {
+  const uint16_t* base;
+  long ldw;        // elements between rows
+  int r0;          // first row (or pair) of the tile
+  int nrows;       // tile rows (2 per pair for the paired modes)
+  int K;           // reduction length (multiple of 8)
+  int mode;        // ROW_*
+  int half;        // ROW_ROPE_PAIRS: hd/2; ROW_GATE_UP: I (offset of the up rows)
+  int hd;
+  int xstride;     // floats between staged x rows in LDS
+  int nb;          // live batch rows
+  // output
+  float* out;      // mode 0: out[b*ob + r]; null: LDS ys[r*NBMAX + b]
+  long ob;
+};
+
+__device__ __forceinline__ const uint16_t* gemv_row(const GemvArgs& g, int r) {
+  if (g.mode == ROW_PLAIN) return g.base + (long)(g.r0 + r) * g.ldw;
+  const int p = g.r0 + (r >> 1), upper = r & 1;
+  if (g.mode == ROW_ROPE_PAIRS) {
+    const int head = p / g.half, i = p - head * g.half;
+    return g.base + (long)(head * g.hd + i + upper * g.half) * g.ldw;
+  }
+  return g.base + (long)(p + upper * g.half) * g.ldw;
+}
+
+template <int NB, int KCH, int RPW>
+struct GemvTile {
+  u32x4 w[RPW][KCH];
+
+  __device__ __forceinline__ void load(const GemvArgs& g, int grp) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+    for (int j = 0; j < RPW; ++j) {
+      const int r = (grp * MK_WAVES + wave) * RPW + j;
+      const bool rv = r < g.nrows;
+      const uint16_t* rp = rv ? gemv_row(g, r) : g.base;
+#pragma unroll
+      for (int c = 0; c < KCH; ++c) {
+        const int seg = lane + 64 * c;
+        if (rv && seg * 8 < g.K) w[j][c] = ldg_nt(rp + seg * 8);
+        else w[j][c] = (u32x4){0u, 0u, 0u, 0u};
+      }
+    }
+  }
+
+  __device__ __forceinline__ void compute(const GemvArgs& g, int grp, const float* xs, float* ys) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    float acc[RPW][NB];
+#pragma unroll
+    for (int j = 0; j < RPW; ++j)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) acc[j][b] = 0.f;
+#pragma unroll
+    for (int c = 0; c < KCH; ++c) {
+      const int seg = lane + 64 * c;
+      if (seg * 8 < g.K) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          const f32x4* xp = reinterpret_cast<const f32x4*>(xs + b * g.xstride + seg * 8);
+          const f32x4 x0 = xp[0], x1 = xp[1];
+#pragma unroll
+          for (int j = 0; j < RPW; ++j) {
+            const u32x4 v = w[j][c];
+            float s = acc[j][b];
+            s = fmaf(bf_lo(v.x), x0.x, s);
+            s = fmaf(bf_hi(v.x), x0.y, s);
+            s = fmaf(bf_lo(v.y), x0.z, s);
+            s = fmaf(bf_hi(v.y), x0.w, s);
+            s = fmaf(bf_lo(v.z), x1.x, s);
+            s = fmaf(bf_hi(v.z), x1.y, s);
+            s = fmaf(bf_lo(v.w), x1.z, s);
+            s = fmaf(bf_hi(v.w), x1.w, s);
+            acc[j][b] = s;
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < RPW; ++j) {
+      const int r = (grp * MK_WAVES + wave) * RPW + j;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const float s = wave_sum(acc[j][b]);
+        if (lane == 0 && r < g.nrows && b < g.nb) {
+          if (g.out) g.out[(long)b * g.ob + r] = s;
+          else ys[r * NBMAX + b] = s;
+        }
+      }
+    }
+  }
+};
+
+// Staging of the activation rows a tile multiplies: nb rows of K floats.
+struct StageArgs {
+  const float* base;
+  long ld;
+  const int32_t* map;   // row of x for batch row j: map[map0 + j], or j if null
+  int map0;
+  int nb;
+  int K;
+  int wait_idx;         // counter waited on before staging (-1: none)
+  int wait_target;
+  int task;
+};
+
+__device__ bool wait_and_stage(const mk_kargs& a, Smem& sm, const StageArgs& s) {
+  if (!wg_wait(a, sm, s.wait_idx, s.wait_target, s.task)) return false;
+  const int kv = s.K >> 2;
+  for (int i = threadIdx.x; i < s.nb * kv; i += MK_THREADS) {
+    const int j = i / kv, c = i - j * kv;
+    const int row = s.map ? s.map[s.map0 + j] : j;
+    const f32x4 v = *reinterpret_cast<const f32x4*>(s.base + (long)row * s.ld + c * 4);
+    *reinterpret_cast<f32x4*>(sm.xs + j * s.K + c * 4) = v;
+  }
+  __syncthreads();
+  return true;
+}
+
+template <int NB, int KCH, int RPW>
+__device__ bool gemv_run(const mk_kargs& a, Smem& sm, const GemvArgs& g, const StageArgs& s) {
+  GemvTile<NB, KCH, RPW> A, Bt;
+  const int per = MK_WAVES * RPW;
+  const int ng = (g.nrows + per - 1) / per;
+  A.load(g, 0);                       // weight prefetch before the dependency
+  if (!wait_and_stage(a, sm, s)) return false;
+  for (int grp = 0; grp < ng; grp += 2) {
+    if (grp + 1 < ng) Bt.load(g, grp + 1);
+    A.compute(g, grp, sm.xs, sm.ys);
+    if (grp + 1 < ng) {
+      if (grp + 2 < ng) A.load(g, grp + 2);
+      Bt.compute(g, grp + 1, sm.xs, sm.ys);
+    }
+  }
+  return true;
+}
+
+template <int NB, int KCH>
+__device__ bool gemv_rpw(const mk_kargs& a, Smem& sm, const GemvArgs& g, const StageArgs& s, int rpw) {
+  // register budget: 2 * RPW * KCH uint4 weights and RPW * NB accumulators
+  constexpr int WBUD = NB == 1 ? 16 : 8;
+  constexpr int RMAX_W = (WBUD / KCH) < 1 ? 1 : (WBUD / KCH);
+  constexpr int RMAX_A = 16 / NB < 1 ? 1 : 16 / NB;
+  constexpr int RMAX = RMAX_W < RMAX_A ? RMAX_W : RMAX_A;
+  if (rpw >= 8 && RMAX >= 8) return gemv_run<NB, KCH, (RMAX >= 8 ? 8 : 1)>(a, sm, g, s);
+  if (rpw >= 4 && RMAX >= 4) return gemv_run<NB, KCH, (RMAX >= 4 ? 4 : 1)>(a, sm, g, s);
+  if (rpw >= 2 && RMAX >= 2) return gemv_run<NB, KCH, (RMAX >= 2 ? 2 : 1)>(a, sm, g, s);
+  return gemv_run<NB, KCH, 1>(a, sm, g, s);
+}
+
+template <int NB>
+__device__ bool gemv_k(const mk_kargs& a, Smem& sm, const GemvArgs& g, const StageArgs& s, int rpw) {
+  const int kch = (g.K + 511) / 512;
+  if (kch <= 1) return gemv_rpw<NB, 1>(a, sm, g, s, rpw);
+  if (kch <= 2) return gemv_rpw<NB, 2>(a, sm, g, s, rpw);
+  if (kch <= 4) return gemv_rpw<NB, 4>(a, sm, g, s, rpw);
+  if (kch <= 8) return gemv_rpw<NB, 8>(a, sm, g, s, rpw);
+  return gemv_rpw<NB, 16>(a, sm, g, s, rpw);
+}
+
+// Runs one GEMV tile: prefetch, wait, stage x, multiply.  Returns false if
+// the step was aborted while waiting.
+__device__ bool gemv(const mk_kargs& a, Smem& sm, const GemvArgs& g, const StageArgs& s) {
+  const int rows_per_wave = (g.nrows + MK_WAVES - 1) / MK_WAVES;
+  const int rpw = rows_per_wave >= 8 ? 8 : rows_per_wave >= 4 ? 4 : rows_per_wave >= 2 ? 2 : 1;
+  if (g.nb <= 1) return gemv_k<1>(a, sm, g, s, rpw);
+  if (g.nb <= 2) return gemv_k<2>(a, sm, g, s, rpw);
+  if (g.nb <= 4) return gemv_k<4>(a, sm, g, s, rpw);
+  return gemv_k<8>(a, sm, g, s, rpw);
+}
+
+// ------------------------------------------------------------- ADD_RMSNORM
+// x_l = x_{l-1} + sum_g O-proj partial_g + sum_j w_j Y_j (parallel block), or
+// the embedding row at layer 0; xn_l = x_l / sqrt(mean(x_l^2) + eps) * gain.
+// One wave per batch row.  The MoE combine (gate-weighted sum of the routed
+// expert outputs, in top-k order) is folded into this task.
+__device__ __noinline__ void op_add_rmsnorm(const mk_kargs& a, Smem& sm, const mk_task& t, int ti) {
+  if (!wg_wait(a, sm, t.wait_ctr, t.wait_target, ti)) return;
+  const int l = t.layer, d = a.d, B = a.B;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const bool mid = t.flags & MK_F_MID;
+  const bool fin = t.flags & MK_F_FINAL;
+  for (int b = wave; b < B; b += MK_WAVES) {
+    float* xo = (mid ? a.xmid + ((long)l * B + b) * d : a.x + ((long)l * B + b) * d);
+    float* xno = (mid ? a.xn2 + ((long)l * B + b) * d : a.xn + ((long)l * B + b) * d);
+    const uint16_t* gain = fin ? a.final_norm : (mid ? a.layers[l].ffn_norm : a.layers[l].attn_norm);
+    if (a.seq_lens[b] <= 0) {
+      for (int i = lane; i < d; i += 64) { xo[i] = 0.f; xno[i] = 0.f; }
+      continue;
+    }
+    float ss = 0.f;
+    if (t.flags & MK_F_EMBED) {
+      if (lane == 0 && a.seq_lens[b] > a.max_blocks * a.page)
+        report(a, MK_E_DEVICE, ti, -5, a.seq_lens[b], a.max_blocks * a.page);
+      int tok = a.tokens[b];
+      if (tok < 0 || tok >= a.V) {
+        if (lane == 0) report(a, MK_E_DEVICE, ti, -1, tok, a.V);
+        tok = 0;
+      }
+      const uint16_t* e = a.embed + (long)tok * d;
+      for (int i = lane; i < d; i += 64) {
+        const float v = bf16_to_f(e[i]);
+        xo[i] = v;
+        ss += v * v;
+      }
+    } else if (mid) {
+      // sequential block: x_mid = x_l + attention output
+      const float* xp = a.x + ((long)l * B + b) * d;
+      float* oo = a.oout + ((long)l * B + b) * d;
+      for (int i = lane; i < d; i += 64) {
+        float o = 0.f;
+        for (int g = 0; g < a.Hkv; ++g) o += a.opart[(((long)l * a.Hkv + g) * B + b) * d + i];
+        oo[i] = o;
+        const float v = xp[i] + o;
+        xo[i] = v;
+        ss += v * v;
+      }
+    } else if (a.parallel) {
+      const int lp = l - 1;
+      const float* xp = a.x + ((long)lp * B + b) * d;
+      float* oo = a.oout + ((long)lp * B + b) * d;
+      float* fo = a.fo + ((long)lp * B + b) * d;
+      const int32_t* meta = a.moe + (long)lp * a.moe_stride;
+      const int32_t* slot = meta + 4 + a.bk + (a.bk + 1) + a.bk;
+      const float* w = a.topw + ((long)lp * B + b) * a.topk;
+      for (int i = lane; i < d; i += 64) {
+        float o = 0.f;
+        for (int g = 0; g < a.Hkv; ++g) o += a.opart[(((long)lp * a.Hkv + g) * B + b) * d + i];
+        float m = 0.f;
+        for (int j = 0; j < a.topk; ++j) {
+          const int row = slot[b * a.topk + j];
+          m += w[j] * a.Y[((long)lp * a.bk + row) * d + i];
+        }
+        oo[i] = o;
+        fo[i] = m;
+        const float v = xp[i] + o + m;
+        xo[i] = v;
+        ss += v * v;
+      }
+    } else {
+      // sequential block: x_l = x_mid + FFN output
+      const int lp = l - 1;
+      const float* xp = a.xmid + ((long)lp * B + b) * d;
+      const float* fo = a.fo + ((long)lp * B + b) * d;
+      for (int i = lane; i < d; i += 64) {
+        const float v = xp[i] + fo[i];
+        xo[i] = v;
+        ss += v * v;
+      }
+    }
+    ss = wave_sum(ss);
+    const float r = 1.0f / sqrtf(ss / (float)d + a.eps);
+    for (int i = lane; i < d; i += 64) xno[i] = xo[i] * r * bf16_to_f(gain[i]);
+  }
+  wg_signal(a, t.signal_ctr, 1);
+}
+
+// ---------------------------------------------------------------- QKV_PROJ
+// Tile = rotation pairs [n0, n1) over all heads (pair p of head h is rows
+// h*hd + p and h*hd + p + hd/2).  Epilogue: RoPE (rotate-half, angle
+// pos * theta^(-2i/hd) in double) on q and k; k and v rounded to bf16 and
+// written to the sequence's page at its position.
+__device__ __noinline__ void op_qkv(const mk_kargs& a, Smem& sm, const mk_task& t, int ti) {
+  const int l = t.layer, hd = a.hd, half = hd / 2, B = a.B;
+  const int np = t.n1 - t.n0;
+  const int rows = (a.Hq + 2 * a.Hkv) * hd;
+  GemvArgs g;
+  g.base = a.layers[l].w_qkv; g.ldw = a.d; g.r0 = t.n0; g.nrows = 2 * np; g.K = a.d;
+  g.mode = ROW_ROPE_PAIRS; g.half = half; g.hd = hd; g.xstride = a.d; g.nb = B;
+  g.out = nullptr; g.ob = 0;
+  StageArgs s;
+  s.base = a.xn + (long)l * B * a.d; s.ld = a.d; s.map = nullptr; s.map0 = 0; s.nb = B; s.K = a.d;
+  s.wait_idx = t.wait_ctr; s.wait_target = t.wait_target; s.task = ti;
+  if (!gemv(a, sm, g, s)) return;
+  __syncthreads();
+  uint16_t* kpool = a.layers[l].k;
+  uint16_t* vpool = a.layers[l].v;
+  for (int idx = threadIdx.x; idx < np * B; idx += MK_THREADS) {
+    const int p = idx / B, b = idx - p * B;
+    const int sl = a.seq_lens[b];
+    if (sl <= 0) continue;
+    const int gp = t.n0 + p, head = gp / half, i = gp - head * half;
+    float ya = sm.ys[(2 * p) * NBMAX + b], yb = sm.ys[(2 * p + 1) * NBMAX + b];
+    const int pos = a.positions[b];
+    if (head < a.Hq + a.Hkv) {
+      double sn, cs;
+      sincos((double)pos * a.inv_freq[i], &sn, &cs);
+      const float c = (float)cs, s_ = (float)sn;
+      const float ra = ya * c - yb * s_;
+      const float rb = yb * c + ya * s_;
+      ya = ra;
+      yb = rb;
+    }
+    float* qo = a.qkv + ((long)l * B + b) * rows;
+    qo[head * hd + i] = ya;
+    qo[head * hd + i + half] = yb;
+    if (head >= a.Hq) {
+      const bool isk = head < a.Hq + a.Hkv;
+      const int kvh = isk ? head - a.Hq : head - a.Hq - a.Hkv;
+      const int blk = pos / a.page;
+      int page = (blk >= 0 && blk < a.max_blocks) ? a.block_tables[b * a.max_blocks + blk] : -1;
+      if (page < 0 || page >= a.num_pages || pos < 0) {
+        report(a, MK_E_DEVICE, ti, -2, page, a.num_pages);
+        continue;
+      }
+      uint16_t* dst = (isk ? kpool : vpool) + (((long)page * a.Hkv + kvh) * a.page + (pos % a.page)) * hd;
+      dst[i] = f_to_bf16(ya);
+      dst[i + half] = f_to_bf16(yb);
+    }
+  }
+  wg_signal(a, t.signal_ctr, 1);
+}
+
+// ------------------------------------------------------ plain GEMV opcodes
+// ROUTER_GEMM, O_PROJ, FFN_DOWN and LM_HEAD: rows [n0, n1) of one matrix
+// times staged activation rows, results stored to global memory.
+__device__ __noinline__ void op_plain_gemv(const mk_kargs& a, Smem& sm, const mk_task& t, int ti) {
+  const int l = t.layer, B = a.B;
+  GemvArgs g;
+  StageArgs s;
+  g.r0 = t.n0; g.nrows = t.n1 - t.n0; g.mode = ROW_PLAIN; g.half = 0; g.hd = a.hd; g.nb = B;
+  s.map = nullptr; s.map0 = 0; s.nb = B; s.wait_idx = t.wait_ctr; s.wait_target = t.wait_target; s.task = ti;
+  switch (t.op) {
+    case MK_OP_ROUTER_GEMM:
+      g.base = a.layers[l].w_router; g.ldw = a.d; g.K = a.d;
+      g.out = a.rlog + (long)l * B * a.E + t.n0; g.ob = a.E;
+      s.base = a.xn + (long)l * B * a.d; s.ld = a.d; s.K = a.d;
+      break;
+    case MK_OP_O_PROJ: {
+      const int gd = a.G * a.hd, grp = t.group;
+      g.base = a.layers[l].w_o + (long)grp * gd; g.ldw = (long)a.Hq * a.hd; g.K = gd;
+      g.out = a.opart + (((long)l * a.Hkv + grp) * B) * a.d + t.n0; g.ob = a.d;
+      s.base = a.attn + (long)l * B * a.Hq * a.hd + (long)grp * gd; s.ld = (long)a.Hq * a.hd; s.K = gd;
+      break;
+    }
+    case MK_OP_FFN_DOWN:
+      g.base = a.layers[l].w_down; g.ldw = a.F; g.K = a.F;
+      g.out = a.fo + (long)l * B * a.d + t.n0; g.ob = a.d;
+      s.base = a.fh + (long)l * B * a.F; s.ld = a.F; s.K = a.F;
+      break;
+    default:  // MK_OP_LM_HEAD
+      g.base = a.lm_head; g.ldw = a.d; g.K = a.d;
+      g.out = a.logits + t.n0; g.ob = a.V;
+      s.base = a.xn + (long)a.L * B * a.d; s.ld = a.d; s.K = a.d;
+      break;
+  }
+  g.xstride = s.K;
+  if (!gemv(a, sm, g, s)) return;
+  wg_signal(a, t.signal_ctr, 1);
+}
+
+// ---------------------------------------------------------- FFN_UPGATE_ACT
+// Dense SwiGLU gate/up tile over pairs [n0, n1): h_i = silu(gate_i . x) * (up_i . x).
+__device__ __noinline__ void op_ffn_upgate(const mk_kargs& a, Smem& sm, const mk_task& t, int ti) {
+  const int l = t.layer, B = a.B, np = t.n1 - t.n0;
+  GemvArgs g;
+  g.base = a.layers[l].w_upgate; g.ldw = a.d; g.r0 = t.n0; g.nrows = 2 * np; g.K = a.d;
+  g.mode = ROW_GATE_UP; g.half = a.F; g.hd = a.hd; g.xstride = a.d; g.nb = B; g.out = nullptr; g.ob = 0;
+  StageArgs s;
+  s.base = (a.parallel ? a.xn : a.xn2) + (long)l * B * a.d; s.ld = a.d; s.map = nullptr; s.map0 = 0;
+  s.nb = B; s.K = a.d; s.wait_idx = t.wait_ctr; s.wait_target = t.wait_target; s.task = ti;
+  if (!gemv(a, sm, g, s)) return;
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < np * B; idx += MK_THREADS) {
+    const int p = idx / B, b = idx - p * B;
+    const float gv = sm.ys[(2 * p) * NBMAX + b], uv = sm.ys[(2 * p + 1) * NBMAX + b];
+    a.fh[((long)l * B + b) * a.F + t.n0 + p] = silu(gv) * uv;
+  }
+  wg_signal(a, t.signal_ctr, 1);
+}
+
+// ---------------------------------------------------------- ROUTER_TOPK
+// Per token: top-k router logits (ties to the lower expert id); gate weights
+// are the softmax probabilities of the selected experts renormalised to sum
+// to 1, i.e. exp(r_j - r_max) / sum over the selected.  With
+// MK_F_FUSE_FINALIZE it then runs ROUTE_FINALIZE.
+__device__ void route_finalize(const mk_kargs& a, Smem& sm, int l);
+
+__device__ __noinline__ void op_router_topk(const mk_kargs& a, Smem& sm, const mk_task& t, int ti) {
+  if (!wg_wait(a, sm, t.wait_ctr, t.wait_target, ti)) return;
+  const int l = t.layer, B = a.B, E = a.E, K = a.topk;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  for (int b = wave; b < B; b += MK_WAVES) {
+    float v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = lane + 64 * u;
+      v[u] = e < E ? a.rlog[((long)l * B + b) * E + e] : -INFINITY;
+    }
+    float top0 = 0.f, wsum = 0.f;
+    float myw = 0.f;
+    int myid = 0;
+    for (int j = 0; j < K; ++j) {
+      float bv = -INFINITY;
+      int be = 0x7FFFFFFF;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int e = lane + 64 * u;
+        if (e < E && (v[u] > bv || (v[u] == bv && e < be))) { bv = v[u]; be = e; }
+      }
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) {
+        const float ov = __shfl_xor(bv, m);
+        const int oe = __shfl_xor(be, m);
+        if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (lane + 64 * u == be) v[u] = -INFINITY;
+      if (j == 0) top0 = bv;
+      const float ew = expf(bv - top0);
+      wsum += ew;
+      if (lane == j) { myw = ew; myid = be; }
+    }
+    if (lane < K) {
+      a.topi[((long)l * B + b) * K + lane] = myid;
+      a.topw[((long)l * B + b) * K + lane] = myw / wsum;
+      sm.misc[64 + b * K + lane] = a.seq_lens[b] > 0 ? myid : -1;
+    }
+  }
+  __syncthreads();
+  if (t.flags & MK_F_FUSE_FINALIZE) route_finalize(a, sm, l);
+  wg_signal(a, t.signal_ctr, 1);
+}
+
+// ---------------------------------------------------------- ROUTE_FINALIZE
+// From the B*k routed (token, slot) pairs: sort by (expert, token slot) with a
+// bitonic network across one wave; row r of the sorted order is the r-th
+// routed row.  Writes the active expert list (ascending ids), each expert's
+// first row, the token of each row, the row of each (token, slot), and the
+// lengths of the up-gate and down claim queues.  Uses misc[64..] ids.
+__device__ void route_finalize(const mk_kargs& a, Smem& sm, int l) {
+  if ((threadIdx.x >> 6) != 0) return;
+  const int lane = threadIdx.x & 63, K = a.topk, BK = a.B * K;
+  int32_t* meta = a.moe + (long)l * a.moe_stride;
+  int32_t* act = meta + 4;
+  int32_t* row_off = act + a.bk;
+  int32_t* row_tok = row_off + a.bk + 1;
+  int32_t* slot = row_tok + a.bk;
+  uint32_t key = 0xFFFFFFFFu;
+  if (lane < BK) {
+    const int id = sm.misc[64 + lane];
+    if (id >= 0) key = ((uint32_t)id << 8) | (uint32_t)lane;
+  }
+  for (int k = 2; k <= 64; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      const uint32_t other = (uint32_t)__shfl_xor((int)key, j);
+      const bool up = (lane & k) == 0, lower = (lane & j) == 0;
+      key = (lower == up) ? (key < other ? key : other) : (key > other ? key : other);
+    }
+  }
+  const bool valid = key != 0xFFFFFFFFu;
+  const uint32_t prev = (uint32_t)__shfl((int)key, lane > 0 ? lane - 1 : 0);
+  const int e = (int)(key >> 8), src = (int)(key & 0xFF);
+  const bool start = valid && (lane == 0 || (prev >> 8) != (key >> 8));
+  const uint64_t vmask = __ballot(valid);
+  const uint64_t smask = __ballot(start);
+  const int nrows = __popcll(vmask), nact = __popcll(smask);
+  const uint64_t le = (lane == 63) ? ~0ull : ((2ull << lane) - 1ull);
+  const int aidx = __popcll(smask & le) - 1;
+  if (valid) {
+    slot[src] = lane;
+    row_tok[lane] = src / K;
+    if (start) { act[aidx] = e; row_off[aidx] = lane; }
+  }
+  if (lane == 0) {
+    row_off[nact] = nrows;
+    meta[0] = nact;
+    meta[1] = nact * a.ug_tiles;
+    meta[2] = nact * a.dn_tiles;
+    meta[3] = nrows;
+  }
+}
+
+// ---------------------------------------------------- MOE_UPGATE_ACT_DRAIN
+// Claimer: each item is (active expert, tile of ug_pairs gate/up pairs);
+// H[row][i] = silu(gate_i . xn[token(row)]) * (up_i . xn[token(row)]) for the
+// rows routed to that expert.  Bumps the expert's up-gate counter per item.
+__device__ __noinline__ void op_moe_upgate(const mk_kargs& a, Smem& sm, const mk_task& t, int ti) {
+  if (!wg_wait(a, sm, t.wait_ctr, t.wait_target, ti)) return;
+  const int l = t.layer;
+  const int32_t* meta = a.moe + (long)l * a.moe_stride;
+  const int32_t* act = meta + 4;
+  const int32_t* row_off = act + a.bk;
+  const int32_t* row_tok = row_off + a.bk + 1;
+  const int n_items = meta[1];
+  const int qidx = layer_ctr(a, l, MK_CTR_QUG);
+  bool first = true;
+  for (;;) {
+    const int item = next_item(a, sm, t, n_items, qidx, first);
+    if (item < 0) break;
+    const int ae = item / a.ug_tiles, tt = item - ae * a.ug_tiles;
+    const int e = act[ae], r0 = row_off[ae], nr = row_off[ae + 1] - r0;
+    const int p0 = tt * a.ug_pairs;
+    const int np = min(a.ug_pairs, a.I - p0);
+    GemvArgs g;
+    g.base = a.layers[l].w_upgate + (long)e * 2 * a.I * a.d; g.ldw = a.d; g.r0 = p0; g.nrows = 2 * np;
+    g.K = a.d; g.mode = ROW_GATE_UP; g.half = a.I; g.hd = a.hd; g.xstride = a.d; g.nb = nr;
+    g.out = nullptr; g.ob = 0;
+    StageArgs s;
+    s.base = a.xn + (long)l * a.B * a.d; s.ld = a.d; s.map = row_tok; s.map0 = r0; s.nb = nr; s.K = a.d;
+    s.wait_idx = -1; s.wait_target = 0; s.task = ti;
+    if (!gemv(a, sm, g, s)) return;
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < np * nr; idx += MK_THREADS) {
+      const int p = idx / nr, j = idx - p * nr;
+      const float gv = sm.ys[(2 * p) * NBMAX + j], uv = sm.ys[(2 * p + 1) * NBMAX + j];
+      a.H[((long)l * a.bk + r0 + j) * a.I + p0 + p] = silu(gv) * uv;
+    }
+    wg_signal(a, layer_ctr(a, l, a.cl.ug + ae), 1);
+  }
+  wg_signal(a, t.signal_ctr, 1);
+}
+
+// ------------------------------------------------------- MOE_DOWN_DRAIN
+// Claimer: each item is (active expert, tile of dn_rows output rows);
+// Y[row][r] = W_down[e][r] . H[row] for the expert's rows.  The weight tile
+// is loaded before the wait on the expert's up-gate counter.
+__device__ __noinline__ void op_moe_down(const mk_kargs& a, Smem& sm, const mk_task& t, int ti) {
+  if (!wg_wait(a, sm, t.wait_ctr, t.wait_target, ti)) return;
+  const int l = t.layer;
+  const int32_t* meta = a.moe + (long)l * a.moe_stride;
+  const int32_t* act = meta + 4;
+  const int32_t* row_off = act + a.bk;
+  const int n_items = meta[2];
+  const int qidx = layer_ctr(a, l, MK_CTR_QDN);
+  bool first = true;
+  for (;;) {
+    const int item = next_item(a, sm, t, n_items, qidx, first);
+    if (item < 0) break;
+    const int ae = item / a.dn_tiles, tt = item - ae * a.dn_tiles;
+    const int e = act[ae], r0 = row_off[ae], nr = row_off[ae + 1] - r0;
+    const int n0 = tt * a.dn_rows;
+    const int nrow = min(a.dn_rows, a.d - n0);
+    GemvArgs g;
+    g.base = a.layers[l].w_down + (long)e * a.d * a.I; g.ldw = a.I; g.r0 = n0; g.nrows = nrow; g.K = a.I;
+    g.mode = ROW_PLAIN; g.half = 0; g.hd = a.hd; g.xstride = a.I; g.nb = nr;
+    g.out = a.Y + ((long)l * a.bk + r0) * a.d + n0; g.ob = a.d;
+    StageArgs s;
+    s.base = a.H + ((long)l * a.bk + r0) * a.I; s.ld = a.I; s.map = nullptr; s.map0 = 0; s.nb = nr;
+    s.K = a.I; s.wait_idx = layer_ctr(a, l, a.cl.ug + ae); s.wait_target = a.ug_tiles; s.task = ti;
+    if (!gemv(a, sm, g, s)) return;
+  }
+  wg_signal(a, t.signal_ctr, 1);
+}
+
+// ---------------------------------------------------------- attention split
+// Keys [p0, p1) of sequence b, KV group g: scores s_j = q_h . K_j / sqrt(hd)
+// for the G query heads of the group, then m = max s, p = exp(s - m),
+// l = sum p, o = sum p V_j.  Lane layout: hd/8 lanes share one key row (8
+// dims each), so a wave load reads 64/(hd/8) keys; waves take keys in turn.
+template <int HD>
+__device__ void attn_split(const mk_kargs& a, Smem& sm, int l, int b, int g, int s, int p0, int p1,
+                           int ti) {
+  constexpr int LPR = HD / 8;
+  constexpr int PPW = 64 / LPR;
+  const int G = a.G, S = a.attn_split;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int sub = lane / LPR, c = lane - sub * LPR;
+  const int n = p1 - p0;
+  const int rows = (a.Hq + 2 * a.Hkv) * HD;
+  float q[NBMAX][8];
+  const float* qb = a.qkv + ((long)l * a.B + b) * rows + (long)(g * G) * HD + c * 8;
+#pragma unroll
+  for (int h = 0; h < NBMAX; ++h) {
+    if (h < G) {
+      const f32x4 q0 = *reinterpret_cast<const f32x4*>(qb + h * HD);
+      const f32x4 q1 = *reinterpret_cast<const f32x4*>(qb + h * HD + 4);
+      q[h][0] = q0.x * a.attn_scale; q[h][1] = q0.y * a.attn_scale;
+      q[h][2] = q0.z * a.attn_scale; q[h][3] = q0.w * a.attn_scale;
+      q[h][4] = q1.x * a.attn_scale; q[h][5] = q1.y * a.attn_scale;
+      q[h][6] = q1.z * a.attn_scale; q[h][7] = q1.w * a.attn_scale;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) q[h][e] = 0.f;
+    }
+  }
+  const uint16_t* Kp = a.layers[l].k;
+  const uint16_t* Vp = a.layers[l].v;
+  const int32_t* bt = a.block_tables + (long)b * a.max_blocks;
+  float* sc = sm.ys;  // [G][S]
+  // pass 1: scores
+  for (int base = wave * PPW; base < n; base += MK_WAVES * PPW) {
+    const int jj = base + sub;
+    float part[NBMAX];
+#pragma unroll
+    for (int h = 0; h < NBMAX; ++h) part[h] = 0.f;
+    if (jj < n) {
+      const int j = p0 + jj;
+      int pg = bt[j / a.page];
+      if (pg < 0 || pg >= a.num_pages) { report(a, MK_E_DEVICE, ti, -3, pg, a.num_pages); pg = 0; }
+      const u32x4 kv = ldg_nt(Kp + (((long)pg * a.Hkv + g) * a.page + (j % a.page)) * HD + c * 8);
+      const float k0 = bf_lo(kv.x), k1 = bf_hi(kv.x), k2 = bf_lo(kv.y), k3 = bf_hi(kv.y);
+      const float k4 = bf_lo(kv.z), k5 = bf_hi(kv.z), k6 = bf_lo(kv.w), k7 = bf_hi(kv.w);
+#pragma unroll
+      for (int h = 0; h < NBMAX; ++h)
+        part[h] = q[h][0] * k0 + q[h][1] * k1 + q[h][2] * k2 + q[h][3] * k3 + q[h][4] * k4 +
+                  q[h][5] * k5 + q[h][6] * k6 + q[h][7] * k7;
+    }
+#pragma unroll
+    for (int h = 0; h < NBMAX; ++h)
+#pragma unroll
+      for (int m = LPR / 2; m >= 1; m >>= 1) part[h] += __shfl_xor(part[h], m);
+    if (jj < n && c == 0) {
+#pragma unroll
+      for (int h = 0; h < NBMAX; ++h)
+        if (h < G) sc[h * S + jj] = part[h];
+    }
+  }
+  __syncthreads();
+  // pass 2: per-head max, exponentials and their sum
+  float* ml = a.part_ml + ((((long)(l & 1) * a.B + b) * a.Hq + g * G) * a.max_splits) * 2;
+  if (wave < G) {
+    float mx = -INFINITY;
+    for (int jj = lane; jj < n; jj += 64) mx = fmaxf(mx, sc[wave * S + jj]);
+    mx = wave_max(mx);
+    float sum = 0.f;
+    for (int jj = lane; jj < n; jj += 64) {
+      const float pj = expf(sc[wave * S + jj] - mx);
+      sc[wave * S + jj] = pj;
+      sum += pj;
+    }
+    sum = wave_sum(sum);
+    if (lane == 0) {
+      ml[((long)wave * a.max_splits + s) * 2 + 0] = mx;
+      ml[((long)wave * a.max_splits + s) * 2 + 1] = sum;
+    }
+  }
+  __syncthreads();
+  // pass 3: o = sum p V
+  float o[NBMAX][8];
+#pragma unroll
+  for (int h = 0; h < NBMAX; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[h][e] = 0.f;
+  for (int base = wave * PPW; base < n; base += MK_WAVES * PPW) {
+    const int jj = base + sub;
+    if (jj < n) {
+      const int j = p0 + jj;
+      int pg = bt[j / a.page];
+      if (pg < 0 || pg >= a.num_pages) pg = 0;
+      const u32x4 vv = ldg_nt(Vp + (((long)pg * a.Hkv + g) * a.page + (j % a.page)) * HD + c * 8);
+      float vf[8];
+      vf[0] = bf_lo(vv.x); vf[1] = bf_hi(vv.x); vf[2] = bf_lo(vv.y); vf[3] = bf_hi(vv.y);
+      vf[4] = bf_lo(vv.z); vf[5] = bf_hi(vv.z); vf[6] = bf_lo(vv.w); vf[7] = bf_hi(vv.w);
+#pragma unroll
+      for (int h = 0; h < NBMAX; ++h) {
+        if (h < G) {
+          const float pj = sc[h * S + jj];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) o[h][e] = fmaf(pj, vf[e], o[h][e]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < NBMAX; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+#pragma unroll
+      for (int m = LPR; m < 64; m <<= 1) o[h][e] += __shfl_xor(o[h][e], m);
+  if (sub == 0) {
+#pragma unroll
+    for (int h = 0; h < NBMAX; ++h)
+      if (h < G)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sm.red[(wave * NBMAX + h) * HD + c * 8 + e] = o[h][e];
+  }
+  __syncthreads();
+  float* po = a.part_o + ((((long)(l & 1) * a.B + b) * a.Hq + g * G) * a.max_splits) * HD;
+  for (int idx = tid; idx < G * HD; idx += MK_THREADS) {
+    const int h = idx / HD, dd = idx - h * HD;
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < MK_WAVES; ++w) v += sm.red[(w * NBMAX + h) * HD + dd];
+    po[((long)h * a.max_splits + s) * HD + dd] = v;
+  }
+}
+
+__device__ void attn_item(const mk_kargs& a, Smem& sm, int l, int b, int g, int s, int ti) {
+  const int sl = live_len(a, b);
+  const int kv = visible_keys(a, l, sl);
+  const int start = sl - kv;
+  const int p0 = start + s * a.attn_split;
+  const int p1 = min(p0 + a.attn_split, sl);
+  if (a.hd == 128) attn_split<128>(a, sm, l, b, g, s, p0, p1, ti);
+  else attn_split<64>(a, sm, l, b, g, s, p0, p1, ti);
+}
+
+// ATTN_DRAIN: drains the layer's (batch, group, split) items, batch-major.
+// The item count follows from seq_lens alone, so a claimer with nothing to
+// do returns without waiting for the QKV tiles.
+__device__ __noinline__ void op_attn_drain(const mk_kargs& a, Smem& sm, const mk_task& t, int ti) {
+  const int l = t.layer;
+  int n_items = 0;
+  for (int b = 0; b < a.B; ++b) n_items += n_splits(a, l, b) * a.Hkv;
+  if (t.n0 < n_items || n_items > t.n1) {
+    if (!wg_wait(a, sm, t.wait_ctr, t.wait_target, ti)) return;
+    const int qidx = layer_ctr(a, l, MK_CTR_QATTN);
+    bool first = true;
+    for (;;) {
+      int item = next_item(a, sm, t, n_items, qidx, first);
+      if (item < 0) break;
+      int b = 0, g = 0, s = -1;
+      for (; b < a.B; ++b) {
+        const int ns = n_splits(a, l, b);
+        const int cnt = ns * a.Hkv;
+        if (item < cnt) { g = item / ns; s = item - g * ns; break; }
+        item -= cnt;
+      }
+      if (s < 0) break;
+      attn_item(a, sm, l, b, g, s, ti);
+      wg_signal(a, layer_ctr(a, l, a.cl.attn + b * a.Hkv + g), 1);
+    }
+  }
+  wg_signal(a, t.signal_ctr, 1);
+}
+
+// ATTN_DECODE: one statically placed split.
+__device__ __noinline__ void op_attn_decode(const mk_kargs& a, Smem& sm, const mk_task& t, int ti) {
+  if (!wg_wait(a, sm, t.wait_ctr, t.wait_target, ti)) return;
+  const int l = t.layer;
+  if (t.split < n_splits(a, l, t.batch)) attn_item(a, sm, l, t.batch, t.group, t.split, ti);
+  wg_signal(a, layer_ctr(a, l, a.cl.attn + t.batch * a.Hkv + t.group), 1);
+  wg_signal(a, t.signal_ctr, 1);
+}
+
+// ATTN_COMBINE for (batch b, group g): M = max_s m_s;
+// o = sum_s e^(m_s - M) o_s / sum_s e^(m_s - M) l_s.  One wave per head.
+__device__ __noinline__ void op_attn_combine(const mk_kargs& a, Smem& sm, const mk_task& t, int ti) {
+  const int l = t.layer, b = t.batch, g = t.group, G = a.G, hd = a.hd;
+  const int ns = n_splits(a, l, b);
+  if (!wg_wait(a, sm, t.wait_ctr, ns, ti)) return;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  float* out = a.attn + ((long)l * a.B + b) * a.Hq * hd;
+  if (wave < G) {
+    const int h = g * G + wave;
+    const float* ml = a.part_ml + ((((long)(l & 1) * a.B + b) * a.Hq + h) * a.max_splits) * 2;
+    const float* po = a.part_o + ((((long)(l & 1) * a.B + b) * a.Hq + h) * a.max_splits) * hd;
+    float* wts = sm.ys + wave * 1024;
+    float mx = -INFINITY;
+    for (int s = lane; s < ns; s += 64) mx = fmaxf(mx, ml[s * 2]);
+    mx = wave_max(mx);
+    float den = 0.f;
+    for (int s = lane; s < ns; s += 64) {
+      const float w = expf(ml[s * 2] - mx);
+      wts[s] = w;
+      den += w * ml[s * 2 + 1];
+    }
+    den = wave_sum(den);
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    for (int dd = lane; dd < hd; dd += 64) {
+      float num = 0.f;
+      for (int s = 0; s < ns; ++s) num = fmaf(wts[s], po[(long)s * hd + dd], num);
+      out[h * hd + dd] = ns > 0 ? num / den : 0.f;
+    }
+  }
+  wg_signal(a, t.signal_ctr, 1);
+}
+
+// ------------------------------------------------------------------ kernel
+extern "C" __global__ void __launch_bounds__(MK_THREADS, 1) mk_persistent(mk_kargs a, int final_launch) {
+  __shared__ Smem sm;
+  for (int ti = a.task_begin + (int)blockIdx.x; ti < a.task_end; ti += (int)gridDim.x) {
+    const mk_task t = a.tasks[ti];
+    switch (t.op) {
+      case MK_OP_ADD_RMSNORM: op_add_rmsnorm(a, sm, t, ti); break;
+      case MK_OP_QKV_PROJ: op_qkv(a, sm, t, ti); break;
+      case MK_OP_ROUTER_GEMM:
+      case MK_OP_O_PROJ:
+      case MK_OP_FFN_DOWN:
+      case MK_OP_LM_HEAD: op_plain_gemv(a, sm, t, ti); break;
+      case MK_OP_FFN_UPGATE_ACT: op_ffn_upgate(a, sm, t, ti); break;
+      case MK_OP_ROUTER_TOPK: op_router_topk(a, sm, t, ti); break;
+      case MK_OP_ROUTE_FINALIZE:
+        if (wg_wait(a, sm, t.wait_ctr, t.wait_target, ti)) {
+          for (int i = threadIdx.x; i < a.B * a.topk; i += MK_THREADS) {
+            const int b = i / a.topk;
+            sm.misc[64 + i] = a.seq_lens[b] > 0 ? a.topi[((long)t.layer * a.B) * a.topk + i] : -1;
+          }
+          __syncthreads();
+          route_finalize(a, sm, t.layer);
+          wg_signal(a, t.signal_ctr, 1);
+        }
+        break;
+      case MK_OP_MOE_UPGATE_ACT_DRAIN: op_moe_upgate(a, sm, t, ti); break;
+      case MK_OP_MOE_DOWN_DRAIN: op_moe_down(a, sm, t, ti); break;
+      case MK_OP_ATTN_DRAIN: op_attn_drain(a, sm, t, ti); break;
+      case MK_OP_ATTN_DECODE: op_attn_decode(a, sm, t, ti); break;
+      case MK_OP_ATTN_COMBINE: op_attn_combine(a, sm, t, ti); break;
+      default:
+        if (threadIdx.x == 0) report(a, MK_E_INVAL, ti, -4, t.op, MK_NUM_OPCODES);
+        break;
+    }
+    __syncthreads();
+  }
+  // The last workgroup out clears the counters for the next launch.
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int old = __hip_atomic_fetch_add(a.ctr + MK_CG_DONE, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    sm.misc[2] = (old == (int)gridDim.x - 1);
+  }
+  __syncthreads();
+  if (sm.misc[2]) {
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    if (final_launch) {
+      for (int i = threadIdx.x; i < a.n_ctr; i += MK_THREADS) a.ctr[i] = 0;
+    } else if (threadIdx.x == 0) {
+      a.ctr[MK_CG_DONE] = 0;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ launch
+extern "C" int mk_launch(const mk_kargs* args, int launch_mode, const int32_t* wave_bounds, int n_waves,
+                         void* stream) {
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  mk_kargs a = *args;
+  const dim3 grid((unsigned)a.n_wg), block(MK_THREADS);
+  if (launch_mode == MK_LAUNCH_PERSISTENT) {
+    a.task_begin = 0;
+    a.task_end = a.n_tasks;
+    int fin = 1;
+    void* kp[] = {&a, &fin};
+    hipError_t e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(mk_persistent), grid, block, kp, 0, st);
+    return e == hipSuccess ? MK_OK : MK_E_HIP;
+  }
+  // ablation: one launch per task wave; the kernel boundary orders the waves
+  for (int w = 0; w < n_waves; ++w) {
+    a.task_begin = wave_bounds[w];
+    a.task_end = wave_bounds[w + 1];
+    int fin = (w == n_waves - 1) ? 1 : 0;
+    void* kp[] = {&a, &fin};
+    hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(mk_persistent), grid, block, kp, 0, st);
+    if (e != hipSuccess) return MK_E_HIP;
+  }
+  return MK_OK;
+}

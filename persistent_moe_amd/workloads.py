@@ -379,6 +379,43 @@ def fill_normal_(out: torch.Tensor, key: int, mean: float, std: float,
     return out
 
 
+def fill_normal_keyed_(out: torch.Tensor, keys: List[int], mean: float, std: float,
+                       group_elems: int = 1 << 25, backend: str = "auto") -> torch.Tensor:
+    """Fill out[i] (contiguous, bf16) with elements [0, numel/len(keys)) of
+    stream keys[i], for each leading index i.  On a GPU several streams are
+    drawn in one vectorised pass; the bits equal those of ``fill_normal_``."""
+    n_keys = out.shape[0]
+    assert n_keys == len(keys)
+    per = out[0].numel()
+    assert per < (1 << 32)
+    if out.device.type == "cpu" and backend != "torch":
+        for i, k in enumerate(keys):
+            fill_normal_(out[i], k, mean, std)
+        return out
+    ops = _TorchOps(out.device)
+    flat = out.view(n_keys, per)
+    # element i of stream k: h_j = fmix32(i ^ fmix32(0 ^ k_j)), as in _words with hi = 0
+    m1 = [fmix32_int(fmix32_int(k ^ 0x68E31DA4)) for k in keys]
+    m2 = [fmix32_int(fmix32_int(k ^ 0xB5297A4D)) for k in keys]
+    per_chunk = max(1, min(per, group_elems))
+    kpg = max(1, group_elems // per) if per <= group_elems else 1
+    for k0 in range(0, n_keys, kpg):
+        k1 = min(n_keys, k0 + kpg)
+        for s in range(0, per, per_chunk):
+            c = min(per_chunk, per - s)
+            idx = torch.arange(s, s + c, dtype=torch.int64, device=out.device)
+            idx = idx.unsqueeze(0).expand(k1 - k0, c)
+            a1 = torch.tensor(m1[k0:k1], dtype=torch.int64, device=out.device).unsqueeze(1)
+            a2 = torch.tensor(m2[k0:k1], dtype=torch.int64, device=out.device).unsqueeze(1)
+            h1 = _fmix32(idx ^ a1, ops)
+            h2 = _fmix32(idx ^ a2, ops)
+            z = ops.sqrt(_neg2_ln_u(h1, ops)) * _cos_2pi_u(h2, ops)
+            codes = _bf16_bits(z * std + mean, ops)
+            codes = torch.where(codes >= 32768, codes - 65536, codes)
+            flat[k0:k1, s:s + c] = codes.to(torch.int16).view(torch.bfloat16)
+    return out
+
+
 def _cpu_threads() -> int:
     try:
         return max(1, len(os.sched_getaffinity(0)))

@@ -1,0 +1,174 @@
+"""Host-side checks of libmk.so that need no GPU: the exported symbols, the
+argument validation, and the host-built schedule (its structure and a
+discrete-event proof that it cannot deadlock)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from persistent_moe_amd import mk
+from persistent_moe_amd import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(mk.lib_path()):
+        pytest.fail("libmk.so is not built (run python -m persistent_moe_amd.build)")
+    return mk.load()
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "mk.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|void|const char\*)\s+(mk_\w+)\s*\(", src, re.M)))
+
+
+def test_header_declares_the_binding_exports():
+    assert header_functions() == sorted(mk.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", mk.lib_path()], capture_output=True, text=True).stdout
+    syms = set(l.split()[-1] for l in out.splitlines() if l.strip())
+    for f in header_functions():
+        assert f in syms, f
+        assert hasattr(lib, f)
+
+
+def test_strerror_names_every_code(lib):
+    for code in range(0, -8, -1):
+        assert mk.strerror(code) != "unknown error"
+
+
+def test_task_descriptor_is_32_int32():
+    assert ctypes.sizeof(mk.mk_task) == 128
+    assert len(mk.OPCODES) == 16
+
+
+def _cfg(model, B=1):
+    return mk.make_config(model, B)
+
+
+def test_workspace_size_validation(lib):
+    assert mk.mk_workspace_size(_cfg(W.TINY_MOE), 8) > 0
+    bad = _cfg(W.TINY_MOE)
+    bad.head_dim = 96
+    assert mk.mk_workspace_size(bad, 8) == 0
+    bad = _cfg(W.TINY_MOE)
+    bad.n_kv_heads = 3
+    assert mk.mk_workspace_size(bad, 8) == 0
+    assert mk.mk_workspace_size(_cfg(W.TINY_MOE), 0) == 0
+
+
+def test_init_rejects_null_and_small_workspace(lib):
+    cfg = _cfg(W.TINY_MOE)
+    h = ctypes.c_void_p()
+    w = mk.mk_weights()
+    kv = mk.mk_kv_pool()
+    rc = lib.mk_init(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(kv), None, 0, 8, ctypes.byref(h))
+    assert rc == mk.MK_E_INVAL
+    rc = lib.mk_init(ctypes.byref(cfg), None, None, None, 0, 8, ctypes.byref(h))
+    assert rc == mk.MK_E_INVAL
+    # fake (never dereferenced) pointers: the size check comes before any device call
+    L = cfg.n_layers
+    arr = (mk.mk_layer_weights * L)()
+    for l in range(L):
+        for f in ("attn_norm", "w_qkv", "w_o", "w_router", "w_upgate", "w_down"):
+            setattr(arr[l], f, 4096)
+    w = mk.mk_weights(embed=4096, lm_head=4096, final_norm=4096, layers=arr)
+    ptrs = (ctypes.c_void_p * L)(*([4096] * L))
+    kv = mk.mk_kv_pool(k=ptrs, v=ptrs, num_pages=4)
+    rc = lib.mk_init(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(kv), ctypes.c_void_p(4096), 16, 8,
+                     ctypes.byref(h))
+    assert rc == mk.MK_E_NOMEM
+
+
+def test_null_handle_calls_fail_cleanly(lib):
+    assert lib.mk_build_schedule(None, 1, None) == mk.MK_E_INVAL
+    assert lib.mk_decode_step(None, None, None, None, None, None, None) == mk.MK_E_INVAL
+    assert lib.mk_get_status(None, None) == mk.MK_E_INVAL
+    lib.mk_destroy(None)
+
+
+def test_unsupported_shapes(lib):
+    c = _cfg(W.DENSE_1B)
+    c.max_batch = 4            # 4 x 8192 staged floats exceed the LDS staging area
+    assert mk.mk_workspace_size(c, 8) == 0
+    c = _cfg(W.TINY_MOE)
+    c.max_batch = 9
+    assert mk.mk_workspace_size(c, 8) == 0
+
+
+def _plan(model, B, max_blocks, nw=256, order="tuned", split=0):
+    return mk.mk_plan_schedule(_cfg(model, B), B, max_blocks, mk.make_opts(order, attn_split=split), nw)
+
+
+@pytest.mark.parametrize("model,B,mb", [(W.TINY_MOE, 1, 5), (W.MOE_30B, 1, 529), (W.MOE_30B, 8, 1041),
+                                        (W.DENSE_1B, 1, 264), (W.MOE_30B_SWA, 1, 16388)])
+def test_plan_structure(lib, model, B, mb):
+    tasks, nctr = _plan(model, B, mb)
+    ops = [t.op for t in tasks]
+    assert all(0 <= o < 16 for o in ops)
+    L = model.n_layers
+    norms = [t for t in tasks if t.op == 0]
+    assert len(norms) == L + 1 + (0 if model.parallel_block else L)
+    assert sum(1 for t in tasks if t.op == mk.OPCODES.index("LM_HEAD")) > 0
+    lm = [t for t in tasks if t.op == mk.OPCODES.index("LM_HEAD")]
+    assert lm[0].n0 == 0 and lm[-1].n1 == model.vocab
+    assert all(a.n1 == b.n0 for a, b in zip(lm, lm[1:]))
+    # every counter referenced lies inside the counter array
+    for t in tasks:
+        for c in (t.wait_ctr, t.signal_ctr, t.queue):
+            assert -1 <= c < nctr
+    # QKV tiles cover every rotation pair exactly once
+    q = [t for t in tasks if t.op == 1 and t.layer == 0]
+    pairs = (model.n_q_heads + 2 * model.n_kv_heads) * model.head_dim // 2
+    assert q[0].n0 == 0 and q[-1].n1 == pairs and all(a.n1 == b.n0 for a, b in zip(q, q[1:]))
+
+
+def test_static_tiles_dealt_round_robin(lib):
+    # task k runs on workgroup k mod N: with 256 workgroups the 256 QKV tiles
+    # of a layer of the 30B model land on 256 different workgroups
+    tasks, _ = _plan(W.MOE_30B, 1, 529)
+    idx = [i for i, t in enumerate(tasks) if t.op == 1 and t.layer == 3]
+    assert len(idx) == 256
+    assert len({i % 256 for i in idx}) == 256
+
+
+def test_signal_counts_match_wait_targets(lib):
+    # a static wait target must equal the number of tasks that signal it
+    for model, B, mb in [(W.MOE_30B, 1, 529), (W.DENSE_1B, 1, 264), (W.TINY_MOE, 2, 6)]:
+        tasks, _ = _plan(model, B, mb)
+        sig = {}
+        for t in tasks:
+            if t.signal_ctr >= 0:
+                sig[t.signal_ctr] = sig.get(t.signal_ctr, 0) + 1
+        for t in tasks:
+            if t.wait_ctr >= 0 and t.wait_target > 0 and t.op not in (8, 13, 14):
+                assert sig.get(t.wait_ctr, 0) == t.wait_target, (mk.OPCODES[t.op], t.layer)
+
+
+@pytest.mark.parametrize("order", ["tuned", "interleaved", "attention_first"])
+@pytest.mark.parametrize("case", [
+    ("tiny", W.TINY_MOE, 1, 5, [65], [2, 2]),
+    ("moe30b", W.MOE_30B, 1, 529, [8193], [8] * 48),
+    ("moe30b-bs8", W.MOE_30B, 8, 1041, [512, 16384, 700, 3000, 9000, 1200, 15000, 2048], [52] * 48),
+    ("moe30b-bs8-empty-slots", W.MOE_30B, 8, 1041, [0, 16384, 0, 3000, 0, 0, 0, 17], [16] * 48),
+    ("dense", W.DENSE_1B, 1, 264, [4097], []),
+])
+def test_schedule_is_deadlock_free(lib, order, case):
+    name, model, B, mb, sl, na = case
+    for nw in (256, 64, 7):
+        rc, stuck = mk.mk_plan_simulate(_cfg(model, B), B, mb, mk.make_opts(order), nw, sl, na)
+        assert rc == mk.MK_OK, (name, nw, stuck)
+
+
+def test_simulator_detects_a_blocked_schedule(lib):
+    opts = mk.make_opts(flags=mk.MK_SCHED_UNREACHABLE_WAIT)
+    rc, stuck = mk.mk_plan_simulate(_cfg(W.TINY_MOE, 1), 1, 5, opts, 4, [65], [2, 2])
+    assert rc == mk.MK_E_STATE and stuck == 0
+    rc = mk.mk_plan_simulate(_cfg(W.TINY_MOE, 1), 2, 5, mk.make_opts(), 4, [65, 65], [2, 2])[0]
+    assert rc == mk.MK_E_INVAL   # batch above the configured maximum

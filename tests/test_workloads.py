@@ -86,3 +86,12 @@ def test_start_tokens_in_vocab_and_seeded():
     a = [W.start_token(0, i, 1024) for i in range(50)]
     assert a == [W.start_token(0, i, 1024) for i in range(50)]
     assert all(0 <= t < 1024 for t in a) and len(set(a)) > 30
+
+
+def test_keyed_vectorised_generator_matches_per_stream():
+    keys = [W.tensor_key(2, "w_down", 5, e) for e in range(5)]
+    ref = torch.stack([W.gen_tensor(2, "w_down", (40, 24), layer=5, expert=e) for e in range(5)])
+    for ge in (1 << 25, 500, 2000):
+        out = torch.empty(5, 40, 24, dtype=torch.bfloat16)
+        W.fill_normal_keyed_(out, keys, 0.0, 0.02, group_elems=ge, backend="torch")
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
