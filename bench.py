@@ -1,0 +1,247 @@
+"""Decode throughput of the persistent decode megakernel on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload moe30b]
+
+Times K greedy decode steps (after W untimed ones) of the 30B / 3.3B-active
+parallel-block MoE at batch 1 with an 8K-token pre-filled paged KV cache,
+random-init bf16 weights from the seeded generator.  Each step is one
+mk_decode_step launch (the whole decode step in one persistent kernel) plus
+the caller's greedy argmax and position update, all on one stream with no
+host synchronisation inside the timed region.  Prints one JSON line.
+
+Reported next to the throughput:
+* roofline: speed-of-light bytes of every step (active weights read once, KV
+  of every visible key), over the kernel's own average duration measured with
+  events on its stream, against the 8 TB/s HBM peak;
+* cpu_baseline: the CPU oracle timed on a bounded sample of the same step.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+from dataclasses import replace
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode tok/s at bs1 and bs8; % of HBM speed-of-light, 30B/3.3B-active MoE"
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=64)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--workload", default="moe30b")
+    ap.add_argument("--order", default="tuned")
+    ap.add_argument("--launch", default="persistent")
+    ap.add_argument("--attn-split", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--verbose", action="store_true")
+    ap.add_argument("--trace", default="", help="after timing, trace one step and write a summary here")
+    return ap.parse_args()
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(wl, sample_layers: int = 4, lm_frac: int = 16, min_seconds: float = 10.0):
+    """Time the CPU oracle on a bounded sample of one decode step.
+
+    The sample is the first ``sample_layers`` layers of the same seeded model
+    plus 1/``lm_frac`` of its LM-head rows; a layerless run of the same
+    sample isolates the LM-head time.  Weight and cache generation happen
+    before the timed runs.  Scaled to a full step:
+    t = (t_sample - t_head) / sample_layers * n_layers + t_head * lm_frac.
+    """
+    from oracle import decode as O
+    from persistent_moe_amd import workloads as W
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        threads = 1
+    cfg = wl.model
+    V = cfg.vocab // lm_frac
+    swl = wl.with_(model=replace(cfg, n_layers=sample_layers, vocab=V))
+    hwl = wl.with_(model=replace(cfg, n_layers=0, vocab=V))
+    plan = W.plan_batch(swl, 1)
+    seqs0 = [plan.slots[b][0][1] for b in range(wl.batch)]
+
+    def run(w, Wt, keep):
+        seqs = [O.new_sequence(s.seq_id, s.ctx) for s in seqs0]
+        for s, k in zip(seqs, keep):
+            s.prefill_cache = k
+        t0 = time.perf_counter()
+        O.decode_step(w, Wt, seqs, [s.token for s in seqs0])
+        return time.perf_counter() - t0, [s.prefill_cache for s in seqs]
+
+    Ws = O.Weights(swl, cache_limit=64 << 30)
+    Wh = O.Weights(hwl, cache_limit=64 << 30)
+    for w in (Ws, Wh):     # draw the LM-head sample rows once, outside the timing
+        w.lm_head_rows = (lambda f: (lambda r0, r1, _c={}: _c.setdefault((r0, r1), f(r0, r1))))(w.lm_head_rows)
+    _, keep = run(swl, Ws, [{}] * wl.batch)          # warm: generate weights and cache
+    run(hwl, Wh, keep)
+    reps, ts, th = 0, [], []
+    t_begin = time.perf_counter()
+    while True:
+        a, _ = run(swl, Ws, keep)
+        b, _ = run(hwl, Wh, keep)
+        ts.append(a)
+        th.append(b)
+        reps += 1
+        if time.perf_counter() - t_begin >= min_seconds or reps >= 50:
+            break
+    t_s, t_h = float(np.median(ts)), float(np.median(th))
+    t_layer = max(t_s - t_h, 0.0) / sample_layers
+    t_step = t_layer * cfg.n_layers + t_h * lm_frac
+    return {
+        "value": wl.batch / t_step,
+        "unit": "tok/s",
+        "cores": threads,
+        "kind": "oracle",
+        "ms_per_step": t_step * 1e3,
+        "sample": (f"{sample_layers} of {cfg.n_layers} layers and 1/{lm_frac} of the LM-head rows of "
+                   f"step 0 (fp64 numpy, weights drawn before timing), median of {reps} runs, "
+                   f"scaled to a full step"),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(the decode step runs in one persistent kernel on one device).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from persistent_moe_amd import mk, sol
+    from persistent_moe_amd import workloads as W
+    from persistent_moe_amd.runner import DecodeEngine
+
+    wl = W.WORKLOADS[args.workload]
+    cfg = wl.model
+    B = wl.batch
+    total_steps = args.warmup + args.steps
+    log(f"workload {wl.name}: building inputs for {total_steps} steps")
+    t0 = time.time()
+    opts = mk.make_opts(args.order, args.launch, attn_split=args.attn_split)
+    eng = DecodeEngine(wl, steps=total_steps + 1, opts=opts, verbose=args.verbose)
+    log(f"inputs ready in {time.time() - t0:.1f}s ({eng.weight_bytes() / 1e9:.1f} GB weights)")
+    if wl.swap_every:
+        log("note: slot swaps are not applied inside the timed loop")
+    stream = torch.cuda.current_stream()
+    tok, pos, sl = eng.step_inputs()
+    ids_tap = eng.tap("topk_ids") if cfg.is_moe else None
+    L, K = cfg.n_layers, max(cfg.top_k, 1)
+    # distinct experts per layer: top_k at batch 1; logged per step otherwise
+    route_log = (torch.zeros((total_steps, L * B * K), dtype=torch.int32, device="cuda")
+                 if cfg.is_moe and B > 1 else None)
+    pos0 = pos.cpu().numpy().copy()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(total_steps)]
+
+    def one(i):
+        ev[i][0].record(stream)
+        mk.mk_decode_step(eng.h, tok.data_ptr(), pos.data_ptr(), eng.block_tables.data_ptr(), sl.data_ptr(),
+                          eng.logits.data_ptr(), stream.cuda_stream)
+        ev[i][1].record(stream)
+        if route_log is not None:
+            route_log[i].copy_(ids_tap[:L * B * K])
+        torch.argmax(eng.logits, dim=-1, out=argmax_buf)
+        tok.copy_(argmax_buf)
+        pos.add_(1)
+        sl.add_(1)
+
+    argmax_buf = torch.zeros(B, dtype=torch.int64, device="cuda")
+    for i in range(args.warmup):
+        one(i)
+    torch.cuda.synchronize()
+    st = eng.status()
+    if st.code != 0:
+        raise SystemExit(f"device error during warmup: {mk.strerror(st.code)} task {st.task}")
+    t_start = time.perf_counter()
+    for i in range(args.warmup, total_steps):
+        one(i)
+    torch.cuda.synchronize()
+    t_total = time.perf_counter() - t_start
+    st = eng.status()
+    if st.code != 0:
+        raise SystemExit(f"device error: {mk.strerror(st.code)} task {st.task} counter {st.counter}")
+    kern_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(args.warmup, total_steps)]
+    # exact algorithmic bytes of every timed step
+    step_bytes = []
+    rl = route_log.cpu().numpy() if route_log is not None else None
+    for i in range(args.warmup, total_steps):
+        p = (pos0 + i).tolist()
+        if rl is not None:
+            ids = rl[i].reshape(L, B, K)
+            distinct = [len(np.unique(ids[l])) for l in range(L)]
+        else:
+            distinct = [K if cfg.is_moe else 0] * L
+        step_bytes.append(sol.step_bytes(cfg, p, distinct))
+    mean_bytes = float(np.mean(step_bytes))
+    mean_kern_s = float(np.mean(kern_ms)) / 1e3
+    achieved = mean_bytes / mean_kern_s / 1e9
+    ms_per_step = t_total / args.steps * 1e3
+    value = B * args.steps / t_total
+    sol_tok_s = float(np.mean([sol.sol_tok_s(b, B) for b in step_bytes]))
+    log(f"{value:.1f} tok/s, {ms_per_step:.3f} ms/step; kernel {mean_kern_s * 1e3:.3f} ms "
+        f"(min {min(kern_ms):.3f}); {achieved:.0f} GB/s = {achieved / HBM_PEAK_GBS:.1%} of HBM SoL")
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded random-init weights and pre-filled KV)",
+        "config": {"workload": wl.name, "batch": B, "context": W.context_length(wl, 0),
+                   "layers": cfg.n_layers, "experts": cfg.n_experts, "top_k": cfg.top_k,
+                   "order": args.order, "launch": args.launch,
+                   "attn_split": args.attn_split or "auto"},
+        "sol_fraction": round(value / sol_tok_s, 4),
+        "sol_tok_s": round(sol_tok_s, 1),
+        "kernel_ms": round(mean_kern_s * 1e3, 4),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_step": int(mean_bytes), "kernel": "mk_persistent"},
+    }
+    if args.trace:
+        from persistent_moe_amd import trace as T
+        topt = mk.make_opts(args.order, args.launch, attn_split=args.attn_split, flags=mk.MK_SCHED_TRACE)
+        eng.opts = topt
+        mk.mk_build_schedule(eng.h, B, topt)
+        one(total_steps - 1)
+        torch.cuda.synchronize()
+        tr = T.load(eng)
+        summ = T.summarize(tr)
+        with open(args.trace, "w") as fh:
+            json.dump(summ, fh, indent=1)
+        T.chrome_trace(tr, os.path.splitext(args.trace)[0] + ".chrome.json")
+        log(f"trace: step {summ['step_us']:.1f} us; " +
+            ", ".join(f"{k} busy {v['busy_us']:.0f} wait {v['wait_us']:.0f}" for k, v in summ["per_op"].items()))
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        try:
+            out["cpu_baseline"] = cpu_baseline(wl)
+        except Exception as e:  # the GPU figure stands on its own
+            out["cpu_baseline"] = {"error": repr(e)}
+    print(json.dumps(out), flush=True)
+    eng.close()
+
+
+if __name__ == "__main__":
+    main()

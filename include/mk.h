@@ -178,6 +178,9 @@ typedef struct mk_sched_opts {
  * the device watchdog fires (MK_E_TIMEOUT after timeout_ms) and every
  * workgroup leaves the step through its normal exit.                      */
 #define MK_SCHED_UNREACHABLE_WAIT 1
+/* Record, per task, the 100 MHz device clock at task start, when its wait
+ * was satisfied and at its end, into the MK_TAP_TRACE region.             */
+#define MK_SCHED_TRACE 2
 
 #define MK_MIN_SPLIT 64
 
@@ -244,7 +247,8 @@ enum mk_tap {
   MK_TAP_TOPK_WEIGHTS = 6,  /* [L][B][k] f32                                         */
   MK_TAP_FFN_OUT = 7,       /* [L][B][d] f32 MoE (or dense FFN) output               */
   MK_TAP_ATTN_OUT = 8,      /* [L][B][d] f32 output projection (sum over groups)     */
-  MK_NUM_TAPS = 9
+  MK_TAP_TRACE = 9,         /* [n_tasks][4] u64: start, ready, end, workgroup (MK_SCHED_TRACE) */
+  MK_NUM_TAPS = 10
 };
 int mk_tap_offset(const mk_handle* h, int32_t tap, size_t* offset, size_t* bytes);
 

@@ -31,7 +31,7 @@ constexpr int kXsFloats = 16384;   // LDS capacity for staged activations
 struct Layout {
   size_t off_tasks, off_ctr, off_err, off_layers, off_invf;
   size_t off_x, off_xn, off_xmid, off_xn2, off_qkv, off_attn, off_opart, off_rlog, off_topi, off_topw;
-  size_t off_moe, off_H, off_Y, off_fh, off_fo, off_oout, off_pml, off_po;
+  size_t off_moe, off_H, off_Y, off_fh, off_fo, off_oout, off_pml, off_po, off_trace;
   size_t total;
   int32_t max_tasks, n_ctr, max_splits, bk, moe_stride;
   mk_ctr_layout cl;
@@ -62,6 +62,8 @@ int validate_config(const mk_config* c) {
     if ((size_t)c->max_batch * c->ffn_inter > (size_t)kXsFloats) return MK_E_UNSUPPORTED;
   }
   if ((size_t)c->max_batch * c->d_model > (size_t)kXsFloats) return MK_E_UNSUPPORTED;
+  if (c->d_model > 4096) return MK_E_UNSUPPORTED;   // the norm task holds 2 chunks of 4 per thread
+  if (c->top_k > 8 || c->n_kv_heads > 8) return MK_E_UNSUPPORTED;
   const int gd = c->n_q_heads / c->n_kv_heads * c->head_dim;
   if ((size_t)c->max_batch * gd > (size_t)kXsFloats) return MK_E_UNSUPPORTED;
   if (c->swa_window < 0 || c->swa_period < 0) return MK_E_INVAL;
@@ -111,6 +113,7 @@ Layout make_layout(const mk_config* c, int32_t max_blocks) {
   L.off_oout = take((size_t)Lr * B * d * 4);
   L.off_pml = take((size_t)2 * B * c->n_q_heads * L.max_splits * 2 * 4);
   L.off_po = take((size_t)2 * B * c->n_q_heads * L.max_splits * hd * 4);
+  L.off_trace = take((size_t)L.max_tasks * 4 * 8);
   L.total = o;
   return L;
 }
@@ -697,6 +700,7 @@ int mk_decode_step(mk_handle* h, const int32_t* token_ids, const int32_t* positi
   a.oout = reinterpret_cast<float*>(ws + L.off_oout);
   a.part_ml = reinterpret_cast<float*>(ws + L.off_pml);
   a.part_o = reinterpret_cast<float*>(ws + L.off_po);
+  a.trace = (h->opts.flags & MK_SCHED_TRACE) ? reinterpret_cast<uint64_t*>(ws + L.off_trace) : nullptr;
   h->last_stream = reinterpret_cast<hipStream_t>(stream);
   const std::vector<int32_t>& wb = h->plan.wave_bounds;
   return mk_launch(&a, h->opts.launch_mode, wb.data(), (int)wb.size() - 1, stream);
@@ -740,6 +744,7 @@ int mk_tap_offset(const mk_handle* h, int32_t tap, size_t* offset, size_t* bytes
     case MK_TAP_TOPK_WEIGHTS: *offset = L.off_topw; *bytes = c.n_experts > 0 ? Lr * B * c.top_k * 4 : 0; break;
     case MK_TAP_FFN_OUT: *offset = L.off_fo; *bytes = Lr * B * d * 4; break;
     case MK_TAP_ATTN_OUT: *offset = L.off_oout; *bytes = Lr * B * d * 4; break;
+    case MK_TAP_TRACE: *offset = L.off_trace; *bytes = (size_t)(h->have_plan ? h->plan.tasks.size() : 0) * 32; break;
     default: return MK_E_INVAL;
   }
   return MK_OK;

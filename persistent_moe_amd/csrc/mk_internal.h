@@ -131,6 +131,7 @@ struct mk_kargs {
   float* oout;     // [L][B][d]    O-projection output (sum over groups), tap
   float* part_ml;  // [2][B][Hq][max_splits][2]
   float* part_o;   // [2][B][Hq][max_splits][hd]
+  uint64_t* trace; // [n_tasks][4] or null
 };
 
 // host entry of the device code (mk_kernel.hip)

@@ -9,13 +9,17 @@
 // it hand-writable", "Scheduling: mostly static, selectively dynamic"; page 2
 // "Overview"; page 3 on counters that tasks bump and spin on).
 //
-// Memory ordering across the 8 XCDs (each with its own L2): a producer's
-// waves each issue an agent-scope release fence (L2 write-back, wait for
-// their stores), meet at a workgroup barrier, then one lane bumps the counter
-// with an agent-scope atomic.  A consumer spins on agent-scope relaxed loads
-// of the counter with s_sleep between polls and, once the target is reached,
-// issues one agent-scope acquire fence (L1/L2 invalidate) before the
-// workgroup barrier that releases its other waves.
+// Memory ordering across the 8 XCDs (each with its own L2): every value that
+// one workgroup writes and another reads during the step (activations,
+// partials, routing tables, the new K/V slot) is stored and loaded with
+// agent-coherent accesses (the sc1 cache policy, i.e. relaxed agent-scope
+// atomics), so no L2 write-back or invalidate is ever needed.  A producer's
+// waves wait for their stores to complete (s_waitcnt vmcnt(0)), meet at a
+// workgroup barrier, and one lane bumps the counter with an agent-scope
+// atomic; a consumer lane spins on agent-scope loads of the counter with
+// s_sleep between polls, then a workgroup barrier releases its other waves.
+// (Agent-scope release/acquire fences would write back / invalidate the
+// whole L2 of the XCD on every task, which measured 2-30 us per task here.)
 //
 // Weights are immutable during a step, so every GEMV tile issues the loads of
 // its first row group into registers *before* it waits on its activation
@@ -43,6 +47,7 @@ struct __attribute__((aligned(16))) Smem {
   float ys[YS_FLOATS];
   float red[RED_FLOATS];
   int misc[192];
+  uint64_t t_ready;   // trace: when the task's first wait was satisfied
 };
 
 // ------------------------------------------------------------------ helpers
@@ -72,6 +77,41 @@ __device__ __forceinline__ int ld_agent(const int32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Agent-coherent loads and stores of data shared between workgroups.
+__device__ __forceinline__ float ldc(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int ldc(const int32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void stc(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void stc(int32_t* p, int v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void stc(uint16_t* p, uint16_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// 16-byte agent-coherent load at base + byte_off; base must be uniform.
+__device__ __forceinline__ u32x4 ldc16(const void* base, int byte_off) {
+  __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7FFFFFFF,
+                                                               0x00020000);
+  return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 16 /* sc1 */);
+}
+__device__ __forceinline__ void stc16(void* base, int byte_off, u32x4 v) {
+  __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(base, (short)0, 0x7FFFFFFF, 0x00020000);
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, byte_off, 0, 16 /* sc1 */);
+}
+__device__ __forceinline__ f32x4 as_f4(u32x4 v) {
+  return (f32x4){__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w)};
+}
+__device__ __forceinline__ u32x4 as_u4(f32x4 v) {
+  return (u32x4){__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z), __float_as_uint(v.w)};
+}
+// Wait until this wave's stores have completed.
+__device__ __forceinline__ void stores_done() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 __device__ void report(const mk_kargs& a, int code, int task, int ctr, int val, int target) {
   if (atomicCAS(&a.err[0], 0, code) == 0) {
     a.err[1] = task;
@@ -99,26 +139,27 @@ __device__ bool spin_until(const mk_kargs& a, int idx, int target, int task) {
       }
     }
   }
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   return true;
 }
 
 // Workgroup-wide wait; every thread must call it.  Uses misc[0].
 __device__ bool wg_wait(const mk_kargs& a, Smem& sm, int idx, int target, int task) {
-  if (threadIdx.x == 0) sm.misc[0] = (idx < 0 || target <= 0) ? 1 : (int)spin_until(a, idx, target, task);
+  if (threadIdx.x == 0) {
+    sm.misc[0] = (idx < 0 || target <= 0) ? 1 : (int)spin_until(a, idx, target, task);
+    if (a.trace && sm.t_ready == 0) sm.t_ready = wall_clock64();
+  }
   __syncthreads();
   const bool ok = sm.misc[0] != 0;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
   return ok;
 }
 
-// Workgroup-wide signal: every wave makes its stores visible at agent scope,
-// then one lane bumps the counter.
+// Workgroup-wide signal: every wave waits for its (agent-coherent) stores to
+// complete, then one lane bumps the counter.
 __device__ void wg_signal(const mk_kargs& a, int idx, int inc) {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  stores_done();
   __syncthreads();
   if (threadIdx.x == 0 && idx >= 0)
-    __hip_atomic_fetch_add(a.ctr + idx, inc, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_fetch_add(a.ctr + idx, inc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Claim the next item of a queue; every thread must call it.  Uses misc[1].
@@ -263,7 +304,7 @@ struct GemvTile {
       for (int b = 0; b < NB; ++b) {
         const float s = wave_sum(acc[j][b]);
         if (lane == 0 && r < g.nrows && b < g.nb) {
-          if (g.out) g.out[(long)b * g.ob + r] = s;
+          if (g.out) stc(g.out + (long)b * g.ob + r, s);
           else ys[r * NBMAX + b] = s;
         }
       }
@@ -284,17 +325,44 @@ struct StageArgs {
   int task;
 };
 
+// Wave 0 waits (lane 0 spins) and then stages the activation rows into LDS;
+// the other waves only meet it at the barrier.  Wave 0's own weight loads
+// have landed by the time its spin sees the counter, so its staging loads
+// do not queue behind outstanding weight traffic.  Every thread must call it.
 __device__ bool wait_and_stage(const mk_kargs& a, Smem& sm, const StageArgs& s) {
-  if (!wg_wait(a, sm, s.wait_idx, s.wait_target, s.task)) return false;
-  const int kv = s.K >> 2;
-  for (int i = threadIdx.x; i < s.nb * kv; i += MK_THREADS) {
-    const int j = i / kv, c = i - j * kv;
-    const int row = s.map ? s.map[s.map0 + j] : j;
-    const f32x4 v = *reinterpret_cast<const f32x4*>(s.base + (long)row * s.ld + c * 4);
-    *reinterpret_cast<f32x4*>(sm.xs + j * s.K + c * 4) = v;
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    int ok = 1;
+    if (lane == 0) {
+      ok = (s.wait_idx < 0 || s.wait_target <= 0) ? 1 : (int)spin_until(a, s.wait_idx, s.wait_target, s.task);
+      if (a.trace && sm.t_ready == 0) sm.t_ready = wall_clock64();
+    }
+    ok = __shfl(ok, 0);
+    if (lane == 0) sm.misc[0] = ok;
+    if (ok) {
+      const int kv = s.K >> 2, total = s.nb * kv;
+      for (int i0 = 0; i0 < total; i0 += 64 * 8) {
+        u32x4 v[8];
+        int dst[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int i = i0 + u * 64 + lane;
+          dst[u] = -1;
+          if (i < total) {
+            const int j = i / kv, c = i - j * kv;
+            const int row = s.map ? ldc(s.map + s.map0 + j) : j;
+            v[u] = ldc16(s.base, (int)(((long)row * s.ld + c * 4) * 4));
+            dst[u] = j * s.K + c * 4;
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (dst[u] >= 0) *reinterpret_cast<u32x4*>(sm.xs + dst[u]) = v[u];
+      }
+    }
   }
   __syncthreads();
-  return true;
+  return sm.misc[0] != 0;
 }
 
 template <int NB, int KCH, int RPW>
@@ -302,14 +370,16 @@ __device__ bool gemv_run(const mk_kargs& a, Smem& sm, const GemvArgs& g, const S
   GemvTile<NB, KCH, RPW> A, Bt;
   const int per = MK_WAVES * RPW;
   const int ng = (g.nrows + per - 1) / per;
-  A.load(g, 0);                       // weight prefetch before the dependency
+  // the first two row groups are in flight before the dependency resolves
+  A.load(g, 0);
+  if (ng > 1) Bt.load(g, 1);
   if (!wait_and_stage(a, sm, s)) return false;
   for (int grp = 0; grp < ng; grp += 2) {
-    if (grp + 1 < ng) Bt.load(g, grp + 1);
     A.compute(g, grp, sm.xs, sm.ys);
+    if (grp + 2 < ng) A.load(g, grp + 2);
     if (grp + 1 < ng) {
-      if (grp + 2 < ng) A.load(g, grp + 2);
       Bt.compute(g, grp + 1, sm.xs, sm.ys);
+      if (grp + 3 < ng) Bt.load(g, grp + 3);
     }
   }
   return true;
@@ -352,85 +422,131 @@ __device__ bool gemv(const mk_kargs& a, Smem& sm, const GemvArgs& g, const Stage
 // ------------------------------------------------------------- ADD_RMSNORM
 // x_l = x_{l-1} + sum_g O-proj partial_g + sum_j w_j Y_j (parallel block), or
 // the embedding row at layer 0; xn_l = x_l / sqrt(mean(x_l^2) + eps) * gain.
-// One wave per batch row.  The MoE combine (gate-weighted sum of the routed
-// expert outputs, in top-k order) is folded into this task.
+// All 512 threads take 4-element chunks of every batch row (d <= 4096), with
+// every source load issued before any is used.  The MoE combine (the
+// gate-weighted sum of the routed expert outputs, in top-k order) is folded
+// into this task.
 __device__ __noinline__ void op_add_rmsnorm(const mk_kargs& a, Smem& sm, const mk_task& t, int ti) {
   if (!wg_wait(a, sm, t.wait_ctr, t.wait_target, ti)) return;
-  const int l = t.layer, d = a.d, B = a.B;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int l = t.layer, d = a.d, B = a.B, nv = d >> 2, K = a.topk;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const bool mid = t.flags & MK_F_MID;
   const bool fin = t.flags & MK_F_FINAL;
-  for (int b = wave; b < B; b += MK_WAVES) {
-    float* xo = (mid ? a.xmid + ((long)l * B + b) * d : a.x + ((long)l * B + b) * d);
-    float* xno = (mid ? a.xn2 + ((long)l * B + b) * d : a.xn + ((long)l * B + b) * d);
-    const uint16_t* gain = fin ? a.final_norm : (mid ? a.layers[l].ffn_norm : a.layers[l].attn_norm);
-    if (a.seq_lens[b] <= 0) {
-      for (int i = lane; i < d; i += 64) { xo[i] = 0.f; xno[i] = 0.f; }
-      continue;
+  const bool emb = t.flags & MK_F_EMBED;
+  const bool moe_in = !emb && !mid && a.parallel && a.E > 0;
+  const int lp = l - 1;
+  // gate weights and rows of the routed outputs of the previous layer
+  int* srow = sm.misc + 64;                     // [B*K]
+  float* sw = reinterpret_cast<float*>(sm.misc + 128);   // [B*K]
+  if (moe_in) {
+    const int32_t* meta = a.moe + (long)lp * a.moe_stride;
+    const int32_t* slot = meta + 4 + a.bk + (a.bk + 1) + a.bk;
+    if (tid < B * K) {
+      srow[tid] = ldc(slot + tid);
+      sw[tid] = ldc(a.topw + (long)lp * B * K + tid);
     }
-    float ss = 0.f;
-    if (t.flags & MK_F_EMBED) {
-      if (lane == 0 && a.seq_lens[b] > a.max_blocks * a.page)
-        report(a, MK_E_DEVICE, ti, -5, a.seq_lens[b], a.max_blocks * a.page);
-      int tok = a.tokens[b];
-      if (tok < 0 || tok >= a.V) {
-        if (lane == 0) report(a, MK_E_DEVICE, ti, -1, tok, a.V);
-        tok = 0;
-      }
-      const uint16_t* e = a.embed + (long)tok * d;
-      for (int i = lane; i < d; i += 64) {
-        const float v = bf16_to_f(e[i]);
-        xo[i] = v;
-        ss += v * v;
-      }
-    } else if (mid) {
-      // sequential block: x_mid = x_l + attention output
-      const float* xp = a.x + ((long)l * B + b) * d;
-      float* oo = a.oout + ((long)l * B + b) * d;
-      for (int i = lane; i < d; i += 64) {
-        float o = 0.f;
-        for (int g = 0; g < a.Hkv; ++g) o += a.opart[(((long)l * a.Hkv + g) * B + b) * d + i];
-        oo[i] = o;
-        const float v = xp[i] + o;
-        xo[i] = v;
-        ss += v * v;
-      }
-    } else if (a.parallel) {
-      const int lp = l - 1;
-      const float* xp = a.x + ((long)lp * B + b) * d;
-      float* oo = a.oout + ((long)lp * B + b) * d;
-      float* fo = a.fo + ((long)lp * B + b) * d;
-      const int32_t* meta = a.moe + (long)lp * a.moe_stride;
-      const int32_t* slot = meta + 4 + a.bk + (a.bk + 1) + a.bk;
-      const float* w = a.topw + ((long)lp * B + b) * a.topk;
-      for (int i = lane; i < d; i += 64) {
-        float o = 0.f;
-        for (int g = 0; g < a.Hkv; ++g) o += a.opart[(((long)lp * a.Hkv + g) * B + b) * d + i];
-        float m = 0.f;
-        for (int j = 0; j < a.topk; ++j) {
-          const int row = slot[b * a.topk + j];
-          m += w[j] * a.Y[((long)lp * a.bk + row) * d + i];
+    __syncthreads();
+  }
+  const uint16_t* gain = fin ? a.final_norm : (mid ? a.layers[l].ffn_norm : a.layers[l].attn_norm);
+  float* xdst = mid ? a.xmid + (long)l * B * d : a.x + (long)l * B * d;
+  float* xndst = mid ? a.xn2 + (long)l * B * d : a.xn + (long)l * B * d;
+  f32x4 v[NBMAX][2];
+  float ss[NBMAX];
+#pragma unroll
+  for (int b = 0; b < NBMAX; ++b) {
+    ss[b] = 0.f;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) v[b][u] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll
+  for (int b = 0; b < NBMAX; ++b) {
+    if (b < B && a.seq_lens[b] > 0) {
+      int tok = 0;
+      if (emb) {
+        tok = a.tokens[b];
+        if (tok < 0 || tok >= a.V) {
+          if (tid == 0) report(a, MK_E_DEVICE, ti, -1, tok, a.V);
+          tok = 0;
         }
-        oo[i] = o;
-        fo[i] = m;
-        const float v = xp[i] + o + m;
-        xo[i] = v;
-        ss += v * v;
+        if (tid == 0 && a.seq_lens[b] > a.max_blocks * a.page)
+          report(a, MK_E_DEVICE, ti, -5, a.seq_lens[b], a.max_blocks * a.page);
       }
-    } else {
-      // sequential block: x_l = x_mid + FFN output
-      const int lp = l - 1;
-      const float* xp = a.xmid + ((long)lp * B + b) * d;
-      const float* fo = a.fo + ((long)lp * B + b) * d;
-      for (int i = lane; i < d; i += 64) {
-        const float v = xp[i] + fo[i];
-        xo[i] = v;
-        ss += v * v;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int c = tid + u * MK_THREADS;
+        if (c >= nv) continue;
+        const int off = c * 16;   // byte offset of the chunk in a row
+        f32x4 acc;
+        if (emb) {
+          const uint2 e = *reinterpret_cast<const uint2*>(a.embed + (long)tok * d + c * 4);
+          acc = (f32x4){bf_lo(e.x), bf_hi(e.x), bf_lo(e.y), bf_hi(e.y)};
+        } else if (mid || moe_in) {
+          const int lx = mid ? l : lp;     // layer whose attention output is added
+          f32x4 o = (f32x4){0.f, 0.f, 0.f, 0.f};
+          f32x4 og[8];
+#pragma unroll
+          for (int g = 0; g < 8; ++g)
+            if (g < a.Hkv) og[g] = as_f4(ldc16(a.opart + (((long)lx * a.Hkv + g) * B + b) * d, off));
+          f32x4 ym[8];
+          if (moe_in) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+              if (j < K)
+                ym[j] = as_f4(ldc16(a.Y + ((long)lp * a.bk + __builtin_amdgcn_readfirstlane(srow[b * K + j])) * d,
+                                    off));
+          }
+          const f32x4 xp = as_f4(ldc16(a.x + ((long)lx * B + b) * d, off));
+#pragma unroll
+          for (int g = 0; g < 8; ++g)
+            if (g < a.Hkv) o += og[g];
+          stc16(a.oout + ((long)lx * B + b) * d, off, as_u4(o));
+          acc = xp + o;
+          if (moe_in) {
+            f32x4 m = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+              if (j < K) m += sw[b * K + j] * ym[j];
+            stc16(a.fo + ((long)lp * B + b) * d, off, as_u4(m));
+            acc += m;
+          }
+        } else {
+          // sequential block: x_l = x_mid + FFN output
+          acc = as_f4(ldc16(a.xmid + ((long)lp * B + b) * d, off)) +
+                as_f4(ldc16(a.fo + ((long)lp * B + b) * d, off));
+        }
+        stc16(xdst + (long)b * d, off, as_u4(acc));
+        v[b][u] = acc;
+        ss[b] += acc.x * acc.x + acc.y * acc.y + acc.z * acc.z + acc.w * acc.w;
       }
     }
-    ss = wave_sum(ss);
-    const float r = 1.0f / sqrtf(ss / (float)d + a.eps);
-    for (int i = lane; i < d; i += 64) xno[i] = xo[i] * r * bf16_to_f(gain[i]);
+  }
+  float* red = sm.red;
+#pragma unroll
+  for (int b = 0; b < NBMAX; ++b) {
+    if (b < B) {
+      const float r = wave_sum(ss[b]);
+      if (lane == 0) red[wave * NBMAX + b] = r;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int b = 0; b < NBMAX; ++b) {
+    if (b >= B) continue;
+    float tot = 0.f;
+#pragma unroll
+    for (int w = 0; w < MK_WAVES; ++w) tot += red[w * NBMAX + b];
+    const float r = 1.0f / sqrtf(tot / (float)d + a.eps);
+    const bool live = a.seq_lens[b] > 0;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int c = tid + u * MK_THREADS;
+      if (c >= nv) continue;
+      const uint2 gg = *reinterpret_cast<const uint2*>(gain + c * 4);
+      const f32x4 gv = (f32x4){bf_lo(gg.x), bf_hi(gg.x), bf_lo(gg.y), bf_hi(gg.y)};
+      const f32x4 out = live ? v[b][u] * r * gv : (f32x4){0.f, 0.f, 0.f, 0.f};
+      stc16(xndst + (long)b * d, c * 16, as_u4(out));
+      if (!live) stc16(xdst + (long)b * d, c * 16, as_u4(out));
+    }
   }
   wg_signal(a, t.signal_ctr, 1);
 }
@@ -472,8 +588,8 @@ __device__ __noinline__ void op_qkv(const mk_kargs& a, Smem& sm, const mk_task& 
       yb = rb;
     }
     float* qo = a.qkv + ((long)l * B + b) * rows;
-    qo[head * hd + i] = ya;
-    qo[head * hd + i + half] = yb;
+    stc(qo + head * hd + i, ya);
+    stc(qo + head * hd + i + half, yb);
     if (head >= a.Hq) {
       const bool isk = head < a.Hq + a.Hkv;
       const int kvh = isk ? head - a.Hq : head - a.Hq - a.Hkv;
@@ -484,8 +600,8 @@ __device__ __noinline__ void op_qkv(const mk_kargs& a, Smem& sm, const mk_task& 
         continue;
       }
       uint16_t* dst = (isk ? kpool : vpool) + (((long)page * a.Hkv + kvh) * a.page + (pos % a.page)) * hd;
-      dst[i] = f_to_bf16(ya);
-      dst[i + half] = f_to_bf16(yb);
+      stc(dst + i, f_to_bf16(ya));
+      stc(dst + i + half, f_to_bf16(yb));
     }
   }
   wg_signal(a, t.signal_ctr, 1);
@@ -544,7 +660,7 @@ __device__ __noinline__ void op_ffn_upgate(const mk_kargs& a, Smem& sm, const mk
   for (int idx = threadIdx.x; idx < np * B; idx += MK_THREADS) {
     const int p = idx / B, b = idx - p * B;
     const float gv = sm.ys[(2 * p) * NBMAX + b], uv = sm.ys[(2 * p + 1) * NBMAX + b];
-    a.fh[((long)l * B + b) * a.F + t.n0 + p] = silu(gv) * uv;
+    stc(a.fh + ((long)l * B + b) * a.F + t.n0 + p, silu(gv) * uv);
   }
   wg_signal(a, t.signal_ctr, 1);
 }
@@ -565,7 +681,7 @@ __device__ __noinline__ void op_router_topk(const mk_kargs& a, Smem& sm, const m
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int e = lane + 64 * u;
-      v[u] = e < E ? a.rlog[((long)l * B + b) * E + e] : -INFINITY;
+      v[u] = e < E ? ldc(a.rlog + ((long)l * B + b) * E + e) : -INFINITY;
     }
     float top0 = 0.f, wsum = 0.f;
     float myw = 0.f;
@@ -593,8 +709,8 @@ __device__ __noinline__ void op_router_topk(const mk_kargs& a, Smem& sm, const m
       if (lane == j) { myw = ew; myid = be; }
     }
     if (lane < K) {
-      a.topi[((long)l * B + b) * K + lane] = myid;
-      a.topw[((long)l * B + b) * K + lane] = myw / wsum;
+      stc(a.topi + ((long)l * B + b) * K + lane, myid);
+      stc(a.topw + ((long)l * B + b) * K + lane, myw / wsum);
       sm.misc[64 + b * K + lane] = a.seq_lens[b] > 0 ? myid : -1;
     }
   }
@@ -639,16 +755,16 @@ __device__ void route_finalize(const mk_kargs& a, Smem& sm, int l) {
   const uint64_t le = (lane == 63) ? ~0ull : ((2ull << lane) - 1ull);
   const int aidx = __popcll(smask & le) - 1;
   if (valid) {
-    slot[src] = lane;
-    row_tok[lane] = src / K;
-    if (start) { act[aidx] = e; row_off[aidx] = lane; }
+    stc(slot + src, lane);
+    stc(row_tok + lane, src / K);
+    if (start) { stc(act + aidx, e); stc(row_off + aidx, lane); }
   }
   if (lane == 0) {
-    row_off[nact] = nrows;
-    meta[0] = nact;
-    meta[1] = nact * a.ug_tiles;
-    meta[2] = nact * a.dn_tiles;
-    meta[3] = nrows;
+    stc(row_off + nact, nrows);
+    stc(meta + 0, nact);
+    stc(meta + 1, nact * a.ug_tiles);
+    stc(meta + 2, nact * a.dn_tiles);
+    stc(meta + 3, nrows);
   }
 }
 
@@ -663,14 +779,14 @@ __device__ __noinline__ void op_moe_upgate(const mk_kargs& a, Smem& sm, const mk
   const int32_t* act = meta + 4;
   const int32_t* row_off = act + a.bk;
   const int32_t* row_tok = row_off + a.bk + 1;
-  const int n_items = meta[1];
+  const int n_items = ldc(meta + 1);
   const int qidx = layer_ctr(a, l, MK_CTR_QUG);
   bool first = true;
   for (;;) {
     const int item = next_item(a, sm, t, n_items, qidx, first);
     if (item < 0) break;
     const int ae = item / a.ug_tiles, tt = item - ae * a.ug_tiles;
-    const int e = act[ae], r0 = row_off[ae], nr = row_off[ae + 1] - r0;
+    const int e = ldc(act + ae), r0 = ldc(row_off + ae), nr = ldc(row_off + ae + 1) - r0;
     const int p0 = tt * a.ug_pairs;
     const int np = min(a.ug_pairs, a.I - p0);
     GemvArgs g;
@@ -685,7 +801,7 @@ __device__ __noinline__ void op_moe_upgate(const mk_kargs& a, Smem& sm, const mk
     for (int idx = threadIdx.x; idx < np * nr; idx += MK_THREADS) {
       const int p = idx / nr, j = idx - p * nr;
       const float gv = sm.ys[(2 * p) * NBMAX + j], uv = sm.ys[(2 * p + 1) * NBMAX + j];
-      a.H[((long)l * a.bk + r0 + j) * a.I + p0 + p] = silu(gv) * uv;
+      stc(a.H + ((long)l * a.bk + r0 + j) * a.I + p0 + p, silu(gv) * uv);
     }
     wg_signal(a, layer_ctr(a, l, a.cl.ug + ae), 1);
   }
@@ -702,14 +818,14 @@ __device__ __noinline__ void op_moe_down(const mk_kargs& a, Smem& sm, const mk_t
   const int32_t* meta = a.moe + (long)l * a.moe_stride;
   const int32_t* act = meta + 4;
   const int32_t* row_off = act + a.bk;
-  const int n_items = meta[2];
+  const int n_items = ldc(meta + 2);
   const int qidx = layer_ctr(a, l, MK_CTR_QDN);
   bool first = true;
   for (;;) {
     const int item = next_item(a, sm, t, n_items, qidx, first);
     if (item < 0) break;
     const int ae = item / a.dn_tiles, tt = item - ae * a.dn_tiles;
-    const int e = act[ae], r0 = row_off[ae], nr = row_off[ae + 1] - r0;
+    const int e = ldc(act + ae), r0 = ldc(row_off + ae), nr = ldc(row_off + ae + 1) - r0;
     const int n0 = tt * a.dn_rows;
     const int nrow = min(a.dn_rows, a.d - n0);
     GemvArgs g;
@@ -729,62 +845,110 @@ __device__ __noinline__ void op_moe_down(const mk_kargs& a, Smem& sm, const mk_t
 // for the G query heads of the group, then m = max s, p = exp(s - m),
 // l = sum p, o = sum p V_j.  Lane layout: hd/8 lanes share one key row (8
 // dims each), so a wave load reads 64/(hd/8) keys; waves take keys in turn.
+// The K and V rows of the first chunk are loaded before the wait on the QKV
+// tiles (cached keys are immutable); the key appended this step is re-read
+// with a coherent load after the wait.  q goes through LDS, staged by wave 0.
+constexpr int ATT_CH = 4;   // wave loads per chunk
+
 template <int HD>
-__device__ void attn_split(const mk_kargs& a, Smem& sm, int l, int b, int g, int s, int p0, int p1,
-                           int ti) {
+__device__ bool attn_split(const mk_kargs& a, Smem& sm, int l, int b, int g, int s, int p0, int p1, int ti,
+                           int wait_idx, int wait_target) {
   constexpr int LPR = HD / 8;
   constexpr int PPW = 64 / LPR;
+  constexpr int PER_IT = MK_WAVES * PPW;   // keys per iteration of the workgroup
   const int G = a.G, S = a.attn_split;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int sub = lane / LPR, c = lane - sub * LPR;
   const int n = p1 - p0;
+  const int iters = (n + PER_IT - 1) / PER_IT;
   const int rows = (a.Hq + 2 * a.Hkv) * HD;
-  float q[NBMAX][8];
-  const float* qb = a.qkv + ((long)l * a.B + b) * rows + (long)(g * G) * HD + c * 8;
-#pragma unroll
-  for (int h = 0; h < NBMAX; ++h) {
-    if (h < G) {
-      const f32x4 q0 = *reinterpret_cast<const f32x4*>(qb + h * HD);
-      const f32x4 q1 = *reinterpret_cast<const f32x4*>(qb + h * HD + 4);
-      q[h][0] = q0.x * a.attn_scale; q[h][1] = q0.y * a.attn_scale;
-      q[h][2] = q0.z * a.attn_scale; q[h][3] = q0.w * a.attn_scale;
-      q[h][4] = q1.x * a.attn_scale; q[h][5] = q1.y * a.attn_scale;
-      q[h][6] = q1.z * a.attn_scale; q[h][7] = q1.w * a.attn_scale;
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) q[h][e] = 0.f;
-    }
-  }
   const uint16_t* Kp = a.layers[l].k;
   const uint16_t* Vp = a.layers[l].v;
   const int32_t* bt = a.block_tables + (long)b * a.max_blocks;
+  const int newest = a.positions[b];
+  // element offset of key iteration `it` for this lane, or -1
+  auto key_off = [&](int it, int* jpos) -> int {
+    const int jj = it * PER_IT + wave * PPW + sub;
+    if (jj >= n) return -1;
+    const int j = p0 + jj;
+    *jpos = j;
+    int pg = bt[j / a.page];
+    if (pg < 0 || pg >= a.num_pages) {
+      report(a, MK_E_DEVICE, ti, -3, pg, a.num_pages);
+      pg = 0;
+    }
+    return ((pg * a.Hkv + g) * a.page + (j % a.page)) * HD + c * 8;
+  };
+  u32x4 kb[ATT_CH], vb[ATT_CH];
+  int ko[ATT_CH];
+  int kj[ATT_CH];
+#pragma unroll
+  for (int u = 0; u < ATT_CH; ++u) {
+    kj[u] = -1;
+    ko[u] = u < iters ? key_off(u, &kj[u]) : -1;
+    if (ko[u] >= 0) {
+      kb[u] = ldg_nt(Kp + ko[u]);
+      vb[u] = ldg_nt(Vp + ko[u]);
+    }
+  }
+  // wait for the QKV tiles, then wave 0 stages q of the group's heads
+  float* qs = sm.xs;   // [G][HD]
+  if (tid < 64) {
+    int ok = 1;
+    if (lane == 0) {
+      ok = (wait_idx < 0 || wait_target <= 0) ? 1 : (int)spin_until(a, wait_idx, wait_target, ti);
+      if (a.trace && sm.t_ready == 0) sm.t_ready = wall_clock64();
+    }
+    ok = __shfl(ok, 0);
+    if (lane == 0) sm.misc[0] = ok;
+    if (ok) {
+      const float* qb = a.qkv + ((long)l * a.B + b) * rows + (long)(g * G) * HD;
+      for (int i = lane; i < G * HD / 4; i += 64)
+        *reinterpret_cast<u32x4*>(qs + i * 4) = ldc16(qb, i * 16);
+    }
+  }
+  __syncthreads();
+  if (!sm.misc[0]) return false;
+  float q[NBMAX][8];
+#pragma unroll
+  for (int h = 0; h < NBMAX; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) q[h][e] = h < G ? qs[h * HD + c * 8 + e] * a.attn_scale : 0.f;
   float* sc = sm.ys;  // [G][S]
-  // pass 1: scores
-  for (int base = wave * PPW; base < n; base += MK_WAVES * PPW) {
-    const int jj = base + sub;
-    float part[NBMAX];
+  // pass 1: scores, chunk by chunk
+  for (int it0 = 0; it0 < iters; it0 += ATT_CH) {
+    if (it0 > 0) {
 #pragma unroll
-    for (int h = 0; h < NBMAX; ++h) part[h] = 0.f;
-    if (jj < n) {
-      const int j = p0 + jj;
-      int pg = bt[j / a.page];
-      if (pg < 0 || pg >= a.num_pages) { report(a, MK_E_DEVICE, ti, -3, pg, a.num_pages); pg = 0; }
-      const u32x4 kv = ldg_nt(Kp + (((long)pg * a.Hkv + g) * a.page + (j % a.page)) * HD + c * 8);
-      const float k0 = bf_lo(kv.x), k1 = bf_hi(kv.x), k2 = bf_lo(kv.y), k3 = bf_hi(kv.y);
-      const float k4 = bf_lo(kv.z), k5 = bf_hi(kv.z), k6 = bf_lo(kv.w), k7 = bf_hi(kv.w);
-#pragma unroll
-      for (int h = 0; h < NBMAX; ++h)
-        part[h] = q[h][0] * k0 + q[h][1] * k1 + q[h][2] * k2 + q[h][3] * k3 + q[h][4] * k4 +
-                  q[h][5] * k5 + q[h][6] * k6 + q[h][7] * k7;
+      for (int u = 0; u < ATT_CH; ++u) {
+        kj[u] = -1;
+        ko[u] = it0 + u < iters ? key_off(it0 + u, &kj[u]) : -1;
+        if (ko[u] >= 0) kb[u] = ldg_nt(Kp + ko[u]);
+      }
     }
 #pragma unroll
-    for (int h = 0; h < NBMAX; ++h)
+    for (int u = 0; u < ATT_CH; ++u) {
+      float part[NBMAX];
 #pragma unroll
-      for (int m = LPR / 2; m >= 1; m >>= 1) part[h] += __shfl_xor(part[h], m);
-    if (jj < n && c == 0) {
+      for (int h = 0; h < NBMAX; ++h) part[h] = 0.f;
+      if (ko[u] >= 0) {
+        const u32x4 kv = (kj[u] == newest) ? ldc16(Kp, (int)(ko[u] * 2)) : kb[u];
+        const float k0 = bf_lo(kv.x), k1 = bf_hi(kv.x), k2 = bf_lo(kv.y), k3 = bf_hi(kv.y);
+        const float k4 = bf_lo(kv.z), k5 = bf_hi(kv.z), k6 = bf_lo(kv.w), k7 = bf_hi(kv.w);
+#pragma unroll
+        for (int h = 0; h < NBMAX; ++h)
+          part[h] = q[h][0] * k0 + q[h][1] * k1 + q[h][2] * k2 + q[h][3] * k3 + q[h][4] * k4 + q[h][5] * k5 +
+                    q[h][6] * k6 + q[h][7] * k7;
+      }
 #pragma unroll
       for (int h = 0; h < NBMAX; ++h)
-        if (h < G) sc[h * S + jj] = part[h];
+#pragma unroll
+        for (int m = LPR / 2; m >= 1; m >>= 1) part[h] += __shfl_xor(part[h], m);
+      if (ko[u] >= 0 && c == 0) {
+        const int jj = kj[u] - p0;
+#pragma unroll
+        for (int h = 0; h < NBMAX; ++h)
+          if (h < G) sc[h * S + jj] = part[h];
+      }
     }
   }
   __syncthreads();
@@ -802,33 +966,47 @@ __device__ void attn_split(const mk_kargs& a, Smem& sm, int l, int b, int g, int
     }
     sum = wave_sum(sum);
     if (lane == 0) {
-      ml[((long)wave * a.max_splits + s) * 2 + 0] = mx;
-      ml[((long)wave * a.max_splits + s) * 2 + 1] = sum;
+      stc(ml + ((long)wave * a.max_splits + s) * 2 + 0, mx);
+      stc(ml + ((long)wave * a.max_splits + s) * 2 + 1, sum);
     }
   }
   __syncthreads();
-  // pass 3: o = sum p V
+  // pass 3: o = sum p V, chunk by chunk (the first chunk is already loaded)
   float o[NBMAX][8];
 #pragma unroll
   for (int h = 0; h < NBMAX; ++h)
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[h][e] = 0.f;
-  for (int base = wave * PPW; base < n; base += MK_WAVES * PPW) {
-    const int jj = base + sub;
-    if (jj < n) {
-      const int j = p0 + jj;
-      int pg = bt[j / a.page];
-      if (pg < 0 || pg >= a.num_pages) pg = 0;
-      const u32x4 vv = ldg_nt(Vp + (((long)pg * a.Hkv + g) * a.page + (j % a.page)) * HD + c * 8);
-      float vf[8];
-      vf[0] = bf_lo(vv.x); vf[1] = bf_hi(vv.x); vf[2] = bf_lo(vv.y); vf[3] = bf_hi(vv.y);
-      vf[4] = bf_lo(vv.z); vf[5] = bf_hi(vv.z); vf[6] = bf_lo(vv.w); vf[7] = bf_hi(vv.w);
+  for (int it0 = 0; it0 < iters; it0 += ATT_CH) {
+    if (it0 > 0) {
 #pragma unroll
-      for (int h = 0; h < NBMAX; ++h) {
-        if (h < G) {
-          const float pj = sc[h * S + jj];
+      for (int u = 0; u < ATT_CH; ++u) {
+        kj[u] = -1;
+        ko[u] = it0 + u < iters ? key_off(it0 + u, &kj[u]) : -1;
+        if (ko[u] >= 0) vb[u] = ldg_nt(Vp + ko[u]);
+      }
+    } else {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) o[h][e] = fmaf(pj, vf[e], o[h][e]);
+      for (int u = 0; u < ATT_CH; ++u) {
+        kj[u] = -1;
+        ko[u] = u < iters ? key_off(u, &kj[u]) : -1;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < ATT_CH; ++u) {
+      if (ko[u] >= 0) {
+        const u32x4 vv = (kj[u] == newest) ? ldc16(Vp, (int)(ko[u] * 2)) : vb[u];
+        float vf[8];
+        vf[0] = bf_lo(vv.x); vf[1] = bf_hi(vv.x); vf[2] = bf_lo(vv.y); vf[3] = bf_hi(vv.y);
+        vf[4] = bf_lo(vv.z); vf[5] = bf_hi(vv.z); vf[6] = bf_lo(vv.w); vf[7] = bf_hi(vv.w);
+        const int jj = kj[u] - p0;
+#pragma unroll
+        for (int h = 0; h < NBMAX; ++h) {
+          if (h < G) {
+            const float pj = sc[h * S + jj];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[h][e] = fmaf(pj, vf[e], o[h][e]);
+          }
         }
       }
     }
@@ -853,88 +1031,121 @@ __device__ void attn_split(const mk_kargs& a, Smem& sm, int l, int b, int g, int
     float v = 0.f;
 #pragma unroll
     for (int w = 0; w < MK_WAVES; ++w) v += sm.red[(w * NBMAX + h) * HD + dd];
-    po[((long)h * a.max_splits + s) * HD + dd] = v;
+    stc(po + ((long)h * a.max_splits + s) * HD + dd, v);
   }
+  return true;
 }
 
-__device__ void attn_item(const mk_kargs& a, Smem& sm, int l, int b, int g, int s, int ti) {
+__device__ bool attn_item(const mk_kargs& a, Smem& sm, int l, int b, int g, int s, int ti, int wait_idx,
+                          int wait_target) {
   const int sl = live_len(a, b);
   const int kv = visible_keys(a, l, sl);
   const int start = sl - kv;
   const int p0 = start + s * a.attn_split;
   const int p1 = min(p0 + a.attn_split, sl);
-  if (a.hd == 128) attn_split<128>(a, sm, l, b, g, s, p0, p1, ti);
-  else attn_split<64>(a, sm, l, b, g, s, p0, p1, ti);
+  if (a.hd == 128) return attn_split<128>(a, sm, l, b, g, s, p0, p1, ti, wait_idx, wait_target);
+  return attn_split<64>(a, sm, l, b, g, s, p0, p1, ti, wait_idx, wait_target);
 }
 
 // ATTN_DRAIN: drains the layer's (batch, group, split) items, batch-major.
 // The item count follows from seq_lens alone, so a claimer with nothing to
-// do returns without waiting for the QKV tiles.
+// do returns without waiting; the first item's K/V loads are issued before
+// the wait on the QKV tiles.
 __device__ __noinline__ void op_attn_drain(const mk_kargs& a, Smem& sm, const mk_task& t, int ti) {
   const int l = t.layer;
   int n_items = 0;
   for (int b = 0; b < a.B; ++b) n_items += n_splits(a, l, b) * a.Hkv;
-  if (t.n0 < n_items || n_items > t.n1) {
-    if (!wg_wait(a, sm, t.wait_ctr, t.wait_target, ti)) return;
-    const int qidx = layer_ctr(a, l, MK_CTR_QATTN);
-    bool first = true;
-    for (;;) {
-      int item = next_item(a, sm, t, n_items, qidx, first);
-      if (item < 0) break;
-      int b = 0, g = 0, s = -1;
-      for (; b < a.B; ++b) {
-        const int ns = n_splits(a, l, b);
-        const int cnt = ns * a.Hkv;
-        if (item < cnt) { g = item / ns; s = item - g * ns; break; }
-        item -= cnt;
-      }
-      if (s < 0) break;
-      attn_item(a, sm, l, b, g, s, ti);
-      wg_signal(a, layer_ctr(a, l, a.cl.attn + b * a.Hkv + g), 1);
+  const int qidx = layer_ctr(a, l, MK_CTR_QATTN);
+  bool first = true;
+  int wait_idx = t.wait_ctr, wait_target = t.wait_target;
+  for (;;) {
+    int item = next_item(a, sm, t, n_items, qidx, first);
+    if (item < 0) break;
+    int b = 0, g = 0, s = -1;
+    for (; b < a.B; ++b) {
+      const int ns = n_splits(a, l, b);
+      const int cnt = ns * a.Hkv;
+      if (item < cnt) { g = item / ns; s = item - g * ns; break; }
+      item -= cnt;
     }
+    if (s < 0) break;
+    if (!attn_item(a, sm, l, b, g, s, ti, wait_idx, wait_target)) return;
+    wait_idx = -1;   // satisfied for every later item
+    wg_signal(a, layer_ctr(a, l, a.cl.attn + b * a.Hkv + g), 1);
   }
   wg_signal(a, t.signal_ctr, 1);
 }
 
 // ATTN_DECODE: one statically placed split.
 __device__ __noinline__ void op_attn_decode(const mk_kargs& a, Smem& sm, const mk_task& t, int ti) {
-  if (!wg_wait(a, sm, t.wait_ctr, t.wait_target, ti)) return;
   const int l = t.layer;
-  if (t.split < n_splits(a, l, t.batch)) attn_item(a, sm, l, t.batch, t.group, t.split, ti);
+  if (t.split < n_splits(a, l, t.batch)) {
+    if (!attn_item(a, sm, l, t.batch, t.group, t.split, ti, t.wait_ctr, t.wait_target)) return;
+  } else if (!wg_wait(a, sm, t.wait_ctr, t.wait_target, ti)) {
+    return;
+  }
   wg_signal(a, layer_ctr(a, l, a.cl.attn + t.batch * a.Hkv + t.group), 1);
   wg_signal(a, t.signal_ctr, 1);
 }
 
 // ATTN_COMBINE for (batch b, group g): M = max_s m_s;
-// o = sum_s e^(m_s - M) o_s / sum_s e^(m_s - M) l_s.  One wave per head.
+// o = sum_s e^(m_s - M) o_s / sum_s e^(m_s - M) l_s.  Wave h computes head
+// h's weights; then every thread accumulates 4 dims of one head over the
+// splits with its loads issued 8 splits at a time.
 __device__ __noinline__ void op_attn_combine(const mk_kargs& a, Smem& sm, const mk_task& t, int ti) {
   const int l = t.layer, b = t.batch, g = t.group, G = a.G, hd = a.hd;
   const int ns = n_splits(a, l, b);
   if (!wg_wait(a, sm, t.wait_ctr, ns, ti)) return;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   float* out = a.attn + ((long)l * a.B + b) * a.Hq * hd;
+  const long hstride = (long)a.max_splits;
+  const float* ml0 = a.part_ml + ((((long)(l & 1) * a.B + b) * a.Hq + g * G) * hstride) * 2;
+  const float* po0 = a.part_o + ((((long)(l & 1) * a.B + b) * a.Hq + g * G) * hstride) * hd;
+  float* wts = sm.ys;                 // [G][max_splits]
+  float* den = sm.red;                // [G]
   if (wave < G) {
-    const int h = g * G + wave;
-    const float* ml = a.part_ml + ((((long)(l & 1) * a.B + b) * a.Hq + h) * a.max_splits) * 2;
-    const float* po = a.part_o + ((((long)(l & 1) * a.B + b) * a.Hq + h) * a.max_splits) * hd;
-    float* wts = sm.ys + wave * 1024;
+    const float* ml = ml0 + (long)wave * hstride * 2;
+    float m[16], lsum[16];
     float mx = -INFINITY;
-    for (int s = lane; s < ns; s += 64) mx = fmaxf(mx, ml[s * 2]);
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int s = lane + 64 * u;
+      m[u] = s < ns ? ldc(ml + s * 2) : -INFINITY;
+      lsum[u] = s < ns ? ldc(ml + s * 2 + 1) : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 16; ++u) mx = fmaxf(mx, m[u]);
     mx = wave_max(mx);
-    float den = 0.f;
-    for (int s = lane; s < ns; s += 64) {
-      const float w = expf(ml[s * 2] - mx);
-      wts[s] = w;
-      den += w * ml[s * 2 + 1];
+    float dsum = 0.f;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int s = lane + 64 * u;
+      if (s < ns) {
+        const float w = expf(m[u] - mx);
+        wts[wave * hstride + s] = w;
+        dsum += w * lsum[u];
+      }
     }
-    den = wave_sum(den);
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-    for (int dd = lane; dd < hd; dd += 64) {
-      float num = 0.f;
-      for (int s = 0; s < ns; ++s) num = fmaf(wts[s], po[(long)s * hd + dd], num);
-      out[h * hd + dd] = ns > 0 ? num / den : 0.f;
+    dsum = wave_sum(dsum);
+    if (lane == 0) den[wave] = dsum;
+  }
+  __syncthreads();
+  const int q4 = hd / 4;   // float4 chunks per head
+  for (int idx = tid; idx < G * q4; idx += MK_THREADS) {
+    const int h = idx / q4, cq = idx - h * q4;
+    const float* po = po0 + (long)h * hstride * hd;
+    f32x4 num = (f32x4){0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < ns; s0 += 8) {
+      f32x4 pv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (s0 + u < ns) pv[u] = as_f4(ldc16(po, (int)(((long)(s0 + u) * hd + cq * 4) * 4)));
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (s0 + u < ns) num += wts[h * hstride + s0 + u] * pv[u];
     }
+    const f32x4 r = ns > 0 ? num / den[h] : (f32x4){0.f, 0.f, 0.f, 0.f};
+    stc16(out, ((g * G + h) * hd + cq * 4) * 4, as_u4(r));
   }
   wg_signal(a, t.signal_ctr, 1);
 }
@@ -944,6 +1155,11 @@ extern "C" __global__ void __launch_bounds__(MK_THREADS, 1) mk_persistent(mk_kar
   __shared__ Smem sm;
   for (int ti = a.task_begin + (int)blockIdx.x; ti < a.task_end; ti += (int)gridDim.x) {
     const mk_task t = a.tasks[ti];
+    uint64_t t_start = 0;
+    if (a.trace && threadIdx.x == 0) {
+      t_start = wall_clock64();
+      sm.t_ready = 0;
+    }
     switch (t.op) {
       case MK_OP_ADD_RMSNORM: op_add_rmsnorm(a, sm, t, ti); break;
       case MK_OP_QKV_PROJ: op_qkv(a, sm, t, ti); break;
@@ -957,7 +1173,7 @@ extern "C" __global__ void __launch_bounds__(MK_THREADS, 1) mk_persistent(mk_kar
         if (wg_wait(a, sm, t.wait_ctr, t.wait_target, ti)) {
           for (int i = threadIdx.x; i < a.B * a.topk; i += MK_THREADS) {
             const int b = i / a.topk;
-            sm.misc[64 + i] = a.seq_lens[b] > 0 ? a.topi[((long)t.layer * a.B) * a.topk + i] : -1;
+            sm.misc[64 + i] = a.seq_lens[b] > 0 ? ldc(a.topi + ((long)t.layer * a.B) * a.topk + i) : -1;
           }
           __syncthreads();
           route_finalize(a, sm, t.layer);
@@ -974,20 +1190,26 @@ extern "C" __global__ void __launch_bounds__(MK_THREADS, 1) mk_persistent(mk_kar
         break;
     }
     __syncthreads();
+    if (a.trace && threadIdx.x == 0) {
+      uint64_t* tr = a.trace + (long)ti * 4;
+      tr[0] = t_start;
+      tr[1] = sm.t_ready ? sm.t_ready : t_start;
+      tr[2] = wall_clock64();
+      tr[3] = blockIdx.x;
+    }
   }
   // The last workgroup out clears the counters for the next launch.
   __syncthreads();
   if (threadIdx.x == 0) {
-    const int old = __hip_atomic_fetch_add(a.ctr + MK_CG_DONE, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    const int old = __hip_atomic_fetch_add(a.ctr + MK_CG_DONE, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     sm.misc[2] = (old == (int)gridDim.x - 1);
   }
   __syncthreads();
   if (sm.misc[2]) {
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     if (final_launch) {
-      for (int i = threadIdx.x; i < a.n_ctr; i += MK_THREADS) a.ctr[i] = 0;
+      for (int i = threadIdx.x; i < a.n_ctr; i += MK_THREADS) stc(a.ctr + i, 0);
     } else if (threadIdx.x == 0) {
-      a.ctr[MK_CG_DONE] = 0;
+      stc(a.ctr + MK_CG_DONE, 0);
     }
   }
 }

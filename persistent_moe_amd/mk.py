@@ -30,7 +30,7 @@ MK_WAIT_SPLITS = -2
 ORDER = {"tuned": 0, "interleaved": 1, "attention_first": 2}
 LAUNCH = {"persistent": 0, "per_opcode": 1}
 TAPS = {"x": 0, "xn": 1, "qkv": 2, "attn": 3, "router_logits": 4, "topk_ids": 5, "topk_weights": 6,
-        "ffn_out": 7, "attn_out": 8}
+        "ffn_out": 7, "attn_out": 8, "trace": 9}
 EXPORTS = ["mk_workspace_size", "mk_init", "mk_build_schedule", "mk_decode_step", "mk_get_status",
            "mk_tap_offset", "mk_plan_schedule", "mk_plan_simulate", "mk_destroy", "mk_strerror"]
 
@@ -145,6 +145,7 @@ def make_config(model, max_batch: int) -> mk_config:
 
 
 MK_SCHED_UNREACHABLE_WAIT = 1
+MK_SCHED_TRACE = 2
 
 
 def make_opts(wave_order="tuned", launch_mode="persistent", attn_split=0, n_workgroups=0,

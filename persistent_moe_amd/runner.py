@@ -213,7 +213,7 @@ class DecodeEngine:
         """A per-layer debug tap of the last step, viewed in the workspace."""
         off, nb = mk.mk_tap_offset(self.h, name)
         raw = self.workspace[self.ws_off + off:self.ws_off + off + nb]
-        dt = torch.int32 if name == "topk_ids" else torch.float32
+        dt = {"topk_ids": torch.int32, "trace": torch.int64}.get(name, torch.float32)
         return raw.view(dt)
 
     def close(self):

@@ -1,0 +1,86 @@
+"""Analysis of the device task trace (schedule flag MK_SCHED_TRACE).
+
+Each task records the 100 MHz device clock when its workgroup reached it,
+when its wait was satisfied, and when it finished.  From that:
+
+* per opcode: tasks, total busy time (ready -> end) and total wait time
+  (start -> ready) summed over workgroups;
+* per layer: when its first task started and its last task ended;
+* idle time of each workgroup between its tasks;
+* a Chrome trace-event JSON (one row per workgroup) for a timeline viewer.
+
+The wait time splits the bandwidth the pages say a conventional decode loses
+(page 4, the four sources of lost bandwidth): time spent waiting on a
+producer (false dependencies and the critical path), and time a workgroup
+sits idle at the end of the step (the tail a kernel boundary would round up).
+"""
+from __future__ import annotations
+
+import json
+from collections import defaultdict
+
+import numpy as np
+
+from .mk import OPCODES
+
+TICK_US = 0.01   # 100 MHz clock
+
+
+def load(eng) -> dict:
+    """Trace of the last step of a DecodeEngine built with MK_SCHED_TRACE."""
+    from . import mk
+    tasks, _ = mk.mk_plan_schedule(eng.mkcfg, eng.wl.batch, eng.max_blocks, eng.opts, _n_wg(eng))
+    raw = eng.tap("trace").cpu().numpy().reshape(-1, 4)[:len(tasks)]
+    return {"tasks": tasks, "raw": raw}
+
+
+def _n_wg(eng):
+    import torch
+    if eng.opts.n_workgroups > 0:
+        return eng.opts.n_workgroups
+    return torch.cuda.get_device_properties(eng.dev).multi_processor_count
+
+
+def summarize(tr: dict) -> dict:
+    tasks, raw = tr["tasks"], tr["raw"].astype(np.int64)
+    t0 = raw[:, 0].min()
+    start, ready, end, wg = raw[:, 0] - t0, raw[:, 1] - t0, raw[:, 2] - t0, raw[:, 3]
+    per_op = defaultdict(lambda: [0, 0.0, 0.0])
+    per_layer = defaultdict(lambda: [np.inf, 0.0])
+    for i, t in enumerate(tasks):
+        name = OPCODES[t.op]
+        s = per_op[name]
+        s[0] += 1
+        s[1] += (end[i] - ready[i]) * TICK_US
+        s[2] += (ready[i] - start[i]) * TICK_US
+        pl = per_layer[t.layer]
+        pl[0] = min(pl[0], start[i] * TICK_US)
+        pl[1] = max(pl[1], end[i] * TICK_US)
+    step_us = (end.max()) * TICK_US
+    n_wg = int(wg.max()) + 1
+    idle_tail = float(np.mean([step_us - end[wg == w].max() * TICK_US for w in range(n_wg)]))
+    return {
+        "step_us": float(step_us),
+        "workgroups": n_wg,
+        "mean_tail_idle_us": idle_tail,
+        "per_op": {k: {"tasks": v[0], "busy_us": round(v[1], 1), "wait_us": round(v[2], 1)}
+                   for k, v in sorted(per_op.items(), key=lambda kv: -kv[1][1])},
+        "per_layer": {int(k): {"first_start_us": round(v[0], 2), "last_end_us": round(v[1], 2)}
+                      for k, v in sorted(per_layer.items())},
+    }
+
+
+def chrome_trace(tr: dict, path: str) -> None:
+    tasks, raw = tr["tasks"], tr["raw"].astype(np.int64)
+    t0 = raw[:, 0].min()
+    ev = []
+    for i, t in enumerate(tasks):
+        s, r, e, w = (raw[i, 0] - t0) * TICK_US, (raw[i, 1] - t0) * TICK_US, (raw[i, 2] - t0) * TICK_US, raw[i, 3]
+        name = f"{OPCODES[t.op]} L{t.layer}"
+        if r > s:
+            ev.append({"name": "wait " + name, "ph": "X", "ts": float(s), "dur": float(r - s), "pid": 0,
+                       "tid": int(w), "cat": "wait"})
+        ev.append({"name": name, "ph": "X", "ts": float(r), "dur": float(max(e - r, 0)), "pid": 0,
+                   "tid": int(w), "cat": OPCODES[t.op]})
+    with open(path, "w") as fh:
+        json.dump({"traceEvents": ev}, fh)
