@@ -181,6 +181,9 @@ typedef struct mk_sched_opts {
 /* Record, per task, the 100 MHz device clock at task start, when its wait
  * was satisfied and at its end, into the MK_TAP_TRACE region.             */
 #define MK_SCHED_TRACE 2
+/* Emit ROUTER_TOPK as its own task instead of running it in the last router
+ * tile to finish (one more counter hop per layer).                        */
+#define MK_SCHED_SEPARATE_TOPK 4
 
 #define MK_MIN_SPLIT 64
 
@@ -247,7 +250,8 @@ enum mk_tap {
   MK_TAP_TOPK_WEIGHTS = 6,  /* [L][B][k] f32                                         */
   MK_TAP_FFN_OUT = 7,       /* [L][B][d] f32 MoE (or dense FFN) output               */
   MK_TAP_ATTN_OUT = 8,      /* [L][B][d] f32 output projection (sum over groups)     */
-  MK_TAP_TRACE = 9,         /* [n_tasks][4] u64: start, ready, end, workgroup (MK_SCHED_TRACE) */
+  MK_TAP_TRACE = 9,         /* [n_tasks][8] u64: start, ready, staged, computed, stored, end,
+                               workgroup, opcode (MK_SCHED_TRACE; 100 MHz clock, 0 = not reached) */
   MK_NUM_TAPS = 10
 };
 int mk_tap_offset(const mk_handle* h, int32_t tap, size_t* offset, size_t* bytes);

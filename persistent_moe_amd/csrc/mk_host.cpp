@@ -113,7 +113,7 @@ Layout make_layout(const mk_config* c, int32_t max_blocks) {
   L.off_oout = take((size_t)Lr * B * d * 4);
   L.off_pml = take((size_t)2 * B * c->n_q_heads * L.max_splits * 2 * 4);
   L.off_po = take((size_t)2 * B * c->n_q_heads * L.max_splits * hd * 4);
-  L.off_trace = take((size_t)L.max_tasks * 4 * 8);
+  L.off_trace = take((size_t)L.max_tasks * 8 * 8);
   L.total = o;
   return L;
 }
@@ -292,6 +292,7 @@ int build_plan(const mk_config* c, int B, int32_t max_blocks, const mk_sched_opt
     if (moe) {
       const int cROUTE = ctr_of(p.cl, l, MK_CTR_ROUTE);
       const int cLAYER = ctr_of(p.cl, l, MK_CTR_LAYER);
+      const bool fuse_topk = !(o.flags & MK_SCHED_SEPARATE_TOPK);
       auto emit_router = [&]() {
         wave();
         for (int i = 0; i < n_r; ++i) {
@@ -301,8 +302,13 @@ int build_plan(const mk_config* c, int B, int32_t max_blocks, const mk_sched_opt
           t.wait_ctr = cNORM;
           t.wait_target = 1;
           t.signal_ctr = ctr_of(p.cl, l, MK_CTR_ROUTER);
+          if (fuse_topk) {
+            t.flags |= MK_F_FUSE_TOPK;
+            t.aux[0] = n_r;
+          }
           T.push_back(t);
         }
+        if (fuse_topk) return;
         wave();
         mk_task t = blank(MK_OP_ROUTER_TOPK, l);
         t.flags |= MK_F_FUSE_FINALIZE;
@@ -494,6 +500,8 @@ int simulate(const mk_config* c, int B, const Plan& p, int NW, const int32_t* se
           phase[w] = 0;
         }
         if (t.signal_ctr >= 0) ctr[t.signal_ctr]++;
+        if ((t.flags & MK_F_FUSE_TOPK) && ctr[t.signal_ctr] == t.aux[0])
+          ctr[ctr_of(p.cl, t.layer, MK_CTR_ROUTE)]++;   // the last router tile runs top-k
         cursor[w] += NW;
         progress = true;
       }
@@ -744,7 +752,7 @@ int mk_tap_offset(const mk_handle* h, int32_t tap, size_t* offset, size_t* bytes
     case MK_TAP_TOPK_WEIGHTS: *offset = L.off_topw; *bytes = c.n_experts > 0 ? Lr * B * c.top_k * 4 : 0; break;
     case MK_TAP_FFN_OUT: *offset = L.off_fo; *bytes = Lr * B * d * 4; break;
     case MK_TAP_ATTN_OUT: *offset = L.off_oout; *bytes = Lr * B * d * 4; break;
-    case MK_TAP_TRACE: *offset = L.off_trace; *bytes = (size_t)(h->have_plan ? h->plan.tasks.size() : 0) * 32; break;
+    case MK_TAP_TRACE: *offset = L.off_trace; *bytes = (size_t)(h->have_plan ? h->plan.tasks.size() : 0) * 64; break;
     default: return MK_E_INVAL;
   }
   return MK_OK;

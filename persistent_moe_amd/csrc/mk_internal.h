@@ -14,7 +14,9 @@ enum {
   MK_F_FINAL = 1 << 1,      // ADD_RMSNORM: final norm (gain = final_norm)
   MK_F_MID = 1 << 2,        // ADD_RMSNORM: sequential block, pre-FFN norm
   MK_F_FUSE_FINALIZE = 1 << 3,  // ROUTER_TOPK also runs ROUTE_FINALIZE
-  MK_F_SEQ = 1 << 4,        // O_PROJ of a sequential block
+  MK_F_FUSE_TOPK = 1 << 4,  // ROUTER_GEMM: the last tile to finish runs top-k and
+                            // ROUTE_FINALIZE and signals the layer's ROUTE counter
+                            // (aux[0] = number of router tiles)
 };
 
 // ---------------------------------------------------------------- counters

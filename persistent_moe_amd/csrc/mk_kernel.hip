@@ -48,6 +48,7 @@ struct __attribute__((aligned(16))) Smem {
   float red[RED_FLOATS];
   int misc[192];
   uint64_t t_ready;   // trace: when the task's first wait was satisfied
+  uint64_t t_mark[3]; // trace: activations staged, tile computed, stores acknowledged
 };
 
 // ------------------------------------------------------------------ helpers
@@ -112,7 +113,7 @@ __device__ __forceinline__ u32x4 as_u4(f32x4 v) {
 // Wait until this wave's stores have completed.
 __device__ __forceinline__ void stores_done() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-__device__ void report(const mk_kargs& a, int code, int task, int ctr, int val, int target) {
+__device__ __noinline__ void report(const mk_kargs& a, int code, int task, int ctr, int val, int target) {
   if (atomicCAS(&a.err[0], 0, code) == 0) {
     a.err[1] = task;
     a.err[2] = ctr;
@@ -124,7 +125,7 @@ __device__ void report(const mk_kargs& a, int code, int task, int ctr, int val, 
 
 // One lane spins until ctr[idx] >= target.  false if the watchdog fired or
 // another workgroup aborted the step.
-__device__ bool spin_until(const mk_kargs& a, int idx, int target, int task) {
+__device__ __forceinline__ bool spin_until(const mk_kargs& a, int idx, int target, int task) {
   const int32_t* p = a.ctr + idx;
   if (ld_agent(p) < target) {
     const uint64_t t0 = wall_clock64();
@@ -143,7 +144,7 @@ __device__ bool spin_until(const mk_kargs& a, int idx, int target, int task) {
 }
 
 // Workgroup-wide wait; every thread must call it.  Uses misc[0].
-__device__ bool wg_wait(const mk_kargs& a, Smem& sm, int idx, int target, int task) {
+__device__ __forceinline__ bool wg_wait(const mk_kargs& a, Smem& sm, int idx, int target, int task) {
   if (threadIdx.x == 0) {
     sm.misc[0] = (idx < 0 || target <= 0) ? 1 : (int)spin_until(a, idx, target, task);
     if (a.trace && sm.t_ready == 0) sm.t_ready = wall_clock64();
@@ -153,17 +154,20 @@ __device__ bool wg_wait(const mk_kargs& a, Smem& sm, int idx, int target, int ta
   return ok;
 }
 
+__shared__ uint64_t* sm_trace_mark;   // trace: where wg_signal records its time
+
 // Workgroup-wide signal: every wave waits for its (agent-coherent) stores to
 // complete, then one lane bumps the counter.
-__device__ void wg_signal(const mk_kargs& a, int idx, int inc) {
+__device__ __forceinline__ void wg_signal(const mk_kargs& a, int idx, int inc) {
   stores_done();
   __syncthreads();
+  if (a.trace && threadIdx.x == 0 && sm_trace_mark) *sm_trace_mark = wall_clock64();
   if (threadIdx.x == 0 && idx >= 0)
     __hip_atomic_fetch_add(a.ctr + idx, inc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Claim the next item of a queue; every thread must call it.  Uses misc[1].
-__device__ int wg_claim(const mk_kargs& a, Smem& sm, int qidx) {
+__device__ __forceinline__ int wg_claim(const mk_kargs& a, Smem& sm, int qidx) {
   __syncthreads();
   if (threadIdx.x == 0) {
     sm.misc[1] = ld_agent(a.ctr + MK_CG_ABORT)
@@ -177,7 +181,7 @@ __device__ int wg_claim(const mk_kargs& a, Smem& sm, int qidx) {
 // Claimer item order: claimer c of a wave owns item c of the queue; items
 // past the number of claimers are pulled one at a time from the atomic queue
 // head.  Returns -1 when the queue is exhausted.  Every thread must call it.
-__device__ int next_item(const mk_kargs& a, Smem& sm, const mk_task& t, int n_items, int qidx, bool& first) {
+__device__ __forceinline__ int next_item(const mk_kargs& a, Smem& sm, const mk_task& t, int n_items, int qidx, bool& first) {
   if (first) {
     first = false;
     if (t.n0 < n_items) return t.n0;
@@ -329,7 +333,7 @@ struct StageArgs {
 // the other waves only meet it at the barrier.  Wave 0's own weight loads
 // have landed by the time its spin sees the counter, so its staging loads
 // do not queue behind outstanding weight traffic.  Every thread must call it.
-__device__ bool wait_and_stage(const mk_kargs& a, Smem& sm, const StageArgs& s) {
+__device__ __forceinline__ bool wait_and_stage(const mk_kargs& a, Smem& sm, const StageArgs& s) {
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
     int ok = 1;
@@ -362,6 +366,7 @@ __device__ bool wait_and_stage(const mk_kargs& a, Smem& sm, const StageArgs& s) 
     }
   }
   __syncthreads();
+  if (a.trace && threadIdx.x == 0 && sm.t_mark[0] == 0) sm.t_mark[0] = wall_clock64();
   return sm.misc[0] != 0;
 }
 
@@ -382,52 +387,51 @@ __device__ bool gemv_run(const mk_kargs& a, Smem& sm, const GemvArgs& g, const S
       if (grp + 3 < ng) Bt.load(g, grp + 3);
     }
   }
+  if (a.trace && threadIdx.x == 0 && sm.t_mark[1] == 0) sm.t_mark[1] = wall_clock64();
   return true;
 }
 
+// One rows-per-wave choice per (batch rows, K chunks): the largest the
+// register budget allows (2 row groups of RPW x KCH 16-byte loads per lane
+// and RPW x NB accumulators).  Rows past the tile are masked.
 template <int NB, int KCH>
-__device__ bool gemv_rpw(const mk_kargs& a, Smem& sm, const GemvArgs& g, const StageArgs& s, int rpw) {
-  // register budget: 2 * RPW * KCH uint4 weights and RPW * NB accumulators
+__device__ __forceinline__ bool gemv_k2(const mk_kargs& a, Smem& sm, const GemvArgs& g, const StageArgs& s) {
   constexpr int WBUD = NB == 1 ? 16 : 8;
   constexpr int RMAX_W = (WBUD / KCH) < 1 ? 1 : (WBUD / KCH);
   constexpr int RMAX_A = 16 / NB < 1 ? 1 : 16 / NB;
-  constexpr int RMAX = RMAX_W < RMAX_A ? RMAX_W : RMAX_A;
-  if (rpw >= 8 && RMAX >= 8) return gemv_run<NB, KCH, (RMAX >= 8 ? 8 : 1)>(a, sm, g, s);
-  if (rpw >= 4 && RMAX >= 4) return gemv_run<NB, KCH, (RMAX >= 4 ? 4 : 1)>(a, sm, g, s);
-  if (rpw >= 2 && RMAX >= 2) return gemv_run<NB, KCH, (RMAX >= 2 ? 2 : 1)>(a, sm, g, s);
-  return gemv_run<NB, KCH, 1>(a, sm, g, s);
+  constexpr int R0 = RMAX_W < RMAX_A ? RMAX_W : RMAX_A;
+  constexpr int RPW = R0 >= 8 ? 8 : R0 >= 4 ? 4 : R0 >= 2 ? 2 : 1;
+  return gemv_run<NB, KCH, RPW>(a, sm, g, s);
 }
 
 template <int NB>
-__device__ bool gemv_k(const mk_kargs& a, Smem& sm, const GemvArgs& g, const StageArgs& s, int rpw) {
+__device__ __forceinline__ bool gemv_nb(const mk_kargs& a, Smem& sm, const GemvArgs& g, const StageArgs& s) {
   const int kch = (g.K + 511) / 512;
-  if (kch <= 1) return gemv_rpw<NB, 1>(a, sm, g, s, rpw);
-  if (kch <= 2) return gemv_rpw<NB, 2>(a, sm, g, s, rpw);
-  if (kch <= 4) return gemv_rpw<NB, 4>(a, sm, g, s, rpw);
-  if (kch <= 8) return gemv_rpw<NB, 8>(a, sm, g, s, rpw);
-  return gemv_rpw<NB, 16>(a, sm, g, s, rpw);
+  if (kch <= 1) return gemv_k2<NB, 1>(a, sm, g, s);
+  if (kch <= 2) return gemv_k2<NB, 2>(a, sm, g, s);
+  if (kch <= 4) return gemv_k2<NB, 4>(a, sm, g, s);
+  if (kch <= 8) return gemv_k2<NB, 8>(a, sm, g, s);
+  return gemv_k2<NB, 16>(a, sm, g, s);
 }
 
-// Runs one GEMV tile: prefetch, wait, stage x, multiply.  Returns false if
-// the step was aborted while waiting.
-__device__ bool gemv(const mk_kargs& a, Smem& sm, const GemvArgs& g, const StageArgs& s) {
-  const int rows_per_wave = (g.nrows + MK_WAVES - 1) / MK_WAVES;
-  const int rpw = rows_per_wave >= 8 ? 8 : rows_per_wave >= 4 ? 4 : rows_per_wave >= 2 ? 2 : 1;
-  if (g.nb <= 1) return gemv_k<1>(a, sm, g, s, rpw);
-  if (g.nb <= 2) return gemv_k<2>(a, sm, g, s, rpw);
-  if (g.nb <= 4) return gemv_k<4>(a, sm, g, s, rpw);
-  return gemv_k<8>(a, sm, g, s, rpw);
+// Runs one GEMV tile: prefetch, wait, stage x, multiply.  false if the step
+// was aborted while waiting.
+__device__ __forceinline__ bool gemv(const mk_kargs& a, Smem& sm, const GemvArgs& g, const StageArgs& s) {
+  if (g.nb <= 1) return gemv_nb<1>(a, sm, g, s);
+  if (g.nb <= 2) return gemv_nb<2>(a, sm, g, s);
+  if (g.nb <= 4) return gemv_nb<4>(a, sm, g, s);
+  return gemv_nb<8>(a, sm, g, s);
 }
 
 // ------------------------------------------------------------- ADD_RMSNORM
 // x_l = x_{l-1} + sum_g O-proj partial_g + sum_j w_j Y_j (parallel block), or
 // the embedding row at layer 0; xn_l = x_l / sqrt(mean(x_l^2) + eps) * gain.
-// All 512 threads take 4-element chunks of every batch row (d <= 4096), with
-// every source load issued before any is used.  The MoE combine (the
-// gate-weighted sum of the routed expert outputs, in top-k order) is folded
-// into this task.
-__device__ __noinline__ void op_add_rmsnorm(const mk_kargs& a, Smem& sm, const mk_task& t, int ti) {
-  if (!wg_wait(a, sm, t.wait_ctr, t.wait_target, ti)) return;
+// All 512 threads take 4-element chunks of a batch row (rows in turn), with
+// the ~Hkv + k + 1 source loads of a chunk issued together.  x is kept in
+// LDS between the two passes.  The MoE combine (the gate-weighted sum of the
+// routed expert outputs, in top-k order) is folded into this task.
+__device__ __forceinline__ bool op_add_rmsnorm(const mk_kargs& a, Smem& sm, const mk_task& t, int ti) {
+  if (!wg_wait(a, sm, t.wait_ctr, t.wait_target, ti)) return false;
   const int l = t.layer, d = a.d, B = a.B, nv = d >> 2, K = a.topk;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const bool mid = t.flags & MK_F_MID;
@@ -435,8 +439,9 @@ __device__ __noinline__ void op_add_rmsnorm(const mk_kargs& a, Smem& sm, const m
   const bool emb = t.flags & MK_F_EMBED;
   const bool moe_in = !emb && !mid && a.parallel && a.E > 0;
   const int lp = l - 1;
+  const int lx = mid ? l : lp;     // layer whose attention output is added
   // gate weights and rows of the routed outputs of the previous layer
-  int* srow = sm.misc + 64;                     // [B*K]
+  int* srow = sm.misc + 64;                              // [B*K]
   float* sw = reinterpret_cast<float*>(sm.misc + 128);   // [B*K]
   if (moe_in) {
     const int32_t* meta = a.moe + (long)lp * a.moe_stride;
@@ -450,131 +455,100 @@ __device__ __noinline__ void op_add_rmsnorm(const mk_kargs& a, Smem& sm, const m
   const uint16_t* gain = fin ? a.final_norm : (mid ? a.layers[l].ffn_norm : a.layers[l].attn_norm);
   float* xdst = mid ? a.xmid + (long)l * B * d : a.x + (long)l * B * d;
   float* xndst = mid ? a.xn2 + (long)l * B * d : a.xn + (long)l * B * d;
-  f32x4 v[NBMAX][2];
-  float ss[NBMAX];
-#pragma unroll
-  for (int b = 0; b < NBMAX; ++b) {
-    ss[b] = 0.f;
-#pragma unroll
-    for (int u = 0; u < 2; ++u) v[b][u] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  }
-#pragma unroll
-  for (int b = 0; b < NBMAX; ++b) {
-    if (b < B && a.seq_lens[b] > 0) {
-      int tok = 0;
-      if (emb) {
-        tok = a.tokens[b];
-        if (tok < 0 || tok >= a.V) {
-          if (tid == 0) report(a, MK_E_DEVICE, ti, -1, tok, a.V);
-          tok = 0;
-        }
-        if (tid == 0 && a.seq_lens[b] > a.max_blocks * a.page)
-          report(a, MK_E_DEVICE, ti, -5, a.seq_lens[b], a.max_blocks * a.page);
+  float* red = sm.red;      // [MK_WAVES][NBMAX] partial sums of squares
+  float* xv = sm.xs;        // [B][d] the new residual rows
+#pragma unroll 1
+  for (int b = 0; b < B; ++b) {
+    const bool live = a.seq_lens[b] > 0;
+    int tok = 0;
+    if (emb && live) {
+      tok = a.tokens[b];
+      if (tok < 0 || tok >= a.V) {
+        if (tid == 0) report(a, MK_E_DEVICE, ti, -1, tok, a.V);
+        tok = 0;
       }
+      if (tid == 0 && a.seq_lens[b] > a.max_blocks * a.page)
+        report(a, MK_E_DEVICE, ti, -5, a.seq_lens[b], a.max_blocks * a.page);
+    }
+    float ss = 0.f;
+#pragma unroll 1
+    for (int c = tid; c < nv; c += MK_THREADS) {
+      const int off = c * 16;   // byte offset of the chunk in a row
+      f32x4 acc = (f32x4){0.f, 0.f, 0.f, 0.f};
+      if (!live) {
+      } else if (emb) {
+        const uint2 e = *reinterpret_cast<const uint2*>(a.embed + (long)tok * d + c * 4);
+        acc = (f32x4){bf_lo(e.x), bf_hi(e.x), bf_lo(e.y), bf_hi(e.y)};
+      } else if (mid || moe_in) {
+        u32x4 og[8], ym[8];
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int c = tid + u * MK_THREADS;
-        if (c >= nv) continue;
-        const int off = c * 16;   // byte offset of the chunk in a row
-        f32x4 acc;
-        if (emb) {
-          const uint2 e = *reinterpret_cast<const uint2*>(a.embed + (long)tok * d + c * 4);
-          acc = (f32x4){bf_lo(e.x), bf_hi(e.x), bf_lo(e.y), bf_hi(e.y)};
-        } else if (mid || moe_in) {
-          const int lx = mid ? l : lp;     // layer whose attention output is added
-          f32x4 o = (f32x4){0.f, 0.f, 0.f, 0.f};
-          f32x4 og[8];
+        for (int g = 0; g < 8; ++g)
+          if (g < a.Hkv) og[g] = ldc16(a.opart + (((long)lx * a.Hkv + g) * B + b) * d, off);
+        if (moe_in) {
 #pragma unroll
-          for (int g = 0; g < 8; ++g)
-            if (g < a.Hkv) og[g] = as_f4(ldc16(a.opart + (((long)lx * a.Hkv + g) * B + b) * d, off));
-          f32x4 ym[8];
-          if (moe_in) {
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-              if (j < K)
-                ym[j] = as_f4(ldc16(a.Y + ((long)lp * a.bk + __builtin_amdgcn_readfirstlane(srow[b * K + j])) * d,
-                                    off));
-          }
-          const f32x4 xp = as_f4(ldc16(a.x + ((long)lx * B + b) * d, off));
-#pragma unroll
-          for (int g = 0; g < 8; ++g)
-            if (g < a.Hkv) o += og[g];
-          stc16(a.oout + ((long)lx * B + b) * d, off, as_u4(o));
-          acc = xp + o;
-          if (moe_in) {
-            f32x4 m = (f32x4){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-              if (j < K) m += sw[b * K + j] * ym[j];
-            stc16(a.fo + ((long)lp * B + b) * d, off, as_u4(m));
-            acc += m;
-          }
-        } else {
-          // sequential block: x_l = x_mid + FFN output
-          acc = as_f4(ldc16(a.xmid + ((long)lp * B + b) * d, off)) +
-                as_f4(ldc16(a.fo + ((long)lp * B + b) * d, off));
+          for (int j = 0; j < 8; ++j)
+            if (j < K)
+              ym[j] = ldc16(a.Y + ((long)lp * a.bk + __builtin_amdgcn_readfirstlane(srow[b * K + j])) * d, off);
         }
-        stc16(xdst + (long)b * d, off, as_u4(acc));
-        v[b][u] = acc;
-        ss[b] += acc.x * acc.x + acc.y * acc.y + acc.z * acc.z + acc.w * acc.w;
-      }
-    }
-  }
-  float* red = sm.red;
+        const f32x4 xp = as_f4(ldc16(a.x + ((long)lx * B + b) * d, off));
+        f32x4 o = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int b = 0; b < NBMAX; ++b) {
-    if (b < B) {
-      const float r = wave_sum(ss[b]);
-      if (lane == 0) red[wave * NBMAX + b] = r;
+        for (int g = 0; g < 8; ++g)
+          if (g < a.Hkv) o += as_f4(og[g]);
+        stc16(a.oout + ((long)lx * B + b) * d, off, as_u4(o));
+        acc = xp + o;
+        if (moe_in) {
+          f32x4 m = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            if (j < K) m += sw[b * K + j] * as_f4(ym[j]);
+          stc16(a.fo + ((long)lp * B + b) * d, off, as_u4(m));
+          acc += m;
+        }
+      } else {
+        // sequential block: x_l = x_mid + FFN output
+        acc = as_f4(ldc16(a.xmid + ((long)lp * B + b) * d, off)) + as_f4(ldc16(a.fo + ((long)lp * B + b) * d, off));
+      }
+      stc16(xdst + (long)b * d, off, as_u4(acc));
+      *reinterpret_cast<f32x4*>(xv + b * d + c * 4) = acc;
+      ss += acc.x * acc.x + acc.y * acc.y + acc.z * acc.z + acc.w * acc.w;
     }
+    ss = wave_sum(ss);
+    if (lane == 0) red[wave * NBMAX + b] = ss;
   }
   __syncthreads();
-#pragma unroll
-  for (int b = 0; b < NBMAX; ++b) {
-    if (b >= B) continue;
+#pragma unroll 1
+  for (int b = 0; b < B; ++b) {
     float tot = 0.f;
 #pragma unroll
     for (int w = 0; w < MK_WAVES; ++w) tot += red[w * NBMAX + b];
     const float r = 1.0f / sqrtf(tot / (float)d + a.eps);
-    const bool live = a.seq_lens[b] > 0;
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int c = tid + u * MK_THREADS;
-      if (c >= nv) continue;
+#pragma unroll 1
+    for (int c = tid; c < nv; c += MK_THREADS) {
       const uint2 gg = *reinterpret_cast<const uint2*>(gain + c * 4);
       const f32x4 gv = (f32x4){bf_lo(gg.x), bf_hi(gg.x), bf_lo(gg.y), bf_hi(gg.y)};
-      const f32x4 out = live ? v[b][u] * r * gv : (f32x4){0.f, 0.f, 0.f, 0.f};
-      stc16(xndst + (long)b * d, c * 16, as_u4(out));
-      if (!live) stc16(xdst + (long)b * d, c * 16, as_u4(out));
+      const f32x4 xb = *reinterpret_cast<const f32x4*>(xv + b * d + c * 4);
+      stc16(xndst + (long)b * d, c * 16, as_u4(xb * r * gv));
     }
   }
   wg_signal(a, t.signal_ctr, 1);
+  return true;
 }
 
-// ---------------------------------------------------------------- QKV_PROJ
-// Tile = rotation pairs [n0, n1) over all heads (pair p of head h is rows
-// h*hd + p and h*hd + p + hd/2).  Epilogue: RoPE (rotate-half, angle
+// ------------------------------------------------------------ epilogues
+// QKV_PROJ: tile = rotation pairs [n0, n1) over all heads (pair p of head h
+// is rows h*hd + p and h*hd + p + hd/2).  RoPE (rotate-half, angle
 // pos * theta^(-2i/hd) in double) on q and k; k and v rounded to bf16 and
 // written to the sequence's page at its position.
-__device__ __noinline__ void op_qkv(const mk_kargs& a, Smem& sm, const mk_task& t, int ti) {
+__device__ __forceinline__ void epi_qkv(const mk_kargs& a, Smem& sm, const mk_task& t, int ti) {
   const int l = t.layer, hd = a.hd, half = hd / 2, B = a.B;
   const int np = t.n1 - t.n0;
   const int rows = (a.Hq + 2 * a.Hkv) * hd;
-  GemvArgs g;
-  g.base = a.layers[l].w_qkv; g.ldw = a.d; g.r0 = t.n0; g.nrows = 2 * np; g.K = a.d;
-  g.mode = ROW_ROPE_PAIRS; g.half = half; g.hd = hd; g.xstride = a.d; g.nb = B;
-  g.out = nullptr; g.ob = 0;
-  StageArgs s;
-  s.base = a.xn + (long)l * B * a.d; s.ld = a.d; s.map = nullptr; s.map0 = 0; s.nb = B; s.K = a.d;
-  s.wait_idx = t.wait_ctr; s.wait_target = t.wait_target; s.task = ti;
-  if (!gemv(a, sm, g, s)) return;
-  __syncthreads();
   uint16_t* kpool = a.layers[l].k;
   uint16_t* vpool = a.layers[l].v;
   for (int idx = threadIdx.x; idx < np * B; idx += MK_THREADS) {
     const int p = idx / B, b = idx - p * B;
-    const int sl = a.seq_lens[b];
-    if (sl <= 0) continue;
+    if (a.seq_lens[b] <= 0) continue;
     const int gp = t.n0 + p, head = gp / half, i = gp - head * half;
     float ya = sm.ys[(2 * p) * NBMAX + b], yb = sm.ys[(2 * p + 1) * NBMAX + b];
     const int pos = a.positions[b];
@@ -594,7 +568,7 @@ __device__ __noinline__ void op_qkv(const mk_kargs& a, Smem& sm, const mk_task& 
       const bool isk = head < a.Hq + a.Hkv;
       const int kvh = isk ? head - a.Hq : head - a.Hq - a.Hkv;
       const int blk = pos / a.page;
-      int page = (blk >= 0 && blk < a.max_blocks) ? a.block_tables[b * a.max_blocks + blk] : -1;
+      const int page = (blk >= 0 && blk < a.max_blocks) ? a.block_tables[b * a.max_blocks + blk] : -1;
       if (page < 0 || page >= a.num_pages || pos < 0) {
         report(a, MK_E_DEVICE, ti, -2, page, a.num_pages);
         continue;
@@ -604,77 +578,25 @@ __device__ __noinline__ void op_qkv(const mk_kargs& a, Smem& sm, const mk_task& 
       stc(dst + i + half, f_to_bf16(yb));
     }
   }
-  wg_signal(a, t.signal_ctr, 1);
 }
 
-// ------------------------------------------------------ plain GEMV opcodes
-// ROUTER_GEMM, O_PROJ, FFN_DOWN and LM_HEAD: rows [n0, n1) of one matrix
-// times staged activation rows, results stored to global memory.
-__device__ __noinline__ void op_plain_gemv(const mk_kargs& a, Smem& sm, const mk_task& t, int ti) {
-  const int l = t.layer, B = a.B;
-  GemvArgs g;
-  StageArgs s;
-  g.r0 = t.n0; g.nrows = t.n1 - t.n0; g.mode = ROW_PLAIN; g.half = 0; g.hd = a.hd; g.nb = B;
-  s.map = nullptr; s.map0 = 0; s.nb = B; s.wait_idx = t.wait_ctr; s.wait_target = t.wait_target; s.task = ti;
-  switch (t.op) {
-    case MK_OP_ROUTER_GEMM:
-      g.base = a.layers[l].w_router; g.ldw = a.d; g.K = a.d;
-      g.out = a.rlog + (long)l * B * a.E + t.n0; g.ob = a.E;
-      s.base = a.xn + (long)l * B * a.d; s.ld = a.d; s.K = a.d;
-      break;
-    case MK_OP_O_PROJ: {
-      const int gd = a.G * a.hd, grp = t.group;
-      g.base = a.layers[l].w_o + (long)grp * gd; g.ldw = (long)a.Hq * a.hd; g.K = gd;
-      g.out = a.opart + (((long)l * a.Hkv + grp) * B) * a.d + t.n0; g.ob = a.d;
-      s.base = a.attn + (long)l * B * a.Hq * a.hd + (long)grp * gd; s.ld = (long)a.Hq * a.hd; s.K = gd;
-      break;
-    }
-    case MK_OP_FFN_DOWN:
-      g.base = a.layers[l].w_down; g.ldw = a.F; g.K = a.F;
-      g.out = a.fo + (long)l * B * a.d + t.n0; g.ob = a.d;
-      s.base = a.fh + (long)l * B * a.F; s.ld = a.F; s.K = a.F;
-      break;
-    default:  // MK_OP_LM_HEAD
-      g.base = a.lm_head; g.ldw = a.d; g.K = a.d;
-      g.out = a.logits + t.n0; g.ob = a.V;
-      s.base = a.xn + (long)a.L * B * a.d; s.ld = a.d; s.K = a.d;
-      break;
+// SiLU-and-multiply epilogue of the gate/up tiles: out[j][p] = silu(g) * u
+// from the paired tile rows 2p (gate) and 2p+1 (up).
+__device__ __forceinline__ void epi_swiglu(Smem& sm, int np, int nb, float* out, long ob) {
+  for (int idx = threadIdx.x; idx < np * nb; idx += MK_THREADS) {
+    const int p = idx / nb, j = idx - p * nb;
+    const float gv = sm.ys[(2 * p) * NBMAX + j], uv = sm.ys[(2 * p + 1) * NBMAX + j];
+    stc(out + (long)j * ob + p, silu(gv) * uv);
   }
-  g.xstride = s.K;
-  if (!gemv(a, sm, g, s)) return;
-  wg_signal(a, t.signal_ctr, 1);
-}
-
-// ---------------------------------------------------------- FFN_UPGATE_ACT
-// Dense SwiGLU gate/up tile over pairs [n0, n1): h_i = silu(gate_i . x) * (up_i . x).
-__device__ __noinline__ void op_ffn_upgate(const mk_kargs& a, Smem& sm, const mk_task& t, int ti) {
-  const int l = t.layer, B = a.B, np = t.n1 - t.n0;
-  GemvArgs g;
-  g.base = a.layers[l].w_upgate; g.ldw = a.d; g.r0 = t.n0; g.nrows = 2 * np; g.K = a.d;
-  g.mode = ROW_GATE_UP; g.half = a.F; g.hd = a.hd; g.xstride = a.d; g.nb = B; g.out = nullptr; g.ob = 0;
-  StageArgs s;
-  s.base = (a.parallel ? a.xn : a.xn2) + (long)l * B * a.d; s.ld = a.d; s.map = nullptr; s.map0 = 0;
-  s.nb = B; s.K = a.d; s.wait_idx = t.wait_ctr; s.wait_target = t.wait_target; s.task = ti;
-  if (!gemv(a, sm, g, s)) return;
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < np * B; idx += MK_THREADS) {
-    const int p = idx / B, b = idx - p * B;
-    const float gv = sm.ys[(2 * p) * NBMAX + b], uv = sm.ys[(2 * p + 1) * NBMAX + b];
-    stc(a.fh + ((long)l * B + b) * a.F + t.n0 + p, silu(gv) * uv);
-  }
-  wg_signal(a, t.signal_ctr, 1);
 }
 
 // ---------------------------------------------------------- ROUTER_TOPK
 // Per token: top-k router logits (ties to the lower expert id); gate weights
 // are the softmax probabilities of the selected experts renormalised to sum
-// to 1, i.e. exp(r_j - r_max) / sum over the selected.  With
-// MK_F_FUSE_FINALIZE it then runs ROUTE_FINALIZE.
-__device__ void route_finalize(const mk_kargs& a, Smem& sm, int l);
-
-__device__ __noinline__ void op_router_topk(const mk_kargs& a, Smem& sm, const mk_task& t, int ti) {
-  if (!wg_wait(a, sm, t.wait_ctr, t.wait_target, ti)) return;
-  const int l = t.layer, B = a.B, E = a.E, K = a.topk;
+// to 1, i.e. exp(r_j - r_max) / sum over the selected.  One wave per token;
+// leaves the selected ids in misc[64 + b*k + j] for ROUTE_FINALIZE.
+__device__ __forceinline__ void router_topk(const mk_kargs& a, Smem& sm, int l) {
+  const int B = a.B, E = a.E, K = a.topk;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   for (int b = wave; b < B; b += MK_WAVES) {
     float v[4];
@@ -715,8 +637,6 @@ __device__ __noinline__ void op_router_topk(const mk_kargs& a, Smem& sm, const m
     }
   }
   __syncthreads();
-  if (t.flags & MK_F_FUSE_FINALIZE) route_finalize(a, sm, l);
-  wg_signal(a, t.signal_ctr, 1);
 }
 
 // ---------------------------------------------------------- ROUTE_FINALIZE
@@ -725,7 +645,7 @@ __device__ __noinline__ void op_router_topk(const mk_kargs& a, Smem& sm, const m
 // routed row.  Writes the active expert list (ascending ids), each expert's
 // first row, the token of each row, the row of each (token, slot), and the
 // lengths of the up-gate and down claim queues.  Uses misc[64..] ids.
-__device__ void route_finalize(const mk_kargs& a, Smem& sm, int l) {
+__device__ __forceinline__ void route_finalize(const mk_kargs& a, Smem& sm, int l) {
   if ((threadIdx.x >> 6) != 0) return;
   const int lane = threadIdx.x & 63, K = a.topk, BK = a.B * K;
   int32_t* meta = a.moe + (long)l * a.moe_stride;
@@ -768,78 +688,6 @@ __device__ void route_finalize(const mk_kargs& a, Smem& sm, int l) {
   }
 }
 
-// ---------------------------------------------------- MOE_UPGATE_ACT_DRAIN
-// Claimer: each item is (active expert, tile of ug_pairs gate/up pairs);
-// H[row][i] = silu(gate_i . xn[token(row)]) * (up_i . xn[token(row)]) for the
-// rows routed to that expert.  Bumps the expert's up-gate counter per item.
-__device__ __noinline__ void op_moe_upgate(const mk_kargs& a, Smem& sm, const mk_task& t, int ti) {
-  if (!wg_wait(a, sm, t.wait_ctr, t.wait_target, ti)) return;
-  const int l = t.layer;
-  const int32_t* meta = a.moe + (long)l * a.moe_stride;
-  const int32_t* act = meta + 4;
-  const int32_t* row_off = act + a.bk;
-  const int32_t* row_tok = row_off + a.bk + 1;
-  const int n_items = ldc(meta + 1);
-  const int qidx = layer_ctr(a, l, MK_CTR_QUG);
-  bool first = true;
-  for (;;) {
-    const int item = next_item(a, sm, t, n_items, qidx, first);
-    if (item < 0) break;
-    const int ae = item / a.ug_tiles, tt = item - ae * a.ug_tiles;
-    const int e = ldc(act + ae), r0 = ldc(row_off + ae), nr = ldc(row_off + ae + 1) - r0;
-    const int p0 = tt * a.ug_pairs;
-    const int np = min(a.ug_pairs, a.I - p0);
-    GemvArgs g;
-    g.base = a.layers[l].w_upgate + (long)e * 2 * a.I * a.d; g.ldw = a.d; g.r0 = p0; g.nrows = 2 * np;
-    g.K = a.d; g.mode = ROW_GATE_UP; g.half = a.I; g.hd = a.hd; g.xstride = a.d; g.nb = nr;
-    g.out = nullptr; g.ob = 0;
-    StageArgs s;
-    s.base = a.xn + (long)l * a.B * a.d; s.ld = a.d; s.map = row_tok; s.map0 = r0; s.nb = nr; s.K = a.d;
-    s.wait_idx = -1; s.wait_target = 0; s.task = ti;
-    if (!gemv(a, sm, g, s)) return;
-    __syncthreads();
-    for (int idx = threadIdx.x; idx < np * nr; idx += MK_THREADS) {
-      const int p = idx / nr, j = idx - p * nr;
-      const float gv = sm.ys[(2 * p) * NBMAX + j], uv = sm.ys[(2 * p + 1) * NBMAX + j];
-      stc(a.H + ((long)l * a.bk + r0 + j) * a.I + p0 + p, silu(gv) * uv);
-    }
-    wg_signal(a, layer_ctr(a, l, a.cl.ug + ae), 1);
-  }
-  wg_signal(a, t.signal_ctr, 1);
-}
-
-// ------------------------------------------------------- MOE_DOWN_DRAIN
-// Claimer: each item is (active expert, tile of dn_rows output rows);
-// Y[row][r] = W_down[e][r] . H[row] for the expert's rows.  The weight tile
-// is loaded before the wait on the expert's up-gate counter.
-__device__ __noinline__ void op_moe_down(const mk_kargs& a, Smem& sm, const mk_task& t, int ti) {
-  if (!wg_wait(a, sm, t.wait_ctr, t.wait_target, ti)) return;
-  const int l = t.layer;
-  const int32_t* meta = a.moe + (long)l * a.moe_stride;
-  const int32_t* act = meta + 4;
-  const int32_t* row_off = act + a.bk;
-  const int n_items = ldc(meta + 2);
-  const int qidx = layer_ctr(a, l, MK_CTR_QDN);
-  bool first = true;
-  for (;;) {
-    const int item = next_item(a, sm, t, n_items, qidx, first);
-    if (item < 0) break;
-    const int ae = item / a.dn_tiles, tt = item - ae * a.dn_tiles;
-    const int e = ldc(act + ae), r0 = ldc(row_off + ae), nr = ldc(row_off + ae + 1) - r0;
-    const int n0 = tt * a.dn_rows;
-    const int nrow = min(a.dn_rows, a.d - n0);
-    GemvArgs g;
-    g.base = a.layers[l].w_down + (long)e * a.d * a.I; g.ldw = a.I; g.r0 = n0; g.nrows = nrow; g.K = a.I;
-    g.mode = ROW_PLAIN; g.half = 0; g.hd = a.hd; g.xstride = a.I; g.nb = nr;
-    g.out = a.Y + ((long)l * a.bk + r0) * a.d + n0; g.ob = a.d;
-    StageArgs s;
-    s.base = a.H + ((long)l * a.bk + r0) * a.I; s.ld = a.I; s.map = nullptr; s.map0 = 0; s.nb = nr;
-    s.K = a.I; s.wait_idx = layer_ctr(a, l, a.cl.ug + ae); s.wait_target = a.ug_tiles; s.task = ti;
-    if (!gemv(a, sm, g, s)) return;
-  }
-  wg_signal(a, t.signal_ctr, 1);
-}
-
 // ---------------------------------------------------------- attention split
 // Keys [p0, p1) of sequence b, KV group g: scores s_j = q_h . K_j / sqrt(hd)
 // for the G query heads of the group, then m = max s, p = exp(s - m),
@@ -851,7 +699,7 @@ __device__ __noinline__ void op_moe_down(const mk_kargs& a, Smem& sm, const mk_t
 constexpr int ATT_CH = 4;   // wave loads per chunk
 
 template <int HD>
-__device__ bool attn_split(const mk_kargs& a, Smem& sm, int l, int b, int g, int s, int p0, int p1, int ti,
+__device__ __forceinline__ bool attn_split(const mk_kargs& a, Smem& sm, int l, int b, int g, int s, int p0, int p1, int ti,
                            int wait_idx, int wait_target) {
   constexpr int LPR = HD / 8;
   constexpr int PPW = 64 / LPR;
@@ -1036,7 +884,7 @@ __device__ bool attn_split(const mk_kargs& a, Smem& sm, int l, int b, int g, int
   return true;
 }
 
-__device__ bool attn_item(const mk_kargs& a, Smem& sm, int l, int b, int g, int s, int ti, int wait_idx,
+__device__ __forceinline__ bool attn_item(const mk_kargs& a, Smem& sm, int l, int b, int g, int s, int ti, int wait_idx,
                           int wait_target) {
   const int sl = live_len(a, b);
   const int kv = visible_keys(a, l, sl);
@@ -1047,55 +895,14 @@ __device__ bool attn_item(const mk_kargs& a, Smem& sm, int l, int b, int g, int 
   return attn_split<64>(a, sm, l, b, g, s, p0, p1, ti, wait_idx, wait_target);
 }
 
-// ATTN_DRAIN: drains the layer's (batch, group, split) items, batch-major.
-// The item count follows from seq_lens alone, so a claimer with nothing to
-// do returns without waiting; the first item's K/V loads are issued before
-// the wait on the QKV tiles.
-__device__ __noinline__ void op_attn_drain(const mk_kargs& a, Smem& sm, const mk_task& t, int ti) {
-  const int l = t.layer;
-  int n_items = 0;
-  for (int b = 0; b < a.B; ++b) n_items += n_splits(a, l, b) * a.Hkv;
-  const int qidx = layer_ctr(a, l, MK_CTR_QATTN);
-  bool first = true;
-  int wait_idx = t.wait_ctr, wait_target = t.wait_target;
-  for (;;) {
-    int item = next_item(a, sm, t, n_items, qidx, first);
-    if (item < 0) break;
-    int b = 0, g = 0, s = -1;
-    for (; b < a.B; ++b) {
-      const int ns = n_splits(a, l, b);
-      const int cnt = ns * a.Hkv;
-      if (item < cnt) { g = item / ns; s = item - g * ns; break; }
-      item -= cnt;
-    }
-    if (s < 0) break;
-    if (!attn_item(a, sm, l, b, g, s, ti, wait_idx, wait_target)) return;
-    wait_idx = -1;   // satisfied for every later item
-    wg_signal(a, layer_ctr(a, l, a.cl.attn + b * a.Hkv + g), 1);
-  }
-  wg_signal(a, t.signal_ctr, 1);
-}
-
-// ATTN_DECODE: one statically placed split.
-__device__ __noinline__ void op_attn_decode(const mk_kargs& a, Smem& sm, const mk_task& t, int ti) {
-  const int l = t.layer;
-  if (t.split < n_splits(a, l, t.batch)) {
-    if (!attn_item(a, sm, l, t.batch, t.group, t.split, ti, t.wait_ctr, t.wait_target)) return;
-  } else if (!wg_wait(a, sm, t.wait_ctr, t.wait_target, ti)) {
-    return;
-  }
-  wg_signal(a, layer_ctr(a, l, a.cl.attn + t.batch * a.Hkv + t.group), 1);
-  wg_signal(a, t.signal_ctr, 1);
-}
-
 // ATTN_COMBINE for (batch b, group g): M = max_s m_s;
 // o = sum_s e^(m_s - M) o_s / sum_s e^(m_s - M) l_s.  Wave h computes head
 // h's weights; then every thread accumulates 4 dims of one head over the
 // splits with its loads issued 8 splits at a time.
-__device__ __noinline__ void op_attn_combine(const mk_kargs& a, Smem& sm, const mk_task& t, int ti) {
+__device__ __forceinline__ bool op_attn_combine(const mk_kargs& a, Smem& sm, const mk_task& t, int ti) {
   const int l = t.layer, b = t.batch, g = t.group, G = a.G, hd = a.hd;
   const int ns = n_splits(a, l, b);
-  if (!wg_wait(a, sm, t.wait_ctr, ns, ti)) return;
+  if (!wg_wait(a, sm, t.wait_ctr, ns, ti)) return false;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   float* out = a.attn + ((long)l * a.B + b) * a.Hq * hd;
   const long hstride = (long)a.max_splits;
@@ -1148,67 +955,321 @@ __device__ __noinline__ void op_attn_combine(const mk_kargs& a, Smem& sm, const 
     stc16(out, ((g * G + h) * hd + cq * 4) * 4, as_u4(r));
   }
   wg_signal(a, t.signal_ctr, 1);
+  return true;
 }
 
 // ------------------------------------------------------------------ kernel
-extern "C" __global__ void __launch_bounds__(MK_THREADS, 1) mk_persistent(mk_kargs a, int final_launch) {
+// The persistent loop walks work units: a static task is one unit; a
+// claimer task yields one unit per queue item it owns or claims.  Every GEMV
+// opcode only fills a GemvArgs/StageArgs pair before the single GEMV site
+// below and then runs its epilogue, so the whole step is one function with
+// no calls (a call would save and restore ~100 callee-saved VGPRs per wave
+// on every task).
+enum { U_NONE = 0, U_GEMV = 1 };
+
+__device__ __forceinline__ bool is_claimer(int op) {
+  return op == MK_OP_ATTN_DRAIN || op == MK_OP_MOE_UPGATE_ACT_DRAIN || op == MK_OP_MOE_DOWN_DRAIN;
+}
+
+// The argument block is copied to LDS once and read through a pointer the
+// compiler cannot see through, once per work unit.  Otherwise loop-invariant
+// code motion hoists dozens of argument-derived values to the kernel entry,
+// where they no longer fit in registers and are spilled to scratch.
+__device__ __forceinline__ const mk_kargs& launder(const mk_kargs* p) {
+  uint32_t v = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const mk_kargs*)p;
+  asm volatile("" : "+v"(v));
+  return *(const mk_kargs*)(__attribute__((address_space(3))) const mk_kargs*)(uintptr_t)v;
+}
+
+extern "C" __global__ void __launch_bounds__(MK_THREADS, 1) mk_persistent(mk_kargs a_arg, int final_launch) {
   __shared__ Smem sm;
-  for (int ti = a.task_begin + (int)blockIdx.x; ti < a.task_end; ti += (int)gridDim.x) {
-    const mk_task t = a.tasks[ti];
-    uint64_t t_start = 0;
-    if (a.trace && threadIdx.x == 0) {
-      t_start = wall_clock64();
-      sm.t_ready = 0;
-    }
-    switch (t.op) {
-      case MK_OP_ADD_RMSNORM: op_add_rmsnorm(a, sm, t, ti); break;
-      case MK_OP_QKV_PROJ: op_qkv(a, sm, t, ti); break;
-      case MK_OP_ROUTER_GEMM:
-      case MK_OP_O_PROJ:
-      case MK_OP_FFN_DOWN:
-      case MK_OP_LM_HEAD: op_plain_gemv(a, sm, t, ti); break;
-      case MK_OP_FFN_UPGATE_ACT: op_ffn_upgate(a, sm, t, ti); break;
-      case MK_OP_ROUTER_TOPK: op_router_topk(a, sm, t, ti); break;
-      case MK_OP_ROUTE_FINALIZE:
-        if (wg_wait(a, sm, t.wait_ctr, t.wait_target, ti)) {
-          for (int i = threadIdx.x; i < a.B * a.topk; i += MK_THREADS) {
-            const int b = i / a.topk;
-            sm.misc[64 + i] = a.seq_lens[b] > 0 ? ldc(a.topi + ((long)t.layer * a.B) * a.topk + i) : -1;
-          }
-          __syncthreads();
-          route_finalize(a, sm, t.layer);
-          wg_signal(a, t.signal_ctr, 1);
-        }
-        break;
-      case MK_OP_MOE_UPGATE_ACT_DRAIN: op_moe_upgate(a, sm, t, ti); break;
-      case MK_OP_MOE_DOWN_DRAIN: op_moe_down(a, sm, t, ti); break;
-      case MK_OP_ATTN_DRAIN: op_attn_drain(a, sm, t, ti); break;
-      case MK_OP_ATTN_DECODE: op_attn_decode(a, sm, t, ti); break;
-      case MK_OP_ATTN_COMBINE: op_attn_combine(a, sm, t, ti); break;
-      default:
-        if (threadIdx.x == 0) report(a, MK_E_INVAL, ti, -4, t.op, MK_NUM_OPCODES);
-        break;
-    }
+  __shared__ mk_kargs ka;
+  const int tid = threadIdx.x;
+  {
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(&a_arg);
+    uint32_t* dst = reinterpret_cast<uint32_t*>(&ka);
+    for (int i = tid; i < (int)(sizeof(mk_kargs) / 4); i += MK_THREADS) dst[i] = src[i];
+  }
+  int ti = a_arg.task_begin + (int)blockIdx.x;
+  const int task_end = a_arg.task_end;
+  bool claiming = false, first = false, aborted = false;
+  int n_items = 0, qidx = -1, attn_wait = -1;
+  uint64_t t_start = 0;
+  mk_task t;
+  for (;;) {
     __syncthreads();
-    if (a.trace && threadIdx.x == 0) {
-      uint64_t* tr = a.trace + (long)ti * 4;
+    const mk_kargs& a = launder(&ka);
+    int item = -1;
+    if (!claiming) {
+      if (ti >= task_end) break;
+      t = a.tasks[ti];
+      if (a.trace && tid == 0) {
+        t_start = wall_clock64();
+        sm.t_ready = 0;
+        sm.t_mark[0] = sm.t_mark[1] = sm.t_mark[2] = 0;
+        sm_trace_mark = &sm.t_mark[2];
+      }
+      if (is_claimer(t.op)) {
+        const int l = t.layer;
+        if (aborted) {
+          n_items = 0;
+        } else if (t.op == MK_OP_ATTN_DRAIN) {
+          n_items = 0;
+          for (int b = 0; b < a.B; ++b) n_items += n_splits(a, l, b) * a.Hkv;
+          qidx = layer_ctr(a, l, MK_CTR_QATTN);
+          attn_wait = t.wait_ctr;       // waited for inside the first item
+        } else {
+          if (!wg_wait(a, sm, t.wait_ctr, t.wait_target, ti)) {
+            aborted = true;
+            n_items = 0;
+          } else {
+            const int32_t* meta = a.moe + (long)l * a.moe_stride;
+            n_items = ldc(meta + (t.op == MK_OP_MOE_UPGATE_ACT_DRAIN ? 1 : 2));
+          }
+          qidx = layer_ctr(a, l, t.op == MK_OP_MOE_UPGATE_ACT_DRAIN ? MK_CTR_QUG : MK_CTR_QDN);
+        }
+        claiming = true;
+        first = true;
+      }
+    }
+    if (claiming) {
+      item = next_item(a, sm, t, n_items, qidx, first);
+      if (item < 0) {
+        claiming = false;
+        wg_signal(a, aborted ? -1 : t.signal_ctr, 1);
+        goto task_done;
+      }
+    }
+    if (aborted) goto unit_done;
+    {
+      const int l = t.layer, B = a.B;
+      GemvArgs g;
+      StageArgs st;
+      int kind = U_NONE;
+      int epi_ae = 0, epi_r0 = 0, epi_nr = 0, epi_p0 = 0, epi_np = 0;
+      g.mode = ROW_PLAIN; g.half = 0; g.hd = a.hd; g.nb = B; g.out = nullptr; g.ob = 0;
+      g.r0 = t.n0; g.nrows = t.n1 - t.n0;
+      st.map = nullptr; st.map0 = 0; st.nb = B; st.wait_idx = t.wait_ctr; st.wait_target = t.wait_target;
+      st.task = ti;
+      switch (t.op) {
+        case MK_OP_QKV_PROJ:
+          kind = U_GEMV;
+          g.base = a.layers[l].w_qkv; g.ldw = a.d; g.K = a.d; g.nrows = 2 * (t.n1 - t.n0);
+          g.mode = ROW_ROPE_PAIRS; g.half = a.hd / 2;
+          st.base = a.xn + (long)l * B * a.d; st.ld = a.d; st.K = a.d;
+          break;
+        case MK_OP_ROUTER_GEMM:
+          kind = U_GEMV;
+          g.base = a.layers[l].w_router; g.ldw = a.d; g.K = a.d;
+          g.out = a.rlog + (long)l * B * a.E + t.n0; g.ob = a.E;
+          st.base = a.xn + (long)l * B * a.d; st.ld = a.d; st.K = a.d;
+          break;
+        case MK_OP_O_PROJ: {
+          kind = U_GEMV;
+          const int gd = a.G * a.hd, grp = t.group;
+          g.base = a.layers[l].w_o + (long)grp * gd; g.ldw = (long)a.Hq * a.hd; g.K = gd;
+          g.out = a.opart + (((long)l * a.Hkv + grp) * B) * a.d + t.n0; g.ob = a.d;
+          st.base = a.attn + (long)l * B * a.Hq * a.hd + (long)grp * gd; st.ld = (long)a.Hq * a.hd; st.K = gd;
+          break;
+        }
+        case MK_OP_FFN_UPGATE_ACT:
+          kind = U_GEMV;
+          g.base = a.layers[l].w_upgate; g.ldw = a.d; g.K = a.d; g.nrows = 2 * (t.n1 - t.n0);
+          g.mode = ROW_GATE_UP; g.half = a.F;
+          st.base = (a.parallel ? a.xn : a.xn2) + (long)l * B * a.d; st.ld = a.d; st.K = a.d;
+          epi_p0 = t.n0; epi_np = t.n1 - t.n0;
+          break;
+        case MK_OP_FFN_DOWN:
+          kind = U_GEMV;
+          g.base = a.layers[l].w_down; g.ldw = a.F; g.K = a.F;
+          g.out = a.fo + (long)l * B * a.d + t.n0; g.ob = a.d;
+          st.base = a.fh + (long)l * B * a.F; st.ld = a.F; st.K = a.F;
+          break;
+        case MK_OP_LM_HEAD:
+          kind = U_GEMV;
+          g.base = a.lm_head; g.ldw = a.d; g.K = a.d;
+          g.out = a.logits + t.n0; g.ob = a.V;
+          st.base = a.xn + (long)a.L * B * a.d; st.ld = a.d; st.K = a.d;
+          break;
+        case MK_OP_MOE_UPGATE_ACT_DRAIN: {
+          // item = (active expert, tile of ug_pairs gate/up pairs) over that expert's rows
+          kind = U_GEMV;
+          const int32_t* act = a.moe + (long)l * a.moe_stride + 4;
+          const int32_t* row_off = act + a.bk;
+          const int32_t* row_tok = row_off + a.bk + 1;
+          epi_ae = item / a.ug_tiles;
+          const int tt = item - epi_ae * a.ug_tiles;
+          const int e = ldc(act + epi_ae);
+          epi_r0 = ldc(row_off + epi_ae);
+          epi_nr = ldc(row_off + epi_ae + 1) - epi_r0;
+          epi_p0 = tt * a.ug_pairs;
+          epi_np = min(a.ug_pairs, a.I - epi_p0);
+          g.base = a.layers[l].w_upgate + (long)e * 2 * a.I * a.d; g.ldw = a.d; g.r0 = epi_p0;
+          g.nrows = 2 * epi_np; g.K = a.d; g.mode = ROW_GATE_UP; g.half = a.I; g.nb = epi_nr;
+          st.base = a.xn + (long)l * B * a.d; st.ld = a.d; st.map = row_tok; st.map0 = epi_r0; st.nb = epi_nr;
+          st.K = a.d; st.wait_idx = -1;
+          break;
+        }
+        case MK_OP_MOE_DOWN_DRAIN: {
+          // item = (active expert, tile of dn_rows output rows); waits on the
+          // expert's up-gate tiles after its weights are in flight
+          kind = U_GEMV;
+          const int32_t* act = a.moe + (long)l * a.moe_stride + 4;
+          const int32_t* row_off = act + a.bk;
+          const int ae = item / a.dn_tiles, tt = item - ae * a.dn_tiles;
+          const int e = ldc(act + ae), r0 = ldc(row_off + ae), nr = ldc(row_off + ae + 1) - r0;
+          const int n0 = tt * a.dn_rows;
+          g.base = a.layers[l].w_down + (long)e * a.d * a.I; g.ldw = a.I; g.r0 = n0;
+          g.nrows = min(a.dn_rows, a.d - n0); g.K = a.I; g.nb = nr;
+          g.out = a.Y + ((long)l * a.bk + r0) * a.d + n0; g.ob = a.d;
+          st.base = a.H + ((long)l * a.bk + r0) * a.I; st.ld = a.I; st.nb = nr; st.K = a.I;
+          st.wait_idx = layer_ctr(a, l, a.cl.ug + ae); st.wait_target = a.ug_tiles;
+          break;
+        }
+        default:
+          break;
+      }
+      if (kind == U_GEMV) {
+        g.xstride = st.K;
+        if (!gemv(a, sm, g, st)) {
+          aborted = true;
+          goto unit_done;
+        }
+        switch (t.op) {
+          case MK_OP_QKV_PROJ:
+            __syncthreads();
+            epi_qkv(a, sm, t, ti);
+            wg_signal(a, t.signal_ctr, 1);
+            break;
+          case MK_OP_FFN_UPGATE_ACT:
+            __syncthreads();
+            epi_swiglu(sm, epi_np, B, a.fh + (long)l * B * a.F + epi_p0, a.F);
+            wg_signal(a, t.signal_ctr, 1);
+            break;
+          case MK_OP_MOE_UPGATE_ACT_DRAIN:
+            __syncthreads();
+            epi_swiglu(sm, epi_np, epi_nr, a.H + ((long)l * a.bk + epi_r0) * a.I + epi_p0, a.I);
+            wg_signal(a, layer_ctr(a, l, a.cl.ug + epi_ae), 1);
+            break;
+          case MK_OP_MOE_DOWN_DRAIN:
+            break;   // the claimer signals once its queue is drained
+          case MK_OP_ROUTER_GEMM:
+            if (t.flags & MK_F_FUSE_TOPK) {
+              // the last router tile to finish runs top-k and ROUTE_FINALIZE
+              stores_done();
+              __syncthreads();
+              if (tid == 0)
+                sm.misc[3] = __hip_atomic_fetch_add(a.ctr + t.signal_ctr, 1, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT) == t.aux[0] - 1;
+              __syncthreads();
+              if (sm.misc[3]) {
+                router_topk(a, sm, l);
+                route_finalize(a, sm, l);
+                wg_signal(a, layer_ctr(a, l, MK_CTR_ROUTE), 1);
+              }
+            } else {
+              wg_signal(a, t.signal_ctr, 1);
+            }
+            break;
+          default:
+            wg_signal(a, t.signal_ctr, 1);
+            break;
+        }
+        goto unit_done;
+      }
+      switch (t.op) {
+        case MK_OP_ADD_RMSNORM:
+          if (!op_add_rmsnorm(a, sm, t, ti)) aborted = true;
+          break;
+        case MK_OP_ROUTER_TOPK:
+          if (wg_wait(a, sm, t.wait_ctr, t.wait_target, ti)) {
+            router_topk(a, sm, l);
+            if (t.flags & MK_F_FUSE_FINALIZE) route_finalize(a, sm, l);
+            wg_signal(a, t.signal_ctr, 1);
+          } else {
+            aborted = true;
+          }
+          break;
+        case MK_OP_ROUTE_FINALIZE:
+          if (wg_wait(a, sm, t.wait_ctr, t.wait_target, ti)) {
+            for (int i = tid; i < B * a.topk; i += MK_THREADS) {
+              const int b = i / a.topk;
+              sm.misc[64 + i] = a.seq_lens[b] > 0 ? ldc(a.topi + ((long)l * B) * a.topk + i) : -1;
+            }
+            __syncthreads();
+            route_finalize(a, sm, l);
+            wg_signal(a, t.signal_ctr, 1);
+          } else {
+            aborted = true;
+          }
+          break;
+        case MK_OP_ATTN_DRAIN: {
+          int it = item, b = 0, gq = 0, sp = -1;
+          for (; b < B; ++b) {
+            const int ns = n_splits(a, l, b);
+            const int cnt = ns * a.Hkv;
+            if (it < cnt) { gq = it / ns; sp = it - gq * ns; break; }
+            it -= cnt;
+          }
+          if (sp >= 0) {
+            if (!attn_item(a, sm, l, b, gq, sp, ti, attn_wait, t.wait_target)) {
+              aborted = true;
+              break;
+            }
+            attn_wait = -1;   // satisfied for every later item
+            wg_signal(a, layer_ctr(a, l, a.cl.attn + b * a.Hkv + gq), 1);
+          }
+          break;
+        }
+        case MK_OP_ATTN_DECODE:
+          if (t.split < n_splits(a, l, t.batch)) {
+            if (!attn_item(a, sm, l, t.batch, t.group, t.split, ti, t.wait_ctr, t.wait_target)) {
+              aborted = true;
+              break;
+            }
+          } else if (!wg_wait(a, sm, t.wait_ctr, t.wait_target, ti)) {
+            aborted = true;
+            break;
+          }
+          wg_signal(a, layer_ctr(a, l, a.cl.attn + t.batch * a.Hkv + t.group), 1);
+          wg_signal(a, t.signal_ctr, 1);
+          break;
+        case MK_OP_ATTN_COMBINE:
+          if (!op_attn_combine(a, sm, t, ti)) aborted = true;
+          break;
+        default:
+          if (tid == 0) report(a, MK_E_INVAL, ti, -4, t.op, MK_NUM_OPCODES);
+          break;
+      }
+    }
+  unit_done:
+    if (claiming) continue;
+  task_done:
+    if (a.trace && tid == 0) {
+      uint64_t* tr = a.trace + (long)ti * 8;
       tr[0] = t_start;
       tr[1] = sm.t_ready ? sm.t_ready : t_start;
-      tr[2] = wall_clock64();
-      tr[3] = blockIdx.x;
+      tr[2] = sm.t_mark[0];
+      tr[3] = sm.t_mark[1];
+      tr[4] = sm.t_mark[2];
+      tr[5] = wall_clock64();
+      tr[6] = blockIdx.x;
+      tr[7] = t.op;
     }
+    ti += (int)gridDim.x;
   }
   // The last workgroup out clears the counters for the next launch.
   __syncthreads();
-  if (threadIdx.x == 0) {
+  const mk_kargs& a = a_arg;
+  if (tid == 0) {
     const int old = __hip_atomic_fetch_add(a.ctr + MK_CG_DONE, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     sm.misc[2] = (old == (int)gridDim.x - 1);
   }
   __syncthreads();
   if (sm.misc[2]) {
     if (final_launch) {
-      for (int i = threadIdx.x; i < a.n_ctr; i += MK_THREADS) stc(a.ctr + i, 0);
-    } else if (threadIdx.x == 0) {
+      for (int i = tid; i < a.n_ctr; i += MK_THREADS) stc(a.ctr + i, 0);
+    } else if (tid == 0) {
       stc(a.ctr + MK_CG_DONE, 0);
     }
   }

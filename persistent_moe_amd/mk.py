@@ -146,6 +146,7 @@ def make_config(model, max_batch: int) -> mk_config:
 
 MK_SCHED_UNREACHABLE_WAIT = 1
 MK_SCHED_TRACE = 2
+MK_SCHED_SEPARATE_TOPK = 4
 
 
 def make_opts(wave_order="tuned", launch_mode="persistent", attn_split=0, n_workgroups=0,

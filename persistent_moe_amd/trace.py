@@ -30,7 +30,7 @@ def load(eng) -> dict:
     """Trace of the last step of a DecodeEngine built with MK_SCHED_TRACE."""
     from . import mk
     tasks, _ = mk.mk_plan_schedule(eng.mkcfg, eng.wl.batch, eng.max_blocks, eng.opts, _n_wg(eng))
-    raw = eng.tap("trace").cpu().numpy().reshape(-1, 4)[:len(tasks)]
+    raw = eng.tap("trace").cpu().numpy().reshape(-1, 8)[:len(tasks)]
     return {"tasks": tasks, "raw": raw}
 
 
@@ -44,8 +44,9 @@ def _n_wg(eng):
 def summarize(tr: dict) -> dict:
     tasks, raw = tr["tasks"], tr["raw"].astype(np.int64)
     t0 = raw[:, 0].min()
-    start, ready, end, wg = raw[:, 0] - t0, raw[:, 1] - t0, raw[:, 2] - t0, raw[:, 3]
+    start, ready, end, wg = raw[:, 0] - t0, raw[:, 1] - t0, raw[:, 5] - t0, raw[:, 6]
     per_op = defaultdict(lambda: [0, 0.0, 0.0])
+    phases = defaultdict(lambda: [[], [], [], []])   # ready->staged, staged->computed, computed->stored, stored->end
     per_layer = defaultdict(lambda: [np.inf, 0.0])
     for i, t in enumerate(tasks):
         name = OPCODES[t.op]
@@ -53,6 +54,13 @@ def summarize(tr: dict) -> dict:
         s[0] += 1
         s[1] += (end[i] - ready[i]) * TICK_US
         s[2] += (ready[i] - start[i]) * TICK_US
+        st, cp, so = raw[i, 2], raw[i, 3], raw[i, 4]
+        if st and cp and so:
+            ph = phases[name]
+            ph[0].append((st - raw[i, 1]) * TICK_US)
+            ph[1].append((cp - st) * TICK_US)
+            ph[2].append((so - cp) * TICK_US)
+            ph[3].append((raw[i, 5] - so) * TICK_US)
         pl = per_layer[t.layer]
         pl[0] = min(pl[0], start[i] * TICK_US)
         pl[1] = max(pl[1], end[i] * TICK_US)
@@ -67,6 +75,11 @@ def summarize(tr: dict) -> dict:
                    for k, v in sorted(per_op.items(), key=lambda kv: -kv[1][1])},
         "per_layer": {int(k): {"first_start_us": round(v[0], 2), "last_end_us": round(v[1], 2)}
                       for k, v in sorted(per_layer.items())},
+        "phases_median_us": {k: {"stage": round(float(np.median(v[0])), 2),
+                                 "compute": round(float(np.median(v[1])), 2),
+                                 "store_ack": round(float(np.median(v[2])), 2),
+                                 "tail": round(float(np.median(v[3])), 2)}
+                             for k, v in phases.items() if v[0]},
     }
 
 
@@ -75,7 +88,7 @@ def chrome_trace(tr: dict, path: str) -> None:
     t0 = raw[:, 0].min()
     ev = []
     for i, t in enumerate(tasks):
-        s, r, e, w = (raw[i, 0] - t0) * TICK_US, (raw[i, 1] - t0) * TICK_US, (raw[i, 2] - t0) * TICK_US, raw[i, 3]
+        s, r, e, w = (raw[i, 0] - t0) * TICK_US, (raw[i, 1] - t0) * TICK_US, (raw[i, 5] - t0) * TICK_US, raw[i, 6]
         name = f"{OPCODES[t.op]} L{t.layer}"
         if r > s:
             ev.append({"name": "wait " + name, "ph": "X", "ts": float(s), "dur": float(r - s), "pid": 0,

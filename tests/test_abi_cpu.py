@@ -143,15 +143,24 @@ def test_signal_counts_match_wait_targets(lib):
     for model, B, mb in [(W.MOE_30B, 1, 529), (W.DENSE_1B, 1, 264), (W.TINY_MOE, 2, 6)]:
         tasks, _ = _plan(model, B, mb)
         sig = {}
+        fused = {}
         for t in tasks:
             if t.signal_ctr >= 0:
                 sig[t.signal_ctr] = sig.get(t.signal_ctr, 0) + 1
+            if t.flags & 16:           # router tile with fused top-k: one ROUTE signal per layer
+                fused[t.layer] = t.signal_ctr
+        stride = None
+        for t in tasks:
+            if t.op == mk.OPCODES.index("MOE_UPGATE_ACT_DRAIN"):
+                route = t.wait_ctr
+                if t.layer in fused:
+                    sig[route] = 1
         for t in tasks:
             if t.wait_ctr >= 0 and t.wait_target > 0 and t.op not in (8, 13, 14):
                 assert sig.get(t.wait_ctr, 0) == t.wait_target, (mk.OPCODES[t.op], t.layer)
 
 
-@pytest.mark.parametrize("order", ["tuned", "interleaved", "attention_first"])
+@pytest.mark.parametrize("order", ["tuned", "interleaved", "attention_first", "tuned-separate-topk"])
 @pytest.mark.parametrize("case", [
     ("tiny", W.TINY_MOE, 1, 5, [65], [2, 2]),
     ("moe30b", W.MOE_30B, 1, 529, [8193], [8] * 48),
@@ -161,8 +170,10 @@ def test_signal_counts_match_wait_targets(lib):
 ])
 def test_schedule_is_deadlock_free(lib, order, case):
     name, model, B, mb, sl, na = case
+    flags = mk.MK_SCHED_SEPARATE_TOPK if order.endswith("separate-topk") else 0
+    opts = mk.make_opts(order.replace("-separate-topk", ""), flags=flags)
     for nw in (256, 64, 7):
-        rc, stuck = mk.mk_plan_simulate(_cfg(model, B), B, mb, mk.make_opts(order), nw, sl, na)
+        rc, stuck = mk.mk_plan_simulate(_cfg(model, B), B, mb, opts, nw, sl, na)
         assert rc == mk.MK_OK, (name, nw, stuck)
 
 
