@@ -250,8 +250,9 @@ enum mk_tap {
   MK_TAP_TOPK_WEIGHTS = 6,  /* [L][B][k] f32                                         */
   MK_TAP_FFN_OUT = 7,       /* [L][B][d] f32 MoE (or dense FFN) output               */
   MK_TAP_ATTN_OUT = 8,      /* [L][B][d] f32 output projection (sum over groups)     */
-  MK_TAP_TRACE = 9,         /* [n_tasks][8] u64: start, ready, staged, computed, stored, end,
-                               workgroup, opcode (MK_SCHED_TRACE; 100 MHz clock, 0 = not reached) */
+  MK_TAP_TRACE = 9,         /* [n_tasks][16] u64: start, ready, marks[10] (0 staged, 1 computed,
+                               2 stored, 3..9 opcode-specific), end, workgroup, opcode, 0
+                               (MK_SCHED_TRACE; 100 MHz clock, 0 = mark not reached)          */
   MK_NUM_TAPS = 10
 };
 int mk_tap_offset(const mk_handle* h, int32_t tap, size_t* offset, size_t* bytes);

@@ -29,7 +29,7 @@ constexpr int kYsFloats = 8192;    // LDS capacity for scores / tile outputs (mk
 constexpr int kXsFloats = 16384;   // LDS capacity for staged activations
 
 struct Layout {
-  size_t off_tasks, off_ctr, off_err, off_layers, off_invf;
+  size_t off_tasks, off_ctr, off_err, off_layers, off_invf, off_rope;
   size_t off_x, off_xn, off_xmid, off_xn2, off_qkv, off_attn, off_opart, off_rlog, off_topi, off_topw;
   size_t off_moe, off_H, off_Y, off_fh, off_fo, off_oout, off_pml, off_po, off_trace;
   size_t total;
@@ -91,10 +91,11 @@ Layout make_layout(const mk_config* c, int32_t max_blocks) {
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t r = o; o = align_up(o + bytes, 256); return r; };
   L.off_tasks = take((size_t)L.max_tasks * sizeof(mk_task));
-  L.off_ctr = take((size_t)L.n_ctr * 4);
+  L.off_ctr = take((size_t)L.n_ctr * MK_CTR_PAD * 4);
   L.off_err = take(MK_ERR_WORDS * 4);
   L.off_layers = take((size_t)Lr * sizeof(mk_layer_dev));
   L.off_invf = take((size_t)(hd / 2) * 8);
+  L.off_rope = take((size_t)B * (hd / 2) * 2 * 4);
   L.off_x = take((size_t)(Lr + 1) * B * d * 4);
   L.off_xn = take((size_t)(Lr + 1) * B * d * 4);
   L.off_xmid = take(c->parallel_block ? 4 : (size_t)Lr * B * d * 4);
@@ -113,7 +114,7 @@ Layout make_layout(const mk_config* c, int32_t max_blocks) {
   L.off_oout = take((size_t)Lr * B * d * 4);
   L.off_pml = take((size_t)2 * B * c->n_q_heads * L.max_splits * 2 * 4);
   L.off_po = take((size_t)2 * B * c->n_q_heads * L.max_splits * hd * 4);
-  L.off_trace = take((size_t)L.max_tasks * 8 * 8);
+  L.off_trace = take((size_t)L.max_tasks * 16 * 8);
   L.total = o;
   return L;
 }
@@ -636,7 +637,7 @@ int mk_build_schedule(mk_handle* h, int32_t batch_size, const mk_sched_opts* opt
   if (p.max_splits > h->lay.max_splits) return MK_E_UNSUPPORTED;
   if (hipMemcpy(h->ws + h->lay.off_tasks, p.tasks.data(), p.tasks.size() * sizeof(mk_task),
                 hipMemcpyHostToDevice) != hipSuccess ||
-      hipMemset(h->ws + h->lay.off_ctr, 0, (size_t)h->lay.n_ctr * 4) != hipSuccess ||
+      hipMemset(h->ws + h->lay.off_ctr, 0, (size_t)h->lay.n_ctr * MK_CTR_PAD * 4) != hipSuccess ||
       hipDeviceSynchronize() != hipSuccess)
     return MK_E_HIP;
   h->plan = std::move(p);
@@ -668,6 +669,7 @@ int mk_decode_step(mk_handle* h, const int32_t* token_ids, const int32_t* positi
   a.lm_head = h->lm_head;
   a.final_norm = h->final_norm;
   a.inv_freq = reinterpret_cast<const double*>(ws + L.off_invf);
+  a.rope = reinterpret_cast<float*>(ws + L.off_rope);
   a.tokens = token_ids;
   a.positions = positions;
   a.block_tables = block_tables;
@@ -722,7 +724,8 @@ int mk_get_status(mk_handle* h, mk_status* st) {
   if (e[0] != 0) {
     if (hipMemset(h->ws + h->lay.off_err, 0, sizeof e) != hipSuccess) return MK_E_HIP;
     // a timed-out step may leave counters behind; clear them for the next step
-    if (e[0] == MK_E_TIMEOUT && hipMemset(h->ws + h->lay.off_ctr, 0, (size_t)h->lay.n_ctr * 4) != hipSuccess)
+    if (e[0] == MK_E_TIMEOUT &&
+        hipMemset(h->ws + h->lay.off_ctr, 0, (size_t)h->lay.n_ctr * MK_CTR_PAD * 4) != hipSuccess)
       return MK_E_HIP;
     if (hipDeviceSynchronize() != hipSuccess) return MK_E_HIP;
   }
@@ -752,7 +755,7 @@ int mk_tap_offset(const mk_handle* h, int32_t tap, size_t* offset, size_t* bytes
     case MK_TAP_TOPK_WEIGHTS: *offset = L.off_topw; *bytes = c.n_experts > 0 ? Lr * B * c.top_k * 4 : 0; break;
     case MK_TAP_FFN_OUT: *offset = L.off_fo; *bytes = Lr * B * d * 4; break;
     case MK_TAP_ATTN_OUT: *offset = L.off_oout; *bytes = Lr * B * d * 4; break;
-    case MK_TAP_TRACE: *offset = L.off_trace; *bytes = (size_t)(h->have_plan ? h->plan.tasks.size() : 0) * 64; break;
+    case MK_TAP_TRACE: *offset = L.off_trace; *bytes = (size_t)(h->have_plan ? h->plan.tasks.size() : 0) * 128; break;
     default: return MK_E_INVAL;
   }
   return MK_OK;

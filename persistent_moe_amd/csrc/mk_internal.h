@@ -42,6 +42,8 @@ enum {
   MK_CTR_FIXED = 11   // then: COMB[Hkv], ATTN[B*Hkv], UG[B*k]
 };
 
+#define MK_CTR_PAD 64   // ints between consecutive counters (one 256-byte line each)
+
 struct mk_ctr_layout {
   int32_t stride;     // counters per layer block
   int32_t comb;       // offset of COMB[g]
@@ -63,8 +65,9 @@ static inline mk_ctr_layout mk_make_ctr_layout(int32_t L, int32_t Hkv, int32_t B
 
 // ---------------------------------------------------------------- MoE routing
 // Per layer (ints): [0] n_active, [1] up-gate items, [2] down items,
-// [3] rows, then act_expert[BK], row_off[BK+1], row_tok[BK], slot[BK].
-static inline int32_t mk_moe_stride(int32_t bk) { return 4 + bk + (bk + 1) + bk + bk; }
+// [3] rows, then slot[BK] (row of each (token, k)), then one 16-int record
+// per active expert: expert id, first row, rows, 0, token of each row (8).
+static inline int32_t mk_moe_stride(int32_t bk) { return 4 + bk + 16 * bk; }
 
 // ---------------------------------------------------------------- error record
 // err[0] code, [1] task, [2] counter, [3] value, [4] target, [5] workgroup
@@ -96,6 +99,7 @@ struct mk_kargs {
   const uint16_t* lm_head;
   const uint16_t* final_norm;
   const double* inv_freq;         // [hd/2] RoPE inverse frequencies
+  float* rope;                    // [B][hd/2][2] cos, sin of this step's angles
   // step inputs
   const int32_t* tokens;
   const int32_t* positions;

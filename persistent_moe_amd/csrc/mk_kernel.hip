@@ -38,9 +38,31 @@
 #define YS_FLOATS 8192    // tile outputs / attention scores, 32 KB
 #define RED_FLOATS 8192   // attention cross-wave reduction, 32 KB
 #define NBMAX 8
+#ifndef MK_WBUD1
+#define MK_WBUD1 4        // 16-byte loads per lane per row group (batch 1): bounds bytes in flight
+#endif
+#define MK_CW 7           // compute waves: wave 0 is the control wave (spins, stages)
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// The argument block stays in the kernarg segment and is read with scalar
+// loads through a pointer laundered once per work unit (KA::operator->).
+// Reading it directly would let loop-invariant code motion hoist dozens of
+// argument-derived values to the kernel entry, where they no longer fit in
+// registers and are spilled; reading it from LDS or through a generic
+// pointer would turn every field access into a vector-memory load that
+// waits behind the wave's in-flight weight loads.
+typedef __attribute__((address_space(4))) const mk_kargs kargs_c;
+struct KA {
+  kargs_c* p;
+  __device__ __forceinline__ kargs_c* operator->() const { return p; }
+};
+__device__ __forceinline__ KA kargs() {
+  kargs_c* p = (kargs_c*)(__builtin_amdgcn_kernarg_segment_ptr());
+  asm volatile("" : "+s"(p));
+  return KA{p};
+}
 
 struct __attribute__((aligned(16))) Smem {
   float xs[XS_FLOATS];
@@ -48,7 +70,7 @@ struct __attribute__((aligned(16))) Smem {
   float red[RED_FLOATS];
   int misc[192];
   uint64_t t_ready;   // trace: when the task's first wait was satisfied
-  uint64_t t_mark[3]; // trace: activations staged, tile computed, stores acknowledged
+  uint64_t t_mark[10]; // trace: [0] staged, [1] computed, [2] stores acknowledged, [3..9] free marks
 };
 
 // ------------------------------------------------------------------ helpers
@@ -73,6 +95,10 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
+
+// Each counter owns a 256-byte line (MK_CTR_PAD ints), so that workgroups
+// polling different counters do not share a line.
+__device__ __forceinline__ int32_t* ctrp(const KA a, int idx) { return a->ctr + (long)idx * MK_CTR_PAD; }
 
 __device__ __forceinline__ int ld_agent(const int32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -113,29 +139,33 @@ __device__ __forceinline__ u32x4 as_u4(f32x4 v) {
 // Wait until this wave's stores have completed.
 __device__ __forceinline__ void stores_done() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-__device__ __noinline__ void report(const mk_kargs& a, int code, int task, int ctr, int val, int target) {
-  if (atomicCAS(&a.err[0], 0, code) == 0) {
-    a.err[1] = task;
-    a.err[2] = ctr;
-    a.err[3] = val;
-    a.err[4] = target;
-    a.err[5] = (int)blockIdx.x;
+__device__ __noinline__ void report(const KA a, int code, int task, int ctr, int val, int target) {
+  if (atomicCAS(&a->err[0], 0, code) == 0) {
+    a->err[1] = task;
+    a->err[2] = ctr;
+    a->err[3] = val;
+    a->err[4] = target;
+    a->err[5] = (int)blockIdx.x;
   }
 }
 
 // One lane spins until ctr[idx] >= target.  false if the watchdog fired or
 // another workgroup aborted the step.
-__device__ __forceinline__ bool spin_until(const mk_kargs& a, int idx, int target, int task) {
-  const int32_t* p = a.ctr + idx;
+__device__ __forceinline__ bool spin_until(const KA a, int idx, int target, int task) {
+  const int32_t* p = ctrp(a, idx);
   if (ld_agent(p) < target) {
     const uint64_t t0 = wall_clock64();
+    int backoff = 1;
     for (;;) {
-      __builtin_amdgcn_s_sleep(2);
+      // back off to at most ~0.4 us between polls: a poll is a memory
+      // transaction on a line that up to every CU is reading
+      for (int k = 0; k < backoff; ++k) __builtin_amdgcn_s_sleep(3);
+      if (backoff < 8) backoff <<= 1;
       if (ld_agent(p) >= target) break;
-      if (ld_agent(a.ctr + MK_CG_ABORT)) return false;
-      if (wall_clock64() - t0 > a.timeout_ticks) {
+      if (ld_agent(ctrp(a, MK_CG_ABORT))) return false;
+      if (wall_clock64() - t0 > a->timeout_ticks) {
         report(a, MK_E_TIMEOUT, task, idx, ld_agent(p), target);
-        __hip_atomic_store(a.ctr + MK_CG_ABORT, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(ctrp(a, MK_CG_ABORT), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         return false;
       }
     }
@@ -144,10 +174,10 @@ __device__ __forceinline__ bool spin_until(const mk_kargs& a, int idx, int targe
 }
 
 // Workgroup-wide wait; every thread must call it.  Uses misc[0].
-__device__ __forceinline__ bool wg_wait(const mk_kargs& a, Smem& sm, int idx, int target, int task) {
+__device__ __forceinline__ bool wg_wait(const KA a, Smem& sm, int idx, int target, int task) {
   if (threadIdx.x == 0) {
     sm.misc[0] = (idx < 0 || target <= 0) ? 1 : (int)spin_until(a, idx, target, task);
-    if (a.trace && sm.t_ready == 0) sm.t_ready = wall_clock64();
+    if (a->trace && sm.t_ready == 0) sm.t_ready = wall_clock64();
   }
   __syncthreads();
   const bool ok = sm.misc[0] != 0;
@@ -155,24 +185,29 @@ __device__ __forceinline__ bool wg_wait(const mk_kargs& a, Smem& sm, int idx, in
 }
 
 __shared__ uint64_t* sm_trace_mark;   // trace: where wg_signal records its time
+// trace: first time this task passes mark k (thread 0)
+#define MK_MARK(k)                                                              \
+  do {                                                                          \
+    if (a->trace && threadIdx.x == 0 && sm.t_mark[k] == 0) sm.t_mark[k] = wall_clock64(); \
+  } while (0)
 
 // Workgroup-wide signal: every wave waits for its (agent-coherent) stores to
 // complete, then one lane bumps the counter.
-__device__ __forceinline__ void wg_signal(const mk_kargs& a, int idx, int inc) {
+__device__ __forceinline__ void wg_signal(const KA a, int idx, int inc) {
   stores_done();
   __syncthreads();
-  if (a.trace && threadIdx.x == 0 && sm_trace_mark) *sm_trace_mark = wall_clock64();
+  if (a->trace && threadIdx.x == 0 && sm_trace_mark) *sm_trace_mark = wall_clock64();
   if (threadIdx.x == 0 && idx >= 0)
-    __hip_atomic_fetch_add(a.ctr + idx, inc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_fetch_add(ctrp(a, idx), inc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Claim the next item of a queue; every thread must call it.  Uses misc[1].
-__device__ __forceinline__ int wg_claim(const mk_kargs& a, Smem& sm, int qidx) {
+__device__ __forceinline__ int wg_claim(const KA a, Smem& sm, int qidx) {
   __syncthreads();
   if (threadIdx.x == 0) {
-    sm.misc[1] = ld_agent(a.ctr + MK_CG_ABORT)
+    sm.misc[1] = ld_agent(ctrp(a, MK_CG_ABORT))
                      ? 0x3FFFFFFF
-                     : __hip_atomic_fetch_add(a.ctr + qidx, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                     : __hip_atomic_fetch_add(ctrp(a, qidx), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
   return sm.misc[1];
@@ -181,7 +216,7 @@ __device__ __forceinline__ int wg_claim(const mk_kargs& a, Smem& sm, int qidx) {
 // Claimer item order: claimer c of a wave owns item c of the queue; items
 // past the number of claimers are pulled one at a time from the atomic queue
 // head.  Returns -1 when the queue is exhausted.  Every thread must call it.
-__device__ __forceinline__ int next_item(const mk_kargs& a, Smem& sm, const mk_task& t, int n_items, int qidx, bool& first) {
+__device__ __forceinline__ int next_item(const KA a, Smem& sm, const mk_task& t, int n_items, int qidx, bool& first) {
   if (first) {
     first = false;
     if (t.n0 < n_items) return t.n0;
@@ -191,26 +226,26 @@ __device__ __forceinline__ int next_item(const mk_kargs& a, Smem& sm, const mk_t
   return it < n_items ? it : -1;
 }
 
-__device__ __forceinline__ int layer_ctr(const mk_kargs& a, int layer, int off) {
-  return MK_CG_COUNT + layer * a.cl.stride + off;
+__device__ __forceinline__ int layer_ctr(const KA a, int layer, int off) {
+  return MK_CG_COUNT + layer * a->cl.stride + off;
 }
 
-__device__ __forceinline__ int visible_keys(const mk_kargs& a, int layer, int seq_len) {
-  if (a.swa_window > 0 && a.swa_period > 0 && (layer % a.swa_period) != a.swa_period - 1)
-    return seq_len < a.swa_window ? seq_len : a.swa_window;
+__device__ __forceinline__ int visible_keys(const KA a, int layer, int seq_len) {
+  if (a->swa_window > 0 && a->swa_period > 0 && (layer % a->swa_period) != a->swa_period - 1)
+    return seq_len < a->swa_window ? seq_len : a->swa_window;
   return seq_len;
 }
 // Live length of slot b, clamped to what its block table can hold (a longer
 // length is reported by the layer-0 norm task).
-__device__ __forceinline__ int live_len(const mk_kargs& a, int b) {
-  const int sl = a.seq_lens[b];
-  const int cap = a.max_blocks * a.page;
+__device__ __forceinline__ int live_len(const KA a, int b) {
+  const int sl = a->seq_lens[b];
+  const int cap = a->max_blocks * a->page;
   return sl < cap ? sl : cap;
 }
-__device__ __forceinline__ int n_splits(const mk_kargs& a, int layer, int b) {
+__device__ __forceinline__ int n_splits(const KA a, int layer, int b) {
   const int sl = live_len(a, b);
   if (sl <= 0) return 0;
-  return (visible_keys(a, layer, sl) + a.attn_split - 1) / a.attn_split;
+  return (visible_keys(a, layer, sl) + a->attn_split - 1) / a->attn_split;
 }
 
 // --------------------------------------------------------- the GEMV pipeline
@@ -253,11 +288,14 @@ template <int NB, int KCH, int RPW>
 struct GemvTile {
   u32x4 w[RPW][KCH];
 
+  // tile row j of compute wave cw (1..7) in row group grp
+  __device__ __forceinline__ static int row_of(int grp, int cw, int j) { return (grp * MK_CW + cw - 1) * RPW + j; }
+
   __device__ __forceinline__ void load(const GemvArgs& g, int grp) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
 #pragma unroll
     for (int j = 0; j < RPW; ++j) {
-      const int r = (grp * MK_WAVES + wave) * RPW + j;
+      const int r = row_of(grp, wave, j);
       const bool rv = r < g.nrows;
       const uint16_t* rp = rv ? gemv_row(g, r) : g.base;
 #pragma unroll
@@ -271,6 +309,7 @@ struct GemvTile {
 
   __device__ __forceinline__ void compute(const GemvArgs& g, int grp, const float* xs, float* ys) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    if (row_of(grp, wave, 0) >= g.nrows) return;   // wave-uniform: no rows in this group
     float acc[RPW][NB];
 #pragma unroll
     for (int j = 0; j < RPW; ++j)
@@ -303,7 +342,7 @@ struct GemvTile {
     }
 #pragma unroll
     for (int j = 0; j < RPW; ++j) {
-      const int r = (grp * MK_WAVES + wave) * RPW + j;
+      const int r = row_of(grp, wave, j);
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
         const float s = wave_sum(acc[j][b]);
@@ -320,8 +359,8 @@ struct GemvTile {
 struct StageArgs {
   const float* base;
   long ld;
-  const int32_t* map;   // row of x for batch row j: map[map0 + j], or j if null
-  int map0;
+  bool use_tok;         // row of x for batch row j: tok[j] (else j)
+  int tok[NBMAX];
   int nb;
   int K;
   int wait_idx;         // counter waited on before staging (-1: none)
@@ -333,13 +372,13 @@ struct StageArgs {
 // the other waves only meet it at the barrier.  Wave 0's own weight loads
 // have landed by the time its spin sees the counter, so its staging loads
 // do not queue behind outstanding weight traffic.  Every thread must call it.
-__device__ __forceinline__ bool wait_and_stage(const mk_kargs& a, Smem& sm, const StageArgs& s) {
+__device__ __forceinline__ bool wait_and_stage(const KA a, Smem& sm, const StageArgs& s) {
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
     int ok = 1;
     if (lane == 0) {
       ok = (s.wait_idx < 0 || s.wait_target <= 0) ? 1 : (int)spin_until(a, s.wait_idx, s.wait_target, s.task);
-      if (a.trace && sm.t_ready == 0) sm.t_ready = wall_clock64();
+      if (a->trace && sm.t_ready == 0) sm.t_ready = wall_clock64();
     }
     ok = __shfl(ok, 0);
     if (lane == 0) sm.misc[0] = ok;
@@ -354,7 +393,12 @@ __device__ __forceinline__ bool wait_and_stage(const mk_kargs& a, Smem& sm, cons
           dst[u] = -1;
           if (i < total) {
             const int j = i / kv, c = i - j * kv;
-            const int row = s.map ? ldc(s.map + s.map0 + j) : j;
+            int row = j;
+            if (s.use_tok) {
+#pragma unroll
+              for (int q = 0; q < NBMAX; ++q)
+                if (q == j) row = s.tok[q];
+            }
             v[u] = ldc16(s.base, (int)(((long)row * s.ld + c * 4) * 4));
             dst[u] = j * s.K + c * 4;
           }
@@ -366,28 +410,34 @@ __device__ __forceinline__ bool wait_and_stage(const mk_kargs& a, Smem& sm, cons
     }
   }
   __syncthreads();
-  if (a.trace && threadIdx.x == 0 && sm.t_mark[0] == 0) sm.t_mark[0] = wall_clock64();
+  if (a->trace && threadIdx.x == 0 && sm.t_mark[0] == 0) sm.t_mark[0] = wall_clock64();
   return sm.misc[0] != 0;
 }
 
 template <int NB, int KCH, int RPW>
-__device__ bool gemv_run(const mk_kargs& a, Smem& sm, const GemvArgs& g, const StageArgs& s) {
+__device__ bool gemv_run(const KA a, Smem& sm, const GemvArgs& g, const StageArgs& s) {
   GemvTile<NB, KCH, RPW> A, Bt;
-  const int per = MK_WAVES * RPW;
+  const int per = MK_CW * RPW;
   const int ng = (g.nrows + per - 1) / per;
-  // the first two row groups are in flight before the dependency resolves
-  A.load(g, 0);
-  if (ng > 1) Bt.load(g, 1);
+  const bool cw = (threadIdx.x >> 6) != 0;
+  // the first two row groups are in flight before the dependency resolves;
+  // the control wave loads no weights, so its staging loads queue behind nothing
+  if (cw) {
+    A.load(g, 0);
+    if (ng > 1) Bt.load(g, 1);
+  }
   if (!wait_and_stage(a, sm, s)) return false;
-  for (int grp = 0; grp < ng; grp += 2) {
-    A.compute(g, grp, sm.xs, sm.ys);
-    if (grp + 2 < ng) A.load(g, grp + 2);
-    if (grp + 1 < ng) {
-      Bt.compute(g, grp + 1, sm.xs, sm.ys);
-      if (grp + 3 < ng) Bt.load(g, grp + 3);
+  if (cw) {
+    for (int grp = 0; grp < ng; grp += 2) {
+      A.compute(g, grp, sm.xs, sm.ys);
+      if (grp + 2 < ng) A.load(g, grp + 2);
+      if (grp + 1 < ng) {
+        Bt.compute(g, grp + 1, sm.xs, sm.ys);
+        if (grp + 3 < ng) Bt.load(g, grp + 3);
+      }
     }
   }
-  if (a.trace && threadIdx.x == 0 && sm.t_mark[1] == 0) sm.t_mark[1] = wall_clock64();
+  if (a->trace && threadIdx.x == 0 && sm.t_mark[1] == 0) sm.t_mark[1] = wall_clock64();
   return true;
 }
 
@@ -395,8 +445,8 @@ __device__ bool gemv_run(const mk_kargs& a, Smem& sm, const GemvArgs& g, const S
 // register budget allows (2 row groups of RPW x KCH 16-byte loads per lane
 // and RPW x NB accumulators).  Rows past the tile are masked.
 template <int NB, int KCH>
-__device__ __forceinline__ bool gemv_k2(const mk_kargs& a, Smem& sm, const GemvArgs& g, const StageArgs& s) {
-  constexpr int WBUD = NB == 1 ? 16 : 8;
+__device__ __forceinline__ bool gemv_k2(const KA a, Smem& sm, const GemvArgs& g, const StageArgs& s) {
+  constexpr int WBUD = NB == 1 ? MK_WBUD1 : 8;
   constexpr int RMAX_W = (WBUD / KCH) < 1 ? 1 : (WBUD / KCH);
   constexpr int RMAX_A = 16 / NB < 1 ? 1 : 16 / NB;
   constexpr int R0 = RMAX_W < RMAX_A ? RMAX_W : RMAX_A;
@@ -405,7 +455,7 @@ __device__ __forceinline__ bool gemv_k2(const mk_kargs& a, Smem& sm, const GemvA
 }
 
 template <int NB>
-__device__ __forceinline__ bool gemv_nb(const mk_kargs& a, Smem& sm, const GemvArgs& g, const StageArgs& s) {
+__device__ __forceinline__ bool gemv_nb(const KA a, Smem& sm, const GemvArgs& g, const StageArgs& s) {
   const int kch = (g.K + 511) / 512;
   if (kch <= 1) return gemv_k2<NB, 1>(a, sm, g, s);
   if (kch <= 2) return gemv_k2<NB, 2>(a, sm, g, s);
@@ -416,7 +466,7 @@ __device__ __forceinline__ bool gemv_nb(const mk_kargs& a, Smem& sm, const GemvA
 
 // Runs one GEMV tile: prefetch, wait, stage x, multiply.  false if the step
 // was aborted while waiting.
-__device__ __forceinline__ bool gemv(const mk_kargs& a, Smem& sm, const GemvArgs& g, const StageArgs& s) {
+__device__ __forceinline__ bool gemv(const KA a, Smem& sm, const GemvArgs& g, const StageArgs& s) {
   if (g.nb <= 1) return gemv_nb<1>(a, sm, g, s);
   if (g.nb <= 2) return gemv_nb<2>(a, sm, g, s);
   if (g.nb <= 4) return gemv_nb<4>(a, sm, g, s);
@@ -430,45 +480,56 @@ __device__ __forceinline__ bool gemv(const mk_kargs& a, Smem& sm, const GemvArgs
 // the ~Hkv + k + 1 source loads of a chunk issued together.  x is kept in
 // LDS between the two passes.  The MoE combine (the gate-weighted sum of the
 // routed expert outputs, in top-k order) is folded into this task.
-__device__ __forceinline__ bool op_add_rmsnorm(const mk_kargs& a, Smem& sm, const mk_task& t, int ti) {
+__device__ __forceinline__ bool op_add_rmsnorm(const KA a, Smem& sm, const mk_task& t, int ti) {
   if (!wg_wait(a, sm, t.wait_ctr, t.wait_target, ti)) return false;
-  const int l = t.layer, d = a.d, B = a.B, nv = d >> 2, K = a.topk;
+  const int l = t.layer, d = a->d, B = a->B, nv = d >> 2, K = a->topk;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const bool mid = t.flags & MK_F_MID;
   const bool fin = t.flags & MK_F_FINAL;
   const bool emb = t.flags & MK_F_EMBED;
-  const bool moe_in = !emb && !mid && a.parallel && a.E > 0;
+  const bool moe_in = !emb && !mid && a->parallel && a->E > 0;
   const int lp = l - 1;
   const int lx = mid ? l : lp;     // layer whose attention output is added
   // gate weights and rows of the routed outputs of the previous layer
   int* srow = sm.misc + 64;                              // [B*K]
   float* sw = reinterpret_cast<float*>(sm.misc + 128);   // [B*K]
   if (moe_in) {
-    const int32_t* meta = a.moe + (long)lp * a.moe_stride;
-    const int32_t* slot = meta + 4 + a.bk + (a.bk + 1) + a.bk;
+    const int32_t* slot = a->moe + (long)lp * a->moe_stride + 4;
     if (tid < B * K) {
       srow[tid] = ldc(slot + tid);
-      sw[tid] = ldc(a.topw + (long)lp * B * K + tid);
+      sw[tid] = ldc(a->topw + (long)lp * B * K + tid);
     }
     __syncthreads();
   }
-  const uint16_t* gain = fin ? a.final_norm : (mid ? a.layers[l].ffn_norm : a.layers[l].attn_norm);
-  float* xdst = mid ? a.xmid + (long)l * B * d : a.x + (long)l * B * d;
-  float* xndst = mid ? a.xn2 + (long)l * B * d : a.xn + (long)l * B * d;
+  const uint16_t* gain = fin ? a->final_norm : (mid ? a->layers[l].ffn_norm : a->layers[l].attn_norm);
+  float* xdst = mid ? a->xmid + (long)l * B * d : a->x + (long)l * B * d;
+  float* xndst = mid ? a->xn2 + (long)l * B * d : a->xn + (long)l * B * d;
   float* red = sm.red;      // [MK_WAVES][NBMAX] partial sums of squares
   float* xv = sm.xs;        // [B][d] the new residual rows
+  if (emb) {
+    // cos/sin of pos * theta^(-2i/hd) for this step's positions, in double,
+    // read by every QKV tile's RoPE epilogue
+    const int half = a->hd / 2;
+    for (int idx = tid; idx < B * half; idx += MK_THREADS) {
+      const int b = idx / half, i = idx - b * half;
+      double sn, cs;
+      sincos((double)a->positions[b] * a->inv_freq[i], &sn, &cs);
+      stc(a->rope + (long)idx * 2, (float)cs);
+      stc(a->rope + (long)idx * 2 + 1, (float)sn);
+    }
+  }
 #pragma unroll 1
   for (int b = 0; b < B; ++b) {
-    const bool live = a.seq_lens[b] > 0;
+    const bool live = a->seq_lens[b] > 0;
     int tok = 0;
     if (emb && live) {
-      tok = a.tokens[b];
-      if (tok < 0 || tok >= a.V) {
-        if (tid == 0) report(a, MK_E_DEVICE, ti, -1, tok, a.V);
+      tok = a->tokens[b];
+      if (tok < 0 || tok >= a->V) {
+        if (tid == 0) report(a, MK_E_DEVICE, ti, -1, tok, a->V);
         tok = 0;
       }
-      if (tid == 0 && a.seq_lens[b] > a.max_blocks * a.page)
-        report(a, MK_E_DEVICE, ti, -5, a.seq_lens[b], a.max_blocks * a.page);
+      if (tid == 0 && a->seq_lens[b] > a->max_blocks * a->page)
+        report(a, MK_E_DEVICE, ti, -5, a->seq_lens[b], a->max_blocks * a->page);
     }
     float ss = 0.f;
 #pragma unroll 1
@@ -477,37 +538,37 @@ __device__ __forceinline__ bool op_add_rmsnorm(const mk_kargs& a, Smem& sm, cons
       f32x4 acc = (f32x4){0.f, 0.f, 0.f, 0.f};
       if (!live) {
       } else if (emb) {
-        const uint2 e = *reinterpret_cast<const uint2*>(a.embed + (long)tok * d + c * 4);
+        const uint2 e = *reinterpret_cast<const uint2*>(a->embed + (long)tok * d + c * 4);
         acc = (f32x4){bf_lo(e.x), bf_hi(e.x), bf_lo(e.y), bf_hi(e.y)};
       } else if (mid || moe_in) {
         u32x4 og[8], ym[8];
 #pragma unroll
         for (int g = 0; g < 8; ++g)
-          if (g < a.Hkv) og[g] = ldc16(a.opart + (((long)lx * a.Hkv + g) * B + b) * d, off);
+          if (g < a->Hkv) og[g] = ldc16(a->opart + (((long)lx * a->Hkv + g) * B + b) * d, off);
         if (moe_in) {
 #pragma unroll
           for (int j = 0; j < 8; ++j)
             if (j < K)
-              ym[j] = ldc16(a.Y + ((long)lp * a.bk + __builtin_amdgcn_readfirstlane(srow[b * K + j])) * d, off);
+              ym[j] = ldc16(a->Y + ((long)lp * a->bk + __builtin_amdgcn_readfirstlane(srow[b * K + j])) * d, off);
         }
-        const f32x4 xp = as_f4(ldc16(a.x + ((long)lx * B + b) * d, off));
+        const f32x4 xp = as_f4(ldc16(a->x + ((long)lx * B + b) * d, off));
         f32x4 o = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int g = 0; g < 8; ++g)
-          if (g < a.Hkv) o += as_f4(og[g]);
-        stc16(a.oout + ((long)lx * B + b) * d, off, as_u4(o));
+          if (g < a->Hkv) o += as_f4(og[g]);
+        stc16(a->oout + ((long)lx * B + b) * d, off, as_u4(o));
         acc = xp + o;
         if (moe_in) {
           f32x4 m = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int j = 0; j < 8; ++j)
             if (j < K) m += sw[b * K + j] * as_f4(ym[j]);
-          stc16(a.fo + ((long)lp * B + b) * d, off, as_u4(m));
+          stc16(a->fo + ((long)lp * B + b) * d, off, as_u4(m));
           acc += m;
         }
       } else {
         // sequential block: x_l = x_mid + FFN output
-        acc = as_f4(ldc16(a.xmid + ((long)lp * B + b) * d, off)) + as_f4(ldc16(a.fo + ((long)lp * B + b) * d, off));
+        acc = as_f4(ldc16(a->xmid + ((long)lp * B + b) * d, off)) + as_f4(ldc16(a->fo + ((long)lp * B + b) * d, off));
       }
       stc16(xdst + (long)b * d, off, as_u4(acc));
       *reinterpret_cast<f32x4*>(xv + b * d + c * 4) = acc;
@@ -522,7 +583,7 @@ __device__ __forceinline__ bool op_add_rmsnorm(const mk_kargs& a, Smem& sm, cons
     float tot = 0.f;
 #pragma unroll
     for (int w = 0; w < MK_WAVES; ++w) tot += red[w * NBMAX + b];
-    const float r = 1.0f / sqrtf(tot / (float)d + a.eps);
+    const float r = 1.0f / sqrtf(tot / (float)d + a->eps);
 #pragma unroll 1
     for (int c = tid; c < nv; c += MK_THREADS) {
       const uint2 gg = *reinterpret_cast<const uint2*>(gain + c * 4);
@@ -540,40 +601,38 @@ __device__ __forceinline__ bool op_add_rmsnorm(const mk_kargs& a, Smem& sm, cons
 // is rows h*hd + p and h*hd + p + hd/2).  RoPE (rotate-half, angle
 // pos * theta^(-2i/hd) in double) on q and k; k and v rounded to bf16 and
 // written to the sequence's page at its position.
-__device__ __forceinline__ void epi_qkv(const mk_kargs& a, Smem& sm, const mk_task& t, int ti) {
-  const int l = t.layer, hd = a.hd, half = hd / 2, B = a.B;
+__device__ __forceinline__ void epi_qkv(const KA a, Smem& sm, const mk_task& t, int ti) {
+  const int l = t.layer, hd = a->hd, half = hd / 2, B = a->B;
   const int np = t.n1 - t.n0;
-  const int rows = (a.Hq + 2 * a.Hkv) * hd;
-  uint16_t* kpool = a.layers[l].k;
-  uint16_t* vpool = a.layers[l].v;
+  const int rows = (a->Hq + 2 * a->Hkv) * hd;
+  uint16_t* kpool = a->layers[l].k;
+  uint16_t* vpool = a->layers[l].v;
   for (int idx = threadIdx.x; idx < np * B; idx += MK_THREADS) {
     const int p = idx / B, b = idx - p * B;
-    if (a.seq_lens[b] <= 0) continue;
+    if (a->seq_lens[b] <= 0) continue;
     const int gp = t.n0 + p, head = gp / half, i = gp - head * half;
     float ya = sm.ys[(2 * p) * NBMAX + b], yb = sm.ys[(2 * p + 1) * NBMAX + b];
-    const int pos = a.positions[b];
-    if (head < a.Hq + a.Hkv) {
-      double sn, cs;
-      sincos((double)pos * a.inv_freq[i], &sn, &cs);
-      const float c = (float)cs, s_ = (float)sn;
+    const int pos = a->positions[b];
+    if (head < a->Hq + a->Hkv) {
+      const float c = ldc(a->rope + ((long)b * half + i) * 2), s_ = ldc(a->rope + ((long)b * half + i) * 2 + 1);
       const float ra = ya * c - yb * s_;
       const float rb = yb * c + ya * s_;
       ya = ra;
       yb = rb;
     }
-    float* qo = a.qkv + ((long)l * B + b) * rows;
+    float* qo = a->qkv + ((long)l * B + b) * rows;
     stc(qo + head * hd + i, ya);
     stc(qo + head * hd + i + half, yb);
-    if (head >= a.Hq) {
-      const bool isk = head < a.Hq + a.Hkv;
-      const int kvh = isk ? head - a.Hq : head - a.Hq - a.Hkv;
-      const int blk = pos / a.page;
-      const int page = (blk >= 0 && blk < a.max_blocks) ? a.block_tables[b * a.max_blocks + blk] : -1;
-      if (page < 0 || page >= a.num_pages || pos < 0) {
-        report(a, MK_E_DEVICE, ti, -2, page, a.num_pages);
+    if (head >= a->Hq) {
+      const bool isk = head < a->Hq + a->Hkv;
+      const int kvh = isk ? head - a->Hq : head - a->Hq - a->Hkv;
+      const int blk = pos / a->page;
+      const int page = (blk >= 0 && blk < a->max_blocks) ? a->block_tables[b * a->max_blocks + blk] : -1;
+      if (page < 0 || page >= a->num_pages || pos < 0) {
+        report(a, MK_E_DEVICE, ti, -2, page, a->num_pages);
         continue;
       }
-      uint16_t* dst = (isk ? kpool : vpool) + (((long)page * a.Hkv + kvh) * a.page + (pos % a.page)) * hd;
+      uint16_t* dst = (isk ? kpool : vpool) + (((long)page * a->Hkv + kvh) * a->page + (pos % a->page)) * hd;
       stc(dst + i, f_to_bf16(ya));
       stc(dst + i + half, f_to_bf16(yb));
     }
@@ -595,15 +654,15 @@ __device__ __forceinline__ void epi_swiglu(Smem& sm, int np, int nb, float* out,
 // are the softmax probabilities of the selected experts renormalised to sum
 // to 1, i.e. exp(r_j - r_max) / sum over the selected.  One wave per token;
 // leaves the selected ids in misc[64 + b*k + j] for ROUTE_FINALIZE.
-__device__ __forceinline__ void router_topk(const mk_kargs& a, Smem& sm, int l) {
-  const int B = a.B, E = a.E, K = a.topk;
+__device__ __forceinline__ void router_topk(const KA a, Smem& sm, int l) {
+  const int B = a->B, E = a->E, K = a->topk;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   for (int b = wave; b < B; b += MK_WAVES) {
     float v[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int e = lane + 64 * u;
-      v[u] = e < E ? ldc(a.rlog + ((long)l * B + b) * E + e) : -INFINITY;
+      v[u] = e < E ? ldc(a->rlog + ((long)l * B + b) * E + e) : -INFINITY;
     }
     float top0 = 0.f, wsum = 0.f;
     float myw = 0.f;
@@ -631,9 +690,9 @@ __device__ __forceinline__ void router_topk(const mk_kargs& a, Smem& sm, int l) 
       if (lane == j) { myw = ew; myid = be; }
     }
     if (lane < K) {
-      stc(a.topi + ((long)l * B + b) * K + lane, myid);
-      stc(a.topw + ((long)l * B + b) * K + lane, myw / wsum);
-      sm.misc[64 + b * K + lane] = a.seq_lens[b] > 0 ? myid : -1;
+      stc(a->topi + ((long)l * B + b) * K + lane, myid);
+      stc(a->topw + ((long)l * B + b) * K + lane, myw / wsum);
+      sm.misc[64 + b * K + lane] = a->seq_lens[b] > 0 ? myid : -1;
     }
   }
   __syncthreads();
@@ -645,14 +704,12 @@ __device__ __forceinline__ void router_topk(const mk_kargs& a, Smem& sm, int l) 
 // routed row.  Writes the active expert list (ascending ids), each expert's
 // first row, the token of each row, the row of each (token, slot), and the
 // lengths of the up-gate and down claim queues.  Uses misc[64..] ids.
-__device__ __forceinline__ void route_finalize(const mk_kargs& a, Smem& sm, int l) {
+__device__ __forceinline__ void route_finalize(const KA a, Smem& sm, int l) {
   if ((threadIdx.x >> 6) != 0) return;
-  const int lane = threadIdx.x & 63, K = a.topk, BK = a.B * K;
-  int32_t* meta = a.moe + (long)l * a.moe_stride;
-  int32_t* act = meta + 4;
-  int32_t* row_off = act + a.bk;
-  int32_t* row_tok = row_off + a.bk + 1;
-  int32_t* slot = row_tok + a.bk;
+  const int lane = threadIdx.x & 63, K = a->topk, BK = a->B * K;
+  int32_t* meta = a->moe + (long)l * a->moe_stride;
+  int32_t* slot = meta + 4;
+  int32_t* rec = slot + a->bk;            // [bk][16]: e, r0, nr, 0, token of each row
   uint32_t key = 0xFFFFFFFFu;
   if (lane < BK) {
     const int id = sm.misc[64 + lane];
@@ -675,15 +732,21 @@ __device__ __forceinline__ void route_finalize(const mk_kargs& a, Smem& sm, int 
   const uint64_t le = (lane == 63) ? ~0ull : ((2ull << lane) - 1ull);
   const int aidx = __popcll(smask & le) - 1;
   if (valid) {
+    const int r0 = 63 - __clzll(smask & le);           // first row of this expert
     stc(slot + src, lane);
-    stc(row_tok + lane, src / K);
-    if (start) { stc(act + aidx, e); stc(row_off + aidx, lane); }
+    stc(rec + aidx * 16 + 4 + (lane - r0), src / K);  // token of this row
+    if (start) {
+      const uint64_t after = smask & ~le;
+      const int next = after ? __ffsll((long long)after) - 1 : nrows;
+      stc(rec + aidx * 16 + 0, e);
+      stc(rec + aidx * 16 + 1, lane);
+      stc(rec + aidx * 16 + 2, next - lane);
+    }
   }
   if (lane == 0) {
-    stc(row_off + nact, nrows);
     stc(meta + 0, nact);
-    stc(meta + 1, nact * a.ug_tiles);
-    stc(meta + 2, nact * a.dn_tiles);
+    stc(meta + 1, nact * a->ug_tiles);
+    stc(meta + 2, nact * a->dn_tiles);
     stc(meta + 3, nrows);
   }
 }
@@ -696,36 +759,37 @@ __device__ __forceinline__ void route_finalize(const mk_kargs& a, Smem& sm, int 
 // The K and V rows of the first chunk are loaded before the wait on the QKV
 // tiles (cached keys are immutable); the key appended this step is re-read
 // with a coherent load after the wait.  q goes through LDS, staged by wave 0.
-constexpr int ATT_CH = 4;   // wave loads per chunk
+constexpr int ATT_CH = 8;   // wave loads per chunk
 
 template <int HD>
-__device__ __forceinline__ bool attn_split(const mk_kargs& a, Smem& sm, int l, int b, int g, int s, int p0, int p1, int ti,
+__device__ __forceinline__ bool attn_split(const KA a, Smem& sm, int l, int b, int g, int s, int p0, int p1, int ti,
                            int wait_idx, int wait_target) {
   constexpr int LPR = HD / 8;
   constexpr int PPW = 64 / LPR;
-  constexpr int PER_IT = MK_WAVES * PPW;   // keys per iteration of the workgroup
-  const int G = a.G, S = a.attn_split;
+  constexpr int PER_IT = MK_CW * PPW;     // keys per iteration of the workgroup
+  const int G = a->G, S = a->attn_split;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int sub = lane / LPR, c = lane - sub * LPR;
   const int n = p1 - p0;
   const int iters = (n + PER_IT - 1) / PER_IT;
-  const int rows = (a.Hq + 2 * a.Hkv) * HD;
-  const uint16_t* Kp = a.layers[l].k;
-  const uint16_t* Vp = a.layers[l].v;
-  const int32_t* bt = a.block_tables + (long)b * a.max_blocks;
-  const int newest = a.positions[b];
+  const int rows = (a->Hq + 2 * a->Hkv) * HD;
+  const uint16_t* Kp = a->layers[l].k;
+  const uint16_t* Vp = a->layers[l].v;
+  const int32_t* bt = a->block_tables + (long)b * a->max_blocks;
+  const int newest = a->positions[b];
   // element offset of key iteration `it` for this lane, or -1
   auto key_off = [&](int it, int* jpos) -> int {
-    const int jj = it * PER_IT + wave * PPW + sub;
+    if (wave == 0) return -1;   // the control wave holds no keys
+    const int jj = it * PER_IT + (wave - 1) * PPW + sub;
     if (jj >= n) return -1;
     const int j = p0 + jj;
     *jpos = j;
-    int pg = bt[j / a.page];
-    if (pg < 0 || pg >= a.num_pages) {
-      report(a, MK_E_DEVICE, ti, -3, pg, a.num_pages);
+    int pg = bt[j / a->page];
+    if (pg < 0 || pg >= a->num_pages) {
+      report(a, MK_E_DEVICE, ti, -3, pg, a->num_pages);
       pg = 0;
     }
-    return ((pg * a.Hkv + g) * a.page + (j % a.page)) * HD + c * 8;
+    return ((pg * a->Hkv + g) * a->page + (j % a->page)) * HD + c * 8;
   };
   u32x4 kb[ATT_CH], vb[ATT_CH];
   int ko[ATT_CH];
@@ -739,29 +803,31 @@ __device__ __forceinline__ bool attn_split(const mk_kargs& a, Smem& sm, int l, i
       vb[u] = ldg_nt(Vp + ko[u]);
     }
   }
+  MK_MARK(3);
   // wait for the QKV tiles, then wave 0 stages q of the group's heads
   float* qs = sm.xs;   // [G][HD]
   if (tid < 64) {
     int ok = 1;
     if (lane == 0) {
       ok = (wait_idx < 0 || wait_target <= 0) ? 1 : (int)spin_until(a, wait_idx, wait_target, ti);
-      if (a.trace && sm.t_ready == 0) sm.t_ready = wall_clock64();
+      if (a->trace && sm.t_ready == 0) sm.t_ready = wall_clock64();
     }
     ok = __shfl(ok, 0);
     if (lane == 0) sm.misc[0] = ok;
     if (ok) {
-      const float* qb = a.qkv + ((long)l * a.B + b) * rows + (long)(g * G) * HD;
+      const float* qb = a->qkv + ((long)l * a->B + b) * rows + (long)(g * G) * HD;
       for (int i = lane; i < G * HD / 4; i += 64)
         *reinterpret_cast<u32x4*>(qs + i * 4) = ldc16(qb, i * 16);
     }
   }
   __syncthreads();
+  MK_MARK(4);
   if (!sm.misc[0]) return false;
   float q[NBMAX][8];
 #pragma unroll
   for (int h = 0; h < NBMAX; ++h)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) q[h][e] = h < G ? qs[h * HD + c * 8 + e] * a.attn_scale : 0.f;
+    for (int e = 0; e < 8; ++e) q[h][e] = h < G ? qs[h * HD + c * 8 + e] * a->attn_scale : 0.f;
   float* sc = sm.ys;  // [G][S]
   // pass 1: scores, chunk by chunk
   for (int it0 = 0; it0 < iters; it0 += ATT_CH) {
@@ -800,8 +866,9 @@ __device__ __forceinline__ bool attn_split(const mk_kargs& a, Smem& sm, int l, i
     }
   }
   __syncthreads();
+  if (a->trace && tid == 0 && sm.t_mark[0] == 0) sm.t_mark[0] = wall_clock64();
   // pass 2: per-head max, exponentials and their sum
-  float* ml = a.part_ml + ((((long)(l & 1) * a.B + b) * a.Hq + g * G) * a.max_splits) * 2;
+  float* ml = a->part_ml + ((((long)(l & 1) * a->B + b) * a->Hq + g * G) * a->max_splits) * 2;
   if (wave < G) {
     float mx = -INFINITY;
     for (int jj = lane; jj < n; jj += 64) mx = fmaxf(mx, sc[wave * S + jj]);
@@ -814,11 +881,12 @@ __device__ __forceinline__ bool attn_split(const mk_kargs& a, Smem& sm, int l, i
     }
     sum = wave_sum(sum);
     if (lane == 0) {
-      stc(ml + ((long)wave * a.max_splits + s) * 2 + 0, mx);
-      stc(ml + ((long)wave * a.max_splits + s) * 2 + 1, sum);
+      stc(ml + ((long)wave * a->max_splits + s) * 2 + 0, mx);
+      stc(ml + ((long)wave * a->max_splits + s) * 2 + 1, sum);
     }
   }
   __syncthreads();
+  MK_MARK(6);
   // pass 3: o = sum p V, chunk by chunk (the first chunk is already loaded)
   float o[NBMAX][8];
 #pragma unroll
@@ -859,6 +927,7 @@ __device__ __forceinline__ bool attn_split(const mk_kargs& a, Smem& sm, int l, i
       }
     }
   }
+  if (a->trace && tid == 0 && sm.t_mark[1] == 0) sm.t_mark[1] = wall_clock64();
 #pragma unroll
   for (int h = 0; h < NBMAX; ++h)
 #pragma unroll
@@ -873,25 +942,26 @@ __device__ __forceinline__ bool attn_split(const mk_kargs& a, Smem& sm, int l, i
         for (int e = 0; e < 8; ++e) sm.red[(wave * NBMAX + h) * HD + c * 8 + e] = o[h][e];
   }
   __syncthreads();
-  float* po = a.part_o + ((((long)(l & 1) * a.B + b) * a.Hq + g * G) * a.max_splits) * HD;
+  float* po = a->part_o + ((((long)(l & 1) * a->B + b) * a->Hq + g * G) * a->max_splits) * HD;
   for (int idx = tid; idx < G * HD; idx += MK_THREADS) {
     const int h = idx / HD, dd = idx - h * HD;
     float v = 0.f;
 #pragma unroll
     for (int w = 0; w < MK_WAVES; ++w) v += sm.red[(w * NBMAX + h) * HD + dd];
-    stc(po + ((long)h * a.max_splits + s) * HD + dd, v);
+    stc(po + ((long)h * a->max_splits + s) * HD + dd, v);
   }
+  MK_MARK(7);
   return true;
 }
 
-__device__ __forceinline__ bool attn_item(const mk_kargs& a, Smem& sm, int l, int b, int g, int s, int ti, int wait_idx,
+__device__ __forceinline__ bool attn_item(const KA a, Smem& sm, int l, int b, int g, int s, int ti, int wait_idx,
                           int wait_target) {
   const int sl = live_len(a, b);
   const int kv = visible_keys(a, l, sl);
   const int start = sl - kv;
-  const int p0 = start + s * a.attn_split;
-  const int p1 = min(p0 + a.attn_split, sl);
-  if (a.hd == 128) return attn_split<128>(a, sm, l, b, g, s, p0, p1, ti, wait_idx, wait_target);
+  const int p0 = start + s * a->attn_split;
+  const int p1 = min(p0 + a->attn_split, sl);
+  if (a->hd == 128) return attn_split<128>(a, sm, l, b, g, s, p0, p1, ti, wait_idx, wait_target);
   return attn_split<64>(a, sm, l, b, g, s, p0, p1, ti, wait_idx, wait_target);
 }
 
@@ -899,15 +969,15 @@ __device__ __forceinline__ bool attn_item(const mk_kargs& a, Smem& sm, int l, in
 // o = sum_s e^(m_s - M) o_s / sum_s e^(m_s - M) l_s.  Wave h computes head
 // h's weights; then every thread accumulates 4 dims of one head over the
 // splits with its loads issued 8 splits at a time.
-__device__ __forceinline__ bool op_attn_combine(const mk_kargs& a, Smem& sm, const mk_task& t, int ti) {
-  const int l = t.layer, b = t.batch, g = t.group, G = a.G, hd = a.hd;
+__device__ __forceinline__ bool op_attn_combine(const KA a, Smem& sm, const mk_task& t, int ti) {
+  const int l = t.layer, b = t.batch, g = t.group, G = a->G, hd = a->hd;
   const int ns = n_splits(a, l, b);
   if (!wg_wait(a, sm, t.wait_ctr, ns, ti)) return false;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  float* out = a.attn + ((long)l * a.B + b) * a.Hq * hd;
-  const long hstride = (long)a.max_splits;
-  const float* ml0 = a.part_ml + ((((long)(l & 1) * a.B + b) * a.Hq + g * G) * hstride) * 2;
-  const float* po0 = a.part_o + ((((long)(l & 1) * a.B + b) * a.Hq + g * G) * hstride) * hd;
+  float* out = a->attn + ((long)l * a->B + b) * a->Hq * hd;
+  const long hstride = (long)a->max_splits;
+  const float* ml0 = a->part_ml + ((((long)(l & 1) * a->B + b) * a->Hq + g * G) * hstride) * 2;
+  const float* po0 = a->part_o + ((((long)(l & 1) * a->B + b) * a->Hq + g * G) * hstride) * hd;
   float* wts = sm.ys;                 // [G][max_splits]
   float* den = sm.red;                // [G]
   if (wave < G) {
@@ -971,25 +1041,9 @@ __device__ __forceinline__ bool is_claimer(int op) {
   return op == MK_OP_ATTN_DRAIN || op == MK_OP_MOE_UPGATE_ACT_DRAIN || op == MK_OP_MOE_DOWN_DRAIN;
 }
 
-// The argument block is copied to LDS once and read through a pointer the
-// compiler cannot see through, once per work unit.  Otherwise loop-invariant
-// code motion hoists dozens of argument-derived values to the kernel entry,
-// where they no longer fit in registers and are spilled to scratch.
-__device__ __forceinline__ const mk_kargs& launder(const mk_kargs* p) {
-  uint32_t v = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const mk_kargs*)p;
-  asm volatile("" : "+v"(v));
-  return *(const mk_kargs*)(__attribute__((address_space(3))) const mk_kargs*)(uintptr_t)v;
-}
-
 extern "C" __global__ void __launch_bounds__(MK_THREADS, 1) mk_persistent(mk_kargs a_arg, int final_launch) {
   __shared__ Smem sm;
-  __shared__ mk_kargs ka;
   const int tid = threadIdx.x;
-  {
-    const uint32_t* src = reinterpret_cast<const uint32_t*>(&a_arg);
-    uint32_t* dst = reinterpret_cast<uint32_t*>(&ka);
-    for (int i = tid; i < (int)(sizeof(mk_kargs) / 4); i += MK_THREADS) dst[i] = src[i];
-  }
   int ti = a_arg.task_begin + (int)blockIdx.x;
   const int task_end = a_arg.task_end;
   bool claiming = false, first = false, aborted = false;
@@ -998,15 +1052,15 @@ extern "C" __global__ void __launch_bounds__(MK_THREADS, 1) mk_persistent(mk_kar
   mk_task t;
   for (;;) {
     __syncthreads();
-    const mk_kargs& a = launder(&ka);
+    const KA a = kargs();
     int item = -1;
     if (!claiming) {
       if (ti >= task_end) break;
-      t = a.tasks[ti];
-      if (a.trace && tid == 0) {
+      t = a->tasks[ti];
+      if (a->trace && tid == 0) {
         t_start = wall_clock64();
         sm.t_ready = 0;
-        sm.t_mark[0] = sm.t_mark[1] = sm.t_mark[2] = 0;
+        for (int q = 0; q < 10; ++q) sm.t_mark[q] = 0;
         sm_trace_mark = &sm.t_mark[2];
       }
       if (is_claimer(t.op)) {
@@ -1015,7 +1069,7 @@ extern "C" __global__ void __launch_bounds__(MK_THREADS, 1) mk_persistent(mk_kar
           n_items = 0;
         } else if (t.op == MK_OP_ATTN_DRAIN) {
           n_items = 0;
-          for (int b = 0; b < a.B; ++b) n_items += n_splits(a, l, b) * a.Hkv;
+          for (int b = 0; b < a->B; ++b) n_items += n_splits(a, l, b) * a->Hkv;
           qidx = layer_ctr(a, l, MK_CTR_QATTN);
           attn_wait = t.wait_ctr;       // waited for inside the first item
         } else {
@@ -1023,7 +1077,7 @@ extern "C" __global__ void __launch_bounds__(MK_THREADS, 1) mk_persistent(mk_kar
             aborted = true;
             n_items = 0;
           } else {
-            const int32_t* meta = a.moe + (long)l * a.moe_stride;
+            const int32_t* meta = a->moe + (long)l * a->moe_stride;
             n_items = ldc(meta + (t.op == MK_OP_MOE_UPGATE_ACT_DRAIN ? 1 : 2));
           }
           qidx = layer_ctr(a, l, t.op == MK_OP_MOE_UPGATE_ACT_DRAIN ? MK_CTR_QUG : MK_CTR_QDN);
@@ -1042,88 +1096,92 @@ extern "C" __global__ void __launch_bounds__(MK_THREADS, 1) mk_persistent(mk_kar
     }
     if (aborted) goto unit_done;
     {
-      const int l = t.layer, B = a.B;
+      const int l = t.layer, B = a->B;
       GemvArgs g;
       StageArgs st;
       int kind = U_NONE;
       int epi_ae = 0, epi_r0 = 0, epi_nr = 0, epi_p0 = 0, epi_np = 0;
-      g.mode = ROW_PLAIN; g.half = 0; g.hd = a.hd; g.nb = B; g.out = nullptr; g.ob = 0;
+      g.mode = ROW_PLAIN; g.half = 0; g.hd = a->hd; g.nb = B; g.out = nullptr; g.ob = 0;
       g.r0 = t.n0; g.nrows = t.n1 - t.n0;
-      st.map = nullptr; st.map0 = 0; st.nb = B; st.wait_idx = t.wait_ctr; st.wait_target = t.wait_target;
+      st.use_tok = false; st.nb = B; st.wait_idx = t.wait_ctr; st.wait_target = t.wait_target;
       st.task = ti;
       switch (t.op) {
         case MK_OP_QKV_PROJ:
           kind = U_GEMV;
-          g.base = a.layers[l].w_qkv; g.ldw = a.d; g.K = a.d; g.nrows = 2 * (t.n1 - t.n0);
-          g.mode = ROW_ROPE_PAIRS; g.half = a.hd / 2;
-          st.base = a.xn + (long)l * B * a.d; st.ld = a.d; st.K = a.d;
+          g.base = a->layers[l].w_qkv; g.ldw = a->d; g.K = a->d; g.nrows = 2 * (t.n1 - t.n0);
+          g.mode = ROW_ROPE_PAIRS; g.half = a->hd / 2;
+          st.base = a->xn + (long)l * B * a->d; st.ld = a->d; st.K = a->d;
           break;
         case MK_OP_ROUTER_GEMM:
           kind = U_GEMV;
-          g.base = a.layers[l].w_router; g.ldw = a.d; g.K = a.d;
-          g.out = a.rlog + (long)l * B * a.E + t.n0; g.ob = a.E;
-          st.base = a.xn + (long)l * B * a.d; st.ld = a.d; st.K = a.d;
+          g.base = a->layers[l].w_router; g.ldw = a->d; g.K = a->d;
+          g.out = a->rlog + (long)l * B * a->E + t.n0; g.ob = a->E;
+          st.base = a->xn + (long)l * B * a->d; st.ld = a->d; st.K = a->d;
           break;
         case MK_OP_O_PROJ: {
           kind = U_GEMV;
-          const int gd = a.G * a.hd, grp = t.group;
-          g.base = a.layers[l].w_o + (long)grp * gd; g.ldw = (long)a.Hq * a.hd; g.K = gd;
-          g.out = a.opart + (((long)l * a.Hkv + grp) * B) * a.d + t.n0; g.ob = a.d;
-          st.base = a.attn + (long)l * B * a.Hq * a.hd + (long)grp * gd; st.ld = (long)a.Hq * a.hd; st.K = gd;
+          const int gd = a->G * a->hd, grp = t.group;
+          g.base = a->layers[l].w_o + (long)grp * gd; g.ldw = (long)a->Hq * a->hd; g.K = gd;
+          g.out = a->opart + (((long)l * a->Hkv + grp) * B) * a->d + t.n0; g.ob = a->d;
+          st.base = a->attn + (long)l * B * a->Hq * a->hd + (long)grp * gd; st.ld = (long)a->Hq * a->hd; st.K = gd;
           break;
         }
         case MK_OP_FFN_UPGATE_ACT:
           kind = U_GEMV;
-          g.base = a.layers[l].w_upgate; g.ldw = a.d; g.K = a.d; g.nrows = 2 * (t.n1 - t.n0);
-          g.mode = ROW_GATE_UP; g.half = a.F;
-          st.base = (a.parallel ? a.xn : a.xn2) + (long)l * B * a.d; st.ld = a.d; st.K = a.d;
+          g.base = a->layers[l].w_upgate; g.ldw = a->d; g.K = a->d; g.nrows = 2 * (t.n1 - t.n0);
+          g.mode = ROW_GATE_UP; g.half = a->F;
+          st.base = (a->parallel ? a->xn : a->xn2) + (long)l * B * a->d; st.ld = a->d; st.K = a->d;
           epi_p0 = t.n0; epi_np = t.n1 - t.n0;
           break;
         case MK_OP_FFN_DOWN:
           kind = U_GEMV;
-          g.base = a.layers[l].w_down; g.ldw = a.F; g.K = a.F;
-          g.out = a.fo + (long)l * B * a.d + t.n0; g.ob = a.d;
-          st.base = a.fh + (long)l * B * a.F; st.ld = a.F; st.K = a.F;
+          g.base = a->layers[l].w_down; g.ldw = a->F; g.K = a->F;
+          g.out = a->fo + (long)l * B * a->d + t.n0; g.ob = a->d;
+          st.base = a->fh + (long)l * B * a->F; st.ld = a->F; st.K = a->F;
           break;
         case MK_OP_LM_HEAD:
           kind = U_GEMV;
-          g.base = a.lm_head; g.ldw = a.d; g.K = a.d;
-          g.out = a.logits + t.n0; g.ob = a.V;
-          st.base = a.xn + (long)a.L * B * a.d; st.ld = a.d; st.K = a.d;
+          g.base = a->lm_head; g.ldw = a->d; g.K = a->d;
+          g.out = a->logits + t.n0; g.ob = a->V;
+          st.base = a->xn + (long)a->L * B * a->d; st.ld = a->d; st.K = a->d;
           break;
         case MK_OP_MOE_UPGATE_ACT_DRAIN: {
           // item = (active expert, tile of ug_pairs gate/up pairs) over that expert's rows
           kind = U_GEMV;
-          const int32_t* act = a.moe + (long)l * a.moe_stride + 4;
-          const int32_t* row_off = act + a.bk;
-          const int32_t* row_tok = row_off + a.bk + 1;
-          epi_ae = item / a.ug_tiles;
-          const int tt = item - epi_ae * a.ug_tiles;
-          const int e = ldc(act + epi_ae);
-          epi_r0 = ldc(row_off + epi_ae);
-          epi_nr = ldc(row_off + epi_ae + 1) - epi_r0;
-          epi_p0 = tt * a.ug_pairs;
-          epi_np = min(a.ug_pairs, a.I - epi_p0);
-          g.base = a.layers[l].w_upgate + (long)e * 2 * a.I * a.d; g.ldw = a.d; g.r0 = epi_p0;
-          g.nrows = 2 * epi_np; g.K = a.d; g.mode = ROW_GATE_UP; g.half = a.I; g.nb = epi_nr;
-          st.base = a.xn + (long)l * B * a.d; st.ld = a.d; st.map = row_tok; st.map0 = epi_r0; st.nb = epi_nr;
-          st.K = a.d; st.wait_idx = -1;
+          const int32_t* rec = a->moe + (long)l * a->moe_stride + 4 + a->bk;
+          epi_ae = item / a->ug_tiles;
+          const int tt = item - epi_ae * a->ug_tiles;
+          const u32x4 r0v = ldc16(rec, epi_ae * 64);
+          const u32x4 r1v = ldc16(rec, epi_ae * 64 + 16);
+          const u32x4 r2v = ldc16(rec, epi_ae * 64 + 32);
+          const int e = (int)r0v.x;
+          epi_r0 = (int)r0v.y;
+          epi_nr = (int)r0v.z;
+          st.use_tok = true;
+          st.tok[0] = (int)r1v.x; st.tok[1] = (int)r1v.y; st.tok[2] = (int)r1v.z; st.tok[3] = (int)r1v.w;
+          st.tok[4] = (int)r2v.x; st.tok[5] = (int)r2v.y; st.tok[6] = (int)r2v.z; st.tok[7] = (int)r2v.w;
+          epi_p0 = tt * a->ug_pairs;
+          epi_np = min(a->ug_pairs, a->I - epi_p0);
+          g.base = a->layers[l].w_upgate + (long)e * 2 * a->I * a->d; g.ldw = a->d; g.r0 = epi_p0;
+          g.nrows = 2 * epi_np; g.K = a->d; g.mode = ROW_GATE_UP; g.half = a->I; g.nb = epi_nr;
+          st.base = a->xn + (long)l * B * a->d; st.ld = a->d; st.nb = epi_nr;
+          st.K = a->d; st.wait_idx = -1;
           break;
         }
         case MK_OP_MOE_DOWN_DRAIN: {
           // item = (active expert, tile of dn_rows output rows); waits on the
           // expert's up-gate tiles after its weights are in flight
           kind = U_GEMV;
-          const int32_t* act = a.moe + (long)l * a.moe_stride + 4;
-          const int32_t* row_off = act + a.bk;
-          const int ae = item / a.dn_tiles, tt = item - ae * a.dn_tiles;
-          const int e = ldc(act + ae), r0 = ldc(row_off + ae), nr = ldc(row_off + ae + 1) - r0;
-          const int n0 = tt * a.dn_rows;
-          g.base = a.layers[l].w_down + (long)e * a.d * a.I; g.ldw = a.I; g.r0 = n0;
-          g.nrows = min(a.dn_rows, a.d - n0); g.K = a.I; g.nb = nr;
-          g.out = a.Y + ((long)l * a.bk + r0) * a.d + n0; g.ob = a.d;
-          st.base = a.H + ((long)l * a.bk + r0) * a.I; st.ld = a.I; st.nb = nr; st.K = a.I;
-          st.wait_idx = layer_ctr(a, l, a.cl.ug + ae); st.wait_target = a.ug_tiles;
+          const int32_t* rec = a->moe + (long)l * a->moe_stride + 4 + a->bk;
+          const int ae = item / a->dn_tiles, tt = item - ae * a->dn_tiles;
+          const u32x4 r0v = ldc16(rec, ae * 64);
+          const int e = (int)r0v.x, r0 = (int)r0v.y, nr = (int)r0v.z;
+          const int n0 = tt * a->dn_rows;
+          g.base = a->layers[l].w_down + (long)e * a->d * a->I; g.ldw = a->I; g.r0 = n0;
+          g.nrows = min(a->dn_rows, a->d - n0); g.K = a->I; g.nb = nr;
+          g.out = a->Y + ((long)l * a->bk + r0) * a->d + n0; g.ob = a->d;
+          st.base = a->H + ((long)l * a->bk + r0) * a->I; st.ld = a->I; st.nb = nr; st.K = a->I;
+          st.wait_idx = layer_ctr(a, l, a->cl.ug + ae); st.wait_target = a->ug_tiles;
           break;
         }
         default:
@@ -1143,13 +1201,13 @@ extern "C" __global__ void __launch_bounds__(MK_THREADS, 1) mk_persistent(mk_kar
             break;
           case MK_OP_FFN_UPGATE_ACT:
             __syncthreads();
-            epi_swiglu(sm, epi_np, B, a.fh + (long)l * B * a.F + epi_p0, a.F);
+            epi_swiglu(sm, epi_np, B, a->fh + (long)l * B * a->F + epi_p0, a->F);
             wg_signal(a, t.signal_ctr, 1);
             break;
           case MK_OP_MOE_UPGATE_ACT_DRAIN:
             __syncthreads();
-            epi_swiglu(sm, epi_np, epi_nr, a.H + ((long)l * a.bk + epi_r0) * a.I + epi_p0, a.I);
-            wg_signal(a, layer_ctr(a, l, a.cl.ug + epi_ae), 1);
+            epi_swiglu(sm, epi_np, epi_nr, a->H + ((long)l * a->bk + epi_r0) * a->I + epi_p0, a->I);
+            wg_signal(a, layer_ctr(a, l, a->cl.ug + epi_ae), 1);
             break;
           case MK_OP_MOE_DOWN_DRAIN:
             break;   // the claimer signals once its queue is drained
@@ -1159,7 +1217,7 @@ extern "C" __global__ void __launch_bounds__(MK_THREADS, 1) mk_persistent(mk_kar
               stores_done();
               __syncthreads();
               if (tid == 0)
-                sm.misc[3] = __hip_atomic_fetch_add(a.ctr + t.signal_ctr, 1, __ATOMIC_RELAXED,
+                sm.misc[3] = __hip_atomic_fetch_add(ctrp(a, t.signal_ctr), 1, __ATOMIC_RELAXED,
                                                     __HIP_MEMORY_SCOPE_AGENT) == t.aux[0] - 1;
               __syncthreads();
               if (sm.misc[3]) {
@@ -1192,9 +1250,9 @@ extern "C" __global__ void __launch_bounds__(MK_THREADS, 1) mk_persistent(mk_kar
           break;
         case MK_OP_ROUTE_FINALIZE:
           if (wg_wait(a, sm, t.wait_ctr, t.wait_target, ti)) {
-            for (int i = tid; i < B * a.topk; i += MK_THREADS) {
-              const int b = i / a.topk;
-              sm.misc[64 + i] = a.seq_lens[b] > 0 ? ldc(a.topi + ((long)l * B) * a.topk + i) : -1;
+            for (int i = tid; i < B * a->topk; i += MK_THREADS) {
+              const int b = i / a->topk;
+              sm.misc[64 + i] = a->seq_lens[b] > 0 ? ldc(a->topi + ((long)l * B) * a->topk + i) : -1;
             }
             __syncthreads();
             route_finalize(a, sm, l);
@@ -1207,7 +1265,7 @@ extern "C" __global__ void __launch_bounds__(MK_THREADS, 1) mk_persistent(mk_kar
           int it = item, b = 0, gq = 0, sp = -1;
           for (; b < B; ++b) {
             const int ns = n_splits(a, l, b);
-            const int cnt = ns * a.Hkv;
+            const int cnt = ns * a->Hkv;
             if (it < cnt) { gq = it / ns; sp = it - gq * ns; break; }
             it -= cnt;
           }
@@ -1217,7 +1275,7 @@ extern "C" __global__ void __launch_bounds__(MK_THREADS, 1) mk_persistent(mk_kar
               break;
             }
             attn_wait = -1;   // satisfied for every later item
-            wg_signal(a, layer_ctr(a, l, a.cl.attn + b * a.Hkv + gq), 1);
+            wg_signal(a, layer_ctr(a, l, a->cl.attn + b * a->Hkv + gq), 1);
           }
           break;
         }
@@ -1231,7 +1289,7 @@ extern "C" __global__ void __launch_bounds__(MK_THREADS, 1) mk_persistent(mk_kar
             aborted = true;
             break;
           }
-          wg_signal(a, layer_ctr(a, l, a.cl.attn + t.batch * a.Hkv + t.group), 1);
+          wg_signal(a, layer_ctr(a, l, a->cl.attn + t.batch * a->Hkv + t.group), 1);
           wg_signal(a, t.signal_ctr, 1);
           break;
         case MK_OP_ATTN_COMBINE:
@@ -1245,32 +1303,31 @@ extern "C" __global__ void __launch_bounds__(MK_THREADS, 1) mk_persistent(mk_kar
   unit_done:
     if (claiming) continue;
   task_done:
-    if (a.trace && tid == 0) {
-      uint64_t* tr = a.trace + (long)ti * 8;
+    if (a->trace && tid == 0) {
+      uint64_t* tr = a->trace + (long)ti * 16;
       tr[0] = t_start;
       tr[1] = sm.t_ready ? sm.t_ready : t_start;
-      tr[2] = sm.t_mark[0];
-      tr[3] = sm.t_mark[1];
-      tr[4] = sm.t_mark[2];
-      tr[5] = wall_clock64();
-      tr[6] = blockIdx.x;
-      tr[7] = t.op;
+      for (int q = 0; q < 10; ++q) tr[2 + q] = sm.t_mark[q];
+      tr[12] = wall_clock64();
+      tr[13] = blockIdx.x;
+      tr[14] = t.op;
+      tr[15] = 0;
     }
     ti += (int)gridDim.x;
   }
   // The last workgroup out clears the counters for the next launch.
   __syncthreads();
-  const mk_kargs& a = a_arg;
+  const KA a = kargs();
   if (tid == 0) {
-    const int old = __hip_atomic_fetch_add(a.ctr + MK_CG_DONE, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int old = __hip_atomic_fetch_add(ctrp(a, MK_CG_DONE), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     sm.misc[2] = (old == (int)gridDim.x - 1);
   }
   __syncthreads();
   if (sm.misc[2]) {
     if (final_launch) {
-      for (int i = tid; i < a.n_ctr; i += MK_THREADS) stc(a.ctr + i, 0);
+      for (int i = tid; i < a->n_ctr; i += MK_THREADS) stc(ctrp(a, i), 0);
     } else if (tid == 0) {
-      stc(a.ctr + MK_CG_DONE, 0);
+      stc(ctrp(a, MK_CG_DONE), 0);
     }
   }
 }
@@ -1279,22 +1336,22 @@ extern "C" __global__ void __launch_bounds__(MK_THREADS, 1) mk_persistent(mk_kar
 extern "C" int mk_launch(const mk_kargs* args, int launch_mode, const int32_t* wave_bounds, int n_waves,
                          void* stream) {
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  mk_kargs a = *args;
-  const dim3 grid((unsigned)a.n_wg), block(MK_THREADS);
+  mk_kargs k = *args;
+  const dim3 grid((unsigned)k.n_wg), block(MK_THREADS);
   if (launch_mode == MK_LAUNCH_PERSISTENT) {
-    a.task_begin = 0;
-    a.task_end = a.n_tasks;
+    k.task_begin = 0;
+    k.task_end = k.n_tasks;
     int fin = 1;
-    void* kp[] = {&a, &fin};
+    void* kp[] = {&k, &fin};
     hipError_t e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(mk_persistent), grid, block, kp, 0, st);
     return e == hipSuccess ? MK_OK : MK_E_HIP;
   }
   // ablation: one launch per task wave; the kernel boundary orders the waves
   for (int w = 0; w < n_waves; ++w) {
-    a.task_begin = wave_bounds[w];
-    a.task_end = wave_bounds[w + 1];
+    k.task_begin = wave_bounds[w];
+    k.task_end = wave_bounds[w + 1];
     int fin = (w == n_waves - 1) ? 1 : 0;
-    void* kp[] = {&a, &fin};
+    void* kp[] = {&k, &fin};
     hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(mk_persistent), grid, block, kp, 0, st);
     if (e != hipSuccess) return MK_E_HIP;
   }

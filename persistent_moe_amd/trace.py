@@ -30,7 +30,7 @@ def load(eng) -> dict:
     """Trace of the last step of a DecodeEngine built with MK_SCHED_TRACE."""
     from . import mk
     tasks, _ = mk.mk_plan_schedule(eng.mkcfg, eng.wl.batch, eng.max_blocks, eng.opts, _n_wg(eng))
-    raw = eng.tap("trace").cpu().numpy().reshape(-1, 8)[:len(tasks)]
+    raw = eng.tap("trace").cpu().numpy().reshape(-1, 16)[:len(tasks)]
     return {"tasks": tasks, "raw": raw}
 
 
@@ -44,9 +44,10 @@ def _n_wg(eng):
 def summarize(tr: dict) -> dict:
     tasks, raw = tr["tasks"], tr["raw"].astype(np.int64)
     t0 = raw[:, 0].min()
-    start, ready, end, wg = raw[:, 0] - t0, raw[:, 1] - t0, raw[:, 5] - t0, raw[:, 6]
+    start, ready, end, wg = raw[:, 0] - t0, raw[:, 1] - t0, raw[:, 12] - t0, raw[:, 13]
     per_op = defaultdict(lambda: [0, 0.0, 0.0])
     phases = defaultdict(lambda: [[], [], [], []])   # ready->staged, staged->computed, computed->stored, stored->end
+    mark_times = defaultdict(lambda: defaultdict(list))   # per opcode: mark -> times after task start
     per_layer = defaultdict(lambda: [np.inf, 0.0])
     for i, t in enumerate(tasks):
         name = OPCODES[t.op]
@@ -60,7 +61,15 @@ def summarize(tr: dict) -> dict:
             ph[0].append((st - raw[i, 1]) * TICK_US)
             ph[1].append((cp - st) * TICK_US)
             ph[2].append((so - cp) * TICK_US)
-            ph[3].append((raw[i, 5] - so) * TICK_US)
+            ph[3].append((raw[i, 12] - so) * TICK_US)
+        marks = [raw[i, 2 + q] for q in range(10)]
+        if any(marks[3:]):
+            mm = mark_times[name]
+            for q in range(10):
+                if marks[q]:
+                    mm[q].append((marks[q] - raw[i, 0]) * TICK_US)
+            mm["ready"].append((raw[i, 1] - raw[i, 0]) * TICK_US)
+            mm["end"].append((raw[i, 12] - raw[i, 0]) * TICK_US)
         pl = per_layer[t.layer]
         pl[0] = min(pl[0], start[i] * TICK_US)
         pl[1] = max(pl[1], end[i] * TICK_US)
@@ -80,6 +89,8 @@ def summarize(tr: dict) -> dict:
                                  "store_ack": round(float(np.median(v[2])), 2),
                                  "tail": round(float(np.median(v[3])), 2)}
                              for k, v in phases.items() if v[0]},
+        "marks_median_us_from_start": {k: {str(q): round(float(np.median(v)), 2) for q, v in sorted(m.items(), key=str)}
+                                       for k, m in mark_times.items()},
     }
 
 
@@ -88,7 +99,7 @@ def chrome_trace(tr: dict, path: str) -> None:
     t0 = raw[:, 0].min()
     ev = []
     for i, t in enumerate(tasks):
-        s, r, e, w = (raw[i, 0] - t0) * TICK_US, (raw[i, 1] - t0) * TICK_US, (raw[i, 5] - t0) * TICK_US, raw[i, 6]
+        s, r, e, w = (raw[i, 0] - t0) * TICK_US, (raw[i, 1] - t0) * TICK_US, (raw[i, 12] - t0) * TICK_US, raw[i, 13]
         name = f"{OPCODES[t.op]} L{t.layer}"
         if r > s:
             ev.append({"name": "wait " + name, "ph": "X", "ts": float(s), "dur": float(r - s), "pid": 0,
