@@ -108,7 +108,7 @@ typedef struct mk_config {
   int32_t expert_inter;    /* I, per-expert SwiGLU width (MoE)               */
   int32_t ffn_inter;       /* F, dense SwiGLU width (dense)                  */
   int32_t parallel_block;  /* 1: parallel MoE block; 0: sequential pre-norm  */
-  int32_t page_size;       /* tokens per KV page; 16                         */
+  int32_t page_size;       /* tokens per KV page; must be 16                 */
   int32_t max_batch;       /* 1..8                                           */
   int32_t swa_window;      /* 0: all layers global; else window in tokens    */
   int32_t swa_period;      /* layer l is global iff l % period == period - 1 */
@@ -143,9 +143,15 @@ typedef struct mk_weights {
   const mk_layer_weights* layers; /* host array of n_layers entries (copied) */
 } mk_weights;
 
-/* Paged KV cache: per layer, K and V pools [num_pages][Hkv][page_size][hd]
- * bf16 (device).  One (page, head) block is page_size*hd contiguous values.
- * The kernel writes only the slot of each sequence's new token.           */
+/* Paged KV cache: per layer, a K pool [num_pages][Hkv][page_size][hd] and a
+ * V pool [num_pages][Hkv][hd][page_size], bf16 (device): within a page a K
+ * block holds one key per row, a V block one head dimension per row (V is
+ * stored transposed so that the attention PV product reads 8 consecutive
+ * keys of one dimension as one 16-byte load).  page_size must be 16.  The
+ * kernel writes only the slot of each sequence's new token.  Slots of a
+ * sequence's pages beyond its length are read (and given zero attention
+ * weight), so pools must be initialised (e.g. zeroed): NaN there would
+ * propagate.                                                              */
 typedef struct mk_kv_pool {
   void* const* k;           /* host array of n_layers device pointers        */
   void* const* v;           /* host array of n_layers device pointers        */

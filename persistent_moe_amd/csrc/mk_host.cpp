@@ -27,6 +27,7 @@ namespace {
 constexpr int kMaxWorkgroups = 1024;
 constexpr int kYsFloats = 8192;    // LDS capacity for scores / tile outputs (mk_kernel.hip)
 constexpr int kXsFloats = 16384;   // LDS capacity for staged activations
+constexpr int kMaxGemvK = 8192;    // GEMV reduction length: 16 register slots x 512 (half from 4 rows)
 
 struct Layout {
   size_t off_tasks, off_ctr, off_err, off_layers, off_invf, off_rope;
@@ -45,6 +46,7 @@ int validate_config(const mk_config* c) {
     return MK_E_INVAL;
   if (c->n_q_heads % c->n_kv_heads != 0) return MK_E_INVAL;
   if (c->d_model % 8 != 0 || c->page_size <= 0) return MK_E_INVAL;
+  if (c->page_size != 16) return MK_E_UNSUPPORTED;   // one 16-key MFMA tile per page
   if (c->max_batch < 1 || c->max_batch > 8) return MK_E_UNSUPPORTED;
   if (c->head_dim != 64 && c->head_dim != 128) return MK_E_UNSUPPORTED;
   if (c->n_q_heads / c->n_kv_heads > 8) return MK_E_UNSUPPORTED;
@@ -60,9 +62,11 @@ int validate_config(const mk_config* c) {
     if (c->ffn_inter <= 0 || c->ffn_inter % 8 != 0) return MK_E_INVAL;
     if (c->parallel_block) return MK_E_UNSUPPORTED;
     if ((size_t)c->max_batch * c->ffn_inter > (size_t)kXsFloats) return MK_E_UNSUPPORTED;
+    if (c->ffn_inter > (c->max_batch >= 4 ? kMaxGemvK / 2 : kMaxGemvK)) return MK_E_UNSUPPORTED;
   }
   if ((size_t)c->max_batch * c->d_model > (size_t)kXsFloats) return MK_E_UNSUPPORTED;
   if (c->d_model > 4096) return MK_E_UNSUPPORTED;   // the norm task holds 2 chunks of 4 per thread
+  if (moe && c->expert_inter > (c->max_batch >= 4 ? kMaxGemvK / 2 : kMaxGemvK)) return MK_E_UNSUPPORTED;
   if (c->top_k > 8 || c->n_kv_heads > 8) return MK_E_UNSUPPORTED;
   const int gd = c->n_q_heads / c->n_kv_heads * c->head_dim;
   if ((size_t)c->max_batch * gd > (size_t)kXsFloats) return MK_E_UNSUPPORTED;
@@ -160,7 +164,10 @@ int build_plan(const mk_config* c, int B, int32_t max_blocks, const mk_sched_opt
   p.n_ctr = p.cl.total;
   // attention split length: about NW items per layer at the longest context
   int S = o.attn_split;
-  const int smax = std::min(kYsFloats / G, 1024);
+  // scores of a split live in LDS as [G][S + 32] floats (a split that does
+  // not start on a page boundary touches one extra 16-key tile, and the
+  // PV pass rounds the tiles up to pairs)
+  const int smax = std::min((kYsFloats / G - 32) / 16 * 16, 1024);
   if (S > 0) {
     if (S % c->page_size != 0 || S < MK_MIN_SPLIT || S > smax) return MK_E_INVAL;
   } else {

@@ -1,7 +1,11 @@
 // mk_kernel.hip - the persistent decode megakernel for gfx950 (MI355X).
 //
 // One launch runs one decode step.  The grid holds one workgroup per CU
-// (512 threads = 8 wave64s, ~130 KB of LDS so no second workgroup fits);
+// (256 threads = 4 wave64s, one per SIMD, ~130 KB of LDS so no second
+// workgroup fits).  One wave per SIMD gives each wave the SIMD's whole
+// register file (256 VGPRs + 256 AGPRs), so the compiler spills into AGPRs
+// instead of scratch memory: a scratch reload is a vector-memory load, and
+// it would wait behind every weight load the wave has in flight.
 // workgroup w walks tasks w, w+N, w+2N, ... of the host-built list (task k on
 // workgroup k mod N).  A task waits on one counter in global memory, runs one
 // tile, and bumps one counter (persistent decode megakernel pages: page 1
@@ -32,16 +36,16 @@
 
 #include "mk_internal.h"
 
-#define MK_THREADS 512
-#define MK_WAVES 8
+#define MK_THREADS 256
+#define MK_WAVES 4
 #define XS_FLOATS 16384   // staged activations, 64 KB
 #define YS_FLOATS 8192    // tile outputs / attention scores, 32 KB
 #define RED_FLOATS 8192   // attention cross-wave reduction, 32 KB
 #define NBMAX 8
-#ifndef MK_WBUD1
-#define MK_WBUD1 4        // 16-byte loads per lane per row group (batch 1): bounds bytes in flight
+#ifndef MK_WB
+#define MK_WB 16          // 16-byte weight loads per lane per GEMV row group (2 groups in flight)
 #endif
-#define MK_CW 7           // compute waves: wave 0 is the control wave (spins, stages)
+#define MK_CW 3           // compute waves: wave 0 is the control wave (spins, stages)
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -69,6 +73,7 @@ struct __attribute__((aligned(16))) Smem {
   float ys[YS_FLOATS];
   float red[RED_FLOATS];
   int misc[192];
+  uint32_t sortk[128];
   uint64_t t_ready;   // trace: when the task's first wait was satisfied
   uint64_t t_mark[10]; // trace: [0] staged, [1] computed, [2] stores acknowledged, [3..9] free marks
 };
@@ -81,18 +86,85 @@ __device__ __forceinline__ uint16_t f_to_bf16(float f) {
   uint32_t b = __float_as_uint(f);
   return (uint16_t)((b + 0x7FFFu + ((b >> 16) & 1u)) >> 16);
 }
+// Pointers read from the argument block are generic; a load through a
+// generic pointer is a flat load, which the hardware counts as both a vector
+// memory and an LDS access, so any later LDS read would have to wait for every
+// weight load still in flight.  Global accesses are cast to address space 1.
+#define GLOBAL __attribute__((address_space(1)))
+typedef GLOBAL const u32x4 gc_u32x4;
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef GLOBAL const u32x2 gc_u32x2;
+// 4 bf16 (8 bytes) from global memory
+__device__ __forceinline__ u32x2 ldg8(const uint16_t* p) { return *(gc_u32x2*)p; }
 __device__ __forceinline__ u32x4 ldg_nt(const uint16_t* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return __builtin_nontemporal_load((gc_u32x4*)p);
 }
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+// Cross-lane reductions.  HIP's __shfl_xor is a ds_bpermute through the LDS
+// crossbar: with one wave per SIMD every dependent step would stall the wave
+// for a whole LDS round trip.  Within a row of 16 lanes these use DPP
+// (quad permutes, half-row and row mirrors: for a sum or max each step pairs
+// every lane with one of the other half, like a butterfly); across rows the
+// gfx950 permlane swaps (rows 2r <-> 2r+1, then halves) or v_readlane.
+// All of them must be called with every lane of the wave active.
+enum { DPP_QP_X1 = 0xB1, DPP_QP_X2 = 0x4E, DPP_ROW_ROR8 = 0x128, DPP_ROW_MIRROR = 0x140, DPP_HALF_MIRROR = 0x141 };
+template <int CTRL>
+__device__ __forceinline__ float dppf(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+template <int CTRL>
+__device__ __forceinline__ int dppi(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, true);
+}
+// sum / max over aligned groups of N lanes (N in 2, 4, 8, 16), in every lane
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+  if (N >= 2) v += dppf<DPP_QP_X1>(v);
+  if (N >= 4) v += dppf<DPP_QP_X2>(v);
+  if (N >= 8) v += dppf<DPP_HALF_MIRROR>(v);
+  if (N >= 16) v += dppf<DPP_ROW_MIRROR>(v);
   return v;
+}
+template <int N>
+__device__ __forceinline__ float group_max(float v) {
+  if (N >= 2) v = fmaxf(v, dppf<DPP_QP_X1>(v));
+  if (N >= 4) v = fmaxf(v, dppf<DPP_QP_X2>(v));
+  if (N >= 8) v = fmaxf(v, dppf<DPP_HALF_MIRROR>(v));
+  if (N >= 16) v = fmaxf(v, dppf<DPP_ROW_MIRROR>(v));
+  return v;
+}
+template <int N>
+__device__ __forceinline__ int group_min(int v) {
+  if (N >= 2) v = min(v, dppi<DPP_QP_X1>(v));
+  if (N >= 4) v = min(v, dppi<DPP_QP_X2>(v));
+  if (N >= 8) v = min(v, dppi<DPP_HALF_MIRROR>(v));
+  if (N >= 16) v = min(v, dppi<DPP_ROW_MIRROR>(v));
+  return v;
+}
+// sum of the lanes l, l^16, l^32, l^48 (the same position in the 4 rows)
+__device__ __forceinline__ float cross_row_sum(float v) {
+  const unsigned u = __float_as_uint(v);
+  const auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  v = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  const unsigned w = __float_as_uint(v);
+  const auto q = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
+__device__ __forceinline__ float lane_f(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+// whole-wave sum / max / min, returned uniform
+__device__ __forceinline__ float wave_sum(float v) {
+  v = group_sum<16>(v);
+  return (lane_f(v, 0) + lane_f(v, 16)) + (lane_f(v, 32) + lane_f(v, 48));
 }
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
-  return v;
+  v = group_max<16>(v);
+  return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
+}
+__device__ __forceinline__ int wave_min(int v) {
+  v = group_min<16>(v);
+  return min(min(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+             min(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
 }
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
 
@@ -101,24 +173,24 @@ __device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
 __device__ __forceinline__ int32_t* ctrp(const KA a, int idx) { return a->ctr + (long)idx * MK_CTR_PAD; }
 
 __device__ __forceinline__ int ld_agent(const int32_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return __hip_atomic_load((GLOBAL const int32_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Agent-coherent loads and stores of data shared between workgroups.
 __device__ __forceinline__ float ldc(const float* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return __hip_atomic_load((GLOBAL const float*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ int ldc(const int32_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return __hip_atomic_load((GLOBAL const int32_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void stc(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store((GLOBAL float*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void stc(int32_t* p, int v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store((GLOBAL int32_t*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void stc(uint16_t* p, uint16_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store((GLOBAL uint16_t*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 // 16-byte agent-coherent load at base + byte_off; base must be uniform.
 __device__ __forceinline__ u32x4 ldc16(const void* base, int byte_off) {
@@ -184,7 +256,7 @@ __device__ __forceinline__ bool wg_wait(const KA a, Smem& sm, int idx, int targe
   return ok;
 }
 
-__shared__ uint64_t* sm_trace_mark;   // trace: where wg_signal records its time
+__shared__ uint64_t sm_t_signal;   // trace: when wg_signal last bumped a counter
 // trace: first time this task passes mark k (thread 0)
 #define MK_MARK(k)                                                              \
   do {                                                                          \
@@ -196,7 +268,7 @@ __shared__ uint64_t* sm_trace_mark;   // trace: where wg_signal records its time
 __device__ __forceinline__ void wg_signal(const KA a, int idx, int inc) {
   stores_done();
   __syncthreads();
-  if (a->trace && threadIdx.x == 0 && sm_trace_mark) *sm_trace_mark = wall_clock64();
+  if (a->trace && threadIdx.x == 0) sm_t_signal = wall_clock64();
   if (threadIdx.x == 0 && idx >= 0)
     __hip_atomic_fetch_add(ctrp(a, idx), inc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -252,10 +324,10 @@ __device__ __forceinline__ int n_splits(const KA a, int layer, int b) {
 // y[b][r] = sum_k W[row(r)][k] * x[b][k] for the rows of one tile.  Every
 // GEMV opcode runs through this one routine; they differ in the row mapping,
 // where x comes from, and the epilogue (page 1: all GEMM opcodes share one
-// pipeline).  Each wave owns RPW consecutive tile rows per row group; lane l
-// reads 16-byte segments l, l+64, ... of each row (KCH of them), so one wave
-// load moves 1 KB of contiguous weights.  The register tile of the next row
-// group is loaded while the current one is reduced (double buffering).
+// pipeline).  Lane l reads 16-byte segments l, l+64, ... of each weight row,
+// so one wave load moves 1 KB of contiguous weights.  Two register tiles
+// (row groups) are in flight: the next one loads while the current one is
+// multiplied and reduced.
 enum { ROW_PLAIN = 0, ROW_ROPE_PAIRS = 1, ROW_GATE_UP = 2 };
 
 struct GemvArgs {
@@ -265,7 +337,7 @@ struct GemvArgs {
   int nrows;       // tile rows (2 per pair for the paired modes)
   int K;           // reduction length (multiple of 8)
   int mode;        // ROW_*
-  int half;        // ROW_ROPE_PAIRS: hd/2; ROW_GATE_UP: I (offset of the up rows)
+  int half;        // ROW_ROPE_PAIRS: hd/2 (a power of two); ROW_GATE_UP: I (offset of the up rows)
   int hd;
   int xstride;     // floats between staged x rows in LDS
   int nb;          // live batch rows
@@ -274,81 +346,94 @@ struct GemvArgs {
   long ob;
 };
 
+// Weight row of tile row r, one formula for the three modes: tile rows come
+// singly (plain) or in pairs (paired modes, pm = 1); pair p = r0 + r/2 maps to
+// rows p + (p / (hd/2) + upper) * half, which for RoPE pairs (half = hd/2) is
+// head * hd + i (+ hd/2 for the upper row), and for gate/up pairs (the shift
+// hs = 31 makes p / 2^hs zero) is p (+ I).
 __device__ __forceinline__ const uint16_t* gemv_row(const GemvArgs& g, int r) {
-  if (g.mode == ROW_PLAIN) return g.base + (long)(g.r0 + r) * g.ldw;
-  const int p = g.r0 + (r >> 1), upper = r & 1;
-  if (g.mode == ROW_ROPE_PAIRS) {
-    const int head = p / g.half, i = p - head * g.half;
-    return g.base + (long)(head * g.hd + i + upper * g.half) * g.ldw;
-  }
-  return g.base + (long)(p + upper * g.half) * g.ldw;
+  const int pm = g.mode != ROW_PLAIN ? 1 : 0;
+  const int p = g.r0 + (r >> pm), upper = r & pm;
+  const int hs = g.mode == ROW_ROPE_PAIRS ? 31 - __builtin_clz(g.half) : 31;
+  return g.base + (long)(p + ((p >> hs) + upper) * g.half) * g.ldw;
 }
 
-template <int NB, int KCH, int RPW>
+// Register tile of one row group: WB 16-byte weight loads per lane of each
+// compute wave (MK_WB, halved for 4 or more batch rows, whose accumulators
+// take the registers).  Slot u holds K-chunk (u mod kch) of tile row
+// (u / kch), where a K-chunk is 512 elements (64 lanes x 8) and kch = 2^kl
+// covers K; so a wave owns WB / kch consecutive rows per group.  kch is a
+// runtime value, so one instance per batch width serves every GEMV shape:
+// the step's hot code stays small enough for the instruction cache.
+template <int NB>
 struct GemvTile {
-  u32x4 w[RPW][KCH];
+  static constexpr int WB = NB >= 4 ? MK_WB / 2 : MK_WB;
+  u32x4 w[WB];
 
-  // tile row j of compute wave cw (1..7) in row group grp
-  __device__ __forceinline__ static int row_of(int grp, int cw, int j) { return (grp * MK_CW + cw - 1) * RPW + j; }
+  // first tile row of compute wave cw (1..MK_CW) in row group grp
+  __device__ __forceinline__ static int row0(int grp, int cw, int kl) {
+    return (grp * MK_CW + cw - 1) * (WB >> kl);
+  }
 
-  __device__ __forceinline__ void load(const GemvArgs& g, int grp) {
+  __device__ __forceinline__ void load(const GemvArgs& g, int grp, int kl) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int r0 = row0(grp, wave, kl), cm = (1 << kl) - 1;
 #pragma unroll
-    for (int j = 0; j < RPW; ++j) {
-      const int r = row_of(grp, wave, j);
-      const bool rv = r < g.nrows;
-      const uint16_t* rp = rv ? gemv_row(g, r) : g.base;
-#pragma unroll
-      for (int c = 0; c < KCH; ++c) {
-        const int seg = lane + 64 * c;
-        if (rv && seg * 8 < g.K) w[j][c] = ldg_nt(rp + seg * 8);
-        else w[j][c] = (u32x4){0u, 0u, 0u, 0u};
-      }
+    for (int u = 0; u < WB; ++u) {
+      const int r = r0 + (u >> kl), seg = lane + 64 * (u & cm);
+      if (r < g.nrows && seg * 8 < g.K) w[u] = ldg_nt(gemv_row(g, r) + seg * 8);
+      else w[u] = (u32x4){0u, 0u, 0u, 0u};
     }
   }
 
-  __device__ __forceinline__ void compute(const GemvArgs& g, int grp, const float* xs, float* ys) {
+  __device__ __forceinline__ void compute(const GemvArgs& g, int grp, int kl, const float* xs, float* ys) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    if (row_of(grp, wave, 0) >= g.nrows) return;   // wave-uniform: no rows in this group
-    float acc[RPW][NB];
+    const int r0 = row0(grp, wave, kl), cm = (1 << kl) - 1;
+    if (r0 >= g.nrows) return;   // wave-uniform: no rows in this group
+    float acc[WB][NB];
 #pragma unroll
-    for (int j = 0; j < RPW; ++j)
-#pragma unroll
-      for (int b = 0; b < NB; ++b) acc[j][b] = 0.f;
-#pragma unroll
-    for (int c = 0; c < KCH; ++c) {
-      const int seg = lane + 64 * c;
-      if (seg * 8 < g.K) {
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
-          const f32x4* xp = reinterpret_cast<const f32x4*>(xs + b * g.xstride + seg * 8);
-          const f32x4 x0 = xp[0], x1 = xp[1];
-#pragma unroll
-          for (int j = 0; j < RPW; ++j) {
-            const u32x4 v = w[j][c];
-            float s = acc[j][b];
-            s = fmaf(bf_lo(v.x), x0.x, s);
-            s = fmaf(bf_hi(v.x), x0.y, s);
-            s = fmaf(bf_lo(v.y), x0.z, s);
-            s = fmaf(bf_hi(v.y), x0.w, s);
-            s = fmaf(bf_lo(v.z), x1.x, s);
-            s = fmaf(bf_hi(v.z), x1.y, s);
-            s = fmaf(bf_lo(v.w), x1.z, s);
-            s = fmaf(bf_hi(v.w), x1.w, s);
-            acc[j][b] = s;
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < RPW; ++j) {
-      const int r = row_of(grp, wave, j);
+    for (int u = 0; u < WB; ++u) {
+      const int seg = lane + 64 * (u & cm);
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
-        const float s = wave_sum(acc[j][b]);
-        if (lane == 0 && r < g.nrows && b < g.nb) {
-          if (g.out) stc(g.out + (long)b * g.ob + r, s);
-          else ys[r * NBMAX + b] = s;
+        const f32x4* xp = reinterpret_cast<const f32x4*>(xs + b * g.xstride + (seg * 8 < g.K ? seg * 8 : 0));
+        const f32x4 x0 = xp[0], x1 = xp[1];
+        const u32x4 v = w[u];
+        float s = 0.f;
+        s = fmaf(bf_lo(v.x), x0.x, s);
+        s = fmaf(bf_hi(v.x), x0.y, s);
+        s = fmaf(bf_lo(v.y), x0.z, s);
+        s = fmaf(bf_hi(v.y), x0.w, s);
+        s = fmaf(bf_lo(v.z), x1.x, s);
+        s = fmaf(bf_hi(v.z), x1.y, s);
+        s = fmaf(bf_lo(v.w), x1.z, s);
+        s = fmaf(bf_hi(v.w), x1.w, s);
+        acc[u][b] = s;
+      }
+    }
+    // add the K-chunks of each row: slots 2i and 2i+1 belong to one row
+    // until kch chunks have been folded
+#pragma unroll
+    for (int step = 1; step < WB; step <<= 1) {
+      if ((1 << kl) > step) {
+#pragma unroll
+        for (int i = 0; i < WB / (2 * step); ++i)
+#pragma unroll
+          for (int b = 0; b < NB; ++b) acc[i][b] = acc[2 * i][b] + acc[2 * i + 1][b];
+      }
+    }
+    const int rpw = WB >> kl;
+#pragma unroll
+    for (int j = 0; j < WB; ++j) {
+      if (j < rpw) {
+        const int r = r0 + j;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          const float s = wave_sum(acc[j][b]);
+          if (lane == 0 && r < g.nrows && b < g.nb) {
+            if (g.out) stc(g.out + (long)b * g.ob + r, s);
+            else ys[r * NBMAX + b] = s;
+          }
         }
       }
     }
@@ -380,7 +465,7 @@ __device__ __forceinline__ bool wait_and_stage(const KA a, Smem& sm, const Stage
       ok = (s.wait_idx < 0 || s.wait_target <= 0) ? 1 : (int)spin_until(a, s.wait_idx, s.wait_target, s.task);
       if (a->trace && sm.t_ready == 0) sm.t_ready = wall_clock64();
     }
-    ok = __shfl(ok, 0);
+    ok = __builtin_amdgcn_readfirstlane(ok);
     if (lane == 0) sm.misc[0] = ok;
     if (ok) {
       const int kv = s.K >> 2, total = s.nb * kv;
@@ -414,26 +499,28 @@ __device__ __forceinline__ bool wait_and_stage(const KA a, Smem& sm, const Stage
   return sm.misc[0] != 0;
 }
 
-template <int NB, int KCH, int RPW>
-__device__ bool gemv_run(const KA a, Smem& sm, const GemvArgs& g, const StageArgs& s) {
-  GemvTile<NB, KCH, RPW> A, Bt;
-  const int per = MK_CW * RPW;
+template <int NB>
+__device__ __forceinline__ bool gemv_run(const KA a, Smem& sm, const GemvArgs& g, const StageArgs& s) {
+  GemvTile<NB> A, Bt;
+  const int kch = (g.K + 511) >> 9;
+  const int kl = kch <= 1 ? 0 : 32 - __builtin_clz(kch - 1);   // ceil(log2(kch)); K <= 512 * WB
+  const int per = MK_CW * (GemvTile<NB>::WB >> kl);
   const int ng = (g.nrows + per - 1) / per;
   const bool cw = (threadIdx.x >> 6) != 0;
   // the first two row groups are in flight before the dependency resolves;
   // the control wave loads no weights, so its staging loads queue behind nothing
   if (cw) {
-    A.load(g, 0);
-    if (ng > 1) Bt.load(g, 1);
+    A.load(g, 0, kl);
+    if (ng > 1) Bt.load(g, 1, kl);
   }
   if (!wait_and_stage(a, sm, s)) return false;
   if (cw) {
     for (int grp = 0; grp < ng; grp += 2) {
-      A.compute(g, grp, sm.xs, sm.ys);
-      if (grp + 2 < ng) A.load(g, grp + 2);
+      A.compute(g, grp, kl, sm.xs, sm.ys);
+      if (grp + 2 < ng) A.load(g, grp + 2, kl);
       if (grp + 1 < ng) {
-        Bt.compute(g, grp + 1, sm.xs, sm.ys);
-        if (grp + 3 < ng) Bt.load(g, grp + 3);
+        Bt.compute(g, grp + 1, kl, sm.xs, sm.ys);
+        if (grp + 3 < ng) Bt.load(g, grp + 3, kl);
       }
     }
   }
@@ -441,36 +528,13 @@ __device__ bool gemv_run(const KA a, Smem& sm, const GemvArgs& g, const StageArg
   return true;
 }
 
-// One rows-per-wave choice per (batch rows, K chunks): the largest the
-// register budget allows (2 row groups of RPW x KCH 16-byte loads per lane
-// and RPW x NB accumulators).  Rows past the tile are masked.
-template <int NB, int KCH>
-__device__ __forceinline__ bool gemv_k2(const KA a, Smem& sm, const GemvArgs& g, const StageArgs& s) {
-  constexpr int WBUD = NB == 1 ? MK_WBUD1 : 8;
-  constexpr int RMAX_W = (WBUD / KCH) < 1 ? 1 : (WBUD / KCH);
-  constexpr int RMAX_A = 16 / NB < 1 ? 1 : 16 / NB;
-  constexpr int R0 = RMAX_W < RMAX_A ? RMAX_W : RMAX_A;
-  constexpr int RPW = R0 >= 8 ? 8 : R0 >= 4 ? 4 : R0 >= 2 ? 2 : 1;
-  return gemv_run<NB, KCH, RPW>(a, sm, g, s);
-}
-
-template <int NB>
-__device__ __forceinline__ bool gemv_nb(const KA a, Smem& sm, const GemvArgs& g, const StageArgs& s) {
-  const int kch = (g.K + 511) / 512;
-  if (kch <= 1) return gemv_k2<NB, 1>(a, sm, g, s);
-  if (kch <= 2) return gemv_k2<NB, 2>(a, sm, g, s);
-  if (kch <= 4) return gemv_k2<NB, 4>(a, sm, g, s);
-  if (kch <= 8) return gemv_k2<NB, 8>(a, sm, g, s);
-  return gemv_k2<NB, 16>(a, sm, g, s);
-}
-
 // Runs one GEMV tile: prefetch, wait, stage x, multiply.  false if the step
 // was aborted while waiting.
 __device__ __forceinline__ bool gemv(const KA a, Smem& sm, const GemvArgs& g, const StageArgs& s) {
-  if (g.nb <= 1) return gemv_nb<1>(a, sm, g, s);
-  if (g.nb <= 2) return gemv_nb<2>(a, sm, g, s);
-  if (g.nb <= 4) return gemv_nb<4>(a, sm, g, s);
-  return gemv_nb<8>(a, sm, g, s);
+  if (g.nb <= 1) return gemv_run<1>(a, sm, g, s);
+  if (g.nb <= 2) return gemv_run<2>(a, sm, g, s);
+  if (g.nb <= 4) return gemv_run<4>(a, sm, g, s);
+  return gemv_run<8>(a, sm, g, s);
 }
 
 // ------------------------------------------------------------- ADD_RMSNORM
@@ -538,7 +602,7 @@ __device__ __forceinline__ bool op_add_rmsnorm(const KA a, Smem& sm, const mk_ta
       f32x4 acc = (f32x4){0.f, 0.f, 0.f, 0.f};
       if (!live) {
       } else if (emb) {
-        const uint2 e = *reinterpret_cast<const uint2*>(a->embed + (long)tok * d + c * 4);
+        const u32x2 e = ldg8(a->embed + (long)tok * d + c * 4);
         acc = (f32x4){bf_lo(e.x), bf_hi(e.x), bf_lo(e.y), bf_hi(e.y)};
       } else if (mid || moe_in) {
         u32x4 og[8], ym[8];
@@ -586,7 +650,7 @@ __device__ __forceinline__ bool op_add_rmsnorm(const KA a, Smem& sm, const mk_ta
     const float r = 1.0f / sqrtf(tot / (float)d + a->eps);
 #pragma unroll 1
     for (int c = tid; c < nv; c += MK_THREADS) {
-      const uint2 gg = *reinterpret_cast<const uint2*>(gain + c * 4);
+      const u32x2 gg = ldg8(gain + c * 4);
       const f32x4 gv = (f32x4){bf_lo(gg.x), bf_hi(gg.x), bf_lo(gg.y), bf_hi(gg.y)};
       const f32x4 xb = *reinterpret_cast<const f32x4*>(xv + b * d + c * 4);
       stc16(xndst + (long)b * d, c * 16, as_u4(xb * r * gv));
@@ -600,7 +664,7 @@ __device__ __forceinline__ bool op_add_rmsnorm(const KA a, Smem& sm, const mk_ta
 // QKV_PROJ: tile = rotation pairs [n0, n1) over all heads (pair p of head h
 // is rows h*hd + p and h*hd + p + hd/2).  RoPE (rotate-half, angle
 // pos * theta^(-2i/hd) in double) on q and k; k and v rounded to bf16 and
-// written to the sequence's page at its position.
+// written to the sequence's page at its position (V pages are transposed).
 __device__ __forceinline__ void epi_qkv(const KA a, Smem& sm, const mk_task& t, int ti) {
   const int l = t.layer, hd = a->hd, half = hd / 2, B = a->B;
   const int np = t.n1 - t.n0;
@@ -632,9 +696,15 @@ __device__ __forceinline__ void epi_qkv(const KA a, Smem& sm, const mk_task& t, 
         report(a, MK_E_DEVICE, ti, -2, page, a->num_pages);
         continue;
       }
-      uint16_t* dst = (isk ? kpool : vpool) + (((long)page * a->Hkv + kvh) * a->page + (pos % a->page)) * hd;
-      stc(dst + i, f_to_bf16(ya));
-      stc(dst + i + half, f_to_bf16(yb));
+      if (isk) {   // K page [16 keys][hd]
+        uint16_t* dst = kpool + (((long)page * a->Hkv + kvh) * 16 + (pos & 15)) * hd;
+        stc(dst + i, f_to_bf16(ya));
+        stc(dst + i + half, f_to_bf16(yb));
+      } else {     // V page [hd][16 keys]
+        uint16_t* dst = vpool + ((long)page * a->Hkv + kvh) * hd * 16 + (pos & 15);
+        stc(dst + i * 16, f_to_bf16(ya));
+        stc(dst + (i + half) * 16, f_to_bf16(yb));
+      }
     }
   }
 }
@@ -675,19 +745,16 @@ __device__ __forceinline__ void router_topk(const KA a, Smem& sm, int l) {
         const int e = lane + 64 * u;
         if (e < E && (v[u] > bv || (v[u] == bv && e < be))) { bv = v[u]; be = e; }
       }
-#pragma unroll
-      for (int m = 32; m >= 1; m >>= 1) {
-        const float ov = __shfl_xor(bv, m);
-        const int oe = __shfl_xor(be, m);
-        if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
-      }
+      // the largest logit, then the lowest id among the lanes holding it
+      const float mx = wave_max(bv);
+      const int win = wave_min(bv == mx ? be : 0x7FFFFFFF);
 #pragma unroll
       for (int u = 0; u < 4; ++u)
-        if (lane + 64 * u == be) v[u] = -INFINITY;
-      if (j == 0) top0 = bv;
-      const float ew = expf(bv - top0);
+        if (lane + 64 * u == win) v[u] = -INFINITY;
+      if (j == 0) top0 = mx;
+      const float ew = expf(mx - top0);
       wsum += ew;
-      if (lane == j) { myw = ew; myid = be; }
+      if (lane == j) { myw = ew; myid = win; }
     }
     if (lane < K) {
       stc(a->topi + ((long)l * B + b) * K + lane, myid);
@@ -699,9 +766,9 @@ __device__ __forceinline__ void router_topk(const KA a, Smem& sm, int l) {
 }
 
 // ---------------------------------------------------------- ROUTE_FINALIZE
-// From the B*k routed (token, slot) pairs: sort by (expert, token slot) with a
-// bitonic network across one wave; row r of the sorted order is the r-th
-// routed row.  Writes the active expert list (ascending ids), each expert's
+// From the B*k routed (token, slot) pairs: sort by (expert, token slot) in
+// one wave, each key placed at its rank (the number of smaller keys, counted
+// from a copy in LDS); row r of the sorted order is the r-th routed row.  Writes the active expert list (ascending ids), each expert's
 // first row, the token of each row, the row of each (token, slot), and the
 // lengths of the up-gate and down claim queues.  Uses misc[64..] ids.
 __device__ __forceinline__ void route_finalize(const KA a, Smem& sm, int l) {
@@ -715,15 +782,19 @@ __device__ __forceinline__ void route_finalize(const KA a, Smem& sm, int l) {
     const int id = sm.misc[64 + lane];
     if (id >= 0) key = ((uint32_t)id << 8) | (uint32_t)lane;
   }
-  for (int k = 2; k <= 64; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      const uint32_t other = (uint32_t)__shfl_xor((int)key, j);
-      const bool up = (lane & k) == 0, lower = (lane & j) == 0;
-      key = (lower == up) ? (key < other ? key : other) : (key > other ? key : other);
-    }
-  }
+  // LDS accesses of one wave complete in program order, so the lanes see
+  // each other's stores without a barrier
+  uint32_t* kin = sm.sortk;          // [64] keys in (token, slot) order
+  uint32_t* kso = sm.sortk + 64;     // [64] keys in sorted order
+  kin[lane] = key;
+  int rank = 0;
+#pragma unroll 16
+  for (int j = 0; j < 64; ++j) rank += kin[j] < key ? 1 : 0;
+  if (key != 0xFFFFFFFFu) kso[rank] = key;
+  const int nvalid = __popcll(__ballot(key != 0xFFFFFFFFu));
+  key = lane < nvalid ? kso[lane] : 0xFFFFFFFFu;
   const bool valid = key != 0xFFFFFFFFu;
-  const uint32_t prev = (uint32_t)__shfl((int)key, lane > 0 ? lane - 1 : 0);
+  const uint32_t prev = kso[lane > 0 ? lane - 1 : 0];
   const int e = (int)(key >> 8), src = (int)(key & 0xFF);
   const bool start = valid && (lane == 0 || (prev >> 8) != (key >> 8));
   const uint64_t vmask = __ballot(valid);
@@ -754,53 +825,90 @@ __device__ __forceinline__ void route_finalize(const KA a, Smem& sm, int l) {
 // ---------------------------------------------------------- attention split
 // Keys [p0, p1) of sequence b, KV group g: scores s_j = q_h . K_j / sqrt(hd)
 // for the G query heads of the group, then m = max s, p = exp(s - m),
-// l = sum p, o = sum p V_j.  Lane layout: hd/8 lanes share one key row (8
-// dims each), so a wave load reads 64/(hd/8) keys; waves take keys in turn.
-// The K and V rows of the first chunk are loaded before the wait on the QKV
-// tiles (cached keys are immutable); the key appended this step is re-read
-// with a coherent load after the wait.  q goes through LDS, staged by wave 0.
-constexpr int ATT_CH = 8;   // wave loads per chunk
+// l = sum p, o = sum p V_j (the split partials the combine merges).
+//
+// Both products run on the matrix cores (v_mfma_f32_16x16x32_bf16; one
+// 16-row tile holds the group's <= 8 heads, the other rows are zero).  K and
+// V are bf16 already; the fp32 operands q and p are split into a bf16 high
+// part and a bf16 remainder, and each product is the sum of two MFMAs, so
+// the result keeps about 16 mantissa bits of q and p (fp32 accumulation).  A
+// key tile is one 16-key page.  QK: A = q (bf16), B = K^T: lane l holds key
+// (l mod 16), dims 32s + 8(l/16) .. +7, a 16-byte piece of the key row.
+// PV: A = P (bf16, from LDS), B = V: lane l holds dim (l mod 16) of 8
+// consecutive keys, a 16-byte piece of the transposed V page.  Result tiles:
+// lane l holds rows (heads) 4(l/16) .. +3 of column (key or dim) l mod 16.
+// Compute waves take key tiles (QK) and dim tiles (PV) in turn.  The K and V
+// fragments of the first tiles are loaded before the wait on the QKV tiles
+// (cached keys are immutable); the key appended this step is re-read with a
+// coherent load after the wait.  q goes through LDS, staged by wave 0.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                 0, 0, 0);
+}
+// x = hi + lo with hi = bf16(x) and lo = bf16(x - hi), two values per word
+__device__ __forceinline__ void split_bf16(float x0, float x1, uint32_t& hi, uint32_t& lo) {
+  const uint16_t h0 = f_to_bf16(x0), h1 = f_to_bf16(x1);
+  const uint16_t l0 = f_to_bf16(x0 - bf16_to_f(h0)), l1 = f_to_bf16(x1 - bf16_to_f(h1));
+  hi = (uint32_t)h0 | ((uint32_t)h1 << 16);
+  lo = (uint32_t)l0 | ((uint32_t)l1 << 16);
+}
+constexpr int ATT_PT = 3;   // K tiles in flight per compute wave
+constexpr int ATT_PV = 4;   // V k-steps (32 keys) in flight per compute wave
 
 template <int HD>
 __device__ __forceinline__ bool attn_split(const KA a, Smem& sm, int l, int b, int g, int s, int p0, int p1, int ti,
-                           int wait_idx, int wait_target) {
-  constexpr int LPR = HD / 8;
-  constexpr int PPW = 64 / LPR;
-  constexpr int PER_IT = MK_CW * PPW;     // keys per iteration of the workgroup
-  const int G = a->G, S = a->attn_split;
+                                           int wait_idx, int wait_target) {
+  constexpr int KS = HD / 32;                       // QK k-steps per key tile
+  constexpr int NDT = HD / 16;                      // PV dim tiles
+  constexpr int DTW = (NDT + MK_CW - 1) / MK_CW;    // dim tiles per compute wave
+  const int G = a->G, Hkv = a->Hkv;
+  const int SP = a->attn_split + 32;                // LDS row stride of scores and P
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int sub = lane / LPR, c = lane - sub * LPR;
-  const int n = p1 - p0;
-  const int iters = (n + PER_IT - 1) / PER_IT;
-  const int rows = (a->Hq + 2 * a->Hkv) * HD;
+  const int cw = wave - 1;                          // compute wave index (wave 0: -1)
+  const int c16 = lane & 15, q4 = lane >> 4;
+  const int tb0 = p0 & ~15;                         // first key of the first tile
+  const int nt = (p1 - tb0 + 15) >> 4;              // key tiles
+  const int nks = (nt + 1) >> 1;                    // PV k-steps
+  const int nti = cw >= 0 && cw < nt ? (nt - cw + MK_CW - 1) / MK_CW : 0;   // key tiles of this wave
   const uint16_t* Kp = a->layers[l].k;
   const uint16_t* Vp = a->layers[l].v;
-  const int32_t* bt = a->block_tables + (long)b * a->max_blocks;
+  const int32_t* bt = a->block_tables + (long)b * a->max_blocks + (tb0 >> 4);
   const int newest = a->positions[b];
-  // element offset of key iteration `it` for this lane, or -1
-  auto key_off = [&](int it, int* jpos) -> int {
-    if (wave == 0) return -1;   // the control wave holds no keys
-    const int jj = it * PER_IT + (wave - 1) * PPW + sub;
-    if (jj >= n) return -1;
-    const int j = p0 + jj;
-    *jpos = j;
-    int pg = bt[j / a->page];
+  auto page_of = [&](int t) -> int {
+    int pg = bt[t];
     if (pg < 0 || pg >= a->num_pages) {
       report(a, MK_E_DEVICE, ti, -3, pg, a->num_pages);
       pg = 0;
     }
-    return ((pg * a->Hkv + g) * a->page + (j % a->page)) * HD + c * 8;
+    return pg;
   };
-  u32x4 kb[ATT_CH], vb[ATT_CH];
-  int ko[ATT_CH];
-  int kj[ATT_CH];
+  // element offset of this lane's piece of key tile t (dims 8(l/16) of the row)
+  auto k_off = [&](int t) -> int { return ((page_of(t) * Hkv + g) * 16 + c16) * HD + 8 * q4; };
+  // element offset of this lane's V piece of k-step ks in dim tile 0, or -1
+  // (dim tile dt adds 256 dt)
+  auto v_off = [&](int ks) -> int {
+    const int tt = 2 * ks + (lane >> 5);
+    if (tt >= nt) return -1;
+    return ((page_of(tt) * Hkv + g) * HD + c16) * 16 + 8 * (q4 & 1);
+  };
+  u32x4 kf[ATT_PT][KS], vf[ATT_PV][DTW];
+  if (cw >= 0) {
 #pragma unroll
-  for (int u = 0; u < ATT_CH; ++u) {
-    kj[u] = -1;
-    ko[u] = u < iters ? key_off(u, &kj[u]) : -1;
-    if (ko[u] >= 0) {
-      kb[u] = ldg_nt(Kp + ko[u]);
-      vb[u] = ldg_nt(Vp + ko[u]);
+    for (int u = 0; u < ATT_PT; ++u)
+      if (u < nti) {
+        const int o = k_off(cw + MK_CW * u);
+#pragma unroll
+        for (int k = 0; k < KS; ++k) kf[u][k] = ldg_nt(Kp + o + 32 * k);
+      }
+#pragma unroll
+    for (int u = 0; u < ATT_PV; ++u) {
+      const int o = u < nks ? v_off(u) : -1;
+#pragma unroll
+      for (int j = 0; j < DTW; ++j) {
+        const int dt = cw + MK_CW * j;
+        vf[u][j] = (o >= 0 && dt < NDT) ? ldg_nt(Vp + o + 256 * dt) : (u32x4){0u, 0u, 0u, 0u};
+      }
     }
   }
   MK_MARK(3);
@@ -812,9 +920,10 @@ __device__ __forceinline__ bool attn_split(const KA a, Smem& sm, int l, int b, i
       ok = (wait_idx < 0 || wait_target <= 0) ? 1 : (int)spin_until(a, wait_idx, wait_target, ti);
       if (a->trace && sm.t_ready == 0) sm.t_ready = wall_clock64();
     }
-    ok = __shfl(ok, 0);
+    ok = __builtin_amdgcn_readfirstlane(ok);
     if (lane == 0) sm.misc[0] = ok;
     if (ok) {
+      const int rows = (a->Hq + 2 * Hkv) * HD;
       const float* qb = a->qkv + ((long)l * a->B + b) * rows + (long)(g * G) * HD;
       for (int i = lane; i < G * HD / 4; i += 64)
         *reinterpret_cast<u32x4*>(qs + i * 4) = ldc16(qb, i * 16);
@@ -823,132 +932,132 @@ __device__ __forceinline__ bool attn_split(const KA a, Smem& sm, int l, int b, i
   __syncthreads();
   MK_MARK(4);
   if (!sm.misc[0]) return false;
-  float q[NBMAX][8];
+  float* sc = sm.ys;                                       // [G][SP] scores
+  uint16_t* pbh = reinterpret_cast<uint16_t*>(sm.red);     // [G][SP] p, bf16 high part
+  uint16_t* pbl = pbh + G * SP;                            // [G][SP] p, bf16 remainder
+  // pass 1: scores of this wave's key tiles
+  if (cw >= 0) {
+    u32x4 qh[KS], ql[KS];
 #pragma unroll
-  for (int h = 0; h < NBMAX; ++h)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) q[h][e] = h < G ? qs[h * HD + c * 8 + e] * a->attn_scale : 0.f;
-  float* sc = sm.ys;  // [G][S]
-  // pass 1: scores, chunk by chunk
-  for (int it0 = 0; it0 < iters; it0 += ATT_CH) {
-    if (it0 > 0) {
-#pragma unroll
-      for (int u = 0; u < ATT_CH; ++u) {
-        kj[u] = -1;
-        ko[u] = it0 + u < iters ? key_off(it0 + u, &kj[u]) : -1;
-        if (ko[u] >= 0) kb[u] = ldg_nt(Kp + ko[u]);
+    for (int k = 0; k < KS; ++k) {
+      if (c16 < G) {
+        const f32x4* qp = reinterpret_cast<const f32x4*>(qs + c16 * HD + 32 * k + 8 * q4);
+        const f32x4 x0 = qp[0], x1 = qp[1];
+        uint32_t h0, h1, h2, h3, l0, l1, l2, l3;
+        split_bf16(x0.x, x0.y, h0, l0);
+        split_bf16(x0.z, x0.w, h1, l1);
+        split_bf16(x1.x, x1.y, h2, l2);
+        split_bf16(x1.z, x1.w, h3, l3);
+        qh[k] = (u32x4){h0, h1, h2, h3};
+        ql[k] = (u32x4){l0, l1, l2, l3};
+      } else {
+        qh[k] = (u32x4){0u, 0u, 0u, 0u};
+        ql[k] = (u32x4){0u, 0u, 0u, 0u};
       }
     }
+    for (int i0 = 0; i0 < nti; i0 += ATT_PT) {
 #pragma unroll
-    for (int u = 0; u < ATT_CH; ++u) {
-      float part[NBMAX];
+      for (int u = 0; u < ATT_PT; ++u) {
+        const int i = i0 + u;
+        if (i < nti) {
+          const int t = cw + MK_CW * i;
+          const int kk = 16 * t + c16, kabs = tb0 + kk;
+          if (kabs == newest) {   // appended this step: re-read coherently
+            const int o = k_off(t);
 #pragma unroll
-      for (int h = 0; h < NBMAX; ++h) part[h] = 0.f;
-      if (ko[u] >= 0) {
-        const u32x4 kv = (kj[u] == newest) ? ldc16(Kp, (int)(ko[u] * 2)) : kb[u];
-        const float k0 = bf_lo(kv.x), k1 = bf_hi(kv.x), k2 = bf_lo(kv.y), k3 = bf_hi(kv.y);
-        const float k4 = bf_lo(kv.z), k5 = bf_hi(kv.z), k6 = bf_lo(kv.w), k7 = bf_hi(kv.w);
+            for (int k = 0; k < KS; ++k) kf[u][k] = ldc16(Kp, (o + 32 * k) * 2);
+          }
+          f32x4 c = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int h = 0; h < NBMAX; ++h)
-          part[h] = q[h][0] * k0 + q[h][1] * k1 + q[h][2] * k2 + q[h][3] * k3 + q[h][4] * k4 + q[h][5] * k5 +
-                    q[h][6] * k6 + q[h][7] * k7;
-      }
+          for (int k = 0; k < KS; ++k) {
+            c = mfma_bf16(qh[k], kf[u][k], c);
+            c = mfma_bf16(ql[k], kf[u][k], c);
+          }
+          const bool valid = kabs >= p0 && kabs < p1;
 #pragma unroll
-      for (int h = 0; h < NBMAX; ++h)
+          for (int r = 0; r < 4; ++r) {
+            const int h = 4 * q4 + r;
+            if (h < G) sc[h * SP + kk] = valid ? c[r] * a->attn_scale : -INFINITY;
+          }
+          if (i + ATT_PT < nti) {
+            const int o = k_off(t + MK_CW * ATT_PT);
 #pragma unroll
-        for (int m = LPR / 2; m >= 1; m >>= 1) part[h] += __shfl_xor(part[h], m);
-      if (ko[u] >= 0 && c == 0) {
-        const int jj = kj[u] - p0;
-#pragma unroll
-        for (int h = 0; h < NBMAX; ++h)
-          if (h < G) sc[h * S + jj] = part[h];
-      }
-    }
-  }
-  __syncthreads();
-  if (a->trace && tid == 0 && sm.t_mark[0] == 0) sm.t_mark[0] = wall_clock64();
-  // pass 2: per-head max, exponentials and their sum
-  float* ml = a->part_ml + ((((long)(l & 1) * a->B + b) * a->Hq + g * G) * a->max_splits) * 2;
-  if (wave < G) {
-    float mx = -INFINITY;
-    for (int jj = lane; jj < n; jj += 64) mx = fmaxf(mx, sc[wave * S + jj]);
-    mx = wave_max(mx);
-    float sum = 0.f;
-    for (int jj = lane; jj < n; jj += 64) {
-      const float pj = expf(sc[wave * S + jj] - mx);
-      sc[wave * S + jj] = pj;
-      sum += pj;
-    }
-    sum = wave_sum(sum);
-    if (lane == 0) {
-      stc(ml + ((long)wave * a->max_splits + s) * 2 + 0, mx);
-      stc(ml + ((long)wave * a->max_splits + s) * 2 + 1, sum);
-    }
-  }
-  __syncthreads();
-  MK_MARK(6);
-  // pass 3: o = sum p V, chunk by chunk (the first chunk is already loaded)
-  float o[NBMAX][8];
-#pragma unroll
-  for (int h = 0; h < NBMAX; ++h)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o[h][e] = 0.f;
-  for (int it0 = 0; it0 < iters; it0 += ATT_CH) {
-    if (it0 > 0) {
-#pragma unroll
-      for (int u = 0; u < ATT_CH; ++u) {
-        kj[u] = -1;
-        ko[u] = it0 + u < iters ? key_off(it0 + u, &kj[u]) : -1;
-        if (ko[u] >= 0) vb[u] = ldg_nt(Vp + ko[u]);
-      }
-    } else {
-#pragma unroll
-      for (int u = 0; u < ATT_CH; ++u) {
-        kj[u] = -1;
-        ko[u] = u < iters ? key_off(u, &kj[u]) : -1;
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < ATT_CH; ++u) {
-      if (ko[u] >= 0) {
-        const u32x4 vv = (kj[u] == newest) ? ldc16(Vp, (int)(ko[u] * 2)) : vb[u];
-        float vf[8];
-        vf[0] = bf_lo(vv.x); vf[1] = bf_hi(vv.x); vf[2] = bf_lo(vv.y); vf[3] = bf_hi(vv.y);
-        vf[4] = bf_lo(vv.z); vf[5] = bf_hi(vv.z); vf[6] = bf_lo(vv.w); vf[7] = bf_hi(vv.w);
-        const int jj = kj[u] - p0;
-#pragma unroll
-        for (int h = 0; h < NBMAX; ++h) {
-          if (h < G) {
-            const float pj = sc[h * S + jj];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) o[h][e] = fmaf(pj, vf[e], o[h][e]);
+            for (int k = 0; k < KS; ++k) kf[u][k] = ldg_nt(Kp + o + 32 * k);
           }
         }
       }
     }
   }
-  if (a->trace && tid == 0 && sm.t_mark[1] == 0) sm.t_mark[1] = wall_clock64();
-#pragma unroll
-  for (int h = 0; h < NBMAX; ++h)
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-#pragma unroll
-      for (int m = LPR; m < 64; m <<= 1) o[h][e] += __shfl_xor(o[h][e], m);
-  if (sub == 0) {
-#pragma unroll
-    for (int h = 0; h < NBMAX; ++h)
-      if (h < G)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) sm.red[(wave * NBMAX + h) * HD + c * 8 + e] = o[h][e];
+  __syncthreads();
+  if (a->trace && tid == 0 && sm.t_mark[0] == 0) sm.t_mark[0] = wall_clock64();
+  // pass 2: per-head max, exponentials (as bf16 for the PV product) and sum
+  float* ml = a->part_ml + ((((long)(l & 1) * a->B + b) * a->Hq + g * G) * a->max_splits) * 2;
+  const int nk = 16 * nt, nk2 = 32 * nks;
+  for (int h = wave; h < G; h += MK_WAVES) {
+    float mx = -INFINITY;
+    for (int kk = lane; kk < nk; kk += 64) mx = fmaxf(mx, sc[h * SP + kk]);
+    mx = wave_max(mx);
+    float sum = 0.f;
+    for (int kk = lane; kk < nk2; kk += 64) {
+      const float pj = kk < nk ? expf(sc[h * SP + kk] - mx) : 0.f;
+      const uint16_t ph = f_to_bf16(pj);
+      pbh[h * SP + kk] = ph;
+      pbl[h * SP + kk] = f_to_bf16(pj - bf16_to_f(ph));
+      sum += pj;
+    }
+    sum = wave_sum(sum);
+    if (lane == 0) {
+      stc(ml + ((long)h * a->max_splits + s) * 2 + 0, mx);
+      stc(ml + ((long)h * a->max_splits + s) * 2 + 1, sum);
+    }
   }
   __syncthreads();
+  MK_MARK(6);
+  // pass 3: o = P V over this wave's dim tiles
   float* po = a->part_o + ((((long)(l & 1) * a->B + b) * a->Hq + g * G) * a->max_splits) * HD;
-  for (int idx = tid; idx < G * HD; idx += MK_THREADS) {
-    const int h = idx / HD, dd = idx - h * HD;
-    float v = 0.f;
+  if (cw >= 0) {
+    f32x4 o[DTW];
 #pragma unroll
-    for (int w = 0; w < MK_WAVES; ++w) v += sm.red[(w * NBMAX + h) * HD + dd];
-    stc(po + ((long)h * a->max_splits + s) * HD + dd, v);
+    for (int j = 0; j < DTW; ++j) o[j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    for (int ks0 = 0; ks0 < nks; ks0 += ATT_PV) {
+#pragma unroll
+      for (int u = 0; u < ATT_PV; ++u) {
+        const int ks = ks0 + u;
+        if (ks < nks) {
+          // keys outside [p0, p1) have p = 0; their V values are finite pool
+          // contents (earlier keys of the sequence, or the initialised pool)
+          const int k0 = tb0 + 32 * ks + 8 * q4;   // first key of this lane's V piece
+          const int po_ = c16 * SP + 32 * ks + 8 * q4;
+          const u32x4 ph = c16 < G ? *reinterpret_cast<const u32x4*>(pbh + po_) : (u32x4){0u, 0u, 0u, 0u};
+          const u32x4 pl = c16 < G ? *reinterpret_cast<const u32x4*>(pbl + po_) : (u32x4){0u, 0u, 0u, 0u};
+          const bool fresh = newest >= k0 && newest < k0 + 8;   // holds the key appended this step
+          const int ocur = fresh ? v_off(ks) : -1;
+          const int onext = ks + ATT_PV < nks ? v_off(ks + ATT_PV) : -1;
+#pragma unroll
+          for (int j = 0; j < DTW; ++j) {
+            const int dt = cw + MK_CW * j;
+            if (dt < NDT) {
+              const u32x4 v = ocur >= 0 ? ldc16(Vp, (ocur + 256 * dt) * 2) : vf[u][j];
+              o[j] = mfma_bf16(ph, v, o[j]);
+              o[j] = mfma_bf16(pl, v, o[j]);
+              if (ks + ATT_PV < nks) vf[u][j] = onext >= 0 ? ldg_nt(Vp + onext + 256 * dt) : (u32x4){0u, 0u, 0u, 0u};
+            }
+          }
+        }
+      }
+    }
+    if (a->trace && tid == 64 && sm.t_mark[1] == 0) sm.t_mark[1] = wall_clock64();
+#pragma unroll
+    for (int j = 0; j < DTW; ++j) {
+      const int dt = cw + MK_CW * j;
+      if (dt < NDT) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int h = 4 * q4 + r;
+          if (h < G) stc(po + ((long)h * a->max_splits + s) * HD + 16 * dt + c16, o[j][r]);
+        }
+      }
+    }
   }
   MK_MARK(7);
   return true;
@@ -980,8 +1089,8 @@ __device__ __forceinline__ bool op_attn_combine(const KA a, Smem& sm, const mk_t
   const float* po0 = a->part_o + ((((long)(l & 1) * a->B + b) * a->Hq + g * G) * hstride) * hd;
   float* wts = sm.ys;                 // [G][max_splits]
   float* den = sm.red;                // [G]
-  if (wave < G) {
-    const float* ml = ml0 + (long)wave * hstride * 2;
+  for (int h = wave; h < G; h += MK_WAVES) {
+    const float* ml = ml0 + (long)h * hstride * 2;
     float m[16], lsum[16];
     float mx = -INFINITY;
 #pragma unroll
@@ -999,12 +1108,12 @@ __device__ __forceinline__ bool op_attn_combine(const KA a, Smem& sm, const mk_t
       const int s = lane + 64 * u;
       if (s < ns) {
         const float w = expf(m[u] - mx);
-        wts[wave * hstride + s] = w;
+        wts[h * hstride + s] = w;
         dsum += w * lsum[u];
       }
     }
     dsum = wave_sum(dsum);
-    if (lane == 0) den[wave] = dsum;
+    if (lane == 0) den[h] = dsum;
   }
   __syncthreads();
   const int q4 = hd / 4;   // float4 chunks per head
@@ -1061,7 +1170,7 @@ extern "C" __global__ void __launch_bounds__(MK_THREADS, 1) mk_persistent(mk_kar
         t_start = wall_clock64();
         sm.t_ready = 0;
         for (int q = 0; q < 10; ++q) sm.t_mark[q] = 0;
-        sm_trace_mark = &sm.t_mark[2];
+        sm_t_signal = 0;
       }
       if (is_claimer(t.op)) {
         const int l = t.layer;
@@ -1304,9 +1413,10 @@ extern "C" __global__ void __launch_bounds__(MK_THREADS, 1) mk_persistent(mk_kar
     if (claiming) continue;
   task_done:
     if (a->trace && tid == 0) {
-      uint64_t* tr = a->trace + (long)ti * 16;
+      GLOBAL uint64_t* tr = (GLOBAL uint64_t*)(a->trace + (long)ti * 16);
       tr[0] = t_start;
       tr[1] = sm.t_ready ? sm.t_ready : t_start;
+      if (sm_t_signal) sm.t_mark[2] = sm_t_signal;
       for (int q = 0; q < 10; ++q) tr[2 + q] = sm.t_mark[q];
       tr[12] = wall_clock64();
       tr[13] = blockIdx.x;

@@ -47,9 +47,11 @@ class DecodeEngine:
         torch.cuda.synchronize()
         _log(verbose, "weights %.1f GB in %.1fs" % (self.weight_bytes() / 1e9, time.time() - t0))
         t0 = time.time()
-        shape = (self.plan.num_pages, cfg.n_kv_heads, cfg.page_size, cfg.head_dim)
-        self.kpool = [torch.zeros(shape, dtype=torch.bfloat16, device=self.dev) for _ in range(cfg.n_layers)]
-        self.vpool = [torch.zeros(shape, dtype=torch.bfloat16, device=self.dev) for _ in range(cfg.n_layers)]
+        # K pages hold one key per row, V pages one head dimension per row
+        kshape = (self.plan.num_pages, cfg.n_kv_heads, cfg.page_size, cfg.head_dim)
+        vshape = (self.plan.num_pages, cfg.n_kv_heads, cfg.head_dim, cfg.page_size)
+        self.kpool = [torch.zeros(kshape, dtype=torch.bfloat16, device=self.dev) for _ in range(cfg.n_layers)]
+        self.vpool = [torch.zeros(vshape, dtype=torch.bfloat16, device=self.dev) for _ in range(cfg.n_layers)]
         # slot state
         self.slot_seq: List[W.SequenceSlot] = []
         self.slot_len: List[int] = []
@@ -131,7 +133,8 @@ class DecodeEngine:
                 pad = n_full * ps - seq.ctx
                 if pad:
                     kv = torch.cat([kv, torch.zeros((pad,) + kv.shape[1:], dtype=kv.dtype, device=self.dev)])
-                kv = kv.view(n_full, ps, cfg.n_kv_heads, cfg.head_dim).permute(0, 2, 1, 3)
+                kv = kv.view(n_full, ps, cfg.n_kv_heads, cfg.head_dim)
+                kv = kv.permute(0, 2, 1, 3) if which == "k" else kv.permute(0, 2, 3, 1)
                 pool[pages[:n_full]] = kv
         if first:
             self.slot_seq.append(seq)
