@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--verbose", action="store_true")
     ap.add_argument("--trace", default="", help="after timing, trace one step and write a summary here")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="before the steps, run a plain device copy of this many MiB (3 times): a kernel of "
+                         "known traffic to scale HBM byte counters by")
     return ap.parse_args()
 
 
@@ -160,6 +163,15 @@ def main():
         pos.add_(1)
         sl.add_(1)
 
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration copy: 3 x {args.calib_copy_mib} MiB read + written")
+        del src, dst
     argmax_buf = torch.zeros(B, dtype=torch.int64, device="cuda")
     for i in range(args.warmup):
         one(i)
