@@ -89,7 +89,9 @@ typedef struct mk_task {
   int32_t batch;       /* batch slot (ATTN_COMBINE, ATTN_DECODE)             */
   int32_t split;       /* split index (ATTN_DECODE)                          */
   int32_t queue;       /* queue-head counter index (claimers)                */
-  int32_t aux[18];     /* reserved, zero                                     */
+  int32_t aux[18];     /* opcode-specific words; aux[16] = workgroup the     *
+                        * task runs on, aux[17] = its index in the list     *
+                        * (both set by the schedule builder)                */
 } mk_task;
 
 #define MK_WAIT_NONE (-1)

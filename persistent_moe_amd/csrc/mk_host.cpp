@@ -30,7 +30,7 @@ constexpr int kXsFloats = 16384;   // LDS capacity for staged activations
 constexpr int kMaxGemvK = 8192;    // GEMV reduction length: 16 register slots x 512 (half from 4 rows)
 
 struct Layout {
-  size_t off_tasks, off_ctr, off_err, off_layers, off_invf, off_rope;
+  size_t off_tasks, off_ranges, off_ctr, off_err, off_layers, off_invf, off_rope;
   size_t off_x, off_xn, off_xmid, off_xn2, off_qkv, off_attn, off_opart, off_rlog, off_topi, off_topw;
   size_t off_moe, off_H, off_Y, off_fh, off_fo, off_oout, off_pml, off_po, off_trace;
   size_t total;
@@ -78,6 +78,7 @@ int max_tasks_bound(const mk_config* c) {
   const int per_layer = 8 * kMaxWorkgroups + 2 * c->max_batch * c->n_kv_heads + 64;
   return (c->n_layers + 1) * per_layer + kMaxWorkgroups;
 }
+int max_waves_bound(const mk_config* c) { return (c->n_layers + 1) * 12 + 4; }
 
 Layout make_layout(const mk_config* c, int32_t max_blocks) {
   Layout L{};
@@ -95,6 +96,7 @@ Layout make_layout(const mk_config* c, int32_t max_blocks) {
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t r = o; o = align_up(o + bytes, 256); return r; };
   L.off_tasks = take((size_t)L.max_tasks * sizeof(mk_task));
+  L.off_ranges = take((size_t)(1 + max_waves_bound(c)) * kMaxWorkgroups * 2 * 4);
   L.off_ctr = take((size_t)L.n_ctr * MK_CTR_PAD * 4);
   L.off_err = take(MK_ERR_WORDS * 4);
   L.off_layers = take((size_t)Lr * sizeof(mk_layer_dev));
@@ -125,10 +127,17 @@ Layout make_layout(const mk_config* c, int32_t max_blocks) {
 
 int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
 
+struct Plan;
+void finalize_plan(Plan& p);
+
 // ------------------------------------------------------------ plan builder
 struct Plan {
-  std::vector<mk_task> tasks;
+  std::vector<mk_task> tasks;         // builder order; aux[16] = workgroup, aux[17] = index
   std::vector<int32_t> wave_bounds;   // starts of each named wave, then the end
+  int nw = 0;                         // workgroups
+  std::vector<mk_task> dev_tasks;     // tasks grouped by workgroup (builder order within one)
+  std::vector<int32_t> ranges;        // (1 + waves) blocks of nw [begin, end) pairs into dev_tasks:
+                                      // block 0 = the whole step, block 1 + v = wave v
   int n_ctr = 0;
   int attn_split = 0, max_splits = 0;
   int ug_tiles = 0, ug_pairs = 0, dn_tiles = 0, dn_rows = 0;
@@ -214,6 +223,14 @@ int build_plan(const mk_config* c, int B, int32_t max_blocks, const mk_sched_opt
   std::vector<mk_task>& T = p.tasks;
   T.clear();
   p.wave_bounds.clear();
+  p.nw = NW;
+  // default placement: task k on workgroup k mod NW
+  auto push_on = [&](mk_task t, int wg) {
+    t.aux[MK_AUX_WG] = wg;
+    t.aux[MK_AUX_INDEX] = (int32_t)T.size();
+    T.push_back(t);
+  };
+  auto push = [&](const mk_task& t) { push_on(t, (int)(T.size() % NW)); };
   auto wave = [&]() { p.wave_bounds.push_back((int32_t)T.size()); };
   if (o.flags & MK_SCHED_UNREACHABLE_WAIT) {
     // waits on a global counter slot that nothing signals
@@ -223,7 +240,7 @@ int build_plan(const mk_config* c, int B, int32_t max_blocks, const mk_sched_opt
     t.n1 = std::min(c->vocab, 8);
     t.wait_ctr = MK_CG_COUNT - 1;
     t.wait_target = 1;
-    T.push_back(t);
+    push(t);
   }
 
   int layer_target_prev = 0;
@@ -240,7 +257,7 @@ int build_plan(const mk_config* c, int B, int32_t max_blocks, const mk_sched_opt
       }
       if (l == Lr) t.flags |= MK_F_FINAL;
       t.signal_ctr = ctr_of(p.cl, l, MK_CTR_NORM);
-      T.push_back(t);
+      push(t);
     }
     if (l == Lr) break;
     const int cNORM = ctr_of(p.cl, l, MK_CTR_NORM);
@@ -253,7 +270,7 @@ int build_plan(const mk_config* c, int B, int32_t max_blocks, const mk_sched_opt
         t.wait_ctr = cNORM;
         t.wait_target = 1;
         t.signal_ctr = ctr_of(p.cl, l, MK_CTR_QKV);
-        T.push_back(t);
+        push(t);
       }
     };
     auto emit_attn = [&]() {
@@ -265,7 +282,7 @@ int build_plan(const mk_config* c, int B, int32_t max_blocks, const mk_sched_opt
         t.wait_ctr = ctr_of(p.cl, l, MK_CTR_QKV);
         t.wait_target = n_qkv;
         t.queue = ctr_of(p.cl, l, MK_CTR_QATTN);
-        T.push_back(t);
+        push(t);
       }
     };
     auto emit_combine = [&]() {
@@ -278,7 +295,7 @@ int build_plan(const mk_config* c, int B, int32_t max_blocks, const mk_sched_opt
           t.wait_ctr = ctr_of(p.cl, l, p.cl.attn + b * Hkv + g);
           t.wait_target = MK_WAIT_SPLITS;
           t.signal_ctr = ctr_of(p.cl, l, p.cl.comb + g);
-          T.push_back(t);
+          push(t);
         }
     };
     auto emit_oproj = [&](int signal) {
@@ -294,7 +311,7 @@ int build_plan(const mk_config* c, int B, int32_t max_blocks, const mk_sched_opt
           t.wait_ctr = ctr_of(p.cl, l, p.cl.comb + g);
           t.wait_target = B;
           t.signal_ctr = signal;
-          T.push_back(t);
+          push(t);
         }
     };
     if (moe) {
@@ -314,7 +331,7 @@ int build_plan(const mk_config* c, int B, int32_t max_blocks, const mk_sched_opt
             t.flags |= MK_F_FUSE_TOPK;
             t.aux[0] = n_r;
           }
-          T.push_back(t);
+          push(t);
         }
         if (fuse_topk) return;
         wave();
@@ -323,7 +340,7 @@ int build_plan(const mk_config* c, int B, int32_t max_blocks, const mk_sched_opt
         t.wait_ctr = ctr_of(p.cl, l, MK_CTR_ROUTER);
         t.wait_target = n_r;
         t.signal_ctr = cROUTE;
-        T.push_back(t);
+        push(t);
       };
       auto emit_ug = [&]() {
         wave();
@@ -334,7 +351,7 @@ int build_plan(const mk_config* c, int B, int32_t max_blocks, const mk_sched_opt
           t.wait_ctr = cROUTE;
           t.wait_target = 1;
           t.queue = ctr_of(p.cl, l, MK_CTR_QUG);
-          T.push_back(t);
+          push(t);
         }
       };
       auto emit_dn = [&]() {
@@ -347,7 +364,7 @@ int build_plan(const mk_config* c, int B, int32_t max_blocks, const mk_sched_opt
           t.wait_target = 1;
           t.queue = ctr_of(p.cl, l, MK_CTR_QDN);
           t.signal_ctr = cLAYER;
-          T.push_back(t);
+          push(t);
         }
       };
       switch (o.wave_order) {
@@ -375,7 +392,7 @@ int build_plan(const mk_config* c, int B, int32_t max_blocks, const mk_sched_opt
         t.wait_ctr = cO;
         t.wait_target = Hkv * n_o_g;
         t.signal_ctr = cN2;
-        T.push_back(t);
+        push(t);
       }
       wave();
       for (int i = 0; i < n_fug; ++i) {
@@ -385,7 +402,7 @@ int build_plan(const mk_config* c, int B, int32_t max_blocks, const mk_sched_opt
         t.wait_ctr = cN2;
         t.wait_target = 1;
         t.signal_ctr = cFUG;
-        T.push_back(t);
+        push(t);
       }
       wave();
       for (int i = 0; i < n_fdn; ++i) {
@@ -395,7 +412,7 @@ int build_plan(const mk_config* c, int B, int32_t max_blocks, const mk_sched_opt
         t.wait_ctr = cFUG;
         t.wait_target = n_fug;
         t.signal_ctr = ctr_of(p.cl, l, MK_CTR_LAYER);
-        T.push_back(t);
+        push(t);
       }
       layer_target_prev = n_fdn;
     }
@@ -407,11 +424,43 @@ int build_plan(const mk_config* c, int B, int32_t max_blocks, const mk_sched_opt
     t.n1 = std::min(c->vocab, t.n0 + lm_rows);
     t.wait_ctr = ctr_of(p.cl, Lr, MK_CTR_NORM);
     t.wait_target = 1;
-    T.push_back(t);
+    push(t);
   }
   p.wave_bounds.push_back((int32_t)T.size());
   if ((int)T.size() > max_tasks_bound(c)) return MK_E_NOMEM;
+  if ((int)p.wave_bounds.size() - 1 > max_waves_bound(c)) return MK_E_NOMEM;
+  finalize_plan(p);
   return MK_OK;
+}
+
+// Group the tasks by workgroup (keeping builder order within one) and record,
+// for the whole step and for every wave, the range of each workgroup's tasks.
+void finalize_plan(Plan& p) {
+  const int NW = p.nw, n = (int)p.tasks.size();
+  std::vector<int> order(n);
+  for (int i = 0; i < n; ++i) order[i] = i;
+  std::stable_sort(order.begin(), order.end(),
+                   [&](int x, int y) { return p.tasks[x].aux[MK_AUX_WG] < p.tasks[y].aux[MK_AUX_WG]; });
+  p.dev_tasks.resize(n);
+  for (int i = 0; i < n; ++i) p.dev_tasks[i] = p.tasks[order[i]];
+  const int nwaves = (int)p.wave_bounds.size() - 1;
+  p.ranges.assign((size_t)(1 + nwaves) * NW * 2, 0);
+  // first position of each workgroup in dev_tasks
+  std::vector<int> start(NW + 1, 0);
+  for (int i = 0; i < n; ++i) start[p.tasks[i].aux[MK_AUX_WG] + 1]++;
+  for (int w = 0; w < NW; ++w) start[w + 1] += start[w];
+  for (int w = 0; w < NW; ++w) {
+    p.ranges[2 * w] = start[w];
+    p.ranges[2 * w + 1] = start[w + 1];
+    int pos = start[w];
+    for (int v = 0; v < nwaves; ++v) {
+      int32_t* r = &p.ranges[((size_t)(1 + v) * NW + w) * 2];
+      while (pos < start[w + 1] && p.dev_tasks[pos].aux[MK_AUX_INDEX] < p.wave_bounds[v]) ++pos;
+      r[0] = pos;
+      while (pos < start[w + 1] && p.dev_tasks[pos].aux[MK_AUX_INDEX] < p.wave_bounds[v + 1]) ++pos;
+      r[1] = pos;
+    }
+  }
 }
 
 // ------------------------------------------------------- deadlock checker
@@ -438,8 +487,13 @@ int simulate(const mk_config* c, int B, const Plan& p, int NW, const int32_t* se
     int sl = seq_lens[b];
     return sl <= 0 ? 0 : ceil_div(vis(l, sl), p.attn_split);
   };
-  std::vector<int> cursor(NW);
-  for (int w = 0; w < NW; ++w) cursor[w] = w;
+  if (NW != p.nw) return MK_E_INVAL;
+  // worker w walks dev_tasks [ranges[2w], ranges[2w+1])
+  std::vector<int> cursor(NW), cend(NW);
+  for (int w = 0; w < NW; ++w) {
+    cursor[w] = p.ranges[2 * w];
+    cend[w] = p.ranges[2 * w + 1];
+  }
   // per-claimer state: -1 before the static item, then dynamic claiming
   std::vector<int> phase(NW, 0);
   std::vector<int> cur_item(NW, -1);
@@ -466,9 +520,9 @@ int simulate(const mk_config* c, int B, const Plan& p, int NW, const int32_t* se
   for (long iter = 0;; ++iter) {
     bool progress = false, all_done = true;
     for (int w = 0; w < NW; ++w) {
-      while (cursor[w] < n_tasks) {
+      while (cursor[w] < cend[w]) {
         all_done = false;
-        const mk_task& t = p.tasks[cursor[w]];
+        const mk_task& t = p.dev_tasks[cursor[w]];
         int target = t.wait_target;
         if (target == MK_WAIT_SPLITS) target = nspl(t.layer, t.batch);
         if (t.wait_ctr >= 0 && target > 0 && ctr[t.wait_ctr] < target) break;
@@ -510,14 +564,15 @@ int simulate(const mk_config* c, int B, const Plan& p, int NW, const int32_t* se
         if (t.signal_ctr >= 0) ctr[t.signal_ctr]++;
         if ((t.flags & MK_F_FUSE_TOPK) && ctr[t.signal_ctr] == t.aux[0])
           ctr[ctr_of(p.cl, t.layer, MK_CTR_ROUTE)]++;   // the last router tile runs top-k
-        cursor[w] += NW;
+        cursor[w] += 1;
         progress = true;
       }
     }
     if (all_done) return MK_OK;
     if (!progress) {
       int first = n_tasks;
-      for (int w = 0; w < NW; ++w) first = std::min(first, cursor[w]);
+      for (int w = 0; w < NW; ++w)
+        if (cursor[w] < cend[w]) first = std::min(first, (int)p.dev_tasks[cursor[w]].aux[MK_AUX_INDEX]);
       if (stuck) *stuck = first;
       return MK_E_STATE;
     }
@@ -642,8 +697,10 @@ int mk_build_schedule(mk_handle* h, int32_t batch_size, const mk_sched_opts* opt
   if (rc != MK_OK) return rc;
   if ((int)p.tasks.size() > h->lay.max_tasks) return MK_E_NOMEM;
   if (p.max_splits > h->lay.max_splits) return MK_E_UNSUPPORTED;
-  if (hipMemcpy(h->ws + h->lay.off_tasks, p.tasks.data(), p.tasks.size() * sizeof(mk_task),
+  if (hipMemcpy(h->ws + h->lay.off_tasks, p.dev_tasks.data(), p.dev_tasks.size() * sizeof(mk_task),
                 hipMemcpyHostToDevice) != hipSuccess ||
+      hipMemcpy(h->ws + h->lay.off_ranges, p.ranges.data(), p.ranges.size() * 4, hipMemcpyHostToDevice) !=
+          hipSuccess ||
       hipMemset(h->ws + h->lay.off_ctr, 0, (size_t)h->lay.n_ctr * MK_CTR_PAD * 4) != hipSuccess ||
       hipDeviceSynchronize() != hipSuccess)
     return MK_E_HIP;
@@ -719,8 +776,8 @@ int mk_decode_step(mk_handle* h, const int32_t* token_ids, const int32_t* positi
   a.part_o = reinterpret_cast<float*>(ws + L.off_po);
   a.trace = (h->opts.flags & MK_SCHED_TRACE) ? reinterpret_cast<uint64_t*>(ws + L.off_trace) : nullptr;
   h->last_stream = reinterpret_cast<hipStream_t>(stream);
-  const std::vector<int32_t>& wb = h->plan.wave_bounds;
-  return mk_launch(&a, h->opts.launch_mode, wb.data(), (int)wb.size() - 1, stream);
+  a.wg_range = reinterpret_cast<const int32_t*>(ws + L.off_ranges);
+  return mk_launch(&a, h->opts.launch_mode, a.wg_range, (int)h->plan.wave_bounds.size() - 1, stream);
 }
 
 int mk_get_status(mk_handle* h, mk_status* st) {

@@ -19,6 +19,12 @@ enum {
                             // (aux[0] = number of router tiles)
 };
 
+// descriptor words set by the schedule builder
+enum {
+  MK_AUX_WG = 16,      // aux[16]: workgroup the task runs on
+  MK_AUX_INDEX = 17    // aux[17]: index of the task in the builder's list (trace row)
+};
+
 // ---------------------------------------------------------------- counters
 // Global counters first, then one block of MK_CTR_* counters per layer
 // (n_layers + 1 blocks; block n_layers holds the final norm counter).
@@ -87,9 +93,9 @@ struct mk_layer_dev {
 };
 
 struct mk_kargs {
-  const mk_task* tasks;
+  const mk_task* tasks;            // grouped by workgroup
   int32_t n_tasks;
-  int32_t task_begin, task_end;   // range walked by this launch
+  const int32_t* wg_range;        // [n_wg][2]: tasks [begin, end) this launch runs on each workgroup
   int32_t n_wg;                   // workgroups of the persistent grid
   int32_t* ctr;
   int32_t n_ctr;
@@ -141,5 +147,7 @@ struct mk_kargs {
 };
 
 // host entry of the device code (mk_kernel.hip)
-extern "C" int mk_launch(const mk_kargs* args, int launch_mode, const int32_t* wave_bounds,
-                         int n_waves, void* stream);
+// wg_ranges: (1 + n_waves) blocks of [n_wg][2] (block 0: the whole step,
+// block 1 + v: wave v, used by the one-launch-per-wave ablation)
+extern "C" int mk_launch(const mk_kargs* args, int launch_mode, const int32_t* wg_ranges, int n_waves,
+                         void* stream);

@@ -74,6 +74,7 @@ struct __attribute__((aligned(16))) Smem {
   float red[RED_FLOATS];
   int misc[192];
   uint32_t sortk[128];
+  mk_task tq[2];      // this task's descriptor and the next one (prefetched)
   uint64_t t_ready;   // trace: when the task's first wait was satisfied
   uint64_t t_mark[10]; // trace: [0] staged, [1] computed, [2] stores acknowledged, [3..9] free marks
 };
@@ -1150,22 +1151,49 @@ __device__ __forceinline__ bool is_claimer(int op) {
   return op == MK_OP_ATTN_DRAIN || op == MK_OP_MOE_UPGATE_ACT_DRAIN || op == MK_OP_MOE_DOWN_DRAIN;
 }
 
+// One 16-byte piece (lane 0..7) of task descriptor k.
+__device__ __forceinline__ u32x4 load_task_piece(const mk_task* tasks, int k, int lane) {
+  return *((GLOBAL const u32x4*)(tasks + k) + lane);
+}
+
 extern "C" __global__ void __launch_bounds__(MK_THREADS, 1) mk_persistent(mk_kargs a_arg, int final_launch) {
   __shared__ Smem sm;
   const int tid = threadIdx.x;
-  int ti = a_arg.task_begin + (int)blockIdx.x;
-  const int task_end = a_arg.task_end;
+  // this workgroup's tasks: [k, kend) of the grouped list
+  const int kbeg = ((GLOBAL const int32_t*)a_arg.wg_range)[2 * blockIdx.x];
+  const int kend = ((GLOBAL const int32_t*)a_arg.wg_range)[2 * blockIdx.x + 1];
+  int k = kbeg;
   bool claiming = false, first = false, aborted = false;
-  int n_items = 0, qidx = -1, attn_wait = -1;
+  int n_items = 0, qidx = -1, attn_wait = -1, ti = 0;
   uint64_t t_start = 0;
   mk_task t;
+  // Descriptors go through LDS: lanes 0..7 of wave 1 load the next one while
+  // the current task runs (wave 1 is a compute wave: its first weight load is
+  // issued after this and waits longer anyway), and store it at the top of
+  // the next pass of the loop.
+  int cur = 0;
+  bool pending = false;
+  u32x4 pre = (u32x4){0u, 0u, 0u, 0u};
+  if (tid >= 64 && tid < 72 && k < kend)
+    reinterpret_cast<u32x4*>(&sm.tq[0])[tid - 64] = load_task_piece(a_arg.tasks, k, tid - 64);
   for (;;) {
+    if (pending) {
+      if (tid >= 64 && tid < 72) reinterpret_cast<u32x4*>(&sm.tq[cur ^ 1])[tid - 64] = pre;
+      pending = false;
+    }
     __syncthreads();
     const KA a = kargs();
     int item = -1;
     if (!claiming) {
-      if (ti >= task_end) break;
-      t = a->tasks[ti];
+      if (k >= kend) break;
+      if (k > kbeg) cur ^= 1;
+      t = sm.tq[cur];
+      ti = t.aux[MK_AUX_INDEX];
+      if (k + 1 < kend) {
+        if (tid >= 64 && tid < 72) pre = load_task_piece(a->tasks, k + 1, tid - 64);
+        pending = true;
+      }
+      ++k;
       if (a->trace && tid == 0) {
         t_start = wall_clock64();
         sm.t_ready = 0;
@@ -1423,7 +1451,6 @@ extern "C" __global__ void __launch_bounds__(MK_THREADS, 1) mk_persistent(mk_kar
       tr[14] = t.op;
       tr[15] = 0;
     }
-    ti += (int)gridDim.x;
   }
   // The last workgroup out clears the counters for the next launch.
   __syncthreads();
@@ -1443,14 +1470,13 @@ extern "C" __global__ void __launch_bounds__(MK_THREADS, 1) mk_persistent(mk_kar
 }
 
 // ------------------------------------------------------------------ launch
-extern "C" int mk_launch(const mk_kargs* args, int launch_mode, const int32_t* wave_bounds, int n_waves,
+extern "C" int mk_launch(const mk_kargs* args, int launch_mode, const int32_t* wg_ranges, int n_waves,
                          void* stream) {
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   mk_kargs k = *args;
   const dim3 grid((unsigned)k.n_wg), block(MK_THREADS);
   if (launch_mode == MK_LAUNCH_PERSISTENT) {
-    k.task_begin = 0;
-    k.task_end = k.n_tasks;
+    k.wg_range = wg_ranges;
     int fin = 1;
     void* kp[] = {&k, &fin};
     hipError_t e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(mk_persistent), grid, block, kp, 0, st);
@@ -1458,8 +1484,7 @@ extern "C" int mk_launch(const mk_kargs* args, int launch_mode, const int32_t* w
   }
   // ablation: one launch per task wave; the kernel boundary orders the waves
   for (int w = 0; w < n_waves; ++w) {
-    k.task_begin = wave_bounds[w];
-    k.task_end = wave_bounds[w + 1];
+    k.wg_range = wg_ranges + (size_t)(1 + w) * k.n_wg * 2;
     int fin = (w == n_waves - 1) ? 1 : 0;
     void* kp[] = {&k, &fin};
     hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(mk_persistent), grid, block, kp, 0, st);
