@@ -164,7 +164,11 @@ typedef struct mk_kv_pool {
 enum mk_wave_order {
   MK_ORDER_TUNED = 0,           /* QKV, router, attention, MoE, O-proj, norm */
   MK_ORDER_INTERLEAVED = 1,     /* attention and MoE claimers alternate       */
-  MK_ORDER_ATTENTION_FIRST = 2  /* attention (with O-proj) before routing     */
+  MK_ORDER_ATTENTION_FIRST = 2, /* attention (with O-proj) before routing     */
+  MK_ORDER_PARTITIONED = 3      /* a quarter of the workgroups (spread over all
+                                   XCDs) run attention and O-proj, the rest the
+                                   router and the MoE projections, so the two
+                                   branches of the parallel block overlap      */
 };
 
 enum mk_launch_mode {
@@ -192,6 +196,9 @@ typedef struct mk_sched_opts {
 /* Emit ROUTER_TOPK as its own task instead of running it in the last router
  * tile to finish (one more counter hop per layer).                        */
 #define MK_SCHED_SEPARATE_TOPK 4
+/* Emit ATTN_COMBINE as its own task per (sequence, KV group) instead of
+ * running it in the last attention split of that group to finish.         */
+#define MK_SCHED_SEPARATE_COMBINE 8
 
 #define MK_MIN_SPLIT 64
 

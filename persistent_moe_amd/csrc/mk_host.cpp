@@ -40,6 +40,14 @@ struct Layout {
 
 size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+// Elements of one staged GEMV input row in LDS: K rounded up to a power-of-two
+// number of 512-element chunks (the register tile's K-chunks).
+long staged_row(long K) {
+  long ch = 1;
+  while (ch * 512 < K) ch <<= 1;
+  return ch * 512;
+}
+
 int validate_config(const mk_config* c) {
   if (!c) return MK_E_INVAL;
   if (c->n_layers <= 0 || c->d_model <= 0 || c->n_q_heads <= 0 || c->n_kv_heads <= 0 || c->vocab <= 0)
@@ -71,6 +79,14 @@ int validate_config(const mk_config* c) {
   const int gd = c->n_q_heads / c->n_kv_heads * c->head_dim;
   if ((size_t)c->max_batch * gd > (size_t)kXsFloats) return MK_E_UNSUPPORTED;
   if (c->swa_window < 0 || c->swa_period < 0) return MK_E_INVAL;
+  // staged GEMV inputs (hi and lo bf16 rows, padded) must fit the LDS staging area
+  {
+    const long B = c->max_batch;
+    long kmax = std::max<long>(staged_row(c->d_model), staged_row((long)gd));
+    if (moe) kmax = std::max(kmax, staged_row(c->expert_inter));
+    else kmax = std::max(kmax, staged_row(c->ffn_inter));
+    if (B * kmax > kXsFloats) return MK_E_UNSUPPORTED;
+  }
   return MK_OK;
 }
 
@@ -163,7 +179,7 @@ int build_plan(const mk_config* c, int B, int32_t max_blocks, const mk_sched_opt
   if (B < 1 || B > c->max_batch || NW < 1 || NW > kMaxWorkgroups || max_blocks < 1) return MK_E_INVAL;
   mk_sched_opts o{};
   if (opt) o = *opt;
-  if (o.wave_order < 0 || o.wave_order > 2 || o.launch_mode < 0 || o.launch_mode > 1) return MK_E_INVAL;
+  if (o.wave_order < 0 || o.wave_order > 3 || o.launch_mode < 0 || o.launch_mode > 1) return MK_E_INVAL;
   const int Lr = c->n_layers, d = c->d_model, hd = c->head_dim, Hkv = c->n_kv_heads;
   const int G = c->n_q_heads / Hkv;
   const bool moe = c->n_experts > 0;
@@ -171,7 +187,16 @@ int build_plan(const mk_config* c, int B, int32_t max_blocks, const mk_sched_opt
   Plan& p = *P;
   p.cl = mk_make_ctr_layout(Lr, Hkv, c->max_batch, moe ? c->top_k : 0);
   p.n_ctr = p.cl.total;
-  // attention split length: about NW items per layer at the longest context
+  // workgroup sets of the partitioned order: blocks of 8 consecutive
+  // workgroups (one per XCD, since workgroups are dealt round-robin over the
+  // 8 XCDs), every 4th block runs attention and O-proj
+  std::vector<int> setA, setM;
+  for (int w = 0; w < NW; ++w) ((w / 8) % 4 == 0 ? setA : setM).push_back(w);
+  // (too few workgroups for two sets: the tuned placement)
+  const bool part = o.wave_order == MK_ORDER_PARTITIONED && moe && !setA.empty() && !setM.empty();
+  const int n_attn_wg = part ? (int)setA.size() : NW;
+  // attention split length: about one item per attention workgroup at the
+  // longest context
   int S = o.attn_split;
   // scores of a split live in LDS as [G][S + 32] floats (a split that does
   // not start on a page boundary touches one extra 16-key tile, and the
@@ -180,7 +205,7 @@ int build_plan(const mk_config* c, int B, int32_t max_blocks, const mk_sched_opt
   if (S > 0) {
     if (S % c->page_size != 0 || S < MK_MIN_SPLIT || S > smax) return MK_E_INVAL;
   } else {
-    long want = (max_ctx * B * Hkv + NW - 1) / NW;
+    long want = (max_ctx * B * Hkv + n_attn_wg - 1) / n_attn_wg;
     want = std::max<long>(want, MK_MIN_SPLIT);
     want = (want + c->page_size - 1) / c->page_size * c->page_size;
     S = (int)std::min<long>(want, smax);
@@ -195,7 +220,7 @@ int build_plan(const mk_config* c, int B, int32_t max_blocks, const mk_sched_opt
   const int n_qkv = ceil_div(pairs_tot, qkv_pp);
   if (2 * qkv_pp > kYsFloats / 8) return MK_E_UNSUPPORTED;
   p.n_qkv = n_qkv;
-  const int o_tiles_g = std::max(1, NW / Hkv);
+  const int o_tiles_g = std::max(1, (part ? n_attn_wg : NW) / Hkv);
   const int o_rows = ceil_div(d, o_tiles_g);
   const int n_o_g = ceil_div(d, o_rows);
   const int lm_rows = ceil_div(c->vocab, NW);
@@ -243,6 +268,14 @@ int build_plan(const mk_config* c, int B, int32_t max_blocks, const mk_sched_opt
     push(t);
   }
 
+  // claimers / tiles on a workgroup set, or round-robin over all (null)
+  auto place = [&](const mk_task& t, const std::vector<int>* set, int i) {
+    if (set) push_on(t, (*set)[i % set->size()]);
+    else push(t);
+  };
+  const std::vector<int>* onA = part ? &setA : nullptr;
+  const std::vector<int>* onM = part ? &setM : nullptr;
+  const bool fuse_combine = !(o.flags & MK_SCHED_SEPARATE_COMBINE);
   int layer_target_prev = 0;
   for (int l = 0; l <= Lr; ++l) {
     // ADD_RMSNORM entering layer l (l == Lr: the final norm)
@@ -257,7 +290,7 @@ int build_plan(const mk_config* c, int B, int32_t max_blocks, const mk_sched_opt
       }
       if (l == Lr) t.flags |= MK_F_FINAL;
       t.signal_ctr = ctr_of(p.cl, l, MK_CTR_NORM);
-      push(t);
+      place(t, onA, 0);
     }
     if (l == Lr) break;
     const int cNORM = ctr_of(p.cl, l, MK_CTR_NORM);
@@ -275,17 +308,20 @@ int build_plan(const mk_config* c, int B, int32_t max_blocks, const mk_sched_opt
     };
     auto emit_attn = [&]() {
       wave();
-      for (int i = 0; i < n_claim; ++i) {
+      const int nc = onA ? (int)onA->size() : n_claim;
+      for (int i = 0; i < nc; ++i) {
         mk_task t = blank(MK_OP_ATTN_DRAIN, l);
         t.n0 = i;
-        t.n1 = n_claim;
+        t.n1 = nc;
         t.wait_ctr = ctr_of(p.cl, l, MK_CTR_QKV);
         t.wait_target = n_qkv;
         t.queue = ctr_of(p.cl, l, MK_CTR_QATTN);
-        push(t);
+        if (fuse_combine) t.flags |= MK_F_FUSE_COMBINE;
+        place(t, onA, i);
       }
     };
     auto emit_combine = [&]() {
+      if (fuse_combine) return;
       wave();
       for (int b = 0; b < B; ++b)
         for (int g = 0; g < Hkv; ++g) {
@@ -311,7 +347,7 @@ int build_plan(const mk_config* c, int B, int32_t max_blocks, const mk_sched_opt
           t.wait_ctr = ctr_of(p.cl, l, p.cl.comb + g);
           t.wait_target = B;
           t.signal_ctr = signal;
-          push(t);
+          place(t, onA, g * n_o_g + i);
         }
     };
     if (moe) {
@@ -331,7 +367,7 @@ int build_plan(const mk_config* c, int B, int32_t max_blocks, const mk_sched_opt
             t.flags |= MK_F_FUSE_TOPK;
             t.aux[0] = n_r;
           }
-          push(t);
+          place(t, onM, i);
         }
         if (fuse_topk) return;
         wave();
@@ -340,31 +376,32 @@ int build_plan(const mk_config* c, int B, int32_t max_blocks, const mk_sched_opt
         t.wait_ctr = ctr_of(p.cl, l, MK_CTR_ROUTER);
         t.wait_target = n_r;
         t.signal_ctr = cROUTE;
-        push(t);
+        place(t, onM, 0);
       };
+      const int n_moe_claim = onM ? (int)onM->size() : n_claim;
       auto emit_ug = [&]() {
         wave();
-        for (int i = 0; i < n_claim; ++i) {
+        for (int i = 0; i < n_moe_claim; ++i) {
           mk_task t = blank(MK_OP_MOE_UPGATE_ACT_DRAIN, l);
           t.n0 = i;
-          t.n1 = n_claim;
+          t.n1 = n_moe_claim;
           t.wait_ctr = cROUTE;
           t.wait_target = 1;
           t.queue = ctr_of(p.cl, l, MK_CTR_QUG);
-          push(t);
+          place(t, onM, i);
         }
       };
       auto emit_dn = [&]() {
         wave();
-        for (int i = 0; i < n_claim; ++i) {
+        for (int i = 0; i < n_moe_claim; ++i) {
           mk_task t = blank(MK_OP_MOE_DOWN_DRAIN, l);
           t.n0 = i;
-          t.n1 = n_claim;
+          t.n1 = n_moe_claim;
           t.wait_ctr = cROUTE;
           t.wait_target = 1;
           t.queue = ctr_of(p.cl, l, MK_CTR_QDN);
           t.signal_ctr = cLAYER;
-          push(t);
+          place(t, onM, i);
         }
       };
       switch (o.wave_order) {
@@ -375,11 +412,14 @@ int build_plan(const mk_config* c, int B, int32_t max_blocks, const mk_sched_opt
         case MK_ORDER_INTERLEAVED:
           emit_qkv(); emit_router(); emit_ug(); emit_attn(); emit_dn(); emit_combine(); emit_oproj(cLAYER);
           break;
+        case MK_ORDER_PARTITIONED:   // per set: A = QKV, attention, O-proj; M = QKV, router, up-gate, down
+          emit_qkv(); emit_router(); emit_attn(); emit_ug(); emit_combine(); emit_dn(); emit_oproj(cLAYER);
+          break;
         default:  // tuned: QKV, router, attention, MoE projections, O-proj, norm
           emit_qkv(); emit_router(); emit_attn(); emit_ug(); emit_combine(); emit_dn(); emit_oproj(cLAYER);
           break;
       }
-      layer_target_prev = n_claim + Hkv * n_o_g;
+      layer_target_prev = n_moe_claim + Hkv * n_o_g;
     } else {
       const int cO = ctr_of(p.cl, l, MK_CTR_OPROJ);
       const int cN2 = ctr_of(p.cl, l, MK_CTR_NORM2);
@@ -536,6 +576,10 @@ int simulate(const mk_config* c, int B, const Plan& p, int NW, const int32_t* se
             if (phase[w] == 0) {
               phase[w] = 1;
               if (t.n0 < q.n_items) cur_item[w] = t.n0;
+              if (t.op == MK_OP_ATTN_DRAIN && (t.flags & MK_F_FUSE_COMBINE) && t.n0 == 0)
+                for (int b = 0; b < B; ++b)   // sequences without keys: nothing to combine
+                  if (nspl(t.layer, b) == 0)
+                    for (int g = 0; g < Hkv; ++g) ctr[ctr_of(p.cl, t.layer, p.cl.comb + g)]++;
             }
             if (cur_item[w] < 0) {
               const int item = t.n1 + q.head;
@@ -551,7 +595,9 @@ int simulate(const mk_config* c, int B, const Plan& p, int NW, const int32_t* se
             if (t.op == MK_OP_ATTN_DRAIN) {
               int b, g;
               attn_bg(t.layer, item, &b, &g);
-              ctr[ctr_of(p.cl, t.layer, p.cl.attn + b * Hkv + g)]++;
+              const long v = ++ctr[ctr_of(p.cl, t.layer, p.cl.attn + b * Hkv + g)];
+              if ((t.flags & MK_F_FUSE_COMBINE) && v == nspl(t.layer, b))   // the last split combines
+                ctr[ctr_of(p.cl, t.layer, p.cl.comb + g)]++;
             } else if (t.op == MK_OP_MOE_UPGATE_ACT_DRAIN) {
               ctr[ctr_of(p.cl, t.layer, p.cl.ug + item / p.ug_tiles)]++;
             }

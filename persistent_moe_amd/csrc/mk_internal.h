@@ -17,6 +17,8 @@ enum {
   MK_F_FUSE_TOPK = 1 << 4,  // ROUTER_GEMM: the last tile to finish runs top-k and
                             // ROUTE_FINALIZE and signals the layer's ROUTE counter
                             // (aux[0] = number of router tiles)
+  MK_F_FUSE_COMBINE = 1 << 5   // ATTN_DRAIN: the last split of a (sequence, group) to
+                                // finish runs its combine and bumps COMB[group]
 };
 
 // descriptor words set by the schedule builder

@@ -43,7 +43,10 @@
 #define RED_FLOATS 8192   // attention cross-wave reduction, 32 KB
 #define NBMAX 8
 #ifndef MK_WB
-#define MK_WB 16          // 16-byte weight loads per lane per GEMV row group (2 groups in flight)
+#define MK_WB 16          // 16-byte weight loads per lane per GEMV row group
+#endif
+#ifndef MK_NT
+#define MK_NT 2           // GEMV row groups (register tiles) in flight per compute wave
 #endif
 #define MK_CW 3           // compute waves: wave 0 is the control wave (spins, stages)
 
@@ -168,6 +171,14 @@ __device__ __forceinline__ int wave_min(int v) {
              min(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
 }
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + expf(-g)); }
+
+// x = hi + lo with hi = bf16(x) and lo = bf16(x - hi), two values per word
+__device__ __forceinline__ void split_bf16(float x0, float x1, uint32_t& hi, uint32_t& lo) {
+  const uint16_t h0 = f_to_bf16(x0), h1 = f_to_bf16(x1);
+  const uint16_t l0 = f_to_bf16(x0 - bf16_to_f(h0)), l1 = f_to_bf16(x1 - bf16_to_f(h1));
+  hi = (uint32_t)h0 | ((uint32_t)h1 << 16);
+  lo = (uint32_t)l0 | ((uint32_t)l1 << 16);
+}
 
 // Each counter owns a 256-byte line (MK_CTR_PAD ints), so that workgroups
 // polling different counters do not share a line.
@@ -340,7 +351,7 @@ struct GemvArgs {
   int mode;        // ROW_*
   int half;        // ROW_ROPE_PAIRS: hd/2 (a power of two); ROW_GATE_UP: I (offset of the up rows)
   int hd;
-  int xstride;     // floats between staged x rows in LDS
+  int xstride;     // elements between staged x rows in LDS (set by gemv_run)
   int nb;          // live batch rows
   // output
   float* out;      // mode 0: out[b*ob + r]; null: LDS ys[r*NBMAX + b]
@@ -352,6 +363,34 @@ struct GemvArgs {
 // rows p + (p / (hd/2) + upper) * half, which for RoPE pairs (half = hd/2) is
 // head * hd + i (+ hd/2 for the upper row), and for gate/up pairs (the shift
 // hs = 31 makes p / 2^hs zero) is p (+ I).
+// Every field is the same in all lanes; say so, so that the row arithmetic
+// runs on the scalar unit and buffer descriptors stay in scalar registers.
+template <typename P>
+__device__ __forceinline__ P* uniform_ptr(P* p) {
+  const uint64_t v = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v), hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (P*)(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ long uniform_long(long x) {
+  const uint64_t v = (uint64_t)x;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v), hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (long)(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ void make_uniform(GemvArgs& g) {
+  g.base = uniform_ptr(g.base);
+  g.ldw = uniform_long(g.ldw);
+  g.r0 = __builtin_amdgcn_readfirstlane(g.r0);
+  g.nrows = __builtin_amdgcn_readfirstlane(g.nrows);
+  g.K = __builtin_amdgcn_readfirstlane(g.K);
+  g.mode = __builtin_amdgcn_readfirstlane(g.mode);
+  g.half = __builtin_amdgcn_readfirstlane(g.half);
+  g.hd = __builtin_amdgcn_readfirstlane(g.hd);
+  g.xstride = __builtin_amdgcn_readfirstlane(g.xstride);
+  g.nb = __builtin_amdgcn_readfirstlane(g.nb);
+  g.out = uniform_ptr(g.out);
+  g.ob = uniform_long(g.ob);
+}
+
 __device__ __forceinline__ const uint16_t* gemv_row(const GemvArgs& g, int r) {
   const int pm = g.mode != ROW_PLAIN ? 1 : 0;
   const int p = g.r0 + (r >> pm), upper = r & pm;
@@ -366,6 +405,12 @@ __device__ __forceinline__ const uint16_t* gemv_row(const GemvArgs& g, int r) {
 // covers K; so a wave owns WB / kch consecutive rows per group.  kch is a
 // runtime value, so one instance per batch width serves every GEMV shape:
 // the step's hot code stays small enough for the instruction cache.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+// a.bf16[0] * b.bf16[0] + a.bf16[1] * b.bf16[1] + c (fp32 accumulate)
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
+}
+
 template <int NB>
 struct GemvTile {
   static constexpr int WB = NB >= 4 ? MK_WB / 2 : MK_WB;
@@ -376,39 +421,48 @@ struct GemvTile {
     return (grp * MK_CW + cw - 1) * (WB >> kl);
   }
 
-  __device__ __forceinline__ void load(const GemvArgs& g, int grp, int kl) {
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // One buffer descriptor per weight row (wave-uniform, scalar registers)
+  // whose size is the row's K elements, or 0 for a row past the tile: the
+  // hardware returns zeros for those loads, so nothing is masked.  voff is
+  // the lane's byte offset (16 lane) in a K-chunk.
+  __device__ __forceinline__ void load(const GemvArgs& g, int grp, int kl, int voff) {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r0 = row0(grp, wave, kl), cm = (1 << kl) - 1;
 #pragma unroll
     for (int u = 0; u < WB; ++u) {
-      const int r = r0 + (u >> kl), seg = lane + 64 * (u & cm);
-      if (r < g.nrows && seg * 8 < g.K) w[u] = ldg_nt(gemv_row(g, r) + seg * 8);
-      else w[u] = (u32x4){0u, 0u, 0u, 0u};
+      const int r = r0 + (u >> kl), c = u & cm;
+      __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t*>(gemv_row(g, r < g.nrows ? r : 0)), (short)0, r < g.nrows ? g.K * 2 : 0, 0x00020000);
+      w[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff + c * 1024, 0, 2 /* nontemporal */);
     }
   }
 
-  __device__ __forceinline__ void compute(const GemvArgs& g, int grp, int kl, const float* xs, float* ys) {
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // x comes from LDS as two bf16 arrays (high part, remainder) of the staged
+  // fp32 rows, each row padded with zeros to whole K-chunks; xh and xl point
+  // at the lane's first element.  Each 16-byte weight slot costs 8 bf16 dot
+  // products.
+  __device__ __forceinline__ void compute(const GemvArgs& g, int grp, int kl, const uint16_t* xh, const uint16_t* xl,
+                                          float* ys) {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int r0 = row0(grp, wave, kl), cm = (1 << kl) - 1;
     if (r0 >= g.nrows) return;   // wave-uniform: no rows in this group
     float acc[WB][NB];
 #pragma unroll
     for (int u = 0; u < WB; ++u) {
-      const int seg = lane + 64 * (u & cm);
+      const int e0 = 512 * (u & cm);
+      const u32x4 v = w[u];
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
-        const f32x4* xp = reinterpret_cast<const f32x4*>(xs + b * g.xstride + (seg * 8 < g.K ? seg * 8 : 0));
-        const f32x4 x0 = xp[0], x1 = xp[1];
-        const u32x4 v = w[u];
-        float s = 0.f;
-        s = fmaf(bf_lo(v.x), x0.x, s);
-        s = fmaf(bf_hi(v.x), x0.y, s);
-        s = fmaf(bf_lo(v.y), x0.z, s);
-        s = fmaf(bf_hi(v.y), x0.w, s);
-        s = fmaf(bf_lo(v.z), x1.x, s);
-        s = fmaf(bf_hi(v.z), x1.y, s);
-        s = fmaf(bf_lo(v.w), x1.z, s);
-        s = fmaf(bf_hi(v.w), x1.w, s);
+        const u32x4 h = *reinterpret_cast<const u32x4*>(xh + b * g.xstride + e0);
+        const u32x4 q = *reinterpret_cast<const u32x4*>(xl + b * g.xstride + e0);
+        float s = dot2_bf16(v.x, h.x, 0.f);
+        s = dot2_bf16(v.y, h.y, s);
+        s = dot2_bf16(v.z, h.z, s);
+        s = dot2_bf16(v.w, h.w, s);
+        s = dot2_bf16(v.x, q.x, s);
+        s = dot2_bf16(v.y, q.y, s);
+        s = dot2_bf16(v.z, q.z, s);
+        s = dot2_bf16(v.w, q.w, s);
         acc[u][b] = s;
       }
     }
@@ -458,7 +512,9 @@ struct StageArgs {
 // the other waves only meet it at the barrier.  Wave 0's own weight loads
 // have landed by the time its spin sees the counter, so its staging loads
 // do not queue behind outstanding weight traffic.  Every thread must call it.
-__device__ __forceinline__ bool wait_and_stage(const KA a, Smem& sm, const StageArgs& s) {
+// Rows go to LDS with stride kp (K padded to the GEMV's whole K-chunks),
+// zeros in the padding.
+__device__ __forceinline__ bool wait_and_stage(const KA a, Smem& sm, const StageArgs& s, int kp) {
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
     int ok = 1;
@@ -486,12 +542,31 @@ __device__ __forceinline__ bool wait_and_stage(const KA a, Smem& sm, const Stage
                 if (q == j) row = s.tok[q];
             }
             v[u] = ldc16(s.base, (int)(((long)row * s.ld + c * 4) * 4));
-            dst[u] = j * s.K + c * 4;
+            dst[u] = j * kp + c * 4;
           }
         }
+        // x = hi + lo, both bf16, into two arrays [nb][kp] at the start of xs
+        uint16_t* xh = reinterpret_cast<uint16_t*>(sm.xs);
+        uint16_t* xl = xh + s.nb * kp;
 #pragma unroll
         for (int u = 0; u < 8; ++u)
-          if (dst[u] >= 0) *reinterpret_cast<u32x4*>(sm.xs + dst[u]) = v[u];
+          if (dst[u] >= 0) {
+            uint32_t h0, h1, l0, l1;
+            split_bf16(__uint_as_float(v[u].x), __uint_as_float(v[u].y), h0, l0);
+            split_bf16(__uint_as_float(v[u].z), __uint_as_float(v[u].w), h1, l1);
+            *reinterpret_cast<uint2*>(xh + dst[u]) = make_uint2(h0, h1);
+            *reinterpret_cast<uint2*>(xl + dst[u]) = make_uint2(l0, l1);
+          }
+      }
+      if (kp > s.K) {
+        uint16_t* xh = reinterpret_cast<uint16_t*>(sm.xs);
+        uint16_t* xl = xh + s.nb * kp;
+        const int pw = (kp - s.K) >> 2;   // 4-element pieces of padding per row
+        for (int i = lane; i < s.nb * pw; i += 64) {
+          const int j = i / pw, e = s.K + (i - j * pw) * 4;
+          *reinterpret_cast<uint2*>(xh + j * kp + e) = make_uint2(0u, 0u);
+          *reinterpret_cast<uint2*>(xl + j * kp + e) = make_uint2(0u, 0u);
+        }
       }
     }
   }
@@ -501,27 +576,38 @@ __device__ __forceinline__ bool wait_and_stage(const KA a, Smem& sm, const Stage
 }
 
 template <int NB>
-__device__ __forceinline__ bool gemv_run(const KA a, Smem& sm, const GemvArgs& g, const StageArgs& s) {
-  GemvTile<NB> A, Bt;
+__device__ __forceinline__ bool gemv_run(const KA a, Smem& sm, const GemvArgs& g_in, const StageArgs& s) {
+  GemvTile<NB> T[MK_NT];
+  GemvArgs g = g_in;
+  make_uniform(g);
   const int kch = (g.K + 511) >> 9;
   const int kl = kch <= 1 ? 0 : 32 - __builtin_clz(kch - 1);   // ceil(log2(kch)); K <= 512 * WB
   const int per = MK_CW * (GemvTile<NB>::WB >> kl);
   const int ng = (g.nrows + per - 1) / per;
   const bool cw = (threadIdx.x >> 6) != 0;
-  // the first two row groups are in flight before the dependency resolves;
+  // the first MK_NT row groups are in flight before the dependency resolves;
   // the control wave loads no weights, so its staging loads queue behind nothing
+  const int voff = (threadIdx.x & 63) * 16;
   if (cw) {
-    A.load(g, 0, kl);
-    if (ng > 1) Bt.load(g, 1, kl);
+#pragma unroll
+    for (int u = 0; u < MK_NT; ++u)
+      if (u < ng) T[u].load(g, u, kl, voff);
   }
-  if (!wait_and_stage(a, sm, s)) return false;
+  const int kp = 512 << kl;   // staged row stride (elements): the K-chunks the tiles read
+  if (!wait_and_stage(a, sm, s, kp)) return false;
+  const uint16_t* xh = reinterpret_cast<const uint16_t*>(sm.xs) + (threadIdx.x & 63) * 8;
+  const uint16_t* xl = xh + s.nb * kp;
+  GemvArgs gx = g;
+  gx.xstride = kp;
+  make_uniform(gx);
   if (cw) {
-    for (int grp = 0; grp < ng; grp += 2) {
-      A.compute(g, grp, kl, sm.xs, sm.ys);
-      if (grp + 2 < ng) A.load(g, grp + 2, kl);
-      if (grp + 1 < ng) {
-        Bt.compute(g, grp + 1, kl, sm.xs, sm.ys);
-        if (grp + 3 < ng) Bt.load(g, grp + 3, kl);
+    for (int grp = 0; grp < ng; grp += MK_NT) {
+#pragma unroll
+      for (int u = 0; u < MK_NT; ++u) {
+        if (grp + u < ng) {
+          T[u].compute(gx, grp + u, kl, xh, xl, sm.ys);
+          if (grp + u + MK_NT < ng) T[u].load(g, grp + u + MK_NT, kl, voff);
+        }
       }
     }
   }
@@ -847,13 +933,6 @@ __device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
                                                  0, 0, 0);
 }
-// x = hi + lo with hi = bf16(x) and lo = bf16(x - hi), two values per word
-__device__ __forceinline__ void split_bf16(float x0, float x1, uint32_t& hi, uint32_t& lo) {
-  const uint16_t h0 = f_to_bf16(x0), h1 = f_to_bf16(x1);
-  const uint16_t l0 = f_to_bf16(x0 - bf16_to_f(h0)), l1 = f_to_bf16(x1 - bf16_to_f(h1));
-  hi = (uint32_t)h0 | ((uint32_t)h1 << 16);
-  lo = (uint32_t)l0 | ((uint32_t)l1 << 16);
-}
 constexpr int ATT_PT = 3;   // K tiles in flight per compute wave
 constexpr int ATT_PV = 4;   // V k-steps (32 keys) in flight per compute wave
 
@@ -1075,14 +1154,14 @@ __device__ __forceinline__ bool attn_item(const KA a, Smem& sm, int l, int b, in
   return attn_split<64>(a, sm, l, b, g, s, p0, p1, ti, wait_idx, wait_target);
 }
 
-// ATTN_COMBINE for (batch b, group g): M = max_s m_s;
-// o = sum_s e^(m_s - M) o_s / sum_s e^(m_s - M) l_s.  Wave h computes head
-// h's weights; then every thread accumulates 4 dims of one head over the
-// splits with its loads issued 8 splits at a time.
-__device__ __forceinline__ bool op_attn_combine(const KA a, Smem& sm, const mk_task& t, int ti) {
-  const int l = t.layer, b = t.batch, g = t.group, G = a->G, hd = a->hd;
+// ATTN_COMBINE for (sequence b, group g): M = max_s m_s;
+// o = sum_s e^(m_s - M) o_s / sum_s e^(m_s - M) l_s.  Each thread owns 4 dims
+// of one head; the o partials of the first 16 splits are loaded before the
+// per-head weights are computed (wave h takes heads h, h+4, ...), so up to 16
+// splits cost one round trip.  Writes attn[b][g's heads].
+__device__ __forceinline__ void attn_combine(const KA a, Smem& sm, int l, int b, int g) {
+  const int G = a->G, hd = a->hd;
   const int ns = n_splits(a, l, b);
-  if (!wg_wait(a, sm, t.wait_ctr, ns, ti)) return false;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   float* out = a->attn + ((long)l * a->B + b) * a->Hq * hd;
   const long hstride = (long)a->max_splits;
@@ -1090,8 +1169,16 @@ __device__ __forceinline__ bool op_attn_combine(const KA a, Smem& sm, const mk_t
   const float* po0 = a->part_o + ((((long)(l & 1) * a->B + b) * a->Hq + g * G) * hstride) * hd;
   float* wts = sm.ys;                 // [G][max_splits]
   float* den = sm.red;                // [G]
-  for (int h = wave; h < G; h += MK_WAVES) {
-    const float* ml = ml0 + (long)h * hstride * 2;
+  const int q4 = hd / 4;              // float4 chunks per head
+  const bool mine = tid < G * q4;
+  const int h = mine ? tid / q4 : 0, cq = tid - h * q4;
+  const int obase = (int)((h * hstride * hd + cq * 4) * 4);   // byte offset of split 0
+  f32x4 pv[16];
+#pragma unroll
+  for (int u = 0; u < 16; ++u)
+    pv[u] = (mine && u < ns) ? as_f4(ldc16(po0, obase + u * hd * 4)) : (f32x4){0.f, 0.f, 0.f, 0.f};
+  for (int hh = wave; hh < G; hh += MK_WAVES) {
+    const float* ml = ml0 + (long)hh * hstride * 2;
     float m[16], lsum[16];
     float mx = -INFINITY;
 #pragma unroll
@@ -1109,31 +1196,36 @@ __device__ __forceinline__ bool op_attn_combine(const KA a, Smem& sm, const mk_t
       const int s = lane + 64 * u;
       if (s < ns) {
         const float w = expf(m[u] - mx);
-        wts[h * hstride + s] = w;
+        wts[hh * hstride + s] = w;
         dsum += w * lsum[u];
       }
     }
     dsum = wave_sum(dsum);
-    if (lane == 0) den[h] = dsum;
+    if (lane == 0) den[hh] = dsum;
   }
   __syncthreads();
-  const int q4 = hd / 4;   // float4 chunks per head
-  for (int idx = tid; idx < G * q4; idx += MK_THREADS) {
-    const int h = idx / q4, cq = idx - h * q4;
-    const float* po = po0 + (long)h * hstride * hd;
-    f32x4 num = (f32x4){0.f, 0.f, 0.f, 0.f};
-    for (int s0 = 0; s0 < ns; s0 += 8) {
-      f32x4 pv[8];
+  f32x4 num = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (s0 + u < ns) pv[u] = as_f4(ldc16(po, (int)(((long)(s0 + u) * hd + cq * 4) * 4)));
+  for (int u = 0; u < 16; ++u)
+    if (u < ns) num += wts[h * hstride + u] * pv[u];
+  for (int s0 = 16; s0 < ns; s0 += 16) {
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (s0 + u < ns) num += wts[h * hstride + s0 + u] * pv[u];
-    }
+    for (int u = 0; u < 16; ++u)
+      pv[u] = (mine && s0 + u < ns) ? as_f4(ldc16(po0, obase + (s0 + u) * hd * 4)) : (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      if (s0 + u < ns) num += wts[h * hstride + s0 + u] * pv[u];
+  }
+  if (mine) {
     const f32x4 r = ns > 0 ? num / den[h] : (f32x4){0.f, 0.f, 0.f, 0.f};
     stc16(out, ((g * G + h) * hd + cq * 4) * 4, as_u4(r));
   }
+}
+
+// ATTN_COMBINE as its own task: waits for every split of (b, g).
+__device__ __forceinline__ bool op_attn_combine(const KA a, Smem& sm, const mk_task& t, int ti) {
+  if (!wg_wait(a, sm, t.wait_ctr, n_splits(a, t.layer, t.batch), ti)) return false;
+  attn_combine(a, sm, t.layer, t.batch, t.group);
   wg_signal(a, t.signal_ctr, 1);
   return true;
 }
@@ -1187,7 +1279,12 @@ extern "C" __global__ void __launch_bounds__(MK_THREADS, 1) mk_persistent(mk_kar
     if (!claiming) {
       if (k >= kend) break;
       if (k > kbeg) cur ^= 1;
-      t = sm.tq[cur];
+      {   // the descriptor is the same for every lane: keep it in scalar registers
+        const int* src = reinterpret_cast<const int*>(&sm.tq[cur]);
+        int* dst = reinterpret_cast<int*>(&t);
+#pragma unroll
+        for (int q = 0; q < 32; ++q) dst[q] = __builtin_amdgcn_readfirstlane(src[q]);
+      }
       ti = t.aux[MK_AUX_INDEX];
       if (k + 1 < kend) {
         if (tid >= 64 && tid < 72) pre = load_task_piece(a->tasks, k + 1, tid - 64);
@@ -1209,6 +1306,14 @@ extern "C" __global__ void __launch_bounds__(MK_THREADS, 1) mk_persistent(mk_kar
           for (int b = 0; b < a->B; ++b) n_items += n_splits(a, l, b) * a->Hkv;
           qidx = layer_ctr(a, l, MK_CTR_QATTN);
           attn_wait = t.wait_ctr;       // waited for inside the first item
+          if ((t.flags & MK_F_FUSE_COMBINE) && t.n0 == 0 && tid == 0) {
+            // a sequence without keys (empty slot) has no split to combine it
+            for (int b = 0; b < a->B; ++b)
+              if (n_splits(a, l, b) == 0)
+                for (int g = 0; g < a->Hkv; ++g)
+                  __hip_atomic_fetch_add(ctrp(a, layer_ctr(a, l, a->cl.comb + g)), 1, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+          }
         } else {
           if (!wg_wait(a, sm, t.wait_ctr, t.wait_target, ti)) {
             aborted = true;
@@ -1291,12 +1396,18 @@ extern "C" __global__ void __launch_bounds__(MK_THREADS, 1) mk_persistent(mk_kar
           const u32x4 r0v = ldc16(rec, epi_ae * 64);
           const u32x4 r1v = ldc16(rec, epi_ae * 64 + 16);
           const u32x4 r2v = ldc16(rec, epi_ae * 64 + 32);
-          const int e = (int)r0v.x;
-          epi_r0 = (int)r0v.y;
-          epi_nr = (int)r0v.z;
+          const int e = __builtin_amdgcn_readfirstlane((int)r0v.x);
+          epi_r0 = __builtin_amdgcn_readfirstlane((int)r0v.y);
+          epi_nr = __builtin_amdgcn_readfirstlane((int)r0v.z);
           st.use_tok = true;
-          st.tok[0] = (int)r1v.x; st.tok[1] = (int)r1v.y; st.tok[2] = (int)r1v.z; st.tok[3] = (int)r1v.w;
-          st.tok[4] = (int)r2v.x; st.tok[5] = (int)r2v.y; st.tok[6] = (int)r2v.z; st.tok[7] = (int)r2v.w;
+          st.tok[0] = __builtin_amdgcn_readfirstlane((int)r1v.x);
+          st.tok[1] = __builtin_amdgcn_readfirstlane((int)r1v.y);
+          st.tok[2] = __builtin_amdgcn_readfirstlane((int)r1v.z);
+          st.tok[3] = __builtin_amdgcn_readfirstlane((int)r1v.w);
+          st.tok[4] = __builtin_amdgcn_readfirstlane((int)r2v.x);
+          st.tok[5] = __builtin_amdgcn_readfirstlane((int)r2v.y);
+          st.tok[6] = __builtin_amdgcn_readfirstlane((int)r2v.z);
+          st.tok[7] = __builtin_amdgcn_readfirstlane((int)r2v.w);
           epi_p0 = tt * a->ug_pairs;
           epi_np = min(a->ug_pairs, a->I - epi_p0);
           g.base = a->layers[l].w_upgate + (long)e * 2 * a->I * a->d; g.ldw = a->d; g.r0 = epi_p0;
@@ -1312,7 +1423,9 @@ extern "C" __global__ void __launch_bounds__(MK_THREADS, 1) mk_persistent(mk_kar
           const int32_t* rec = a->moe + (long)l * a->moe_stride + 4 + a->bk;
           const int ae = item / a->dn_tiles, tt = item - ae * a->dn_tiles;
           const u32x4 r0v = ldc16(rec, ae * 64);
-          const int e = (int)r0v.x, r0 = (int)r0v.y, nr = (int)r0v.z;
+          const int e = __builtin_amdgcn_readfirstlane((int)r0v.x);
+          const int r0 = __builtin_amdgcn_readfirstlane((int)r0v.y);
+          const int nr = __builtin_amdgcn_readfirstlane((int)r0v.z);
           const int n0 = tt * a->dn_rows;
           g.base = a->layers[l].w_down + (long)e * a->d * a->I; g.ldw = a->I; g.r0 = n0;
           g.nrows = min(a->dn_rows, a->d - n0); g.K = a->I; g.nb = nr;
@@ -1325,7 +1438,6 @@ extern "C" __global__ void __launch_bounds__(MK_THREADS, 1) mk_persistent(mk_kar
           break;
       }
       if (kind == U_GEMV) {
-        g.xstride = st.K;
         if (!gemv(a, sm, g, st)) {
           aborted = true;
           goto unit_done;
@@ -1412,7 +1524,22 @@ extern "C" __global__ void __launch_bounds__(MK_THREADS, 1) mk_persistent(mk_kar
               break;
             }
             attn_wait = -1;   // satisfied for every later item
-            wg_signal(a, layer_ctr(a, l, a->cl.attn + b * a->Hkv + gq), 1);
+            const int actr = layer_ctr(a, l, a->cl.attn + b * a->Hkv + gq);
+            if (t.flags & MK_F_FUSE_COMBINE) {
+              // the last split of (b, gq) to finish combines them
+              stores_done();
+              __syncthreads();
+              if (tid == 0)
+                sm.misc[3] = __hip_atomic_fetch_add(ctrp(a, actr), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                             n_splits(a, l, b) - 1;
+              __syncthreads();
+              if (sm.misc[3]) {
+                attn_combine(a, sm, l, b, gq);
+                wg_signal(a, layer_ctr(a, l, a->cl.comb + gq), 1);
+              }
+            } else {
+              wg_signal(a, actr, 1);
+            }
           }
           break;
         }

@@ -27,7 +27,7 @@ OPCODES = [
     "ROUTE_FINALIZE", "MOE_GATHER", "MOE_UPGATE_ACT_DRAIN", "MOE_DOWN_DRAIN", "MOE_COMBINE",
 ]
 MK_WAIT_SPLITS = -2
-ORDER = {"tuned": 0, "interleaved": 1, "attention_first": 2}
+ORDER = {"tuned": 0, "interleaved": 1, "attention_first": 2, "partitioned": 3}
 LAUNCH = {"persistent": 0, "per_opcode": 1}
 TAPS = {"x": 0, "xn": 1, "qkv": 2, "attn": 3, "router_logits": 4, "topk_ids": 5, "topk_weights": 6,
         "ffn_out": 7, "attn_out": 8, "trace": 9}
@@ -147,6 +147,7 @@ def make_config(model, max_batch: int) -> mk_config:
 MK_SCHED_UNREACHABLE_WAIT = 1
 MK_SCHED_TRACE = 2
 MK_SCHED_SEPARATE_TOPK = 4
+MK_SCHED_SEPARATE_COMBINE = 8
 
 
 def make_opts(wave_order="tuned", launch_mode="persistent", attn_split=0, n_workgroups=0,

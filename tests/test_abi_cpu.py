@@ -133,9 +133,31 @@ def test_static_tiles_dealt_round_robin(lib):
     # task k runs on workgroup k mod N: with 256 workgroups the 256 QKV tiles
     # of a layer of the 30B model land on 256 different workgroups
     tasks, _ = _plan(W.MOE_30B, 1, 529)
+    assert all(t.aux[16] == i % 256 and t.aux[17] == i for i, t in enumerate(tasks))
     idx = [i for i, t in enumerate(tasks) if t.op == 1 and t.layer == 3]
     assert len(idx) == 256
     assert len({i % 256 for i in idx}) == 256
+
+
+def test_partitioned_order_places_branches_on_disjoint_sets(lib):
+    # attention and O-proj on every 4th block of 8 workgroups (all 8 XCDs),
+    # router and MoE projections on the rest; QKV and LM head on all
+    opts = mk.make_opts("partitioned")
+    tasks, _ = mk.mk_plan_schedule(mk.make_config(W.MOE_30B, 1), 1, 529, opts, 256)
+    set_a = {w for w in range(256) if (w // 8) % 4 == 0}
+    assert len(set_a) == 64 and {w % 8 for w in set_a} == set(range(8))
+    where = {}
+    for t in tasks:
+        where.setdefault(mk.OPCODES[t.op], set()).add(t.aux[16])
+    for op in ("ATTN_DRAIN", "O_PROJ", "ADD_RMSNORM"):
+        assert where[op] <= set_a, op
+    for op in ("ROUTER_GEMM", "MOE_UPGATE_ACT_DRAIN", "MOE_DOWN_DRAIN"):
+        assert not (where[op] & set_a), op
+    assert len(where["QKV_PROJ"]) == 256 and len(where["LM_HEAD"]) == 256
+    # one attention claimer per attention workgroup and layer, combine fused
+    a0 = [t for t in tasks if mk.OPCODES[t.op] == "ATTN_DRAIN" and t.layer == 0]
+    assert len(a0) == 64 and all(t.flags & 32 and t.n1 == 64 for t in a0)
+    assert "ATTN_COMBINE" not in where
 
 
 def test_signal_counts_match_wait_targets(lib):
@@ -149,18 +171,22 @@ def test_signal_counts_match_wait_targets(lib):
                 sig[t.signal_ctr] = sig.get(t.signal_ctr, 0) + 1
             if t.flags & 16:           # router tile with fused top-k: one ROUTE signal per layer
                 fused[t.layer] = t.signal_ctr
-        stride = None
+        fused_comb = {t.layer for t in tasks if t.op == mk.OPCODES.index("ATTN_DRAIN") and t.flags & 32}
         for t in tasks:
             if t.op == mk.OPCODES.index("MOE_UPGATE_ACT_DRAIN"):
                 route = t.wait_ctr
                 if t.layer in fused:
                     sig[route] = 1
+            if t.op == mk.OPCODES.index("O_PROJ") and t.layer in fused_comb:
+                # fused combine: the last split of each sequence bumps its group's counter
+                sig[t.wait_ctr] = B
         for t in tasks:
             if t.wait_ctr >= 0 and t.wait_target > 0 and t.op not in (8, 13, 14):
                 assert sig.get(t.wait_ctr, 0) == t.wait_target, (mk.OPCODES[t.op], t.layer)
 
 
-@pytest.mark.parametrize("order", ["tuned", "interleaved", "attention_first", "tuned-separate-topk"])
+@pytest.mark.parametrize("order", ["tuned", "interleaved", "attention_first", "partitioned", "tuned-separate-topk",
+                                   "tuned-separate-combine", "partitioned-separate-combine"])
 @pytest.mark.parametrize("case", [
     ("tiny", W.TINY_MOE, 1, 5, [65], [2, 2]),
     ("moe30b", W.MOE_30B, 1, 529, [8193], [8] * 48),
@@ -171,7 +197,8 @@ def test_signal_counts_match_wait_targets(lib):
 def test_schedule_is_deadlock_free(lib, order, case):
     name, model, B, mb, sl, na = case
     flags = mk.MK_SCHED_SEPARATE_TOPK if order.endswith("separate-topk") else 0
-    opts = mk.make_opts(order.replace("-separate-topk", ""), flags=flags)
+    flags |= mk.MK_SCHED_SEPARATE_COMBINE if order.endswith("separate-combine") else 0
+    opts = mk.make_opts(order.replace("-separate-topk", "").replace("-separate-combine", ""), flags=flags)
     for nw in (256, 64, 7):
         rc, stuck = mk.mk_plan_simulate(_cfg(model, B), B, mb, opts, nw, sl, na)
         assert rc == mk.MK_OK, (name, nw, stuck)
