@@ -215,8 +215,17 @@ int build_plan(const mk_config* c, int B, int32_t max_blocks, const mk_sched_opt
   p.max_splits = ceil_div(max_ctx, S);
   if (p.max_splits > 1024) return MK_E_UNSUPPORTED;
   // tilings
+  int r_rows = 0, n_r = 0;
+  if (moe) {
+    r_rows = std::max(8, ceil_div(c->n_experts, 8));
+    n_r = ceil_div(c->n_experts, r_rows);
+  }
+  // tuned order: the router tiles (head of the MoE chain) get workgroups of
+  // their own, [0, n_r), and the QKV tiles are spread over the others
+  const bool router_own = moe && o.wave_order == MK_ORDER_TUNED && NW > 2 * n_r;
+  const int qkv_wg = router_own ? NW - n_r : NW;
   const int pairs_tot = (c->n_q_heads + 2 * Hkv) * hd / 2;
-  const int qkv_pp = std::max(1, ceil_div(pairs_tot, NW));
+  const int qkv_pp = std::max(1, ceil_div(pairs_tot, qkv_wg));
   const int n_qkv = ceil_div(pairs_tot, qkv_pp);
   if (2 * qkv_pp > kYsFloats / 8) return MK_E_UNSUPPORTED;
   p.n_qkv = n_qkv;
@@ -225,11 +234,8 @@ int build_plan(const mk_config* c, int B, int32_t max_blocks, const mk_sched_opt
   const int n_o_g = ceil_div(d, o_rows);
   const int lm_rows = ceil_div(c->vocab, NW);
   const int n_lm = ceil_div(c->vocab, lm_rows);
-  int r_rows = 0, n_r = 0;
   if (moe) {
-    const int E = c->n_experts, K = c->top_k, I = c->expert_inter;
-    r_rows = std::max(8, ceil_div(E, 8));
-    n_r = ceil_div(E, r_rows);
+    const int K = c->top_k, I = c->expert_inter;
     p.ug_pairs = std::max(1, ceil_div((long)K * I, NW));
     p.ug_pairs = std::min(p.ug_pairs, kYsFloats / 8 / 2);
     p.ug_tiles = ceil_div(I, p.ug_pairs);
@@ -303,7 +309,8 @@ int build_plan(const mk_config* c, int B, int32_t max_blocks, const mk_sched_opt
         t.wait_ctr = cNORM;
         t.wait_target = 1;
         t.signal_ctr = ctr_of(p.cl, l, MK_CTR_QKV);
-        push(t);
+        if (router_own) push_on(t, n_r + i);
+        else push(t);
       }
     };
     auto emit_attn = [&]() {
@@ -367,7 +374,8 @@ int build_plan(const mk_config* c, int B, int32_t max_blocks, const mk_sched_opt
             t.flags |= MK_F_FUSE_TOPK;
             t.aux[0] = n_r;
           }
-          place(t, onM, i);
+          if (router_own) push_on(t, i);
+          else place(t, onM, i);
         }
         if (fuse_topk) return;
         wave();
@@ -415,8 +423,8 @@ int build_plan(const mk_config* c, int B, int32_t max_blocks, const mk_sched_opt
         case MK_ORDER_PARTITIONED:   // per set: A = QKV, attention, O-proj; M = QKV, router, up-gate, down
           emit_qkv(); emit_router(); emit_attn(); emit_ug(); emit_combine(); emit_dn(); emit_oproj(cLAYER);
           break;
-        default:  // tuned: QKV, router, attention, MoE projections, O-proj, norm
-          emit_qkv(); emit_router(); emit_attn(); emit_ug(); emit_combine(); emit_dn(); emit_oproj(cLAYER);
+        default:  // tuned: router, QKV, attention, up-gate, O-proj, down, norm
+          emit_router(); emit_qkv(); emit_attn(); emit_ug(); emit_combine(); emit_oproj(cLAYER); emit_dn();
           break;
       }
       layer_target_prev = n_moe_claim + Hkv * n_o_g;

@@ -627,12 +627,13 @@ __device__ __forceinline__ bool gemv(const KA a, Smem& sm, const GemvArgs& g, co
 // ------------------------------------------------------------- ADD_RMSNORM
 // x_l = x_{l-1} + sum_g O-proj partial_g + sum_j w_j Y_j (parallel block), or
 // the embedding row at layer 0; xn_l = x_l / sqrt(mean(x_l^2) + eps) * gain.
-// All 512 threads take 4-element chunks of a batch row (rows in turn), with
-// the ~Hkv + k + 1 source loads of a chunk issued together.  x is kept in
-// LDS between the two passes.  The MoE combine (the gate-weighted sum of the
-// routed expert outputs, in top-k order) is folded into this task.
+// Each thread takes up to four 4-element chunks of a batch row (rows in
+// turn); the ~Hkv + k + 1 source loads of all its chunks are issued together,
+// so a row costs one round trip.  x is kept in LDS between the two passes.
+// The MoE combine (the gate-weighted sum of the routed expert outputs, in
+// top-k order) is folded into this task.
 __device__ __forceinline__ bool op_add_rmsnorm(const KA a, Smem& sm, const mk_task& t, int ti) {
-  if (!wg_wait(a, sm, t.wait_ctr, t.wait_target, ti)) return false;
+  constexpr int NCH = 4;            // 4-element chunks per thread (d <= 4096)
   const int l = t.layer, d = a->d, B = a->B, nv = d >> 2, K = a->topk;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const bool mid = t.flags & MK_F_MID;
@@ -641,18 +642,28 @@ __device__ __forceinline__ bool op_add_rmsnorm(const KA a, Smem& sm, const mk_ta
   const bool moe_in = !emb && !mid && a->parallel && a->E > 0;
   const int lp = l - 1;
   const int lx = mid ? l : lp;     // layer whose attention output is added
-  // gate weights and rows of the routed outputs of the previous layer
+  const uint16_t* gain = fin ? a->final_norm : (mid ? a->layers[l].ffn_norm : a->layers[l].attn_norm);
+  // gains do not depend on anything: in flight during the wait
+  u32x2 gg[NCH];
+#pragma unroll
+  for (int q = 0; q < NCH; ++q) {
+    const int c = tid + q * MK_THREADS;
+    gg[q] = c < nv ? ldg8(gain + c * 4) : (u32x2){0u, 0u};
+  }
+  // gate weights and rows of the routed outputs of the previous layer: final
+  // once its routing counter is set, which is long before this layer's
+  // counter completes, so they are read while waiting
   int* srow = sm.misc + 64;                              // [B*K]
   float* sw = reinterpret_cast<float*>(sm.misc + 128);   // [B*K]
   if (moe_in) {
+    if (!wg_wait(a, sm, layer_ctr(a, lp, MK_CTR_ROUTE), 1, ti)) return false;
     const int32_t* slot = a->moe + (long)lp * a->moe_stride + 4;
     if (tid < B * K) {
       srow[tid] = ldc(slot + tid);
       sw[tid] = ldc(a->topw + (long)lp * B * K + tid);
     }
-    __syncthreads();
   }
-  const uint16_t* gain = fin ? a->final_norm : (mid ? a->layers[l].ffn_norm : a->layers[l].attn_norm);
+  if (!wg_wait(a, sm, t.wait_ctr, t.wait_target, ti)) return false;
   float* xdst = mid ? a->xmid + (long)l * B * d : a->x + (long)l * B * d;
   float* xndst = mid ? a->xn2 + (long)l * B * d : a->xn + (long)l * B * d;
   float* red = sm.red;      // [MK_WAVES][NBMAX] partial sums of squares
@@ -682,48 +693,76 @@ __device__ __forceinline__ bool op_add_rmsnorm(const KA a, Smem& sm, const mk_ta
       if (tid == 0 && a->seq_lens[b] > a->max_blocks * a->page)
         report(a, MK_E_DEVICE, ti, -5, a->seq_lens[b], a->max_blocks * a->page);
     }
-    float ss = 0.f;
-#pragma unroll 1
-    for (int c = tid; c < nv; c += MK_THREADS) {
-      const int off = c * 16;   // byte offset of the chunk in a row
-      f32x4 acc = (f32x4){0.f, 0.f, 0.f, 0.f};
-      if (!live) {
-      } else if (emb) {
-        const u32x2 e = ldg8(a->embed + (long)tok * d + c * 4);
-        acc = (f32x4){bf_lo(e.x), bf_hi(e.x), bf_lo(e.y), bf_hi(e.y)};
-      } else if (mid || moe_in) {
-        u32x4 og[8], ym[8];
+    // every source chunk of this thread is loaded before any is used
+    f32x4 acc[NCH];
+    if (!live) {
 #pragma unroll
-        for (int g = 0; g < 8; ++g)
-          if (g < a->Hkv) og[g] = ldc16(a->opart + (((long)lx * a->Hkv + g) * B + b) * d, off);
-        if (moe_in) {
+      for (int q = 0; q < NCH; ++q) acc[q] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    } else if (emb) {
 #pragma unroll
-          for (int j = 0; j < 8; ++j)
-            if (j < K)
-              ym[j] = ldc16(a->Y + ((long)lp * a->bk + __builtin_amdgcn_readfirstlane(srow[b * K + j])) * d, off);
-        }
-        const f32x4 xp = as_f4(ldc16(a->x + ((long)lx * B + b) * d, off));
-        f32x4 o = (f32x4){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int g = 0; g < 8; ++g)
-          if (g < a->Hkv) o += as_f4(og[g]);
-        stc16(a->oout + ((long)lx * B + b) * d, off, as_u4(o));
-        acc = xp + o;
-        if (moe_in) {
-          f32x4 m = (f32x4){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int j = 0; j < 8; ++j)
-            if (j < K) m += sw[b * K + j] * as_f4(ym[j]);
-          stc16(a->fo + ((long)lp * B + b) * d, off, as_u4(m));
-          acc += m;
-        }
-      } else {
-        // sequential block: x_l = x_mid + FFN output
-        acc = as_f4(ldc16(a->xmid + ((long)lp * B + b) * d, off)) + as_f4(ldc16(a->fo + ((long)lp * B + b) * d, off));
+      for (int q = 0; q < NCH; ++q) {
+        const int c = tid + q * MK_THREADS;
+        const u32x2 e = c < nv ? ldg8(a->embed + (long)tok * d + c * 4) : (u32x2){0u, 0u};
+        acc[q] = (f32x4){bf_lo(e.x), bf_hi(e.x), bf_lo(e.y), bf_hi(e.y)};
       }
-      stc16(xdst + (long)b * d, off, as_u4(acc));
-      *reinterpret_cast<f32x4*>(xv + b * d + c * 4) = acc;
-      ss += acc.x * acc.x + acc.y * acc.y + acc.z * acc.z + acc.w * acc.w;
+    } else if (mid || moe_in) {
+      u32x4 og[NCH][8], ym[NCH][8], xq[NCH];
+#pragma unroll
+      for (int q = 0; q < NCH; ++q) {
+        const int c = tid + q * MK_THREADS, off = c * 16;
+        if (c < nv) {
+#pragma unroll
+          for (int g = 0; g < 8; ++g)
+            if (g < a->Hkv) og[q][g] = ldc16(a->opart + (((long)lx * a->Hkv + g) * B + b) * d, off);
+          if (moe_in) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+              if (j < K)
+                ym[q][j] = ldc16(a->Y + ((long)lp * a->bk + __builtin_amdgcn_readfirstlane(srow[b * K + j])) * d, off);
+          }
+          xq[q] = ldc16(a->x + ((long)lx * B + b) * d, off);
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < NCH; ++q) {
+        const int c = tid + q * MK_THREADS, off = c * 16;
+        acc[q] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        if (c < nv) {
+          f32x4 o = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int g = 0; g < 8; ++g)
+            if (g < a->Hkv) o += as_f4(og[q][g]);
+          stc16(a->oout + ((long)lx * B + b) * d, off, as_u4(o));
+          acc[q] = as_f4(xq[q]) + o;
+          if (moe_in) {
+            f32x4 m = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+              if (j < K) m += sw[b * K + j] * as_f4(ym[q][j]);
+            stc16(a->fo + ((long)lp * B + b) * d, off, as_u4(m));
+            acc[q] += m;
+          }
+        }
+      }
+    } else {
+      // sequential block: x_l = x_mid + FFN output
+#pragma unroll
+      for (int q = 0; q < NCH; ++q) {
+        const int c = tid + q * MK_THREADS, off = c * 16;
+        acc[q] = c < nv ? as_f4(ldc16(a->xmid + ((long)lp * B + b) * d, off)) +
+                              as_f4(ldc16(a->fo + ((long)lp * B + b) * d, off))
+                        : (f32x4){0.f, 0.f, 0.f, 0.f};
+      }
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int q = 0; q < NCH; ++q) {
+      const int c = tid + q * MK_THREADS;
+      if (c < nv) {
+        stc16(xdst + (long)b * d, c * 16, as_u4(acc[q]));
+        *reinterpret_cast<f32x4*>(xv + b * d + c * 4) = acc[q];
+        ss += acc[q].x * acc[q].x + acc[q].y * acc[q].y + acc[q].z * acc[q].z + acc[q].w * acc[q].w;
+      }
     }
     ss = wave_sum(ss);
     if (lane == 0) red[wave * NBMAX + b] = ss;
@@ -735,12 +774,14 @@ __device__ __forceinline__ bool op_add_rmsnorm(const KA a, Smem& sm, const mk_ta
 #pragma unroll
     for (int w = 0; w < MK_WAVES; ++w) tot += red[w * NBMAX + b];
     const float r = 1.0f / sqrtf(tot / (float)d + a->eps);
-#pragma unroll 1
-    for (int c = tid; c < nv; c += MK_THREADS) {
-      const u32x2 gg = ldg8(gain + c * 4);
-      const f32x4 gv = (f32x4){bf_lo(gg.x), bf_hi(gg.x), bf_lo(gg.y), bf_hi(gg.y)};
-      const f32x4 xb = *reinterpret_cast<const f32x4*>(xv + b * d + c * 4);
-      stc16(xndst + (long)b * d, c * 16, as_u4(xb * r * gv));
+#pragma unroll
+    for (int q = 0; q < NCH; ++q) {
+      const int c = tid + q * MK_THREADS;
+      if (c < nv) {
+        const f32x4 gv = (f32x4){bf_lo(gg[q].x), bf_hi(gg[q].x), bf_lo(gg[q].y), bf_hi(gg[q].y)};
+        const f32x4 xb = *reinterpret_cast<const f32x4*>(xv + b * d + c * 4);
+        stc16(xndst + (long)b * d, c * 16, as_u4(xb * r * gv));
+      }
     }
   }
   wg_signal(a, t.signal_ctr, 1);
@@ -1156,8 +1197,8 @@ __device__ __forceinline__ bool attn_item(const KA a, Smem& sm, int l, int b, in
 
 // ATTN_COMBINE for (sequence b, group g): M = max_s m_s;
 // o = sum_s e^(m_s - M) o_s / sum_s e^(m_s - M) l_s.  Each thread owns 4 dims
-// of one head; the o partials of the first 16 splits are loaded before the
-// per-head weights are computed (wave h takes heads h, h+4, ...), so up to 16
+// of one head; the o partials of the first CB splits are loaded before the
+// per-head weights are computed (wave h takes heads h, h+4, ...), so up to CB
 // splits cost one round trip.  Writes attn[b][g's heads].
 __device__ __forceinline__ void attn_combine(const KA a, Smem& sm, int l, int b, int g) {
   const int G = a->G, hd = a->hd;
@@ -1173,9 +1214,10 @@ __device__ __forceinline__ void attn_combine(const KA a, Smem& sm, int l, int b,
   const bool mine = tid < G * q4;
   const int h = mine ? tid / q4 : 0, cq = tid - h * q4;
   const int obase = (int)((h * hstride * hd + cq * 4) * 4);   // byte offset of split 0
-  f32x4 pv[16];
+  constexpr int CB = 64;
+  f32x4 pv[CB];
 #pragma unroll
-  for (int u = 0; u < 16; ++u)
+  for (int u = 0; u < CB; ++u)
     pv[u] = (mine && u < ns) ? as_f4(ldc16(po0, obase + u * hd * 4)) : (f32x4){0.f, 0.f, 0.f, 0.f};
   for (int hh = wave; hh < G; hh += MK_WAVES) {
     const float* ml = ml0 + (long)hh * hstride * 2;
@@ -1206,14 +1248,14 @@ __device__ __forceinline__ void attn_combine(const KA a, Smem& sm, int l, int b,
   __syncthreads();
   f32x4 num = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int u = 0; u < 16; ++u)
+  for (int u = 0; u < CB; ++u)
     if (u < ns) num += wts[h * hstride + u] * pv[u];
-  for (int s0 = 16; s0 < ns; s0 += 16) {
+  for (int s0 = CB; s0 < ns; s0 += CB) {
 #pragma unroll
-    for (int u = 0; u < 16; ++u)
+    for (int u = 0; u < CB; ++u)
       pv[u] = (mine && s0 + u < ns) ? as_f4(ldc16(po0, obase + (s0 + u) * hd * 4)) : (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int u = 0; u < 16; ++u)
+    for (int u = 0; u < CB; ++u)
       if (s0 + u < ns) num += wts[h * hstride + s0 + u] * pv[u];
   }
   if (mine) {

@@ -130,13 +130,26 @@ def test_plan_structure(lib, model, B, mb):
 
 
 def test_static_tiles_dealt_round_robin(lib):
-    # task k runs on workgroup k mod N: with 256 workgroups the 256 QKV tiles
-    # of a layer of the 30B model land on 256 different workgroups
-    tasks, _ = _plan(W.MOE_30B, 1, 529)
+    # default placement, task k on workgroup k mod N: with 256 workgroups the
+    # 256 QKV tiles of a layer of the 30B model land on 256 different workgroups
+    tasks, _ = _plan(W.MOE_30B, 1, 529, order="interleaved")
     assert all(t.aux[16] == i % 256 and t.aux[17] == i for i, t in enumerate(tasks))
     idx = [i for i, t in enumerate(tasks) if t.op == 1 and t.layer == 3]
     assert len(idx) == 256
     assert len({i % 256 for i in idx}) == 256
+
+
+def test_tuned_order_gives_router_tiles_their_own_workgroups(lib):
+    tasks, _ = _plan(W.MOE_30B, 1, 529)
+    assert all(t.aux[17] == i for i, t in enumerate(tasks))
+    for l in (0, 7, 47):
+        r = [t for t in tasks if mk.OPCODES[t.op] == "ROUTER_GEMM" and t.layer == l]
+        q = [t for t in tasks if mk.OPCODES[t.op] == "QKV_PROJ" and t.layer == l]
+        assert sorted(t.aux[16] for t in r) == list(range(8))
+        wq = [t.aux[16] for t in q]
+        assert len(set(wq)) == len(wq) and min(wq) >= 8 and max(wq) < 256
+        # router tiles come before the QKV tiles in the list
+        assert max(t.aux[17] for t in r) < min(t.aux[17] for t in q)
 
 
 def test_partitioned_order_places_branches_on_disjoint_sets(lib):
