@@ -55,6 +55,7 @@ int validate_config(const mk_config* c) {
   if (c->n_q_heads % c->n_kv_heads != 0) return MK_E_INVAL;
   if (c->d_model % 8 != 0 || c->page_size <= 0) return MK_E_INVAL;
   if (c->page_size != 16) return MK_E_UNSUPPORTED;   // one 16-key MFMA tile per page
+  if (c->n_layers > 128) return MK_E_UNSUPPORTED;    // the layer table is copied into LDS
   if (c->max_batch < 1 || c->max_batch > 8) return MK_E_UNSUPPORTED;
   if (c->head_dim != 64 && c->head_dim != 128) return MK_E_UNSUPPORTED;
   if (c->n_q_heads / c->n_kv_heads > 8) return MK_E_UNSUPPORTED;

@@ -180,6 +180,30 @@ __device__ __forceinline__ void split_bf16(float x0, float x1, uint32_t& hi, uin
   lo = (uint32_t)l0 | ((uint32_t)l1 << 16);
 }
 
+// A value known to be the same in every lane, moved to scalar registers.
+template <typename P>
+__device__ __forceinline__ P* uniform_ptr(P* p) {
+  const uint64_t v = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v), hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (P*)(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ long uniform_long(long x) {
+  const uint64_t v = (uint64_t)x;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v), hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (long)(((uint64_t)hi << 32) | lo);
+}
+
+// Step metadata, copied into LDS at kernel start: every task reads some of it
+// before it can issue its first load (weight pointers, lengths, positions),
+// and an LDS read avoids a memory round trip on that path.
+#define MK_LDS_LAYERS 128
+__shared__ mk_layer_dev sh_layers[MK_LDS_LAYERS];
+__shared__ int sh_seq_lens[NBMAX], sh_positions[NBMAX], sh_tokens[NBMAX];
+#define LAYER_PTR(l, f) uniform_ptr(sh_layers[l].f)
+__device__ __forceinline__ int seq_len_u(int b) { return __builtin_amdgcn_readfirstlane(sh_seq_lens[b]); }
+__device__ __forceinline__ int position_u(int b) { return __builtin_amdgcn_readfirstlane(sh_positions[b]); }
+__device__ __forceinline__ int token_u(int b) { return __builtin_amdgcn_readfirstlane(sh_tokens[b]); }
+
 // Each counter owns a 256-byte line (MK_CTR_PAD ints), so that workgroups
 // polling different counters do not share a line.
 __device__ __forceinline__ int32_t* ctrp(const KA a, int idx) { return a->ctr + (long)idx * MK_CTR_PAD; }
@@ -322,7 +346,7 @@ __device__ __forceinline__ int visible_keys(const KA a, int layer, int seq_len) 
 // Live length of slot b, clamped to what its block table can hold (a longer
 // length is reported by the layer-0 norm task).
 __device__ __forceinline__ int live_len(const KA a, int b) {
-  const int sl = a->seq_lens[b];
+  const int sl = seq_len_u(b);
   const int cap = a->max_blocks * a->page;
   return sl < cap ? sl : cap;
 }
@@ -365,17 +389,6 @@ struct GemvArgs {
 // hs = 31 makes p / 2^hs zero) is p (+ I).
 // Every field is the same in all lanes; say so, so that the row arithmetic
 // runs on the scalar unit and buffer descriptors stay in scalar registers.
-template <typename P>
-__device__ __forceinline__ P* uniform_ptr(P* p) {
-  const uint64_t v = (uint64_t)p;
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v), hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-  return (P*)(((uint64_t)hi << 32) | lo);
-}
-__device__ __forceinline__ long uniform_long(long x) {
-  const uint64_t v = (uint64_t)x;
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v), hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-  return (long)(((uint64_t)hi << 32) | lo);
-}
 __device__ __forceinline__ void make_uniform(GemvArgs& g) {
   g.base = uniform_ptr(g.base);
   g.ldw = uniform_long(g.ldw);
@@ -642,7 +655,7 @@ __device__ __forceinline__ bool op_add_rmsnorm(const KA a, Smem& sm, const mk_ta
   const bool moe_in = !emb && !mid && a->parallel && a->E > 0;
   const int lp = l - 1;
   const int lx = mid ? l : lp;     // layer whose attention output is added
-  const uint16_t* gain = fin ? a->final_norm : (mid ? a->layers[l].ffn_norm : a->layers[l].attn_norm);
+  const uint16_t* gain = fin ? a->final_norm : (mid ? LAYER_PTR(l, ffn_norm) : LAYER_PTR(l, attn_norm));
   // gains do not depend on anything: in flight during the wait
   u32x2 gg[NCH];
 #pragma unroll
@@ -675,23 +688,23 @@ __device__ __forceinline__ bool op_add_rmsnorm(const KA a, Smem& sm, const mk_ta
     for (int idx = tid; idx < B * half; idx += MK_THREADS) {
       const int b = idx / half, i = idx - b * half;
       double sn, cs;
-      sincos((double)a->positions[b] * a->inv_freq[i], &sn, &cs);
+      sincos((double)sh_positions[b] * a->inv_freq[i], &sn, &cs);
       stc(a->rope + (long)idx * 2, (float)cs);
       stc(a->rope + (long)idx * 2 + 1, (float)sn);
     }
   }
 #pragma unroll 1
   for (int b = 0; b < B; ++b) {
-    const bool live = a->seq_lens[b] > 0;
+    const bool live = seq_len_u(b) > 0;
     int tok = 0;
     if (emb && live) {
-      tok = a->tokens[b];
+      tok = token_u(b);
       if (tok < 0 || tok >= a->V) {
         if (tid == 0) report(a, MK_E_DEVICE, ti, -1, tok, a->V);
         tok = 0;
       }
-      if (tid == 0 && a->seq_lens[b] > a->max_blocks * a->page)
-        report(a, MK_E_DEVICE, ti, -5, a->seq_lens[b], a->max_blocks * a->page);
+      if (tid == 0 && seq_len_u(b) > a->max_blocks * a->page)
+        report(a, MK_E_DEVICE, ti, -5, seq_len_u(b), a->max_blocks * a->page);
     }
     // every source chunk of this thread is loaded before any is used
     f32x4 acc[NCH];
@@ -797,14 +810,14 @@ __device__ __forceinline__ void epi_qkv(const KA a, Smem& sm, const mk_task& t, 
   const int l = t.layer, hd = a->hd, half = hd / 2, B = a->B;
   const int np = t.n1 - t.n0;
   const int rows = (a->Hq + 2 * a->Hkv) * hd;
-  uint16_t* kpool = a->layers[l].k;
-  uint16_t* vpool = a->layers[l].v;
+  uint16_t* kpool = LAYER_PTR(l, k);
+  uint16_t* vpool = LAYER_PTR(l, v);
   for (int idx = threadIdx.x; idx < np * B; idx += MK_THREADS) {
     const int p = idx / B, b = idx - p * B;
-    if (a->seq_lens[b] <= 0) continue;
+    if (sh_seq_lens[b] <= 0) continue;
     const int gp = t.n0 + p, head = gp / half, i = gp - head * half;
     float ya = sm.ys[(2 * p) * NBMAX + b], yb = sm.ys[(2 * p + 1) * NBMAX + b];
-    const int pos = a->positions[b];
+    const int pos = sh_positions[b];
     if (head < a->Hq + a->Hkv) {
       const float c = ldc(a->rope + ((long)b * half + i) * 2), s_ = ldc(a->rope + ((long)b * half + i) * 2 + 1);
       const float ra = ya * c - yb * s_;
@@ -887,7 +900,7 @@ __device__ __forceinline__ void router_topk(const KA a, Smem& sm, int l) {
     if (lane < K) {
       stc(a->topi + ((long)l * B + b) * K + lane, myid);
       stc(a->topw + ((long)l * B + b) * K + lane, myw / wsum);
-      sm.misc[64 + b * K + lane] = a->seq_lens[b] > 0 ? myid : -1;
+      sm.misc[64 + b * K + lane] = seq_len_u(b) > 0 ? myid : -1;
     }
   }
   __syncthreads();
@@ -974,8 +987,8 @@ __device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
                                                  0, 0, 0);
 }
-constexpr int ATT_PT = 3;   // K tiles in flight per compute wave
-constexpr int ATT_PV = 4;   // V k-steps (32 keys) in flight per compute wave
+constexpr int ATT_PT = 4;   // K tiles in flight per compute wave
+constexpr int ATT_PV = 6;   // V k-steps (32 keys) in flight per compute wave
 
 template <int HD>
 __device__ __forceinline__ bool attn_split(const KA a, Smem& sm, int l, int b, int g, int s, int p0, int p1, int ti,
@@ -992,10 +1005,10 @@ __device__ __forceinline__ bool attn_split(const KA a, Smem& sm, int l, int b, i
   const int nt = (p1 - tb0 + 15) >> 4;              // key tiles
   const int nks = (nt + 1) >> 1;                    // PV k-steps
   const int nti = cw >= 0 && cw < nt ? (nt - cw + MK_CW - 1) / MK_CW : 0;   // key tiles of this wave
-  const uint16_t* Kp = a->layers[l].k;
-  const uint16_t* Vp = a->layers[l].v;
+  const uint16_t* Kp = LAYER_PTR(l, k);
+  const uint16_t* Vp = LAYER_PTR(l, v);
   const int32_t* bt = a->block_tables + (long)b * a->max_blocks + (tb0 >> 4);
-  const int newest = a->positions[b];
+  const int newest = position_u(b);
   auto page_of = [&](int t) -> int {
     int pg = bt[t];
     if (pg < 0 || pg >= a->num_pages) {
@@ -1015,22 +1028,42 @@ __device__ __forceinline__ bool attn_split(const KA a, Smem& sm, int l, int b, i
   };
   u32x4 kf[ATT_PT][KS], vf[ATT_PV][DTW];
   if (cw >= 0) {
+    // every page id first (one round trip), then every K and V load
+    int kpg[ATT_PT], vpg[ATT_PV];
+#pragma unroll
+    for (int u = 0; u < ATT_PT; ++u) kpg[u] = u < nti ? bt[cw + MK_CW * u] : 0;
+#pragma unroll
+    for (int u = 0; u < ATT_PV; ++u) {
+      const int tt = 2 * u + (lane >> 5);
+      vpg[u] = (u < nks && tt < nt) ? bt[tt] : -1;
+    }
 #pragma unroll
     for (int u = 0; u < ATT_PT; ++u)
       if (u < nti) {
-        const int o = k_off(cw + MK_CW * u);
+        int pg = kpg[u];
+        if (pg < 0 || pg >= a->num_pages) {
+          report(a, MK_E_DEVICE, ti, -3, pg, a->num_pages);
+          pg = 0;
+        }
+        const int o = ((pg * Hkv + g) * 16 + c16) * HD + 8 * q4;
 #pragma unroll
         for (int k = 0; k < KS; ++k) kf[u][k] = ldg_nt(Kp + o + 32 * k);
       }
 #pragma unroll
     for (int u = 0; u < ATT_PV; ++u) {
-      const int o = u < nks ? v_off(u) : -1;
+      int pg = vpg[u];
+      if (pg >= a->num_pages || (pg < 0 && u < nks && 2 * u + (lane >> 5) < nt)) {
+        report(a, MK_E_DEVICE, ti, -3, pg, a->num_pages);
+        pg = 0;
+      }
+      const int o = pg >= 0 ? ((pg * Hkv + g) * HD + c16) * 16 + 8 * (q4 & 1) : -1;
 #pragma unroll
       for (int j = 0; j < DTW; ++j) {
         const int dt = cw + MK_CW * j;
         vf[u][j] = (o >= 0 && dt < NDT) ? ldg_nt(Vp + o + 256 * dt) : (u32x4){0u, 0u, 0u, 0u};
       }
     }
+    if (a->trace && tid == 64 && sm.t_mark[5] == 0) sm.t_mark[5] = wall_clock64();   // loads issued
   }
   MK_MARK(3);
   // wait for the QKV tiles, then wave 0 stages q of the group's heads
@@ -1214,7 +1247,7 @@ __device__ __forceinline__ void attn_combine(const KA a, Smem& sm, int l, int b,
   const bool mine = tid < G * q4;
   const int h = mine ? tid / q4 : 0, cq = tid - h * q4;
   const int obase = (int)((h * hstride * hd + cq * 4) * 4);   // byte offset of split 0
-  constexpr int CB = 64;
+  constexpr int CB = 16;
   f32x4 pv[CB];
 #pragma unroll
   for (int u = 0; u < CB; ++u)
@@ -1310,6 +1343,16 @@ extern "C" __global__ void __launch_bounds__(MK_THREADS, 1) mk_persistent(mk_kar
   u32x4 pre = (u32x4){0u, 0u, 0u, 0u};
   if (tid >= 64 && tid < 72 && k < kend)
     reinterpret_cast<u32x4*>(&sm.tq[0])[tid - 64] = load_task_piece(a_arg.tasks, k, tid - 64);
+  {   // step metadata into LDS (visible after the loop's first barrier)
+    const int nw = a_arg.L * (int)(sizeof(mk_layer_dev) / 4);
+    for (int i = tid; i < nw; i += MK_THREADS)
+      reinterpret_cast<int*>(sh_layers)[i] = ((GLOBAL const int*)a_arg.layers)[i];
+    if (tid < a_arg.B) {
+      sh_seq_lens[tid] = ((GLOBAL const int*)a_arg.seq_lens)[tid];
+      sh_positions[tid] = ((GLOBAL const int*)a_arg.positions)[tid];
+      sh_tokens[tid] = ((GLOBAL const int*)a_arg.tokens)[tid];
+    }
+  }
   for (;;) {
     if (pending) {
       if (tid >= 64 && tid < 72) reinterpret_cast<u32x4*>(&sm.tq[cur ^ 1])[tid - 64] = pre;
@@ -1392,34 +1435,34 @@ extern "C" __global__ void __launch_bounds__(MK_THREADS, 1) mk_persistent(mk_kar
       switch (t.op) {
         case MK_OP_QKV_PROJ:
           kind = U_GEMV;
-          g.base = a->layers[l].w_qkv; g.ldw = a->d; g.K = a->d; g.nrows = 2 * (t.n1 - t.n0);
+          g.base = LAYER_PTR(l, w_qkv); g.ldw = a->d; g.K = a->d; g.nrows = 2 * (t.n1 - t.n0);
           g.mode = ROW_ROPE_PAIRS; g.half = a->hd / 2;
           st.base = a->xn + (long)l * B * a->d; st.ld = a->d; st.K = a->d;
           break;
         case MK_OP_ROUTER_GEMM:
           kind = U_GEMV;
-          g.base = a->layers[l].w_router; g.ldw = a->d; g.K = a->d;
+          g.base = LAYER_PTR(l, w_router); g.ldw = a->d; g.K = a->d;
           g.out = a->rlog + (long)l * B * a->E + t.n0; g.ob = a->E;
           st.base = a->xn + (long)l * B * a->d; st.ld = a->d; st.K = a->d;
           break;
         case MK_OP_O_PROJ: {
           kind = U_GEMV;
           const int gd = a->G * a->hd, grp = t.group;
-          g.base = a->layers[l].w_o + (long)grp * gd; g.ldw = (long)a->Hq * a->hd; g.K = gd;
+          g.base = LAYER_PTR(l, w_o) + (long)grp * gd; g.ldw = (long)a->Hq * a->hd; g.K = gd;
           g.out = a->opart + (((long)l * a->Hkv + grp) * B) * a->d + t.n0; g.ob = a->d;
           st.base = a->attn + (long)l * B * a->Hq * a->hd + (long)grp * gd; st.ld = (long)a->Hq * a->hd; st.K = gd;
           break;
         }
         case MK_OP_FFN_UPGATE_ACT:
           kind = U_GEMV;
-          g.base = a->layers[l].w_upgate; g.ldw = a->d; g.K = a->d; g.nrows = 2 * (t.n1 - t.n0);
+          g.base = LAYER_PTR(l, w_upgate); g.ldw = a->d; g.K = a->d; g.nrows = 2 * (t.n1 - t.n0);
           g.mode = ROW_GATE_UP; g.half = a->F;
           st.base = (a->parallel ? a->xn : a->xn2) + (long)l * B * a->d; st.ld = a->d; st.K = a->d;
           epi_p0 = t.n0; epi_np = t.n1 - t.n0;
           break;
         case MK_OP_FFN_DOWN:
           kind = U_GEMV;
-          g.base = a->layers[l].w_down; g.ldw = a->F; g.K = a->F;
+          g.base = LAYER_PTR(l, w_down); g.ldw = a->F; g.K = a->F;
           g.out = a->fo + (long)l * B * a->d + t.n0; g.ob = a->d;
           st.base = a->fh + (long)l * B * a->F; st.ld = a->F; st.K = a->F;
           break;
@@ -1452,7 +1495,7 @@ extern "C" __global__ void __launch_bounds__(MK_THREADS, 1) mk_persistent(mk_kar
           st.tok[7] = __builtin_amdgcn_readfirstlane((int)r2v.w);
           epi_p0 = tt * a->ug_pairs;
           epi_np = min(a->ug_pairs, a->I - epi_p0);
-          g.base = a->layers[l].w_upgate + (long)e * 2 * a->I * a->d; g.ldw = a->d; g.r0 = epi_p0;
+          g.base = LAYER_PTR(l, w_upgate) + (long)e * 2 * a->I * a->d; g.ldw = a->d; g.r0 = epi_p0;
           g.nrows = 2 * epi_np; g.K = a->d; g.mode = ROW_GATE_UP; g.half = a->I; g.nb = epi_nr;
           st.base = a->xn + (long)l * B * a->d; st.ld = a->d; st.nb = epi_nr;
           st.K = a->d; st.wait_idx = -1;
@@ -1469,7 +1512,7 @@ extern "C" __global__ void __launch_bounds__(MK_THREADS, 1) mk_persistent(mk_kar
           const int r0 = __builtin_amdgcn_readfirstlane((int)r0v.y);
           const int nr = __builtin_amdgcn_readfirstlane((int)r0v.z);
           const int n0 = tt * a->dn_rows;
-          g.base = a->layers[l].w_down + (long)e * a->d * a->I; g.ldw = a->I; g.r0 = n0;
+          g.base = LAYER_PTR(l, w_down) + (long)e * a->d * a->I; g.ldw = a->I; g.r0 = n0;
           g.nrows = min(a->dn_rows, a->d - n0); g.K = a->I; g.nb = nr;
           g.out = a->Y + ((long)l * a->bk + r0) * a->d + n0; g.ob = a->d;
           st.base = a->H + ((long)l * a->bk + r0) * a->I; st.ld = a->I; st.nb = nr; st.K = a->I;
@@ -1543,7 +1586,7 @@ extern "C" __global__ void __launch_bounds__(MK_THREADS, 1) mk_persistent(mk_kar
           if (wg_wait(a, sm, t.wait_ctr, t.wait_target, ti)) {
             for (int i = tid; i < B * a->topk; i += MK_THREADS) {
               const int b = i / a->topk;
-              sm.misc[64 + i] = a->seq_lens[b] > 0 ? ldc(a->topi + ((long)l * B) * a->topk + i) : -1;
+              sm.misc[64 + i] = sh_seq_lens[b] > 0 ? ldc(a->topi + ((long)l * B) * a->topk + i) : -1;
             }
             __syncthreads();
             route_finalize(a, sm, l);
