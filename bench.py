@@ -67,6 +67,7 @@ def parse():
     ap.add_argument("--order", default="tuned")
     ap.add_argument("--launch", default="persistent")
     ap.add_argument("--attn-split", type=int, default=0)
+    ap.add_argument("--sched-flags", type=int, default=0, help="MK_SCHED_* bits for the schedule")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--verbose", action="store_true")
     ap.add_argument("--trace", default="", help="after timing, trace one step and write a summary here")
@@ -161,7 +162,7 @@ def main():
     total_steps = args.warmup + args.steps
     log(f"workload {wl.name}: building inputs for {total_steps} steps")
     t0 = time.time()
-    opts = mk.make_opts(args.order, args.launch, attn_split=args.attn_split)
+    opts = mk.make_opts(args.order, args.launch, attn_split=args.attn_split, flags=args.sched_flags)
     eng = DecodeEngine(wl, steps=total_steps + 1, opts=opts, verbose=args.verbose)
     log(f"inputs ready in {time.time() - t0:.1f}s ({eng.weight_bytes() / 1e9:.1f} GB weights)")
     if wl.swap_every:
@@ -248,7 +249,7 @@ def main():
         "data": "synthetic (seeded random-init weights and pre-filled KV)",
         "config": {"workload": wl.name, "batch": B, "context": W.context_length(wl, 0),
                    "layers": cfg.n_layers, "experts": cfg.n_experts, "top_k": cfg.top_k,
-                   "order": args.order, "launch": args.launch,
+                   "order": args.order, "launch": args.launch, "sched_flags": args.sched_flags,
                    "attn_split": args.attn_split or "auto"},
         "sol_fraction": round(value / sol_tok_s, 4),
         "sol_tok_s": round(sol_tok_s, 1),
@@ -259,7 +260,8 @@ def main():
     }
     if args.trace:
         from persistent_moe_amd import trace as T
-        topt = mk.make_opts(args.order, args.launch, attn_split=args.attn_split, flags=mk.MK_SCHED_TRACE)
+        topt = mk.make_opts(args.order, args.launch, attn_split=args.attn_split,
+                            flags=args.sched_flags | mk.MK_SCHED_TRACE)
         eng.opts = topt
         mk.mk_build_schedule(eng.h, B, topt)
         one(total_steps - 1)

@@ -199,6 +199,10 @@ typedef struct mk_sched_opts {
 /* Emit ATTN_COMBINE as its own task per (sequence, KV group) instead of
  * running it in the last attention split of that group to finish.         */
 #define MK_SCHED_SEPARATE_COMBINE 8
+/* Claimer c of a MoE up-gate or down queue owns item c in advance (one
+ * fewer atomic per workgroup).  By default every MoE item is pulled from its
+ * claim queue, so the workgroups that finish attention first take them.   */
+#define MK_SCHED_STATIC_MOE 16
 
 #define MK_MIN_SPLIT 64
 

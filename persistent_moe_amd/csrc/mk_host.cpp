@@ -388,12 +388,13 @@ int build_plan(const mk_config* c, int B, int32_t max_blocks, const mk_sched_opt
         place(t, onM, 0);
       };
       const int n_moe_claim = onM ? (int)onM->size() : n_claim;
+      const bool dyn_moe = (o.flags & MK_SCHED_STATIC_MOE) == 0;
       auto emit_ug = [&]() {
         wave();
         for (int i = 0; i < n_moe_claim; ++i) {
           mk_task t = blank(MK_OP_MOE_UPGATE_ACT_DRAIN, l);
-          t.n0 = i;
-          t.n1 = n_moe_claim;
+          t.n0 = dyn_moe ? INT32_MAX : i;
+          t.n1 = dyn_moe ? 0 : n_moe_claim;
           t.wait_ctr = cROUTE;
           t.wait_target = 1;
           t.queue = ctr_of(p.cl, l, MK_CTR_QUG);
@@ -404,8 +405,8 @@ int build_plan(const mk_config* c, int B, int32_t max_blocks, const mk_sched_opt
         wave();
         for (int i = 0; i < n_moe_claim; ++i) {
           mk_task t = blank(MK_OP_MOE_DOWN_DRAIN, l);
-          t.n0 = i;
-          t.n1 = n_moe_claim;
+          t.n0 = dyn_moe ? INT32_MAX : i;
+          t.n1 = dyn_moe ? 0 : n_moe_claim;
           t.wait_ctr = cROUTE;
           t.wait_target = 1;
           t.queue = ctr_of(p.cl, l, MK_CTR_QDN);

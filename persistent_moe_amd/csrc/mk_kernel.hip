@@ -199,6 +199,9 @@ __device__ __forceinline__ long uniform_long(long x) {
 #define MK_LDS_LAYERS 128
 __shared__ mk_layer_dev sh_layers[MK_LDS_LAYERS];
 __shared__ int sh_seq_lens[NBMAX], sh_positions[NBMAX], sh_tokens[NBMAX];
+// block tables too when they are small (batch x max_blocks <= MK_LDS_BT)
+#define MK_LDS_BT 2048
+__shared__ int sh_bt[MK_LDS_BT];
 #define LAYER_PTR(l, f) uniform_ptr(sh_layers[l].f)
 __device__ __forceinline__ int seq_len_u(int b) { return __builtin_amdgcn_readfirstlane(sh_seq_lens[b]); }
 __device__ __forceinline__ int position_u(int b) { return __builtin_amdgcn_readfirstlane(sh_positions[b]); }
@@ -1030,12 +1033,14 @@ __device__ __forceinline__ bool attn_split(const KA a, Smem& sm, int l, int b, i
   if (cw >= 0) {
     // every page id first (one round trip), then every K and V load
     int kpg[ATT_PT], vpg[ATT_PV];
+    const bool bt_lds = a->B * a->max_blocks <= MK_LDS_BT;
+    const int* btl = sh_bt + b * a->max_blocks + (tb0 >> 4);
 #pragma unroll
-    for (int u = 0; u < ATT_PT; ++u) kpg[u] = u < nti ? bt[cw + MK_CW * u] : 0;
+    for (int u = 0; u < ATT_PT; ++u) kpg[u] = u < nti ? (bt_lds ? btl[cw + MK_CW * u] : bt[cw + MK_CW * u]) : 0;
 #pragma unroll
     for (int u = 0; u < ATT_PV; ++u) {
       const int tt = 2 * u + (lane >> 5);
-      vpg[u] = (u < nks && tt < nt) ? bt[tt] : -1;
+      vpg[u] = (u < nks && tt < nt) ? (bt_lds ? btl[tt] : bt[tt]) : -1;
     }
 #pragma unroll
     for (int u = 0; u < ATT_PT; ++u)
@@ -1352,6 +1357,9 @@ extern "C" __global__ void __launch_bounds__(MK_THREADS, 1) mk_persistent(mk_kar
       sh_positions[tid] = ((GLOBAL const int*)a_arg.positions)[tid];
       sh_tokens[tid] = ((GLOBAL const int*)a_arg.tokens)[tid];
     }
+    const int nbt = a_arg.B * a_arg.max_blocks;
+    if (nbt <= MK_LDS_BT)
+      for (int i = tid; i < nbt; i += MK_THREADS) sh_bt[i] = ((GLOBAL const int*)a_arg.block_tables)[i];
   }
   for (;;) {
     if (pending) {

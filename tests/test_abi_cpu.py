@@ -199,7 +199,7 @@ def test_signal_counts_match_wait_targets(lib):
 
 
 @pytest.mark.parametrize("order", ["tuned", "interleaved", "attention_first", "partitioned", "tuned-separate-topk",
-                                   "tuned-separate-combine", "partitioned-separate-combine"])
+                                   "tuned-separate-combine", "partitioned-separate-combine", "tuned-static-moe"])
 @pytest.mark.parametrize("case", [
     ("tiny", W.TINY_MOE, 1, 5, [65], [2, 2]),
     ("moe30b", W.MOE_30B, 1, 529, [8193], [8] * 48),
@@ -211,7 +211,9 @@ def test_schedule_is_deadlock_free(lib, order, case):
     name, model, B, mb, sl, na = case
     flags = mk.MK_SCHED_SEPARATE_TOPK if order.endswith("separate-topk") else 0
     flags |= mk.MK_SCHED_SEPARATE_COMBINE if order.endswith("separate-combine") else 0
-    opts = mk.make_opts(order.replace("-separate-topk", "").replace("-separate-combine", ""), flags=flags)
+    flags |= mk.MK_SCHED_STATIC_MOE if order.endswith("static-moe") else 0
+    base = order.replace("-separate-topk", "").replace("-separate-combine", "").replace("-static-moe", "")
+    opts = mk.make_opts(base, flags=flags)
     for nw in (256, 64, 7):
         rc, stuck = mk.mk_plan_simulate(_cfg(model, B), B, mb, opts, nw, sl, na)
         assert rc == mk.MK_OK, (name, nw, stuck)

@@ -110,7 +110,8 @@ def test_determinism_and_per_opcode_ablation_agree():
     # the same tiles in other placements and orders give the same bits (the
     # attention split length is the minimum for this context in every order)
     for order, flags in (("interleaved", 0), ("attention_first", 0), ("partitioned", 0),
-                         ("tuned", mk.MK_SCHED_SEPARATE_COMBINE | mk.MK_SCHED_SEPARATE_TOPK)):
+                         ("tuned", mk.MK_SCHED_SEPARATE_COMBINE | mk.MK_SCHED_SEPARATE_TOPK),
+                         ("tuned", mk.MK_SCHED_STATIC_MOE)):
         mk.mk_build_schedule(eng.h, wl.batch, mk.make_opts(wave_order=order, flags=flags))
         d = eng.decode(inputs=inp).clone()
         assert eng.status().code == 0
