@@ -145,11 +145,13 @@ typedef struct mk_weights {
   const mk_layer_weights* layers; /* host array of n_layers entries (copied) */
 } mk_weights;
 
-/* Paged KV cache: per layer, a K pool [num_pages][Hkv][page_size][hd] and a
- * V pool [num_pages][Hkv][hd][page_size], bf16 (device): within a page a K
- * block holds one key per row, a V block one head dimension per row (V is
- * stored transposed so that the attention PV product reads 8 consecutive
- * keys of one dimension as one 16-byte load).  page_size must be 16.  The
+/* Paged KV cache: per layer, a K pool [num_pages][Hkv][hd/32][page_size][32]
+ * and a V pool [num_pages][Hkv][hd][page_size], bf16 (device).  Within a page,
+ * a K block holds the keys in 32-dimension slices (slice s of every key, then
+ * slice s+1), and a V block one head dimension per row: the attention
+ * products read each operand fragment as whole contiguous cache lines (a QK
+ * k-step: 32 dims of 16 keys; PV: 8 consecutive keys of one dimension).
+ * page_size must be 16.  The
  * kernel writes only the slot of each sequence's new token.  Slots of a
  * sequence's pages beyond its length are read (and given zero attention
  * weight), so pools must be initialised (e.g. zeroed): NaN there would

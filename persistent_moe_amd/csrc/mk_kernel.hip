@@ -840,10 +840,11 @@ __device__ __forceinline__ void epi_qkv(const KA a, Smem& sm, const mk_task& t, 
         report(a, MK_E_DEVICE, ti, -2, page, a->num_pages);
         continue;
       }
-      if (isk) {   // K page [16 keys][hd]
-        uint16_t* dst = kpool + (((long)page * a->Hkv + kvh) * 16 + (pos & 15)) * hd;
-        stc(dst + i, f_to_bf16(ya));
-        stc(dst + i + half, f_to_bf16(yb));
+      if (isk) {   // K page [hd/32][16 keys][32 dims]
+        uint16_t* dst = kpool + ((long)page * a->Hkv + kvh) * 16 * hd + (pos & 15) * 32;
+        const int e1 = i + half;
+        stc(dst + (i >> 5) * 512 + (i & 31), f_to_bf16(ya));
+        stc(dst + (e1 >> 5) * 512 + (e1 & 31), f_to_bf16(yb));
       } else {     // V page [hd][16 keys]
         uint16_t* dst = vpool + ((long)page * a->Hkv + kvh) * hd * 16 + (pos & 15);
         stc(dst + i * 16, f_to_bf16(ya));
@@ -977,7 +978,8 @@ __device__ __forceinline__ void route_finalize(const KA a, Smem& sm, int l) {
 // part and a bf16 remainder, and each product is the sum of two MFMAs, so
 // the result keeps about 16 mantissa bits of q and p (fp32 accumulation).  A
 // key tile is one 16-key page.  QK: A = q (bf16), B = K^T: lane l holds key
-// (l mod 16), dims 32s + 8(l/16) .. +7, a 16-byte piece of the key row.
+// (l mod 16), dims 32s + 8(l/16) .. +7; a K page is stored as [hd/32][16
+// keys][32 dims], so the 64 lanes of one k-step read 1 KB contiguous.
 // PV: A = P (bf16, from LDS), B = V: lane l holds dim (l mod 16) of 8
 // consecutive keys, a 16-byte piece of the transposed V page.  Result tiles:
 // lane l holds rows (heads) 4(l/16) .. +3 of column (key or dim) l mod 16.
@@ -1021,7 +1023,7 @@ __device__ __forceinline__ bool attn_split(const KA a, Smem& sm, int l, int b, i
     return pg;
   };
   // element offset of this lane's piece of key tile t (dims 8(l/16) of the row)
-  auto k_off = [&](int t) -> int { return ((page_of(t) * Hkv + g) * 16 + c16) * HD + 8 * q4; };
+  auto k_off = [&](int t) -> int { return (page_of(t) * Hkv + g) * 16 * HD + c16 * 32 + 8 * q4; };
   // element offset of this lane's V piece of k-step ks in dim tile 0, or -1
   // (dim tile dt adds 256 dt)
   auto v_off = [&](int ks) -> int {
@@ -1030,6 +1032,7 @@ __device__ __forceinline__ bool attn_split(const KA a, Smem& sm, int l, int b, i
     return ((page_of(tt) * Hkv + g) * HD + c16) * 16 + 8 * (q4 & 1);
   };
   u32x4 kf[ATT_PT][KS], vf[ATT_PV][DTW];
+  if (a->trace && tid == 64 && sm.t_mark[8] == 0) sm.t_mark[8] = wall_clock64();   // compute wave enters
   if (cw >= 0) {
     // every page id first (one round trip), then every K and V load
     int kpg[ATT_PT], vpg[ATT_PV];
@@ -1042,6 +1045,7 @@ __device__ __forceinline__ bool attn_split(const KA a, Smem& sm, int l, int b, i
       const int tt = 2 * u + (lane >> 5);
       vpg[u] = (u < nks && tt < nt) ? (bt_lds ? btl[tt] : bt[tt]) : -1;
     }
+    if (a->trace && tid == 64 && sm.t_mark[9] == 0) sm.t_mark[9] = kpg[0] + vpg[0] >= -2 ? wall_clock64() : 1;
 #pragma unroll
     for (int u = 0; u < ATT_PT; ++u)
       if (u < nti) {
@@ -1050,9 +1054,9 @@ __device__ __forceinline__ bool attn_split(const KA a, Smem& sm, int l, int b, i
           report(a, MK_E_DEVICE, ti, -3, pg, a->num_pages);
           pg = 0;
         }
-        const int o = ((pg * Hkv + g) * 16 + c16) * HD + 8 * q4;
+        const int o = (pg * Hkv + g) * 16 * HD + c16 * 32 + 8 * q4;
 #pragma unroll
-        for (int k = 0; k < KS; ++k) kf[u][k] = ldg_nt(Kp + o + 32 * k);
+        for (int k = 0; k < KS; ++k) kf[u][k] = ldg_nt(Kp + o + 512 * k);
       }
 #pragma unroll
     for (int u = 0; u < ATT_PV; ++u) {
@@ -1124,7 +1128,7 @@ __device__ __forceinline__ bool attn_split(const KA a, Smem& sm, int l, int b, i
           if (kabs == newest) {   // appended this step: re-read coherently
             const int o = k_off(t);
 #pragma unroll
-            for (int k = 0; k < KS; ++k) kf[u][k] = ldc16(Kp, (o + 32 * k) * 2);
+            for (int k = 0; k < KS; ++k) kf[u][k] = ldc16(Kp, (o + 512 * k) * 2);
           }
           f32x4 c = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -1141,7 +1145,7 @@ __device__ __forceinline__ bool attn_split(const KA a, Smem& sm, int l, int b, i
           if (i + ATT_PT < nti) {
             const int o = k_off(t + MK_CW * ATT_PT);
 #pragma unroll
-            for (int k = 0; k < KS; ++k) kf[u][k] = ldg_nt(Kp + o + 32 * k);
+            for (int k = 0; k < KS; ++k) kf[u][k] = ldg_nt(Kp + o + 512 * k);
           }
         }
       }
@@ -1252,7 +1256,7 @@ __device__ __forceinline__ void attn_combine(const KA a, Smem& sm, int l, int b,
   const bool mine = tid < G * q4;
   const int h = mine ? tid / q4 : 0, cq = tid - h * q4;
   const int obase = (int)((h * hstride * hd + cq * 4) * 4);   // byte offset of split 0
-  constexpr int CB = 16;
+  constexpr int CB = 32;
   f32x4 pv[CB];
 #pragma unroll
   for (int u = 0; u < CB; ++u)

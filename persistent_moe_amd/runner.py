@@ -47,8 +47,9 @@ class DecodeEngine:
         torch.cuda.synchronize()
         _log(verbose, "weights %.1f GB in %.1fs" % (self.weight_bytes() / 1e9, time.time() - t0))
         t0 = time.time()
-        # K pages hold one key per row, V pages one head dimension per row
-        kshape = (self.plan.num_pages, cfg.n_kv_heads, cfg.page_size, cfg.head_dim)
+        # K pages hold 32-dim slices of every key in turn, V pages one head
+        # dimension per row
+        kshape = (self.plan.num_pages, cfg.n_kv_heads, cfg.head_dim // 32, cfg.page_size, 32)
         vshape = (self.plan.num_pages, cfg.n_kv_heads, cfg.head_dim, cfg.page_size)
         self.kpool = [torch.zeros(kshape, dtype=torch.bfloat16, device=self.dev) for _ in range(cfg.n_layers)]
         self.vpool = [torch.zeros(vshape, dtype=torch.bfloat16, device=self.dev) for _ in range(cfg.n_layers)]
@@ -134,7 +135,10 @@ class DecodeEngine:
                 if pad:
                     kv = torch.cat([kv, torch.zeros((pad,) + kv.shape[1:], dtype=kv.dtype, device=self.dev)])
                 kv = kv.view(n_full, ps, cfg.n_kv_heads, cfg.head_dim)
-                kv = kv.permute(0, 2, 1, 3) if which == "k" else kv.permute(0, 2, 3, 1)
+                if which == "k":   # [page][head][slice][key][32]
+                    kv = kv.view(n_full, ps, cfg.n_kv_heads, cfg.head_dim // 32, 32).permute(0, 2, 3, 1, 4)
+                else:              # [page][head][dim][key]
+                    kv = kv.permute(0, 2, 3, 1)
                 pool[pages[:n_full]] = kv
         if first:
             self.slot_seq.append(seq)
