@@ -30,7 +30,7 @@ constexpr int kXsFloats = 16384;   // LDS capacity for staged activations
 constexpr int kMaxGemvK = 8192;    // GEMV reduction length: 16 register slots x 512 (half from 4 rows)
 
 struct Layout {
-  size_t off_tasks, off_ranges, off_ctr, off_err, off_layers, off_invf, off_rope;
+  size_t off_tasks, off_ranges, off_ctr, off_err, off_layers, off_invf;
   size_t off_x, off_xn, off_xmid, off_xn2, off_qkv, off_attn, off_opart, off_rlog, off_topi, off_topw;
   size_t off_moe, off_H, off_Y, off_fh, off_fo, off_oout, off_pml, off_po, off_trace;
   size_t total;
@@ -118,7 +118,6 @@ Layout make_layout(const mk_config* c, int32_t max_blocks) {
   L.off_err = take(MK_ERR_WORDS * 4);
   L.off_layers = take((size_t)Lr * sizeof(mk_layer_dev));
   L.off_invf = take((size_t)(hd / 2) * 8);
-  L.off_rope = take((size_t)B * (hd / 2) * 2 * 4);
   L.off_x = take((size_t)(Lr + 1) * B * d * 4);
   L.off_xn = take((size_t)(Lr + 1) * B * d * 4);
   L.off_xmid = take(c->parallel_block ? 4 : (size_t)Lr * B * d * 4);
@@ -159,6 +158,7 @@ struct Plan {
   int attn_split = 0, max_splits = 0;
   int ug_tiles = 0, ug_pairs = 0, dn_tiles = 0, dn_rows = 0;
   int n_qkv = 0;
+  int ncomb = 1;                      // fused combine: workgroups per (sequence, group)
   mk_ctr_layout cl{};
 };
 
@@ -283,6 +283,11 @@ int build_plan(const mk_config* c, int B, int32_t max_blocks, const mk_sched_opt
   const std::vector<int>* onA = part ? &setA : nullptr;
   const std::vector<int>* onM = part ? &setM : nullptr;
   const bool fuse_combine = !(o.flags & MK_SCHED_SEPARATE_COMBINE);
+  // the fused combine of a (sequence, group) is shared by its last ncomb
+  // splits, one share of the G heads each; all but the last wait for the
+  // rest, so at most (ncomb - 1) * B * Hkv workgroups wait at once, and one
+  // more must stay free to claim the remaining splits
+  p.ncomb = std::max(1, std::min(G, (NW - 1) / std::max(1, B * Hkv) + 1));
   int layer_target_prev = 0;
   for (int l = 0; l <= Lr; ++l) {
     // ADD_RMSNORM entering layer l (l == Lr: the final norm)
@@ -353,7 +358,7 @@ int build_plan(const mk_config* c, int B, int32_t max_blocks, const mk_sched_opt
           t.k0 = g * G * hd;
           t.k1 = t.k0 + G * hd;
           t.wait_ctr = ctr_of(p.cl, l, p.cl.comb + g);
-          t.wait_target = B;
+          t.wait_target = B * G;   // every head of every sequence
           t.signal_ctr = signal;
           place(t, onA, g * n_o_g + i);
         }
@@ -547,6 +552,11 @@ int simulate(const mk_config* c, int B, const Plan& p, int NW, const int32_t* se
   // per-claimer state: -1 before the static item, then dynamic claiming
   std::vector<int> phase(NW, 0);
   std::vector<int> cur_item(NW, -1);
+  // a fused-combine share waiting for the other splits of its (b, g):
+  // counter, target, COMB counter, heads
+  struct PendComb { int ctr = -1, target = 0, comb = 0, heads = 0; };
+  std::vector<PendComb> pend(NW);
+  const int G = c->n_q_heads / Hkv;
   std::vector<SimQueue> qa(Lr), qu(Lr), qd(Lr);
   for (int l = 0; l < Lr; ++l) {
     int na = 0;
@@ -572,6 +582,12 @@ int simulate(const mk_config* c, int B, const Plan& p, int NW, const int32_t* se
     for (int w = 0; w < NW; ++w) {
       while (cursor[w] < cend[w]) {
         all_done = false;
+        if (pend[w].ctr >= 0) {
+          if (ctr[pend[w].ctr] < pend[w].target) break;
+          ctr[pend[w].comb] += pend[w].heads;
+          pend[w].ctr = -1;
+          progress = true;
+        }
         const mk_task& t = p.dev_tasks[cursor[w]];
         int target = t.wait_target;
         if (target == MK_WAIT_SPLITS) target = nspl(t.layer, t.batch);
@@ -589,7 +605,7 @@ int simulate(const mk_config* c, int B, const Plan& p, int NW, const int32_t* se
               if (t.op == MK_OP_ATTN_DRAIN && (t.flags & MK_F_FUSE_COMBINE) && t.n0 == 0)
                 for (int b = 0; b < B; ++b)   // sequences without keys: nothing to combine
                   if (nspl(t.layer, b) == 0)
-                    for (int g = 0; g < Hkv; ++g) ctr[ctr_of(p.cl, t.layer, p.cl.comb + g)]++;
+                    for (int g = 0; g < Hkv; ++g) ctr[ctr_of(p.cl, t.layer, p.cl.comb + g)] += G;
             }
             if (cur_item[w] < 0) {
               const int item = t.n1 + q.head;
@@ -605,9 +621,16 @@ int simulate(const mk_config* c, int B, const Plan& p, int NW, const int32_t* se
             if (t.op == MK_OP_ATTN_DRAIN) {
               int b, g;
               attn_bg(t.layer, item, &b, &g);
-              const long v = ++ctr[ctr_of(p.cl, t.layer, p.cl.attn + b * Hkv + g)];
-              if ((t.flags & MK_F_FUSE_COMBINE) && v == nspl(t.layer, b))   // the last split combines
-                ctr[ctr_of(p.cl, t.layer, p.cl.comb + g)]++;
+              const int actr = ctr_of(p.cl, t.layer, p.cl.attn + b * Hkv + g);
+              const long rank = ctr[actr]++;
+              const int ns = nspl(t.layer, b), nc = std::min(ns, p.ncomb);
+              if ((t.flags & MK_F_FUSE_COMBINE) && rank >= ns - nc) {   // one of the last nc splits
+                const int cb = (int)(rank - (ns - nc));
+                pend[w] = PendComb{actr, ns, ctr_of(p.cl, t.layer, p.cl.comb + g), (G - cb + nc - 1) / nc};
+                cur_item[w] = -1;
+                progress = true;
+                continue;   // the share is added once every split is in
+              }
             } else if (t.op == MK_OP_MOE_UPGATE_ACT_DRAIN) {
               ctr[ctr_of(p.cl, t.layer, p.cl.ug + item / p.ug_tiles)]++;
             }
@@ -617,7 +640,7 @@ int simulate(const mk_config* c, int B, const Plan& p, int NW, const int32_t* se
           }
           phase[w] = 0;
         }
-        if (t.signal_ctr >= 0) ctr[t.signal_ctr]++;
+        if (t.signal_ctr >= 0) ctr[t.signal_ctr] += (t.op == MK_OP_ATTN_COMBINE ? G : 1);
         if ((t.flags & MK_F_FUSE_TOPK) && ctr[t.signal_ctr] == t.aux[0])
           ctr[ctr_of(p.cl, t.layer, MK_CTR_ROUTE)]++;   // the last router tile runs top-k
         cursor[w] += 1;
@@ -789,7 +812,6 @@ int mk_decode_step(mk_handle* h, const int32_t* token_ids, const int32_t* positi
   a.lm_head = h->lm_head;
   a.final_norm = h->final_norm;
   a.inv_freq = reinterpret_cast<const double*>(ws + L.off_invf);
-  a.rope = reinterpret_cast<float*>(ws + L.off_rope);
   a.tokens = token_ids;
   a.positions = positions;
   a.block_tables = block_tables;
@@ -807,6 +829,7 @@ int mk_decode_step(mk_handle* h, const int32_t* token_ids, const int32_t* positi
   a.ug_tiles = h->plan.ug_tiles; a.ug_pairs = h->plan.ug_pairs;
   a.dn_tiles = h->plan.dn_tiles; a.dn_rows = h->plan.dn_rows;
   a.n_qkv_tiles = h->plan.n_qkv;
+  a.ncomb = h->plan.ncomb;
   a.bk = L.bk;
   a.moe_stride = L.moe_stride;
   a.cl = h->plan.cl;

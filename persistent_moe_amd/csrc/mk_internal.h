@@ -17,8 +17,9 @@ enum {
   MK_F_FUSE_TOPK = 1 << 4,  // ROUTER_GEMM: the last tile to finish runs top-k and
                             // ROUTE_FINALIZE and signals the layer's ROUTE counter
                             // (aux[0] = number of router tiles)
-  MK_F_FUSE_COMBINE = 1 << 5   // ATTN_DRAIN: the last split of a (sequence, group) to
-                                // finish runs its combine and bumps COMB[group]
+  MK_F_FUSE_COMBINE = 1 << 5   // ATTN_DRAIN: the last min(splits, ncomb) splits of a
+                                // (sequence, group) to finish combine a share of its
+                                // heads each and add their head count to COMB[group]
 };
 
 // descriptor words set by the schedule builder
@@ -107,7 +108,6 @@ struct mk_kargs {
   const uint16_t* lm_head;
   const uint16_t* final_norm;
   const double* inv_freq;         // [hd/2] RoPE inverse frequencies
-  float* rope;                    // [B][hd/2][2] cos, sin of this step's angles
   // step inputs
   const int32_t* tokens;
   const int32_t* positions;
@@ -122,6 +122,7 @@ struct mk_kargs {
   int32_t attn_split, max_splits;
   int32_t ug_tiles, ug_pairs, dn_tiles, dn_rows;  // MoE tiling per expert
   int32_t n_qkv_tiles;
+  int32_t ncomb;                  // fused combine: most workgroups sharing one (sequence, group)
   int32_t bk;                     // max rows of routed tokens (max_batch * top_k)
   int32_t moe_stride;
   mk_ctr_layout cl;

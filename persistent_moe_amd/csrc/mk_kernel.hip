@@ -83,6 +83,16 @@ struct __attribute__((aligned(16))) Smem {
 };
 
 // ------------------------------------------------------------------ helpers
+// The thread index, opaque to the optimiser at each use: otherwise every
+// value derived from it (LDS and global offsets of every op) is hoisted to
+// the kernel entry and kept live for the whole step, where they no longer
+// fit in registers and are spilled to scratch memory.
+__device__ __forceinline__ int tid_v() {
+  int t = __builtin_amdgcn_workitem_id_x();
+  asm volatile("" : "+v"(t));
+  return t;
+}
+
 __device__ __forceinline__ float bf_lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
 __device__ __forceinline__ float bf16_to_f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
@@ -286,7 +296,7 @@ __device__ __forceinline__ bool spin_until(const KA a, int idx, int target, int 
 
 // Workgroup-wide wait; every thread must call it.  Uses misc[0].
 __device__ __forceinline__ bool wg_wait(const KA a, Smem& sm, int idx, int target, int task) {
-  if (threadIdx.x == 0) {
+  if (tid_v() == 0) {
     sm.misc[0] = (idx < 0 || target <= 0) ? 1 : (int)spin_until(a, idx, target, task);
     if (a->trace && sm.t_ready == 0) sm.t_ready = wall_clock64();
   }
@@ -299,7 +309,7 @@ __shared__ uint64_t sm_t_signal;   // trace: when wg_signal last bumped a counte
 // trace: first time this task passes mark k (thread 0)
 #define MK_MARK(k)                                                              \
   do {                                                                          \
-    if (a->trace && threadIdx.x == 0 && sm.t_mark[k] == 0) sm.t_mark[k] = wall_clock64(); \
+    if (a->trace && tid_v() == 0 && sm.t_mark[k] == 0) sm.t_mark[k] = wall_clock64(); \
   } while (0)
 
 // Workgroup-wide signal: every wave waits for its (agent-coherent) stores to
@@ -307,15 +317,15 @@ __shared__ uint64_t sm_t_signal;   // trace: when wg_signal last bumped a counte
 __device__ __forceinline__ void wg_signal(const KA a, int idx, int inc) {
   stores_done();
   __syncthreads();
-  if (a->trace && threadIdx.x == 0) sm_t_signal = wall_clock64();
-  if (threadIdx.x == 0 && idx >= 0)
+  if (a->trace && tid_v() == 0) sm_t_signal = wall_clock64();
+  if (tid_v() == 0 && idx >= 0)
     __hip_atomic_fetch_add(ctrp(a, idx), inc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Claim the next item of a queue; every thread must call it.  Uses misc[1].
 __device__ __forceinline__ int wg_claim(const KA a, Smem& sm, int qidx) {
   __syncthreads();
-  if (threadIdx.x == 0) {
+  if (tid_v() == 0) {
     sm.misc[1] = ld_agent(ctrp(a, MK_CG_ABORT))
                      ? 0x3FFFFFFF
                      : __hip_atomic_fetch_add(ctrp(a, qidx), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -442,7 +452,7 @@ struct GemvTile {
   // hardware returns zeros for those loads, so nothing is masked.  voff is
   // the lane's byte offset (16 lane) in a K-chunk.
   __device__ __forceinline__ void load(const GemvArgs& g, int grp, int kl, int voff) {
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wave = __builtin_amdgcn_readfirstlane(tid_v() >> 6);
     const int r0 = row0(grp, wave, kl), cm = (1 << kl) - 1;
 #pragma unroll
     for (int u = 0; u < WB; ++u) {
@@ -459,7 +469,7 @@ struct GemvTile {
   // products.
   __device__ __forceinline__ void compute(const GemvArgs& g, int grp, int kl, const uint16_t* xh, const uint16_t* xl,
                                           float* ys) {
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid_v() >> 6), lane = tid_v() & 63;
     const int r0 = row0(grp, wave, kl), cm = (1 << kl) - 1;
     if (r0 >= g.nrows) return;   // wave-uniform: no rows in this group
     float acc[WB][NB];
@@ -531,8 +541,8 @@ struct StageArgs {
 // Rows go to LDS with stride kp (K padded to the GEMV's whole K-chunks),
 // zeros in the padding.
 __device__ __forceinline__ bool wait_and_stage(const KA a, Smem& sm, const StageArgs& s, int kp) {
-  if (threadIdx.x < 64) {
-    const int lane = threadIdx.x;
+  if (tid_v() < 64) {
+    const int lane = tid_v();
     int ok = 1;
     if (lane == 0) {
       ok = (s.wait_idx < 0 || s.wait_target <= 0) ? 1 : (int)spin_until(a, s.wait_idx, s.wait_target, s.task);
@@ -587,7 +597,7 @@ __device__ __forceinline__ bool wait_and_stage(const KA a, Smem& sm, const Stage
     }
   }
   __syncthreads();
-  if (a->trace && threadIdx.x == 0 && sm.t_mark[0] == 0) sm.t_mark[0] = wall_clock64();
+  if (a->trace && tid_v() == 0 && sm.t_mark[0] == 0) sm.t_mark[0] = wall_clock64();
   return sm.misc[0] != 0;
 }
 
@@ -600,10 +610,10 @@ __device__ __forceinline__ bool gemv_run(const KA a, Smem& sm, const GemvArgs& g
   const int kl = kch <= 1 ? 0 : 32 - __builtin_clz(kch - 1);   // ceil(log2(kch)); K <= 512 * WB
   const int per = MK_CW * (GemvTile<NB>::WB >> kl);
   const int ng = (g.nrows + per - 1) / per;
-  const bool cw = (threadIdx.x >> 6) != 0;
+  const bool cw = (tid_v() >> 6) != 0;
   // the first MK_NT row groups are in flight before the dependency resolves;
   // the control wave loads no weights, so its staging loads queue behind nothing
-  const int voff = (threadIdx.x & 63) * 16;
+  const int voff = (tid_v() & 63) * 16;
   if (cw) {
 #pragma unroll
     for (int u = 0; u < MK_NT; ++u)
@@ -611,7 +621,7 @@ __device__ __forceinline__ bool gemv_run(const KA a, Smem& sm, const GemvArgs& g
   }
   const int kp = 512 << kl;   // staged row stride (elements): the K-chunks the tiles read
   if (!wait_and_stage(a, sm, s, kp)) return false;
-  const uint16_t* xh = reinterpret_cast<const uint16_t*>(sm.xs) + (threadIdx.x & 63) * 8;
+  const uint16_t* xh = reinterpret_cast<const uint16_t*>(sm.xs) + (tid_v() & 63) * 8;
   const uint16_t* xl = xh + s.nb * kp;
   GemvArgs gx = g;
   gx.xstride = kp;
@@ -627,7 +637,7 @@ __device__ __forceinline__ bool gemv_run(const KA a, Smem& sm, const GemvArgs& g
       }
     }
   }
-  if (a->trace && threadIdx.x == 0 && sm.t_mark[1] == 0) sm.t_mark[1] = wall_clock64();
+  if (a->trace && tid_v() == 0 && sm.t_mark[1] == 0) sm.t_mark[1] = wall_clock64();
   return true;
 }
 
@@ -651,7 +661,7 @@ __device__ __forceinline__ bool gemv(const KA a, Smem& sm, const GemvArgs& g, co
 __device__ __forceinline__ bool op_add_rmsnorm(const KA a, Smem& sm, const mk_task& t, int ti) {
   constexpr int NCH = 4;            // 4-element chunks per thread (d <= 4096)
   const int l = t.layer, d = a->d, B = a->B, nv = d >> 2, K = a->topk;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = tid_v(), wave = tid >> 6, lane = tid & 63;
   const bool mid = t.flags & MK_F_MID;
   const bool fin = t.flags & MK_F_FINAL;
   const bool emb = t.flags & MK_F_EMBED;
@@ -684,18 +694,6 @@ __device__ __forceinline__ bool op_add_rmsnorm(const KA a, Smem& sm, const mk_ta
   float* xndst = mid ? a->xn2 + (long)l * B * d : a->xn + (long)l * B * d;
   float* red = sm.red;      // [MK_WAVES][NBMAX] partial sums of squares
   float* xv = sm.xs;        // [B][d] the new residual rows
-  if (emb) {
-    // cos/sin of pos * theta^(-2i/hd) for this step's positions, in double,
-    // read by every QKV tile's RoPE epilogue
-    const int half = a->hd / 2;
-    for (int idx = tid; idx < B * half; idx += MK_THREADS) {
-      const int b = idx / half, i = idx - b * half;
-      double sn, cs;
-      sincos((double)sh_positions[b] * a->inv_freq[i], &sn, &cs);
-      stc(a->rope + (long)idx * 2, (float)cs);
-      stc(a->rope + (long)idx * 2 + 1, (float)sn);
-    }
-  }
 #pragma unroll 1
   for (int b = 0; b < B; ++b) {
     const bool live = seq_len_u(b) > 0;
@@ -815,14 +813,18 @@ __device__ __forceinline__ void epi_qkv(const KA a, Smem& sm, const mk_task& t, 
   const int rows = (a->Hq + 2 * a->Hkv) * hd;
   uint16_t* kpool = LAYER_PTR(l, k);
   uint16_t* vpool = LAYER_PTR(l, v);
-  for (int idx = threadIdx.x; idx < np * B; idx += MK_THREADS) {
+  for (int idx = tid_v(); idx < np * B; idx += MK_THREADS) {
     const int p = idx / B, b = idx - p * B;
     if (sh_seq_lens[b] <= 0) continue;
     const int gp = t.n0 + p, head = gp / half, i = gp - head * half;
     float ya = sm.ys[(2 * p) * NBMAX + b], yb = sm.ys[(2 * p + 1) * NBMAX + b];
     const int pos = sh_positions[b];
     if (head < a->Hq + a->Hkv) {
-      const float c = ldc(a->rope + ((long)b * half + i) * 2), s_ = ldc(a->rope + ((long)b * half + i) * 2 + 1);
+      // cos/sin of pos * theta^(-2i/hd), evaluated in double here rather than
+      // read from a table (a load would cost a memory round trip)
+      double sn, cs;
+      sincos((double)pos * ((GLOBAL const double*)a->inv_freq)[i], &sn, &cs);
+      const float c = (float)cs, s_ = (float)sn;
       const float ra = ya * c - yb * s_;
       const float rb = yb * c + ya * s_;
       ya = ra;
@@ -857,7 +859,7 @@ __device__ __forceinline__ void epi_qkv(const KA a, Smem& sm, const mk_task& t, 
 // SiLU-and-multiply epilogue of the gate/up tiles: out[j][p] = silu(g) * u
 // from the paired tile rows 2p (gate) and 2p+1 (up).
 __device__ __forceinline__ void epi_swiglu(Smem& sm, int np, int nb, float* out, long ob) {
-  for (int idx = threadIdx.x; idx < np * nb; idx += MK_THREADS) {
+  for (int idx = tid_v(); idx < np * nb; idx += MK_THREADS) {
     const int p = idx / nb, j = idx - p * nb;
     const float gv = sm.ys[(2 * p) * NBMAX + j], uv = sm.ys[(2 * p + 1) * NBMAX + j];
     stc(out + (long)j * ob + p, silu(gv) * uv);
@@ -871,7 +873,7 @@ __device__ __forceinline__ void epi_swiglu(Smem& sm, int np, int nb, float* out,
 // leaves the selected ids in misc[64 + b*k + j] for ROUTE_FINALIZE.
 __device__ __forceinline__ void router_topk(const KA a, Smem& sm, int l) {
   const int B = a->B, E = a->E, K = a->topk;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = tid_v() >> 6, lane = tid_v() & 63;
   for (int b = wave; b < B; b += MK_WAVES) {
     float v[4];
 #pragma unroll
@@ -917,8 +919,8 @@ __device__ __forceinline__ void router_topk(const KA a, Smem& sm, int l) {
 // first row, the token of each row, the row of each (token, slot), and the
 // lengths of the up-gate and down claim queues.  Uses misc[64..] ids.
 __device__ __forceinline__ void route_finalize(const KA a, Smem& sm, int l) {
-  if ((threadIdx.x >> 6) != 0) return;
-  const int lane = threadIdx.x & 63, K = a->topk, BK = a->B * K;
+  if ((tid_v() >> 6) != 0) return;
+  const int lane = tid_v() & 63, K = a->topk, BK = a->B * K;
   int32_t* meta = a->moe + (long)l * a->moe_stride;
   int32_t* slot = meta + 4;
   int32_t* rec = slot + a->bk;            // [bk][16]: e, r0, nr, 0, token of each row
@@ -1003,7 +1005,7 @@ __device__ __forceinline__ bool attn_split(const KA a, Smem& sm, int l, int b, i
   constexpr int DTW = (NDT + MK_CW - 1) / MK_CW;    // dim tiles per compute wave
   const int G = a->G, Hkv = a->Hkv;
   const int SP = a->attn_split + 32;                // LDS row stride of scores and P
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = tid_v(), wave = tid >> 6, lane = tid & 63;
   const int cw = wave - 1;                          // compute wave index (wave 0: -1)
   const int c16 = lane & 15, q4 = lane >> 4;
   const int tb0 = p0 & ~15;                         // first key of the first tile
@@ -1237,39 +1239,40 @@ __device__ __forceinline__ bool attn_item(const KA a, Smem& sm, int l, int b, in
   return attn_split<64>(a, sm, l, b, g, s, p0, p1, ti, wait_idx, wait_target);
 }
 
-// ATTN_COMBINE for (sequence b, group g): M = max_s m_s;
-// o = sum_s e^(m_s - M) o_s / sum_s e^(m_s - M) l_s.  Each thread owns 4 dims
-// of one head; the o partials of the first CB splits are loaded before the
-// per-head weights are computed (wave h takes heads h, h+4, ...), so up to CB
-// splits cost one round trip.  Writes attn[b][g's heads].
-__device__ __forceinline__ void attn_combine(const KA a, Smem& sm, int l, int b, int g) {
-  const int G = a->G, hd = a->hd;
+// ATTN_COMBINE for (sequence b, group g), heads c, c + nc, ... of the group
+// (combiner c of nc): M = max_s m_s; o = sum_s e^(m_s - M) o_s / sum_s
+// e^(m_s - M) l_s.  Thread (sg, cq) owns 4 dims (chunk cq) and the splits
+// s = sg, sg + SG, ... (SG = 256 / (hd/4) split groups), so all threads load
+// partials for one head and up to CB splits each cost one round trip.  The
+// order of every sum is fixed by the head alone (split groups are added in
+// order), so a head's result has the same bits whichever combiner and share
+// count produced it.  Heads of the share are done one after another.
+template <int HD>
+__device__ __forceinline__ void attn_combine_hd(const KA a, Smem& sm, int l, int b, int g, int c, int nc) {
+  const int G = a->G;
+  constexpr int q4 = HD / 4;                // float4 chunks per head
+  constexpr int SG = MK_THREADS / q4;       // split groups
+  constexpr int CB = 16;                    // splits per thread per round trip
   const int ns = n_splits(a, l, b);
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  float* out = a->attn + ((long)l * a->B + b) * a->Hq * hd;
+  const int tid = tid_v(), wave = tid >> 6, lane = tid & 63;
+  float* out = a->attn + ((long)l * a->B + b) * a->Hq * HD;
   const long hstride = (long)a->max_splits;
   const float* ml0 = a->part_ml + ((((long)(l & 1) * a->B + b) * a->Hq + g * G) * hstride) * 2;
-  const float* po0 = a->part_o + ((((long)(l & 1) * a->B + b) * a->Hq + g * G) * hstride) * hd;
-  float* wts = sm.ys;                 // [G][max_splits]
-  float* den = sm.red;                // [G]
-  const int q4 = hd / 4;              // float4 chunks per head
-  const bool mine = tid < G * q4;
-  const int h = mine ? tid / q4 : 0, cq = tid - h * q4;
-  const int obase = (int)((h * hstride * hd + cq * 4) * 4);   // byte offset of split 0
-  constexpr int CB = 32;
-  f32x4 pv[CB];
-#pragma unroll
-  for (int u = 0; u < CB; ++u)
-    pv[u] = (mine && u < ns) ? as_f4(ldc16(po0, obase + u * hd * 4)) : (f32x4){0.f, 0.f, 0.f, 0.f};
-  for (int hh = wave; hh < G; hh += MK_WAVES) {
-    const float* ml = ml0 + (long)hh * hstride * 2;
+  const float* po0 = a->part_o + ((((long)(l & 1) * a->B + b) * a->Hq + g * G) * hstride) * HD;
+  const int nh = (G - c + nc - 1) / nc;     // heads of this share
+  const int sg = tid / q4, cq = tid - sg * q4;
+  float* wts = sm.ys;                       // [nh][max_splits]
+  float* den = sm.red;                      // [nh]
+  f32x4* part = reinterpret_cast<f32x4*>(sm.red + 64);   // [SG][q4] partial numerators
+  for (int hh = wave; hh < nh; hh += MK_WAVES) {
+    const float* ml = ml0 + (long)(c + nc * hh) * hstride * 2;
     float m[16], lsum[16];
     float mx = -INFINITY;
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
-      const int s = lane + 64 * u;
-      m[u] = s < ns ? ldc(ml + s * 2) : -INFINITY;
-      lsum[u] = s < ns ? ldc(ml + s * 2 + 1) : 0.f;
+      const int sp = lane + 64 * u;
+      m[u] = sp < ns ? ldc(ml + sp * 2) : -INFINITY;
+      lsum[u] = sp < ns ? ldc(ml + sp * 2 + 1) : 0.f;
     }
 #pragma unroll
     for (int u = 0; u < 16; ++u) mx = fmaxf(mx, m[u]);
@@ -1277,10 +1280,10 @@ __device__ __forceinline__ void attn_combine(const KA a, Smem& sm, int l, int b,
     float dsum = 0.f;
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
-      const int s = lane + 64 * u;
-      if (s < ns) {
+      const int sp = lane + 64 * u;
+      if (sp < ns) {
         const float w = expf(m[u] - mx);
-        wts[hh * hstride + s] = w;
+        wts[hh * hstride + sp] = w;
         dsum += w * lsum[u];
       }
     }
@@ -1288,29 +1291,46 @@ __device__ __forceinline__ void attn_combine(const KA a, Smem& sm, int l, int b,
     if (lane == 0) den[hh] = dsum;
   }
   __syncthreads();
-  f32x4 num = (f32x4){0.f, 0.f, 0.f, 0.f};
+  for (int hs = 0; hs < nh; ++hs) {
+    const int h = c + nc * hs;
+    const int obase = (int)((h * hstride * HD + cq * 4) * 4);   // byte offset of split 0
+    f32x4 num = (f32x4){0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < ns; s0 += SG * CB) {
+      f32x4 pv[CB];
 #pragma unroll
-  for (int u = 0; u < CB; ++u)
-    if (u < ns) num += wts[h * hstride + u] * pv[u];
-  for (int s0 = CB; s0 < ns; s0 += CB) {
+      for (int u = 0; u < CB; ++u) {
+        const int sp = s0 + sg + SG * u;
+        pv[u] = sp < ns ? as_f4(ldc16(po0, obase + sp * HD * 4)) : (f32x4){0.f, 0.f, 0.f, 0.f};
+      }
 #pragma unroll
-    for (int u = 0; u < CB; ++u)
-      pv[u] = (mine && s0 + u < ns) ? as_f4(ldc16(po0, obase + (s0 + u) * hd * 4)) : (f32x4){0.f, 0.f, 0.f, 0.f};
+      for (int u = 0; u < CB; ++u) {
+        const int sp = s0 + sg + SG * u;
+        if (sp < ns) num += wts[hs * hstride + sp] * pv[u];
+      }
+    }
+    part[sg * q4 + cq] = num;
+    __syncthreads();
+    if (sg == 0) {
+      f32x4 tot = part[cq];
 #pragma unroll
-    for (int u = 0; u < CB; ++u)
-      if (s0 + u < ns) num += wts[h * hstride + s0 + u] * pv[u];
-  }
-  if (mine) {
-    const f32x4 r = ns > 0 ? num / den[h] : (f32x4){0.f, 0.f, 0.f, 0.f};
-    stc16(out, ((g * G + h) * hd + cq * 4) * 4, as_u4(r));
+      for (int k = 1; k < SG; ++k) tot += part[k * q4 + cq];
+      const f32x4 r = ns > 0 ? tot / den[hs] : (f32x4){0.f, 0.f, 0.f, 0.f};
+      stc16(out, ((g * G + h) * HD + cq * 4) * 4, as_u4(r));
+    }
+    __syncthreads();
   }
 }
+__device__ __forceinline__ void attn_combine(const KA a, Smem& sm, int l, int b, int g, int c, int nc) {
+  if (a->hd == 128) attn_combine_hd<128>(a, sm, l, b, g, c, nc);
+  else attn_combine_hd<64>(a, sm, l, b, g, c, nc);
+}
 
-// ATTN_COMBINE as its own task: waits for every split of (b, g).
+// ATTN_COMBINE as its own task: waits for every split of (b, g), combines
+// all its heads and adds the head count to COMB[g].
 __device__ __forceinline__ bool op_attn_combine(const KA a, Smem& sm, const mk_task& t, int ti) {
   if (!wg_wait(a, sm, t.wait_ctr, n_splits(a, t.layer, t.batch), ti)) return false;
-  attn_combine(a, sm, t.layer, t.batch, t.group);
-  wg_signal(a, t.signal_ctr, 1);
+  attn_combine(a, sm, t.layer, t.batch, t.group, 0, 1);
+  wg_signal(a, t.signal_ctr, a->G);
   return true;
 }
 
@@ -1334,7 +1354,7 @@ __device__ __forceinline__ u32x4 load_task_piece(const mk_task* tasks, int k, in
 
 extern "C" __global__ void __launch_bounds__(MK_THREADS, 1) mk_persistent(mk_kargs a_arg, int final_launch) {
   __shared__ Smem sm;
-  const int tid = threadIdx.x;
+  const int tid = tid_v();
   // this workgroup's tasks: [k, kend) of the grouped list
   const int kbeg = ((GLOBAL const int32_t*)a_arg.wg_range)[2 * blockIdx.x];
   const int kend = ((GLOBAL const int32_t*)a_arg.wg_range)[2 * blockIdx.x + 1];
@@ -1408,7 +1428,7 @@ extern "C" __global__ void __launch_bounds__(MK_THREADS, 1) mk_persistent(mk_kar
             for (int b = 0; b < a->B; ++b)
               if (n_splits(a, l, b) == 0)
                 for (int g = 0; g < a->Hkv; ++g)
-                  __hip_atomic_fetch_add(ctrp(a, layer_ctr(a, l, a->cl.comb + g)), 1, __ATOMIC_RELAXED,
+                  __hip_atomic_fetch_add(ctrp(a, layer_ctr(a, l, a->cl.comb + g)), a->G, __ATOMIC_RELAXED,
                                          __HIP_MEMORY_SCOPE_AGENT);
           }
         } else {
@@ -1623,16 +1643,26 @@ extern "C" __global__ void __launch_bounds__(MK_THREADS, 1) mk_persistent(mk_kar
             attn_wait = -1;   // satisfied for every later item
             const int actr = layer_ctr(a, l, a->cl.attn + b * a->Hkv + gq);
             if (t.flags & MK_F_FUSE_COMBINE) {
-              // the last split of (b, gq) to finish combines them
+              // the last nc splits of (b, gq) to finish combine them, one
+              // share of the heads each: those that finish early wait for
+              // the rest (at most ncomb - 1 per (b, g), fewer than the
+              // workgroups, so some workgroup is always free to claim)
               stores_done();
               __syncthreads();
               if (tid == 0)
-                sm.misc[3] = __hip_atomic_fetch_add(ctrp(a, actr), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-                             n_splits(a, l, b) - 1;
+                sm.misc[3] = __hip_atomic_fetch_add(ctrp(a, actr), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
               __syncthreads();
-              if (sm.misc[3]) {
-                attn_combine(a, sm, l, b, gq);
-                wg_signal(a, layer_ctr(a, l, a->cl.comb + gq), 1);
+              const int ns = n_splits(a, l, b);
+              const int nc = min(ns, a->ncomb);
+              const int rank = __builtin_amdgcn_readfirstlane(sm.misc[3]);
+              if (rank >= ns - nc) {
+                const int cb = rank - (ns - nc);
+                if (rank < ns - 1 && !wg_wait(a, sm, actr, ns, ti)) {
+                  aborted = true;
+                  break;
+                }
+                attn_combine(a, sm, l, b, gq, cb, nc);
+                wg_signal(a, layer_ctr(a, l, a->cl.comb + gq), (a->G - cb + nc - 1) / nc);
               }
             } else {
               wg_signal(a, actr, 1);

@@ -179,9 +179,12 @@ def test_signal_counts_match_wait_targets(lib):
         tasks, _ = _plan(model, B, mb)
         sig = {}
         fused = {}
+        G = model.n_q_heads // model.n_kv_heads
         for t in tasks:
             if t.signal_ctr >= 0:
-                sig[t.signal_ctr] = sig.get(t.signal_ctr, 0) + 1
+                # a combine task adds its group's head count
+                inc = G if t.op == mk.OPCODES.index("ATTN_COMBINE") else 1
+                sig[t.signal_ctr] = sig.get(t.signal_ctr, 0) + inc
             if t.flags & 16:           # router tile with fused top-k: one ROUTE signal per layer
                 fused[t.layer] = t.signal_ctr
         fused_comb = {t.layer for t in tasks if t.op == mk.OPCODES.index("ATTN_DRAIN") and t.flags & 32}
@@ -191,8 +194,9 @@ def test_signal_counts_match_wait_targets(lib):
                 if t.layer in fused:
                     sig[route] = 1
             if t.op == mk.OPCODES.index("O_PROJ") and t.layer in fused_comb:
-                # fused combine: the last split of each sequence bumps its group's counter
-                sig[t.wait_ctr] = B
+                # fused combine: the combining splits of each sequence add the
+                # group's head count in all
+                sig[t.wait_ctr] = B * G
         for t in tasks:
             if t.wait_ctr >= 0 and t.wait_target > 0 and t.op not in (8, 13, 14):
                 assert sig.get(t.wait_ctr, 0) == t.wait_target, (mk.OPCODES[t.op], t.layer)
