@@ -32,6 +32,7 @@
 // claim queues whose head is an atomic counter (page 1, "Scheduling").
 
 #include <hip/hip_runtime.h>
+#include <type_traits>
 #include <stdint.h>
 
 #include "mk_internal.h"
@@ -519,6 +520,48 @@ struct GemvTile {
       }
     }
   }
+
+  // One batch row with K <= 512 << KL: the lane's pieces of the 1 << KL
+  // K-chunks of x are in registers (xrh / xrl, loaded once per task), so the
+  // products wait on no LDS read.
+  template <int KL>
+  __device__ __forceinline__ void compute_r(const GemvArgs& g, int grp, const u32x4* xrh, const u32x4* xrl,
+                                            float* ys) {
+    static_assert(NB == 1, "register-resident x holds one batch row");
+    constexpr int CM = (1 << KL) - 1, RPW = WB >> KL;
+    const int wave = __builtin_amdgcn_readfirstlane(tid_v() >> 6), lane = tid_v() & 63;
+    const int r0 = row0(grp, wave, KL);
+    if (r0 >= g.nrows) return;   // wave-uniform: no rows in this group
+    float acc[WB];
+#pragma unroll
+    for (int u = 0; u < WB; ++u) {
+      const u32x4 v = w[u], h = xrh[u & CM], q = xrl[u & CM];
+      float s = dot2_bf16(v.x, h.x, 0.f);
+      s = dot2_bf16(v.y, h.y, s);
+      s = dot2_bf16(v.z, h.z, s);
+      s = dot2_bf16(v.w, h.w, s);
+      s = dot2_bf16(v.x, q.x, s);
+      s = dot2_bf16(v.y, q.y, s);
+      s = dot2_bf16(v.z, q.z, s);
+      s = dot2_bf16(v.w, q.w, s);
+      acc[u] = s;
+    }
+    // add the K-chunks of each row pairwise, as compute() does
+#pragma unroll
+    for (int step = 1; step < (1 << KL); step <<= 1) {
+#pragma unroll
+      for (int i = 0; i < WB / (2 * step); ++i) acc[i] = acc[2 * i] + acc[2 * i + 1];
+    }
+#pragma unroll
+    for (int j = 0; j < RPW; ++j) {
+      const int r = r0 + j;
+      const float s = wave_sum(acc[j]);
+      if (lane == 0 && r < g.nrows && g.nb > 0) {
+        if (g.out) stc(g.out + r, s);
+        else ys[r * NBMAX] = s;
+      }
+    }
+  }
 };
 
 // Staging of the activation rows a tile multiplies: nb rows of K floats.
@@ -626,6 +669,39 @@ __device__ __forceinline__ bool gemv_run(const KA a, Smem& sm, const GemvArgs& g
   GemvArgs gx = g;
   gx.xstride = kp;
   make_uniform(gx);
+  // trace: wave 1 passes the staging barrier (mark 3), finishes its row
+  // groups (mark 4); the epilogue end is mark 5
+  if (a->trace && tid_v() == 64) sm.t_mark[3] = wall_clock64();
+  if constexpr (NB == 1) {
+    if (kl <= 2) {
+      if (cw) {
+        u32x4 xrh[4], xrl[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          xrh[c] = c < (1 << kl) ? *reinterpret_cast<const u32x4*>(xh + 512 * c) : (u32x4){0u, 0u, 0u, 0u};
+          xrl[c] = c < (1 << kl) ? *reinterpret_cast<const u32x4*>(xl + 512 * c) : (u32x4){0u, 0u, 0u, 0u};
+        }
+        auto run = [&](auto klc) {
+          constexpr int KL = decltype(klc)::value;
+          for (int grp = 0; grp < ng; grp += MK_NT) {
+#pragma unroll
+            for (int u = 0; u < MK_NT; ++u) {
+              if (grp + u < ng) {
+                T[u].template compute_r<KL>(gx, grp + u, xrh, xrl, sm.ys);
+                if (grp + u + MK_NT < ng) T[u].load(g, grp + u + MK_NT, kl, voff);
+              }
+            }
+          }
+        };
+        if (kl == 0) run(std::integral_constant<int, 0>{});
+        else if (kl == 1) run(std::integral_constant<int, 1>{});
+        else run(std::integral_constant<int, 2>{});
+      }
+      if (a->trace && tid_v() == 64) sm.t_mark[4] = wall_clock64();
+      if (a->trace && tid_v() == 0 && sm.t_mark[1] == 0) sm.t_mark[1] = wall_clock64();
+      return true;
+    }
+  }
   if (cw) {
     for (int grp = 0; grp < ng; grp += MK_NT) {
 #pragma unroll
@@ -637,6 +713,7 @@ __device__ __forceinline__ bool gemv_run(const KA a, Smem& sm, const GemvArgs& g
       }
     }
   }
+  if (a->trace && tid_v() == 64) sm.t_mark[4] = wall_clock64();
   if (a->trace && tid_v() == 0 && sm.t_mark[1] == 0) sm.t_mark[1] = wall_clock64();
   return true;
 }
@@ -1563,6 +1640,7 @@ extern "C" __global__ void __launch_bounds__(MK_THREADS, 1) mk_persistent(mk_kar
           case MK_OP_QKV_PROJ:
             __syncthreads();
             epi_qkv(a, sm, t, ti);
+            if (a->trace && tid_v() == 64) sm.t_mark[5] = wall_clock64();
             wg_signal(a, t.signal_ctr, 1);
             break;
           case MK_OP_FFN_UPGATE_ACT:
