@@ -391,6 +391,7 @@ struct GemvArgs {
   int hd;
   int xstride;     // elements between staged x rows in LDS (set by gemv_run)
   int nb;          // live batch rows
+  int pm, hs;      // row mapping (set by make_uniform): pairs?, log2 of the pair block
   // output
   float* out;      // mode 0: out[b*ob + r]; null: LDS ys[r*NBMAX + b]
   long ob;
@@ -416,13 +417,16 @@ __device__ __forceinline__ void make_uniform(GemvArgs& g) {
   g.nb = __builtin_amdgcn_readfirstlane(g.nb);
   g.out = uniform_ptr(g.out);
   g.ob = uniform_long(g.ob);
+  g.pm = g.mode != ROW_PLAIN ? 1 : 0;
+  g.hs = g.mode == ROW_ROPE_PAIRS ? 31 - __builtin_clz(g.half) : 31;
 }
 
+// The element offset of a weight row is a 32 x 32 -> 64-bit scalar multiply
+// (row index and row pitch both fit in 32 bits).
 __device__ __forceinline__ const uint16_t* gemv_row(const GemvArgs& g, int r) {
-  const int pm = g.mode != ROW_PLAIN ? 1 : 0;
-  const int p = g.r0 + (r >> pm), upper = r & pm;
-  const int hs = g.mode == ROW_ROPE_PAIRS ? 31 - __builtin_clz(g.half) : 31;
-  return g.base + (long)(p + ((p >> hs) + upper) * g.half) * g.ldw;
+  const int p = g.r0 + (r >> g.pm), upper = r & g.pm;
+  const uint32_t row = (uint32_t)(p + ((p >> g.hs) + upper) * g.half);
+  return g.base + (uint64_t)row * (uint32_t)g.ldw;
 }
 
 // Register tile of one row group: WB 16-byte weight loads per lane of each
@@ -461,6 +465,25 @@ struct GemvTile {
       __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
           const_cast<uint16_t*>(gemv_row(g, r < g.nrows ? r : 0)), (short)0, r < g.nrows ? g.K * 2 : 0, 0x00020000);
       w[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff + c * 1024, 0, 2 /* nontemporal */);
+    }
+  }
+
+  // load() with the K-chunk count 2^KL known: the chunks of one row share
+  // one buffer descriptor, so a row group costs one row-address computation
+  // per row instead of one per 16-byte load.
+  template <int KL>
+  __device__ __forceinline__ void load_k(const GemvArgs& g, int grp, int voff) {
+    constexpr int RPW = WB >> KL;
+    const int wave = __builtin_amdgcn_readfirstlane(tid_v() >> 6);
+    const int r0 = row0(grp, wave, KL);
+#pragma unroll
+    for (int j = 0; j < RPW; ++j) {
+      const int r = r0 + j;
+      __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t*>(gemv_row(g, r < g.nrows ? r : 0)), (short)0, r < g.nrows ? g.K * 2 : 0, 0x00020000);
+#pragma unroll
+      for (int c = 0; c < (1 << KL); ++c)
+        w[(j << KL) + c] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff + c * 1024, 0, 2 /* nontemporal */);
     }
   }
 
@@ -552,13 +575,49 @@ struct GemvTile {
 #pragma unroll
       for (int i = 0; i < WB / (2 * step); ++i) acc[i] = acc[2 * i] + acc[2 * i + 1];
     }
+    if constexpr (RPW == 4 || RPW == 8) {
+      // transpose-reduce: halves, then quarter rows of the wave swap so that
+      // each 16-lane row (RPW = 4) or 8-lane half row (RPW = 8) ends up
+      // holding one tile row, then a sum within it
+      float b[RPW / 2];
 #pragma unroll
-    for (int j = 0; j < RPW; ++j) {
-      const int r = r0 + j;
-      const float s = wave_sum(acc[j]);
-      if (lane == 0 && r < g.nrows && g.nb > 0) {
-        if (g.out) stc(g.out + r, s);
-        else ys[r * NBMAX] = s;
+      for (int j = 0; j < RPW / 2; ++j) {   // rows j (lanes 0-31) and j + RPW/2 (lanes 32-63)
+        const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[j]), __float_as_uint(acc[j + RPW / 2]),
+                                                        false, false);
+        b[j] = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+      }
+      float c[RPW / 4];
+#pragma unroll
+      for (int j = 0; j < RPW / 4; ++j) {   // 16-lane rows: j, j + RPW/4, j + RPW/2, j + 3 RPW/4
+        const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(b[j]), __float_as_uint(b[j + RPW / 4]),
+                                                        false, false);
+        c[j] = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+      }
+      float v;
+      int r;
+      if constexpr (RPW == 4) {
+        v = group_sum<16>(c[0]);
+        r = r0 + (lane >> 4);
+      } else {
+        // lanes 0-7 of each 16-lane row keep c[0]'s row, lanes 8-15 c[1]'s
+        const bool hi8 = (lane & 8) != 0;
+        const float keep = hi8 ? c[1] : c[0], give = hi8 ? c[0] : c[1];
+        v = group_sum<8>(keep + dppf<DPP_ROW_ROR8>(give));
+        r = r0 + 2 * (lane >> 4) + (hi8 ? 1 : 0);
+      }
+      if ((lane & (16 / (RPW / 4) - 1)) == 0 && r < g.nrows && g.nb > 0) {
+        if (g.out) stc(g.out + r, v);
+        else ys[r * NBMAX] = v;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < RPW; ++j) {
+        const int r = r0 + j;
+        const float sv = wave_sum(acc[j]);
+        if (lane == 0 && r < g.nrows && g.nb > 0) {
+          if (g.out) stc(g.out + r, sv);
+          else ys[r * NBMAX] = sv;
+        }
       }
     }
   }
@@ -657,10 +716,23 @@ __device__ __forceinline__ bool gemv_run(const KA a, Smem& sm, const GemvArgs& g
   // the first MK_NT row groups are in flight before the dependency resolves;
   // the control wave loads no weights, so its staging loads queue behind nothing
   const int voff = (tid_v() & 63) * 16;
+  const bool xreg = NB == 1 && kl <= 2;   // x in registers, chunk count known (below)
   if (cw) {
+    if (xreg) {
+      auto pre = [&](auto klc) {
+        constexpr int KL = decltype(klc)::value;
 #pragma unroll
-    for (int u = 0; u < MK_NT; ++u)
-      if (u < ng) T[u].load(g, u, kl, voff);
+        for (int u = 0; u < MK_NT; ++u)
+          if (u < ng) T[u].template load_k<KL>(g, u, voff);
+      };
+      if (kl == 0) pre(std::integral_constant<int, 0>{});
+      else if (kl == 1) pre(std::integral_constant<int, 1>{});
+      else pre(std::integral_constant<int, 2>{});
+    } else {
+#pragma unroll
+      for (int u = 0; u < MK_NT; ++u)
+        if (u < ng) T[u].load(g, u, kl, voff);
+    }
   }
   const int kp = 512 << kl;   // staged row stride (elements): the K-chunks the tiles read
   if (!wait_and_stage(a, sm, s, kp)) return false;
@@ -673,7 +745,7 @@ __device__ __forceinline__ bool gemv_run(const KA a, Smem& sm, const GemvArgs& g
   // groups (mark 4); the epilogue end is mark 5
   if (a->trace && tid_v() == 64) sm.t_mark[3] = wall_clock64();
   if constexpr (NB == 1) {
-    if (kl <= 2) {
+    if (xreg) {
       if (cw) {
         u32x4 xrh[4], xrl[4];
 #pragma unroll
@@ -688,7 +760,7 @@ __device__ __forceinline__ bool gemv_run(const KA a, Smem& sm, const GemvArgs& g
             for (int u = 0; u < MK_NT; ++u) {
               if (grp + u < ng) {
                 T[u].template compute_r<KL>(gx, grp + u, xrh, xrl, sm.ys);
-                if (grp + u + MK_NT < ng) T[u].load(g, grp + u + MK_NT, kl, voff);
+                if (grp + u + MK_NT < ng) T[u].template load_k<KL>(g, grp + u + MK_NT, voff);
               }
             }
           }
