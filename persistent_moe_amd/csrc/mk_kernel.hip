@@ -1164,9 +1164,19 @@ __device__ __forceinline__ bool attn_split(const KA a, Smem& sm, int l, int b, i
   const uint16_t* Kp = LAYER_PTR(l, k);
   const uint16_t* Vp = LAYER_PTR(l, v);
   const int32_t* bt = a->block_tables + (long)b * a->max_blocks + (tb0 >> 4);
+  const bool bt_lds = a->B * a->max_blocks <= MK_LDS_BT;
+  const int* btl = sh_bt + b * a->max_blocks + (tb0 >> 4);
   const int newest = position_u(b);
+  // The key appended this step is not read from its page, whose store may
+  // not be visible yet: its score and its share of P V are computed from the
+  // QKV output (rounded to bf16 like the page copy), outside the MFMA loops,
+  // and its page slot only ever meets p = 0 there.
+  const bool has_new = newest >= p0 && newest < p1;
+  const int kk_new = newest - tb0;
+  float* fresh = reinterpret_cast<float*>(sm.misc + 16);   // [0..7] its scores, [8..15] its p
+  const float* qkv_b = a->qkv + ((long)l * a->B + b) * (a->Hq + 2 * Hkv) * HD;
   auto page_of = [&](int t) -> int {
-    int pg = bt[t];
+    int pg = bt_lds ? btl[t] : bt[t];
     if (pg < 0 || pg >= a->num_pages) {
       report(a, MK_E_DEVICE, ti, -3, pg, a->num_pages);
       pg = 0;
@@ -1187,8 +1197,6 @@ __device__ __forceinline__ bool attn_split(const KA a, Smem& sm, int l, int b, i
   if (cw >= 0) {
     // every page id first (one round trip), then every K and V load
     int kpg[ATT_PT], vpg[ATT_PV];
-    const bool bt_lds = a->B * a->max_blocks <= MK_LDS_BT;
-    const int* btl = sh_bt + b * a->max_blocks + (tb0 >> 4);
 #pragma unroll
     for (int u = 0; u < ATT_PT; ++u) kpg[u] = u < nti ? (bt_lds ? btl[cw + MK_CW * u] : bt[cw + MK_CW * u]) : 0;
 #pragma unroll
@@ -1237,15 +1245,38 @@ __device__ __forceinline__ bool attn_split(const KA a, Smem& sm, int l, int b, i
     ok = __builtin_amdgcn_readfirstlane(ok);
     if (lane == 0) sm.misc[0] = ok;
     if (ok) {
-      const int rows = (a->Hq + 2 * Hkv) * HD;
-      const float* qb = a->qkv + ((long)l * a->B + b) * rows + (long)(g * G) * HD;
+      const float* qb = qkv_b + (long)(g * G) * HD;
       for (int i = lane; i < G * HD / 4; i += 64)
         *reinterpret_cast<u32x4*>(qs + i * 4) = ldc16(qb, i * 16);
+      if (has_new) {
+        // scores of the new key: q . k with k rounded to bf16 like its page copy
+        constexpr int DL = HD / 64;   // dims per lane
+        float kn[DL];
+#pragma unroll
+        for (int e = 0; e < DL; ++e) kn[e] = bf16_to_f(f_to_bf16(ldc(qkv_b + (long)(a->Hq + g) * HD + lane + 64 * e)));
+        for (int h = 0; h < G; ++h) {
+          float t = 0.f;
+#pragma unroll
+          for (int e = 0; e < DL; ++e) t += qs[h * HD + lane + 64 * e] * kn[e];
+          t = wave_sum(t);
+          if (lane == 0) fresh[h] = t * a->attn_scale;
+        }
+      }
     }
   }
   __syncthreads();
   MK_MARK(4);
   if (!sm.misc[0]) return false;
+  // V of the new key (bf16-rounded) for the lanes' output dims, in flight
+  // until after the P V pass
+  float vnew[DTW];
+#pragma unroll
+  for (int j = 0; j < DTW; ++j) {
+    const int dt = cw + MK_CW * j;
+    vnew[j] = (has_new && cw >= 0 && dt < NDT)
+                  ? bf16_to_f(f_to_bf16(ldc(qkv_b + (long)(a->Hq + Hkv + g) * HD + 16 * dt + c16)))
+                  : 0.f;
+  }
   float* sc = sm.ys;                                       // [G][SP] scores
   uint16_t* pbh = reinterpret_cast<uint16_t*>(sm.red);     // [G][SP] p, bf16 high part
   uint16_t* pbl = pbh + G * SP;                            // [G][SP] p, bf16 remainder
@@ -1276,11 +1307,6 @@ __device__ __forceinline__ bool attn_split(const KA a, Smem& sm, int l, int b, i
         if (i < nti) {
           const int t = cw + MK_CW * i;
           const int kk = 16 * t + c16, kabs = tb0 + kk;
-          if (kabs == newest) {   // appended this step: re-read coherently
-            const int o = k_off(t);
-#pragma unroll
-            for (int k = 0; k < KS; ++k) kf[u][k] = ldc16(Kp, (o + 512 * k) * 2);
-          }
           f32x4 c = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int k = 0; k < KS; ++k) {
@@ -1308,15 +1334,22 @@ __device__ __forceinline__ bool attn_split(const KA a, Smem& sm, int l, int b, i
   float* ml = a->part_ml + ((((long)(l & 1) * a->B + b) * a->Hq + g * G) * a->max_splits) * 2;
   const int nk = 16 * nt, nk2 = 32 * nks;
   for (int h = wave; h < G; h += MK_WAVES) {
+    const float fs = has_new ? fresh[h] : 0.f;
     float mx = -INFINITY;
-    for (int kk = lane; kk < nk; kk += 64) mx = fmaxf(mx, sc[h * SP + kk]);
+    for (int kk = lane; kk < nk; kk += 64) mx = fmaxf(mx, (has_new && kk == kk_new) ? fs : sc[h * SP + kk]);
     mx = wave_max(mx);
     float sum = 0.f;
     for (int kk = lane; kk < nk2; kk += 64) {
-      const float pj = kk < nk ? expf(sc[h * SP + kk] - mx) : 0.f;
-      const uint16_t ph = f_to_bf16(pj);
+      const bool isnew = has_new && kk == kk_new;
+      const float pj = kk < nk ? expf((isnew ? fs : sc[h * SP + kk]) - mx) : 0.f;
+      uint16_t ph = f_to_bf16(pj), pl = f_to_bf16(pj - bf16_to_f(ph));
+      if (isnew) {
+        fresh[8 + h] = pj;
+        ph = 0;
+        pl = 0;
+      }
       pbh[h * SP + kk] = ph;
-      pbl[h * SP + kk] = f_to_bf16(pj - bf16_to_f(ph));
+      pbl[h * SP + kk] = pl;
       sum += pj;
     }
     sum = wave_sum(sum);
@@ -1338,20 +1371,18 @@ __device__ __forceinline__ bool attn_split(const KA a, Smem& sm, int l, int b, i
       for (int u = 0; u < ATT_PV; ++u) {
         const int ks = ks0 + u;
         if (ks < nks) {
-          // keys outside [p0, p1) have p = 0; their V values are finite pool
-          // contents (earlier keys of the sequence, or the initialised pool)
-          const int k0 = tb0 + 32 * ks + 8 * q4;   // first key of this lane's V piece
+          // keys outside [p0, p1) and the new key have p = 0 here; their V
+          // values are finite pool contents (earlier keys of the sequence, an
+          // older value of the slot, or the initialised pool)
           const int po_ = c16 * SP + 32 * ks + 8 * q4;
           const u32x4 ph = c16 < G ? *reinterpret_cast<const u32x4*>(pbh + po_) : (u32x4){0u, 0u, 0u, 0u};
           const u32x4 pl = c16 < G ? *reinterpret_cast<const u32x4*>(pbl + po_) : (u32x4){0u, 0u, 0u, 0u};
-          const bool fresh = newest >= k0 && newest < k0 + 8;   // holds the key appended this step
-          const int ocur = fresh ? v_off(ks) : -1;
           const int onext = ks + ATT_PV < nks ? v_off(ks + ATT_PV) : -1;
 #pragma unroll
           for (int j = 0; j < DTW; ++j) {
             const int dt = cw + MK_CW * j;
             if (dt < NDT) {
-              const u32x4 v = ocur >= 0 ? ldc16(Vp, (ocur + 256 * dt) * 2) : vf[u][j];
+              const u32x4 v = vf[u][j];
               o[j] = mfma_bf16(ph, v, o[j]);
               o[j] = mfma_bf16(pl, v, o[j]);
               if (ks + ATT_PV < nks) vf[u][j] = onext >= 0 ? ldg_nt(Vp + onext + 256 * dt) : (u32x4){0u, 0u, 0u, 0u};
@@ -1368,7 +1399,10 @@ __device__ __forceinline__ bool attn_split(const KA a, Smem& sm, int l, int b, i
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int h = 4 * q4 + r;
-          if (h < G) stc(po + ((long)h * a->max_splits + s) * HD + 16 * dt + c16, o[j][r]);
+          if (h < G) {
+            const float ov = has_new ? o[j][r] + fresh[8 + h] * vnew[j] : o[j][r];
+            stc(po + ((long)h * a->max_splits + s) * HD + 16 * dt + c16, ov);
+          }
         }
       }
     }
