@@ -1619,8 +1619,16 @@ extern "C" __global__ void __launch_bounds__(MK_THREADS, 1) mk_persistent(mk_kar
             aborted = true;
             n_items = 0;
           } else {
+            // the item count and every active expert's record, into LDS once
+            // for all the items this workgroup will take (red is free
+            // during the MoE drains)
             const int32_t* meta = a->moe + (long)l * a->moe_stride;
-            n_items = ldc(meta + (t.op == MK_OP_MOE_UPGATE_ACT_DRAIN ? 1 : 2));
+            int* recs = reinterpret_cast<int*>(sm.red);
+            const int nrec = min(a->bk, RED_FLOATS / 16) * 16;
+            for (int i = tid; i < nrec; i += MK_THREADS) recs[i] = ldc(meta + 4 + a->bk + i);
+            if (tid == 0) sm.misc[2] = ldc(meta + (t.op == MK_OP_MOE_UPGATE_ACT_DRAIN ? 1 : 2));
+            __syncthreads();
+            n_items = __builtin_amdgcn_readfirstlane(sm.misc[2]);
           }
           qidx = layer_ctr(a, l, t.op == MK_OP_MOE_UPGATE_ACT_DRAIN ? MK_CTR_QUG : MK_CTR_QDN);
         }
@@ -1690,12 +1698,10 @@ extern "C" __global__ void __launch_bounds__(MK_THREADS, 1) mk_persistent(mk_kar
         case MK_OP_MOE_UPGATE_ACT_DRAIN: {
           // item = (active expert, tile of ug_pairs gate/up pairs) over that expert's rows
           kind = U_GEMV;
-          const int32_t* rec = a->moe + (long)l * a->moe_stride + 4 + a->bk;
           epi_ae = item / a->ug_tiles;
           const int tt = item - epi_ae * a->ug_tiles;
-          const u32x4 r0v = ldc16(rec, epi_ae * 64);
-          const u32x4 r1v = ldc16(rec, epi_ae * 64 + 16);
-          const u32x4 r2v = ldc16(rec, epi_ae * 64 + 32);
+          const u32x4* rec = reinterpret_cast<const u32x4*>(sm.red) + epi_ae * 4;   // this expert's record
+          const u32x4 r0v = rec[0], r1v = rec[1], r2v = rec[2];
           const int e = __builtin_amdgcn_readfirstlane((int)r0v.x);
           epi_r0 = __builtin_amdgcn_readfirstlane((int)r0v.y);
           epi_nr = __builtin_amdgcn_readfirstlane((int)r0v.z);
@@ -1720,9 +1726,8 @@ extern "C" __global__ void __launch_bounds__(MK_THREADS, 1) mk_persistent(mk_kar
           // item = (active expert, tile of dn_rows output rows); waits on the
           // expert's up-gate tiles after its weights are in flight
           kind = U_GEMV;
-          const int32_t* rec = a->moe + (long)l * a->moe_stride + 4 + a->bk;
           const int ae = item / a->dn_tiles, tt = item - ae * a->dn_tiles;
-          const u32x4 r0v = ldc16(rec, ae * 64);
+          const u32x4 r0v = reinterpret_cast<const u32x4*>(sm.red)[ae * 4];   // this expert's record
           const int e = __builtin_amdgcn_readfirstlane((int)r0v.x);
           const int r0 = __builtin_amdgcn_readfirstlane((int)r0v.y);
           const int nr = __builtin_amdgcn_readfirstlane((int)r0v.z);
