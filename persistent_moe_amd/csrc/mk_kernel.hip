@@ -1173,7 +1173,7 @@ __device__ __forceinline__ bool attn_split(const KA a, Smem& sm, int l, int b, i
   // and its page slot only ever meets p = 0 there.
   const bool has_new = newest >= p0 && newest < p1;
   const int kk_new = newest - tb0;
-  float* fresh = reinterpret_cast<float*>(sm.misc + 16);   // [0..7] its scores, [8..15] its p
+  float* fresh = reinterpret_cast<float*>(sm.misc + 16);   // [8..15]: its p per head
   const float* qkv_b = a->qkv + ((long)l * a->B + b) * (a->Hq + 2 * Hkv) * HD;
   auto page_of = [&](int t) -> int {
     int pg = bt_lds ? btl[t] : bt[t];
@@ -1259,7 +1259,7 @@ __device__ __forceinline__ bool attn_split(const KA a, Smem& sm, int l, int b, i
 #pragma unroll
           for (int e = 0; e < DL; ++e) t += qs[h * HD + lane + 64 * e] * kn[e];
           t = wave_sum(t);
-          if (lane == 0) fresh[h] = t * a->attn_scale;
+          if (lane == 0) sm.ys[h * SP + kk_new] = t * a->attn_scale;   // its slot of the score row
         }
       }
     }
@@ -1314,10 +1314,11 @@ __device__ __forceinline__ bool attn_split(const KA a, Smem& sm, int l, int b, i
             c = mfma_bf16(ql[k], kf[u][k], c);
           }
           const bool valid = kabs >= p0 && kabs < p1;
+          const bool mine = !(has_new && kk == kk_new);   // the new key's score comes from wave 0
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int h = 4 * q4 + r;
-            if (h < G) sc[h * SP + kk] = valid ? c[r] * a->attn_scale : -INFINITY;
+            if (h < G && mine) sc[h * SP + kk] = valid ? c[r] * a->attn_scale : -INFINITY;
           }
           if (i + ATT_PT < nti) {
             const int o = k_off(t + MK_CW * ATT_PT);
@@ -1332,30 +1333,75 @@ __device__ __forceinline__ bool attn_split(const KA a, Smem& sm, int l, int b, i
   if (a->trace && tid == 0 && sm.t_mark[0] == 0) sm.t_mark[0] = wall_clock64();
   // pass 2: per-head max, exponentials (as bf16 for the PV product) and sum
   float* ml = a->part_ml + ((((long)(l & 1) * a->B + b) * a->Hq + g * G) * a->max_splits) * 2;
+  // Each wave takes two heads at once (h and h + 4) and four keys per lane
+  // per pass, so the LDS reads of a pass are issued together; p = 2^((s - m)
+  // log2 e) on the hardware exp2.  The new key's p is kept in fp32 for its
+  // own P V term and zeroed in the MFMA operands.
   const int nk = 16 * nt, nk2 = 32 * nks;
-  for (int h = wave; h < G; h += MK_WAVES) {
-    const float fs = has_new ? fresh[h] : 0.f;
-    float mx = -INFINITY;
-    for (int kk = lane; kk < nk; kk += 64) mx = fmaxf(mx, (has_new && kk == kk_new) ? fs : sc[h * SP + kk]);
-    mx = wave_max(mx);
-    float sum = 0.f;
-    for (int kk = lane; kk < nk2; kk += 64) {
-      const bool isnew = has_new && kk == kk_new;
-      const float pj = kk < nk ? expf((isnew ? fs : sc[h * SP + kk]) - mx) : 0.f;
-      uint16_t ph = f_to_bf16(pj), pl = f_to_bf16(pj - bf16_to_f(ph));
-      if (isnew) {
-        fresh[8 + h] = pj;
-        ph = 0;
-        pl = 0;
+  constexpr float L2E = 1.4426950408889634f;
+  for (int h0 = wave; h0 < G; h0 += 2 * MK_WAVES) {
+    const int h1 = h0 + MK_WAVES;
+    const bool two = h1 < G;
+    const int hb = two ? h1 : h0;
+    float m0 = -INFINITY, m1 = -INFINITY;
+    for (int base = 0; base < nk; base += 256) {
+      float v0[4], v1[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int kk = base + lane + 64 * u;
+        v0[u] = kk < nk ? sc[h0 * SP + kk] : -INFINITY;
+        v1[u] = kk < nk ? sc[hb * SP + kk] : -INFINITY;
       }
-      pbh[h * SP + kk] = ph;
-      pbl[h * SP + kk] = pl;
-      sum += pj;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        m0 = fmaxf(m0, v0[u]);
+        m1 = fmaxf(m1, v1[u]);
+      }
     }
-    sum = wave_sum(sum);
+    m0 = wave_max(m0);
+    m1 = wave_max(m1);
+    float s0 = 0.f, s1 = 0.f;
+    for (int base = 0; base < nk2; base += 256) {
+      float v0[4], v1[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int kk = base + lane + 64 * u;
+        v0[u] = kk < nk ? sc[h0 * SP + kk] : -INFINITY;
+        v1[u] = kk < nk ? sc[hb * SP + kk] : -INFINITY;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int kk = base + lane + 64 * u;
+        if (kk < nk2) {
+          const bool isnew = has_new && kk == kk_new;
+          const float pa = __builtin_amdgcn_exp2f((v0[u] - m0) * L2E);
+          const float pb = __builtin_amdgcn_exp2f((v1[u] - m1) * L2E);
+          const uint16_t ha = f_to_bf16(pa), hbv = f_to_bf16(pb);
+          const uint16_t la = f_to_bf16(pa - bf16_to_f(ha)), lb = f_to_bf16(pb - bf16_to_f(hbv));
+          pbh[h0 * SP + kk] = isnew ? (uint16_t)0 : ha;
+          pbl[h0 * SP + kk] = isnew ? (uint16_t)0 : la;
+          if (two) {
+            pbh[h1 * SP + kk] = isnew ? (uint16_t)0 : hbv;
+            pbl[h1 * SP + kk] = isnew ? (uint16_t)0 : lb;
+          }
+          if (isnew) {
+            fresh[8 + h0] = pa;
+            if (two) fresh[8 + h1] = pb;
+          }
+          s0 += pa;
+          s1 += pb;
+        }
+      }
+    }
+    s0 = wave_sum(s0);
+    s1 = wave_sum(s1);
     if (lane == 0) {
-      stc(ml + ((long)h * a->max_splits + s) * 2 + 0, mx);
-      stc(ml + ((long)h * a->max_splits + s) * 2 + 1, sum);
+      stc(ml + ((long)h0 * a->max_splits + s) * 2 + 0, m0);
+      stc(ml + ((long)h0 * a->max_splits + s) * 2 + 1, s0);
+      if (two) {
+        stc(ml + ((long)h1 * a->max_splits + s) * 2 + 0, m1);
+        stc(ml + ((long)h1 * a->max_splits + s) * 2 + 1, s1);
+      }
     }
   }
   __syncthreads();
