@@ -986,7 +986,10 @@ __device__ __forceinline__ void epi_qkv(const KA a, Smem& sm, const mk_task& t, 
       const bool isk = head < a->Hq + a->Hkv;
       const int kvh = isk ? head - a->Hq : head - a->Hq - a->Hkv;
       const int blk = pos / a->page;
-      const int page = (blk >= 0 && blk < a->max_blocks) ? a->block_tables[b * a->max_blocks + blk] : -1;
+      const bool bt_lds = a->B * a->max_blocks <= MK_LDS_BT;   // the step's block table is in LDS
+      const int page = (blk >= 0 && blk < a->max_blocks)
+                           ? (bt_lds ? sh_bt[b * a->max_blocks + blk] : a->block_tables[b * a->max_blocks + blk])
+                           : -1;
       if (page < 0 || page >= a->num_pages || pos < 0) {
         report(a, MK_E_DEVICE, ti, -2, page, a->num_pages);
         continue;
