@@ -71,6 +71,18 @@ def test_moe30b_shape_bs8_ragged_with_swap():
     assert rep.rows == 32
 
 
+@pytest.mark.parametrize("batch,n_wg", [(8, 12), (8, 40), (1, 16)])
+def test_few_workgroups(batch, n_wg):
+    # few workgroups: many attention splits and MoE items per claimer, and the
+    # shared combine capped below one share per head (n_wg 12 and 40 at 8
+    # sequences x 4 KV groups: 1 and 2 shares; 16 at one sequence: 4 shares
+    # of 2 heads), so the spinning shares and the cap run on the device
+    wl = W.Workload(f"moe30b-shape-b{batch}-{n_wg}wg", MOE_SMALL, batch=batch, ctx="loguniform:200:900",
+                    steps=2, seed=17 + n_wg)
+    eng = _engine(wl, opts=mk.make_opts(n_workgroups=n_wg))
+    run_teacher_forced(eng, 2).check()
+
+
 def test_sliding_window_layers():
     wl = W.Workload("moe30b-swa-ctx300", SWA_SMALL, batch=1, ctx="fixed:300", steps=2, seed=14)
     eng = _engine(wl)
