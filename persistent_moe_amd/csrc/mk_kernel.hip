@@ -338,13 +338,22 @@ __device__ __forceinline__ int wg_claim(const KA a, Smem& sm, int qidx) {
 // Claimer item order: claimer c of a wave owns item c of the queue; items
 // past the number of claimers are pulled one at a time from the atomic queue
 // head.  Returns -1 when the queue is exhausted.  Every thread must call it.
-__device__ __forceinline__ int next_item(const KA a, Smem& sm, const mk_task& t, int n_items, int qidx, bool& first) {
+// pre: a queue position claimed ahead (when the claimer started), or -1.
+__device__ __forceinline__ int next_item(const KA a, Smem& sm, const mk_task& t, int n_items, int qidx, bool& first,
+                                         int& pre) {
   if (first) {
     first = false;
     if (t.n0 < n_items) return t.n0;
   }
   if (n_items <= t.n1) return -1;
-  const int it = t.n1 + wg_claim(a, sm, qidx);
+  int c;
+  if (pre >= 0) {
+    c = pre;
+    pre = -1;
+  } else {
+    c = wg_claim(a, sm, qidx);
+  }
+  const int it = t.n1 + c;
   return it < n_items ? it : -1;
 }
 
@@ -1592,6 +1601,7 @@ extern "C" __global__ void __launch_bounds__(MK_THREADS, 1) mk_persistent(mk_kar
   const int kend = ((GLOBAL const int32_t*)a_arg.wg_range)[2 * blockIdx.x + 1];
   int k = kbeg;
   bool claiming = false, first = false, aborted = false;
+  int preclaim = -1;   // a MoE queue position claimed when the claimer started
   int n_items = 0, qidx = -1, attn_wait = -1, ti = 0;
   uint64_t t_start = 0;
   mk_task t;
@@ -1648,6 +1658,7 @@ extern "C" __global__ void __launch_bounds__(MK_THREADS, 1) mk_persistent(mk_kar
       }
       if (is_claimer(t.op)) {
         const int l = t.layer;
+        preclaim = -1;
         if (aborted) {
           n_items = 0;
         } else if (t.op == MK_OP_ATTN_DRAIN) {
@@ -1674,10 +1685,19 @@ extern "C" __global__ void __launch_bounds__(MK_THREADS, 1) mk_persistent(mk_kar
             const int32_t* meta = a->moe + (long)l * a->moe_stride;
             int* recs = reinterpret_cast<int*>(sm.red);
             const int nrec = min(a->bk, RED_FLOATS / 16) * 16;
+            qidx = layer_ctr(a, l, t.op == MK_OP_MOE_UPGATE_ACT_DRAIN ? MK_CTR_QUG : MK_CTR_QDN);
             for (int i = tid; i < nrec; i += MK_THREADS) recs[i] = ldc(meta + 4 + a->bk + i);
-            if (tid == 0) sm.misc[2] = ldc(meta + (t.op == MK_OP_MOE_UPGATE_ACT_DRAIN ? 1 : 2));
+            if (tid == 0) {
+              sm.misc[2] = ldc(meta + (t.op == MK_OP_MOE_UPGATE_ACT_DRAIN ? 1 : 2));
+              // a claimer with no item of its own claims its first queue
+              // position now, in the same round trip as the records
+              sm.misc[3] = t.n0 == INT32_MAX
+                               ? __hip_atomic_fetch_add(ctrp(a, qidx), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                               : -1;
+            }
             __syncthreads();
             n_items = __builtin_amdgcn_readfirstlane(sm.misc[2]);
+            preclaim = __builtin_amdgcn_readfirstlane(sm.misc[3]);
           }
           qidx = layer_ctr(a, l, t.op == MK_OP_MOE_UPGATE_ACT_DRAIN ? MK_CTR_QUG : MK_CTR_QDN);
         }
@@ -1686,7 +1706,7 @@ extern "C" __global__ void __launch_bounds__(MK_THREADS, 1) mk_persistent(mk_kar
       }
     }
     if (claiming) {
-      item = next_item(a, sm, t, n_items, qidx, first);
+      item = next_item(a, sm, t, n_items, qidx, first, preclaim);
       if (item < 0) {
         claiming = false;
         wg_signal(a, aborted ? -1 : t.signal_ctr, 1);
