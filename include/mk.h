@@ -199,7 +199,8 @@ typedef struct mk_sched_opts {
  * tile to finish (one more counter hop per layer).                        */
 #define MK_SCHED_SEPARATE_TOPK 4
 /* Emit ATTN_COMBINE as its own task per (sequence, KV group) instead of
- * running it in the last attention split of that group to finish.         */
+ * sharing it among the last attention splits of that group to finish (one
+ * share of the group's query heads each; both give the same bits).        */
 #define MK_SCHED_SEPARATE_COMBINE 8
 /* Claimer c of a MoE up-gate or down queue owns item c in advance (one
  * fewer atomic per workgroup).  By default every MoE item is pulled from its
