@@ -1187,8 +1187,11 @@ __device__ __forceinline__ bool attn_split(const KA a, Smem& sm, int l, int b, i
   const int kk_new = newest - tb0;
   float* fresh = reinterpret_cast<float*>(sm.misc + 16);   // [8..15]: its p per head
   const float* qkv_b = a->qkv + ((long)l * a->B + b) * (a->Hq + 2 * Hkv) * HD;
+  // the split's page ids in LDS (loaded by wave 0 while it waits for q),
+  // for the K and V loads inside the passes
+  int* spg = reinterpret_cast<int*>(sm.xs + G * HD);
   auto page_of = [&](int t) -> int {
-    int pg = bt_lds ? btl[t] : bt[t];
+    int pg = spg[t];
     if (pg < 0 || pg >= a->num_pages) {
       report(a, MK_E_DEVICE, ti, -3, pg, a->num_pages);
       pg = 0;
@@ -1249,11 +1252,22 @@ __device__ __forceinline__ bool attn_split(const KA a, Smem& sm, int l, int b, i
   // wait for the QKV tiles, then wave 0 stages q of the group's heads
   float* qs = sm.xs;   // [G][HD]
   if (tid < 64) {
+    // page ids of the split's key tiles (at most 2 per lane for a split of
+    // up to 1024 keys + 2 tiles), in flight during the wait
+    int pid[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int t = lane + 64 * u;
+      pid[u] = t < nt ? (bt_lds ? btl[t] : bt[t]) : 0;
+    }
     int ok = 1;
     if (lane == 0) {
       ok = (wait_idx < 0 || wait_target <= 0) ? 1 : (int)spin_until(a, wait_idx, wait_target, ti);
       if (a->trace && sm.t_ready == 0) sm.t_ready = wall_clock64();
     }
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      if (lane + 64 * u < nt) spg[lane + 64 * u] = pid[u];
     ok = __builtin_amdgcn_readfirstlane(ok);
     if (lane == 0) sm.misc[0] = ok;
     if (ok) {
