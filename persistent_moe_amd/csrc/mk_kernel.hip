@@ -1220,18 +1220,21 @@ __device__ __forceinline__ bool attn_split(const KA a, Smem& sm, int l, int b, i
       vpg[u] = (u < nks && tt < nt) ? (bt_lds ? btl[tt] : bt[tt]) : -1;
     }
     if (a->trace && tid == 64 && sm.t_mark[9] == 0) sm.t_mark[9] = kpg[0] + vpg[0] >= -2 ? wall_clock64() : 1;
+    // Every load of the K and V windows is issued unconditionally (a slot
+    // past the split reads the start of the pool, whose values are finite,
+    // and is masked where it is used), so the compiler can count the loads
+    // in flight and each MFMA waits only for its own operands.
 #pragma unroll
-    for (int u = 0; u < ATT_PT; ++u)
-      if (u < nti) {
-        int pg = kpg[u];
-        if (pg < 0 || pg >= a->num_pages) {
-          report(a, MK_E_DEVICE, ti, -3, pg, a->num_pages);
-          pg = 0;
-        }
-        const int o = (pg * Hkv + g) * 16 * HD + c16 * 32 + 8 * q4;
-#pragma unroll
-        for (int k = 0; k < KS; ++k) kf[u][k] = ldg_nt(Kp + o + 512 * k);
+    for (int u = 0; u < ATT_PT; ++u) {
+      int pg = kpg[u];
+      if (u < nti && (pg < 0 || pg >= a->num_pages)) {
+        report(a, MK_E_DEVICE, ti, -3, pg, a->num_pages);
+        pg = 0;
       }
+      const int o = u < nti ? (pg * Hkv + g) * 16 * HD + c16 * 32 + 8 * q4 : 0;
+#pragma unroll
+      for (int k = 0; k < KS; ++k) kf[u][k] = ldg_nt(Kp + o + 512 * k);
+    }
 #pragma unroll
     for (int u = 0; u < ATT_PV; ++u) {
       int pg = vpg[u];
@@ -1243,7 +1246,7 @@ __device__ __forceinline__ bool attn_split(const KA a, Smem& sm, int l, int b, i
 #pragma unroll
       for (int j = 0; j < DTW; ++j) {
         const int dt = cw + MK_CW * j;
-        vf[u][j] = (o >= 0 && dt < NDT) ? ldg_nt(Vp + o + 256 * dt) : (u32x4){0u, 0u, 0u, 0u};
+        vf[u][j] = ldg_nt(Vp + ((o >= 0 && dt < NDT) ? o + 256 * dt : 0));
       }
     }
     if (a->trace && tid == 64 && sm.t_mark[5] == 0) sm.t_mark[5] = wall_clock64();   // loads issued
@@ -1330,28 +1333,24 @@ __device__ __forceinline__ bool attn_split(const KA a, Smem& sm, int l, int b, i
 #pragma unroll
       for (int u = 0; u < ATT_PT; ++u) {
         const int i = i0 + u;
-        if (i < nti) {
-          const int t = cw + MK_CW * i;
-          const int kk = 16 * t + c16, kabs = tb0 + kk;
-          f32x4 c = (f32x4){0.f, 0.f, 0.f, 0.f};
+        const int t = cw + MK_CW * i;
+        const int kk = 16 * t + c16, kabs = tb0 + kk;
+        f32x4 c = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int k = 0; k < KS; ++k) {
-            c = mfma_bf16(qh[k], kf[u][k], c);
-            c = mfma_bf16(ql[k], kf[u][k], c);
-          }
-          const bool valid = kabs >= p0 && kabs < p1;
-          const bool mine = !(has_new && kk == kk_new);   // the new key's score comes from wave 0
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int h = 4 * q4 + r;
-            if (h < G && mine) sc[h * SP + kk] = valid ? c[r] * a->attn_scale : -INFINITY;
-          }
-          if (i + ATT_PT < nti) {
-            const int o = k_off(t + MK_CW * ATT_PT);
-#pragma unroll
-            for (int k = 0; k < KS; ++k) kf[u][k] = ldg_nt(Kp + o + 512 * k);
-          }
+        for (int k = 0; k < KS; ++k) {
+          c = mfma_bf16(qh[k], kf[u][k], c);
+          c = mfma_bf16(ql[k], kf[u][k], c);
         }
+        const bool valid = kabs >= p0 && kabs < p1;
+        const bool mine = i < nti && !(has_new && kk == kk_new);   // the new key's score comes from wave 0
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int h = 4 * q4 + r;
+          if (h < G && mine) sc[h * SP + kk] = valid ? c[r] * a->attn_scale : -INFINITY;
+        }
+        const int o = i + ATT_PT < nti ? k_off(t + MK_CW * ATT_PT) : 0;
+#pragma unroll
+        for (int k = 0; k < KS; ++k) kf[u][k] = ldg_nt(Kp + o + 512 * k);
       }
     }
   }
@@ -1442,24 +1441,23 @@ __device__ __forceinline__ bool attn_split(const KA a, Smem& sm, int l, int b, i
 #pragma unroll
       for (int u = 0; u < ATT_PV; ++u) {
         const int ks = ks0 + u;
-        if (ks < nks) {
-          // keys outside [p0, p1) and the new key have p = 0 here; their V
-          // values are finite pool contents (earlier keys of the sequence, an
-          // older value of the slot, or the initialised pool)
-          const int po_ = c16 * SP + 32 * ks + 8 * q4;
-          const u32x4 ph = c16 < G ? *reinterpret_cast<const u32x4*>(pbh + po_) : (u32x4){0u, 0u, 0u, 0u};
-          const u32x4 pl = c16 < G ? *reinterpret_cast<const u32x4*>(pbl + po_) : (u32x4){0u, 0u, 0u, 0u};
-          const int onext = ks + ATT_PV < nks ? v_off(ks + ATT_PV) : -1;
+        // keys outside [p0, p1), the new key and k-steps past the split have
+        // p = 0 here; their V values are finite pool contents (earlier keys
+        // of the sequence, an older value of the slot, or the initialised
+        // pool).  A dim tile past the head (the last wave's third) is
+        // computed on such values and never stored.
+        const int po_ = c16 * SP + 32 * ks + 8 * q4;
+        const bool pk = ks < nks && c16 < G;
+        const u32x4 ph = pk ? *reinterpret_cast<const u32x4*>(pbh + po_) : (u32x4){0u, 0u, 0u, 0u};
+        const u32x4 pl = pk ? *reinterpret_cast<const u32x4*>(pbl + po_) : (u32x4){0u, 0u, 0u, 0u};
+        const int onext = ks + ATT_PV < nks ? v_off(ks + ATT_PV) : -1;
 #pragma unroll
-          for (int j = 0; j < DTW; ++j) {
-            const int dt = cw + MK_CW * j;
-            if (dt < NDT) {
-              const u32x4 v = vf[u][j];
-              o[j] = mfma_bf16(ph, v, o[j]);
-              o[j] = mfma_bf16(pl, v, o[j]);
-              if (ks + ATT_PV < nks) vf[u][j] = onext >= 0 ? ldg_nt(Vp + onext + 256 * dt) : (u32x4){0u, 0u, 0u, 0u};
-            }
-          }
+        for (int j = 0; j < DTW; ++j) {
+          const int dt = cw + MK_CW * j;
+          const u32x4 v = vf[u][j];
+          o[j] = mfma_bf16(ph, v, o[j]);
+          o[j] = mfma_bf16(pl, v, o[j]);
+          vf[u][j] = ldg_nt(Vp + ((onext >= 0 && dt < NDT) ? onext + 256 * dt : 0));
         }
       }
     }
