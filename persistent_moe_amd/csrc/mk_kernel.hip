@@ -81,6 +81,8 @@ struct __attribute__((aligned(16))) Smem {
   mk_task tq[2];      // this task's descriptor and the next one (prefetched)
   uint64_t t_ready;   // trace: when the task's first wait was satisfied
   uint64_t t_mark[10]; // trace: [0] staged, [1] computed, [2] stores acknowledged, [3..9] free marks
+  int seen_idx;       // the counter of the last wg_wait this workgroup saw satisfied, and its target
+  int seen_val;
 };
 
 // ------------------------------------------------------------------ helpers
@@ -283,9 +285,13 @@ __device__ __forceinline__ bool spin_until(const KA a, int idx, int target, int 
       // transaction on a line that up to every CU is reading
       for (int k = 0; k < backoff; ++k) __builtin_amdgcn_s_sleep(3);
       if (backoff < 8) backoff <<= 1;
-      if (ld_agent(p) >= target) break;
-      if (ld_agent(ctrp(a, MK_CG_ABORT))) return false;
-      if (wall_clock64() - t0 > a->timeout_ticks) {
+      // the clock read and both loads are in flight together: a poll costs
+      // one round trip
+      const uint64_t now = wall_clock64();
+      const int v = ld_agent(p), ab = ld_agent(ctrp(a, MK_CG_ABORT));
+      if (v >= target) break;
+      if (ab) return false;
+      if (now - t0 > a->timeout_ticks) {
         report(a, MK_E_TIMEOUT, task, idx, ld_agent(p), target);
         __hip_atomic_store(ctrp(a, MK_CG_ABORT), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         return false;
@@ -295,10 +301,21 @@ __device__ __forceinline__ bool spin_until(const KA a, int idx, int target, int 
   return true;
 }
 
-// Workgroup-wide wait; every thread must call it.  Uses misc[0].
+// Workgroup-wide wait; every thread must call it.  Uses misc[0].  Counters
+// only grow during a launch, so a wait on the counter this workgroup last saw
+// satisfied, for no more than it saw, costs no poll (the down drain and the
+// next norm wait on the routing counter the up-gate drain already saw).
 __device__ __forceinline__ bool wg_wait(const KA a, Smem& sm, int idx, int target, int task) {
   if (tid_v() == 0) {
-    sm.misc[0] = (idx < 0 || target <= 0) ? 1 : (int)spin_until(a, idx, target, task);
+    int ok = 1;
+    if (idx >= 0 && target > 0 && !(sm.seen_idx == idx && sm.seen_val >= target)) {
+      ok = (int)spin_until(a, idx, target, task);
+      if (ok) {
+        sm.seen_idx = idx;
+        sm.seen_val = target;
+      }
+    }
+    sm.misc[0] = ok;
     if (a->trace && sm.t_ready == 0) sm.t_ready = wall_clock64();
   }
   __syncthreads();
@@ -327,9 +344,12 @@ __device__ __forceinline__ void wg_signal(const KA a, int idx, int inc) {
 __device__ __forceinline__ int wg_claim(const KA a, Smem& sm, int qidx) {
   __syncthreads();
   if (tid_v() == 0) {
-    sm.misc[1] = ld_agent(ctrp(a, MK_CG_ABORT))
-                     ? 0x3FFFFFFF
-                     : __hip_atomic_fetch_add(ctrp(a, qidx), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // the abort flag and the claim travel together (one round trip); a claim
+    // taken during an abort is discarded, and the step's counters are
+    // cleared before the next one
+    const int ab = ld_agent(ctrp(a, MK_CG_ABORT));
+    const int c = __hip_atomic_fetch_add(ctrp(a, qidx), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sm.misc[1] = ab ? 0x3FFFFFFF : c;
   }
   __syncthreads();
   return sm.misc[1];
@@ -1626,6 +1646,7 @@ extern "C" __global__ void __launch_bounds__(MK_THREADS, 1) mk_persistent(mk_kar
   u32x4 pre = (u32x4){0u, 0u, 0u, 0u};
   if (tid >= 64 && tid < 72 && k < kend)
     reinterpret_cast<u32x4*>(&sm.tq[0])[tid - 64] = load_task_piece(a_arg.tasks, k, tid - 64);
+  if (tid == 0) sm.seen_idx = -1;
   {   // step metadata into LDS (visible after the loop's first barrier)
     const int nw = a_arg.L * (int)(sizeof(mk_layer_dev) / 4);
     for (int i = tid; i < nw; i += MK_THREADS)
