@@ -244,14 +244,18 @@ __device__ __forceinline__ void stc(int32_t* p, int v) {
 __device__ __forceinline__ void stc(uint16_t* p, uint16_t v) {
   __hip_atomic_store((GLOBAL uint16_t*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-// 16-byte agent-coherent load at base + byte_off; base must be uniform.
+// 16-byte agent-coherent load at base + byte_off; base must be the same in
+// every lane (the lane's part goes in byte_off).  The base is moved to scalar
+// registers here: a descriptor the compiler cannot prove uniform is applied
+// one lane group at a time in a loop, and a load in such a loop waits for
+// the previous one.
 __device__ __forceinline__ u32x4 ldc16(const void* base, int byte_off) {
-  __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7FFFFFFF,
-                                                               0x00020000);
+  __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(uniform_ptr(base)), (short)0,
+                                                               0x7FFFFFFF, 0x00020000);
   return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 16 /* sc1 */);
 }
 __device__ __forceinline__ void stc16(void* base, int byte_off, u32x4 v) {
-  __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(base, (short)0, 0x7FFFFFFF, 0x00020000);
+  __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(base), (short)0, 0x7FFFFFFF, 0x00020000);
   __builtin_amdgcn_raw_buffer_store_b128(v, r, byte_off, 0, 16 /* sc1 */);
 }
 __device__ __forceinline__ f32x4 as_f4(u32x4 v) {
@@ -1294,15 +1298,33 @@ __device__ __forceinline__ bool attn_split(const KA a, Smem& sm, int l, int b, i
     ok = __builtin_amdgcn_readfirstlane(ok);
     if (lane == 0) sm.misc[0] = ok;
     if (ok) {
+      // q of the group's heads (G <= 8: at most HD / 32 pieces per lane) and
+      // the new key are loaded together, so staging costs one round trip; a
+      // piece past the group's q reads its first piece and is not stored
       const float* qb = qkv_b + (long)(g * G) * HD;
-      for (int i = lane; i < G * HD / 4; i += 64)
-        *reinterpret_cast<u32x4*>(qs + i * 4) = ldc16(qb, i * 16);
+      constexpr int QN = 8 * HD / 4 / 64;
+      const int nq = G * HD / 4;
+      u32x4 qv[QN];
+#pragma unroll
+      for (int u = 0; u < QN; ++u) {
+        const int i = lane + 64 * u;
+        qv[u] = ldc16(qb, (i < nq ? i : 0) * 16);
+      }
+      constexpr int DL = HD / 64;   // new-key dims per lane
+      float kn[DL];
+      if (has_new) {
+#pragma unroll
+        for (int e = 0; e < DL; ++e) kn[e] = ldc(qkv_b + (long)(a->Hq + g) * HD + lane + 64 * e);
+      }
+#pragma unroll
+      for (int u = 0; u < QN; ++u) {
+        const int i = lane + 64 * u;
+        if (i < nq) *reinterpret_cast<u32x4*>(qs + i * 4) = qv[u];
+      }
       if (has_new) {
         // scores of the new key: q . k with k rounded to bf16 like its page copy
-        constexpr int DL = HD / 64;   // dims per lane
-        float kn[DL];
 #pragma unroll
-        for (int e = 0; e < DL; ++e) kn[e] = bf16_to_f(f_to_bf16(ldc(qkv_b + (long)(a->Hq + g) * HD + lane + 64 * e)));
+        for (int e = 0; e < DL; ++e) kn[e] = bf16_to_f(f_to_bf16(kn[e]));
         for (int h = 0; h < G; ++h) {
           float t = 0.f;
 #pragma unroll
