@@ -215,6 +215,7 @@ __shared__ int sh_seq_lens[NBMAX], sh_positions[NBMAX], sh_tokens[NBMAX];
 // block tables too when they are small (batch x max_blocks <= MK_LDS_BT)
 #define MK_LDS_BT 2048
 __shared__ int sh_bt[MK_LDS_BT];
+__shared__ double sh_invf[64];   // RoPE inverse frequencies (head dim <= 128)
 #define LAYER_PTR(l, f) uniform_ptr(sh_layers[l].f)
 __device__ __forceinline__ int seq_len_u(int b) { return __builtin_amdgcn_readfirstlane(sh_seq_lens[b]); }
 __device__ __forceinline__ int position_u(int b) { return __builtin_amdgcn_readfirstlane(sh_positions[b]); }
@@ -1002,10 +1003,11 @@ __device__ __forceinline__ void epi_qkv(const KA a, Smem& sm, const mk_task& t, 
     float ya = sm.ys[(2 * p) * NBMAX + b], yb = sm.ys[(2 * p + 1) * NBMAX + b];
     const int pos = sh_positions[b];
     if (head < a->Hq + a->Hkv) {
-      // cos/sin of pos * theta^(-2i/hd), evaluated in double here rather than
-      // read from a table (a load would cost a memory round trip)
+      // cos/sin of pos * theta^(-2i/hd) (the inverse frequencies are in
+      // LDS), evaluated in double here rather than read from a table of
+      // angles (a load would cost a memory round trip)
       double sn, cs;
-      sincos((double)pos * ((GLOBAL const double*)a->inv_freq)[i], &sn, &cs);
+      sincos((double)pos * sh_invf[i], &sn, &cs);
       const float c = (float)cs, s_ = (float)sn;
       const float ra = ya * c - yb * s_;
       const float rb = yb * c + ya * s_;
@@ -1669,18 +1671,28 @@ extern "C" __global__ void __launch_bounds__(MK_THREADS, 1) mk_persistent(mk_kar
   if (tid >= 64 && tid < 72 && k < kend)
     reinterpret_cast<u32x4*>(&sm.tq[0])[tid - 64] = load_task_piece(a_arg.tasks, k, tid - 64);
   if (tid == 0) sm.seen_idx = -1;
-  {   // step metadata into LDS (visible after the loop's first barrier)
-    const int nw = a_arg.L * (int)(sizeof(mk_layer_dev) / 4);
-    for (int i = tid; i < nw; i += MK_THREADS)
-      reinterpret_cast<int*>(sh_layers)[i] = ((GLOBAL const int*)a_arg.layers)[i];
+  {   // step metadata into LDS (visible after the loop's first barrier);
+      // eight loads per thread are in flight at once
+    auto copy_in = [&](int* dst, GLOBAL const int* src, int n) {
+      for (int i0 = 0; i0 < n; i0 += 8 * MK_THREADS) {
+        int v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = src[min(i0 + u * MK_THREADS + tid, n - 1)];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (i0 + u * MK_THREADS + tid < n) dst[i0 + u * MK_THREADS + tid] = v[u];
+      }
+    };
+    copy_in(reinterpret_cast<int*>(sh_layers), (GLOBAL const int*)a_arg.layers,
+            a_arg.L * (int)(sizeof(mk_layer_dev) / 4));
+    const int nbt = a_arg.B * a_arg.max_blocks;
+    if (nbt <= MK_LDS_BT) copy_in(sh_bt, (GLOBAL const int*)a_arg.block_tables, nbt);
     if (tid < a_arg.B) {
       sh_seq_lens[tid] = ((GLOBAL const int*)a_arg.seq_lens)[tid];
       sh_positions[tid] = ((GLOBAL const int*)a_arg.positions)[tid];
       sh_tokens[tid] = ((GLOBAL const int*)a_arg.tokens)[tid];
     }
-    const int nbt = a_arg.B * a_arg.max_blocks;
-    if (nbt <= MK_LDS_BT)
-      for (int i = tid; i < nbt; i += MK_THREADS) sh_bt[i] = ((GLOBAL const int*)a_arg.block_tables)[i];
+    if (tid < a_arg.hd / 2) sh_invf[tid] = ((GLOBAL const double*)a_arg.inv_freq)[tid];
   }
   for (;;) {
     if (pending) {
@@ -1741,7 +1753,14 @@ extern "C" __global__ void __launch_bounds__(MK_THREADS, 1) mk_persistent(mk_kar
             int* recs = reinterpret_cast<int*>(sm.red);
             const int nrec = min(a->bk, RED_FLOATS / 16) * 16;
             qidx = layer_ctr(a, l, t.op == MK_OP_MOE_UPGATE_ACT_DRAIN ? MK_CTR_QUG : MK_CTR_QDN);
-            for (int i = tid; i < nrec; i += MK_THREADS) recs[i] = ldc(meta + 4 + a->bk + i);
+            for (int i0 = 0; i0 < nrec; i0 += 4 * MK_THREADS) {   // four loads per thread in flight
+              int v[4];
+#pragma unroll
+              for (int u = 0; u < 4; ++u) v[u] = ldc(meta + 4 + a->bk + min(i0 + u * MK_THREADS + tid, nrec - 1));
+#pragma unroll
+              for (int u = 0; u < 4; ++u)
+                if (i0 + u * MK_THREADS + tid < nrec) recs[i0 + u * MK_THREADS + tid] = v[u];
+            }
             if (tid == 0) {
               sm.misc[2] = ldc(meta + (t.op == MK_OP_MOE_UPGATE_ACT_DRAIN ? 1 : 2));
               // a claimer with no item of its own claims its first queue
