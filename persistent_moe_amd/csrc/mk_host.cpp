@@ -196,8 +196,11 @@ int build_plan(const mk_config* c, int B, int32_t max_blocks, const mk_sched_opt
   // (too few workgroups for two sets: the tuned placement)
   const bool part = o.wave_order == MK_ORDER_PARTITIONED && moe && !setA.empty() && !setM.empty();
   const int n_attn_wg = part ? (int)setA.size() : NW;
-  // attention split length: about one item per attention workgroup at the
-  // longest context
+  // attention split length: about one item per three attention workgroups
+  // at the longest context.  Longer splits mean fewer partials to combine and
+  // leave two thirds of the workgroups free for the MoE items; at 8K keys and
+  // bs=1, 384-key splits measured 341 tok/s against 330 for one item per
+  // workgroup (144 keys) and 310 for 128 keys.
   int S = o.attn_split;
   // scores of a split live in LDS as [G][S + 32] floats (a split that does
   // not start on a page boundary touches one extra 16-key tile, and the
@@ -206,9 +209,15 @@ int build_plan(const mk_config* c, int B, int32_t max_blocks, const mk_sched_opt
   if (S > 0) {
     if (S % c->page_size != 0 || S < MK_MIN_SPLIT || S > smax) return MK_E_INVAL;
   } else {
-    long want = (max_ctx * B * Hkv + n_attn_wg - 1) / n_attn_wg;
+    const long per = std::max(1, n_attn_wg / 3);
+    long want = (max_ctx * B * Hkv + per - 1) / per;
     want = std::max<long>(want, MK_MIN_SPLIT);
     want = (want + c->page_size - 1) / c->page_size * c->page_size;
+    // below the LDS cap, a whole number of QK passes: the kernel's three
+    // compute waves take four 16-key tiles each per pass (400 keys ran a
+    // third, almost empty pass and measured 334 tok/s against 341 for 384)
+    constexpr long kPassKeys = 16 * 3 * 4;
+    if (want < smax && want > kPassKeys) want = (want + kPassKeys / 2) / kPassKeys * kPassKeys;
     S = (int)std::min<long>(want, smax);
     S = std::max(S, MK_MIN_SPLIT);
   }
