@@ -213,12 +213,14 @@ int build_plan(const mk_config* c, int B, int32_t max_blocks, const mk_sched_opt
     long want = (max_ctx * B * Hkv + per - 1) / per;
     want = std::max<long>(want, MK_MIN_SPLIT);
     want = (want + c->page_size - 1) / c->page_size * c->page_size;
-    // below the LDS cap, a whole number of QK passes: the kernel's three
-    // compute waves take four 16-key tiles each per pass (400 keys ran a
-    // third, almost empty pass and measured 334 tok/s against 341 for 384)
+    // a whole number of QK passes: the kernel's three compute waves take four
+    // 16-key tiles each per pass (400 keys ran a third, almost empty pass and
+    // measured 334 tok/s against 341 for 384; at the LDS cap, 960 keys ran
+    // the 256K context at 216.7 tok/s against 212.3 for 992)
     constexpr long kPassKeys = 16 * 3 * 4;
-    if (want < smax && want > kPassKeys) want = (want + kPassKeys / 2) / kPassKeys * kPassKeys;
-    S = (int)std::min<long>(want, smax);
+    const long cap = smax >= kPassKeys ? smax / kPassKeys * kPassKeys : smax;
+    if (want < cap && want > kPassKeys) want = (want + kPassKeys / 2) / kPassKeys * kPassKeys;
+    S = (int)std::min<long>(want, cap);
     S = std::max(S, MK_MIN_SPLIT);
   }
   p.attn_split = S;
