@@ -60,16 +60,23 @@ enum mk_opcode {
   MK_OP_FFN_UPGATE_ACT = 3,       /* dense gate/up GEMV + SiLU-and-multiply   */
   MK_OP_FFN_DOWN = 4,             /* dense down projection                    */
   MK_OP_LM_HEAD = 5,              /* vocabulary GEMV into the caller's logits  */
-  MK_OP_ATTN_DECODE = 6,          /* one split of attention (a static task)   */
+  MK_OP_ATTN_DECODE = 6,          /* one split of attention (a static task;
+                                     emitted with MK_SCHED_STATIC_ATTN)       */
   MK_OP_ATTN_COMBINE = 7,         /* log-sum-exp merge of the splits          */
   MK_OP_ATTN_DRAIN = 8,           /* claimer: drains the split queue          */
   MK_OP_ROUTER_GEMM = 9,          /* router logits                            */
   MK_OP_ROUTER_TOPK = 10,         /* top-k + softmax-renormalised gates       */
   MK_OP_ROUTE_FINALIZE = 11,      /* expert histogram, rows, claim queues     */
-  MK_OP_MOE_GATHER = 12,          /* expert-sorted copy of the routed rows    */
+  MK_OP_MOE_GATHER = 12,          /* expert-sorted copy of the routed rows:
+                                     never a task of its own here; the up-gate
+                                     items read each routed row by token id  */
   MK_OP_MOE_UPGATE_ACT_DRAIN = 13,/* claimer: expert gate/up + SiLU-and-mul   */
   MK_OP_MOE_DOWN_DRAIN = 14,      /* claimer: expert down projection          */
-  MK_OP_MOE_COMBINE = 15,         /* gate-weighted sum of the expert outputs  */
+  MK_OP_MOE_COMBINE = 15,         /* gate-weighted sum of the expert outputs:
+                                     never a task of its own here; the next
+                                     ADD_RMSNORM adds the expert rows in top-k
+                                     order (a descriptor with opcode 12 or 15
+                                     reports MK_E_INVAL)                     */
   MK_NUM_OPCODES = 16
 };
 
@@ -198,6 +205,17 @@ typedef struct mk_sched_opts {
 /* Emit ROUTER_TOPK as its own task instead of running it in the last router
  * tile to finish (one more counter hop per layer).                        */
 #define MK_SCHED_SEPARATE_TOPK 4
+/* With MK_SCHED_SEPARATE_TOPK: emit ROUTE_FINALIZE as a task of its own
+ * after ROUTER_TOPK (one more hop) instead of running it inside the top-k
+ * task.                                                                   */
+#define MK_SCHED_SEPARATE_FINALIZE 64
+/* Static attention: one ATTN_DECODE task per (sequence, KV group, split) of
+ * the longest context the block tables allow, dealt round-robin like the
+ * GEMM tiles, plus one ATTN_COMBINE task per (sequence, group); splits past
+ * a sequence's live length return at once.  The default pulls splits from a
+ * claim queue sized by the live lengths (page 1 "Scheduling: mostly static,
+ * selectively dynamic": attention is one of the two dynamic task kinds).  */
+#define MK_SCHED_STATIC_ATTN 128
 /* Emit ATTN_COMBINE as its own task per (sequence, KV group) instead of
  * sharing it among the last attention splits of that group to finish (one
  * share of the group's query heads each; both give the same bits).        */
@@ -222,12 +240,26 @@ typedef struct mk_status {
 typedef struct mk_handle mk_handle;
 
 /* Bytes of device workspace needed for this model with block tables of
- * max_blocks_per_seq pages per sequence.  0 on an invalid config.         */
+ * max_blocks_per_seq pages per sequence.  0 on an invalid config.
+ * The pages give the engine as a shared library that a serving process loads
+ * and drives (page 2, "// Getting started": the server is started with the
+ * path of the built .so); the caller owns every device buffer, so it asks
+ * here how much scratch memory to allocate (descriptors, counters, claim
+ * queues, per-layer activations, attention partials, the error record).
+ * max_blocks_per_seq is the width of the block tables: it bounds the longest
+ * context, hence the attention partials and the task list, so it is fixed for
+ * the life of the handle (it is an argument of mk_init, not of
+ * mk_build_schedule).                                                     */
 size_t mk_workspace_size(const mk_config* cfg, int32_t max_blocks_per_seq);
 
 /* Validate the model, copy the weight and pool pointer tables, lay out the
- * caller's workspace (device, ws_bytes >= mk_workspace_size) and clear it.
- * Synchronous.  On success *out owns host state only.
+ * caller's workspace (device, ws_bytes >= mk_workspace_size, 256-byte
+ * aligned) and clear it.  The weights and KV pools are the caller's, read in
+ * place and never copied: weights are immutable for the life of the handle
+ * (page 3, the weight-prefetch paragraph: weights do not depend on the
+ * step's activations, which is what lets tasks stream them before their
+ * inputs are ready).  max_blocks_per_seq is fixed here (see
+ * mk_workspace_size).  Synchronous.  On success *out owns host state only.
  * Errors: INVAL (null/odd shape), UNSUPPORTED, NOMEM, HIP.                */
 int mk_init(const mk_config* cfg, const mk_weights* w, const mk_kv_pool* kv,
             void* workspace, size_t ws_bytes, int32_t max_blocks_per_seq,
@@ -236,8 +268,11 @@ int mk_init(const mk_config* cfg, const mk_weights* w, const mk_kv_pool* kv,
 /* Build the task list for a batch of `batch_size` slots and upload it to the
  * workspace (the host builds named waves per layer and deals task k to
  * workgroup k mod N: page 1 "Scheduling: mostly static, selectively
- * dynamic").  Call again when the batch shape changes.  Synchronous.
- * opt may be NULL for defaults.  Errors: INVAL, UNSUPPORTED, NOMEM, HIP.  */
+ * dynamic"; page 3, the schedule paragraph).  The schedule is fixed for a
+ * batch shape: call this again when the caller admits, evicts or resizes a
+ * batch, with the decode loop stopped (page 3, the paragraph on the price of
+ * a baked-in schedule).  Synchronous.  opt may be NULL for defaults.
+ * Errors: INVAL, UNSUPPORTED, NOMEM, HIP.                                 */
 int mk_build_schedule(mk_handle* h, int32_t batch_size, const mk_sched_opts* opt);
 
 /* Enqueue one decode step on `stream` (a hipStream_t; NULL = default).
@@ -257,7 +292,13 @@ int mk_decode_step(mk_handle* h, const int32_t* token_ids, const int32_t* positi
                    void* stream);
 
 /* Synchronise the handle's last stream, read and clear the device error
- * record.  st may be NULL.  Returns st->code.                             */
+ * record.  st may be NULL.  Returns st->code.  A persistent kernel has no
+ * kernel boundary at which a failure can surface (page 2, "// Overview":
+ * blocks stay resident for the whole step and wait on counters), so a
+ * failed wait or a bad input found on the device is latched in the
+ * workspace, every workgroup leaves the step, and the host reads it here.
+ * After MK_E_TIMEOUT the counters are cleared, so the next step starts
+ * clean.                                                                  */
 int mk_get_status(mk_handle* h, mk_status* st);
 
 /* Byte offset and size, inside the workspace, of a per-layer debug tap
@@ -294,7 +335,11 @@ int mk_plan_simulate(const mk_config* cfg, int32_t batch_size, int32_t max_block
                      const mk_sched_opts* opt, int32_t n_workgroups, const int32_t* seq_lens,
                      const int32_t* n_active_experts, int32_t* stuck_task);
 
+/* Free the handle's host state.  No device memory is touched or freed (the
+ * caller owns it all); call it after the last step has completed.  Part of
+ * the loaded-library life cycle (page 2, "// Getting started").          */
 void mk_destroy(mk_handle* h);
+/* A static string naming an MK_* code (never NULL).                       */
 const char* mk_strerror(int code);
 
 #ifdef __cplusplus

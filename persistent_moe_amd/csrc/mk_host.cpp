@@ -74,7 +74,7 @@ int validate_config(const mk_config* c) {
     if (c->ffn_inter > (c->max_batch >= 4 ? kMaxGemvK / 2 : kMaxGemvK)) return MK_E_UNSUPPORTED;
   }
   if ((size_t)c->max_batch * c->d_model > (size_t)kXsFloats) return MK_E_UNSUPPORTED;
-  if (c->d_model > 4096) return MK_E_UNSUPPORTED;   // the norm task holds 2 chunks of 4 per thread
+  if (c->d_model > 4096) return MK_E_UNSUPPORTED;   // the norm task holds 4 chunks of 4 per thread
   if (moe && c->expert_inter > (c->max_batch >= 4 ? kMaxGemvK / 2 : kMaxGemvK)) return MK_E_UNSUPPORTED;
   if (c->top_k > 8 || c->n_kv_heads > 8) return MK_E_UNSUPPORTED;
   const int gd = c->n_q_heads / c->n_kv_heads * c->head_dim;
@@ -296,7 +296,8 @@ int build_plan(const mk_config* c, int B, int32_t max_blocks, const mk_sched_opt
   };
   const std::vector<int>* onA = part ? &setA : nullptr;
   const std::vector<int>* onM = part ? &setM : nullptr;
-  const bool fuse_combine = !(o.flags & MK_SCHED_SEPARATE_COMBINE);
+  const bool static_attn = (o.flags & MK_SCHED_STATIC_ATTN) != 0;
+  const bool fuse_combine = !(o.flags & MK_SCHED_SEPARATE_COMBINE) && !static_attn;
   // the fused combine of a (sequence, group) is shared by its last ncomb
   // splits, one share of the G heads each; all but the last wait for the
   // rest, so at most (ncomb - 1) * B * Hkv workgroups wait at once, and one
@@ -335,6 +336,27 @@ int build_plan(const mk_config* c, int B, int32_t max_blocks, const mk_sched_opt
     };
     auto emit_attn = [&]() {
       wave();
+      if (static_attn) {
+        // one task per (sequence, group, split) of the longest visible
+        // context of this layer; splits past a live length return at once
+        const long vis = (c->swa_window > 0 && c->swa_period > 0 && l % c->swa_period != c->swa_period - 1)
+                             ? std::min<long>(max_ctx, c->swa_window)
+                             : max_ctx;
+        const int ns_max = ceil_div(vis, S);
+        for (int b = 0; b < B; ++b)
+          for (int g = 0; g < Hkv; ++g)
+            for (int sp = 0; sp < ns_max; ++sp) {
+              mk_task t = blank(MK_OP_ATTN_DECODE, l);
+              t.batch = b;
+              t.group = g;
+              t.split = sp;
+              t.wait_ctr = ctr_of(p.cl, l, MK_CTR_QKV);
+              t.wait_target = n_qkv;
+              t.signal_ctr = ctr_of(p.cl, l, p.cl.attn + b * Hkv + g);
+              place(t, onA, b * Hkv * ns_max + g * ns_max + sp);
+            }
+        return;
+      }
       const int nc = onA ? (int)onA->size() : n_claim;
       for (int i = 0; i < nc; ++i) {
         mk_task t = blank(MK_OP_ATTN_DRAIN, l);
@@ -399,12 +421,22 @@ int build_plan(const mk_config* c, int B, int32_t max_blocks, const mk_sched_opt
         }
         if (fuse_topk) return;
         wave();
+        const bool sep_fin = (o.flags & MK_SCHED_SEPARATE_FINALIZE) != 0;
         mk_task t = blank(MK_OP_ROUTER_TOPK, l);
-        t.flags |= MK_F_FUSE_FINALIZE;
+        if (!sep_fin) t.flags |= MK_F_FUSE_FINALIZE;
         t.wait_ctr = ctr_of(p.cl, l, MK_CTR_ROUTER);
         t.wait_target = n_r;
-        t.signal_ctr = cROUTE;
+        // top-k alone adds one more to the router counter, which the
+        // finalize task waits for
+        t.signal_ctr = sep_fin ? ctr_of(p.cl, l, MK_CTR_ROUTER) : cROUTE;
         place(t, onM, 0);
+        if (!sep_fin) return;
+        wave();
+        mk_task f = blank(MK_OP_ROUTE_FINALIZE, l);
+        f.wait_ctr = ctr_of(p.cl, l, MK_CTR_ROUTER);
+        f.wait_target = n_r + 1;
+        f.signal_ctr = cROUTE;
+        place(f, onM, 1);
       };
       const int n_moe_claim = onM ? (int)onM->size() : n_claim;
       const bool dyn_moe = (o.flags & MK_SCHED_STATIC_MOE) == 0;
@@ -654,7 +686,12 @@ int simulate(const mk_config* c, int B, const Plan& p, int NW, const int32_t* se
           }
           phase[w] = 0;
         }
-        if (t.signal_ctr >= 0) ctr[t.signal_ctr] += (t.op == MK_OP_ATTN_COMBINE ? G : 1);
+        if (t.op == MK_OP_ATTN_DECODE) {
+          // a split past the live length signals nothing
+          if (t.split < nspl(t.layer, t.batch)) ctr[t.signal_ctr] += 1;
+        } else if (t.signal_ctr >= 0) {
+          ctr[t.signal_ctr] += (t.op == MK_OP_ATTN_COMBINE ? G : 1);
+        }
         if ((t.flags & MK_F_FUSE_TOPK) && ctr[t.signal_ctr] == t.aux[0])
           ctr[ctr_of(p.cl, t.layer, MK_CTR_ROUTE)]++;   // the last router tile runs top-k
         cursor[w] += 1;

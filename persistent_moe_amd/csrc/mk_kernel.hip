@@ -1,7 +1,7 @@
 // mk_kernel.hip - the persistent decode megakernel for gfx950 (MI355X).
 //
 // One launch runs one decode step.  The grid holds one workgroup per CU
-// (256 threads = 4 wave64s, one per SIMD, ~130 KB of LDS so no second
+// (256 threads = 4 wave64s, one per SIMD, about 147 KB of LDS so no second
 // workgroup fits).  One wave per SIMD gives each wave the SIMD's whole
 // register file (256 VGPRs + 256 AGPRs), so the compiler spills into AGPRs
 // instead of scratch memory: a scratch reload is a vector-memory load, and
@@ -26,9 +26,10 @@
 // whole L2 of the XCD on every task, which measured 2-30 us per task here.)
 //
 // Weights are immutable during a step, so every GEMV tile issues the loads of
-// its first row group into registers *before* it waits on its activation
-// dependency (page 1, third gain of the megakernel: weight prefetch across
-// task boundaries).  Attention splits and MoE expert tiles are pulled from
+// its first two row groups (up to 96 KB per CU) into registers *before* it
+// waits on its activation dependency (page 1, third gain of the megakernel:
+// weights stream while the task's input is not ready yet); they are issued
+// when the workgroup reaches the task, not earlier.  Attention splits and MoE expert tiles are pulled from
 // claim queues whose head is an atomic counter (page 1, "Scheduling").
 
 #include <hip/hip_runtime.h>
@@ -2003,17 +2004,16 @@ extern "C" __global__ void __launch_bounds__(MK_THREADS, 1) mk_persistent(mk_kar
           break;
         }
         case MK_OP_ATTN_DECODE:
+          // a static split: one (sequence, group, split) of the longest
+          // context; one past the live length has nothing to do and
+          // signals nothing (the combine waits for the live splits only)
           if (t.split < n_splits(a, l, t.batch)) {
             if (!attn_item(a, sm, l, t.batch, t.group, t.split, ti, t.wait_ctr, t.wait_target)) {
               aborted = true;
               break;
             }
-          } else if (!wg_wait(a, sm, t.wait_ctr, t.wait_target, ti)) {
-            aborted = true;
-            break;
+            wg_signal(a, t.signal_ctr, 1);
           }
-          wg_signal(a, layer_ctr(a, l, a->cl.attn + t.batch * a->Hkv + t.group), 1);
-          wg_signal(a, t.signal_ctr, 1);
           break;
         case MK_OP_ATTN_COMBINE:
           if (!op_attn_combine(a, sm, t, ti)) aborted = true;

@@ -149,6 +149,8 @@ MK_SCHED_TRACE = 2
 MK_SCHED_SEPARATE_TOPK = 4
 MK_SCHED_SEPARATE_COMBINE = 8
 MK_SCHED_STATIC_MOE = 16
+MK_SCHED_SEPARATE_FINALIZE = 64
+MK_SCHED_STATIC_ATTN = 128
 
 
 def make_opts(wave_order="tuned", launch_mode="persistent", attn_split=0, n_workgroups=0,

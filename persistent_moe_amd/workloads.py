@@ -101,7 +101,7 @@ class Workload:
     name: str
     model: ModelConfig
     batch: int
-    ctx: str                   # "fixed:<n>" or "loguniform:<lo>:<hi>"
+    ctx: str                   # "fixed:<n>", "loguniform:<lo>:<hi>" or "list:<n0>,<n1>,..." (per sequence id)
     steps: int
     seed: int
     swap_every: int = 0        # continuous batching: replace one sequence every N steps
@@ -497,6 +497,9 @@ def context_length(wl: Workload, seq_id: int) -> int:
     kind, *args = wl.ctx.split(":")
     if kind == "fixed":
         return int(args[0])
+    if kind == "list":
+        vals = [int(v) for v in args[0].split(",")]
+        return vals[seq_id % len(vals)]
     if kind == "loguniform":
         lo, hi = float(args[0]), float(args[1])
         u = float(uniform_f64(tensor_key(wl.seed, "ctx_len", seq_id), 0, 1)[0])

@@ -102,8 +102,9 @@ def test_unsupported_shapes(lib):
     assert mk.mk_workspace_size(c, 8) == 0
 
 
-def _plan(model, B, max_blocks, nw=256, order="tuned", split=0):
-    return mk.mk_plan_schedule(_cfg(model, B), B, max_blocks, mk.make_opts(order, attn_split=split), nw)
+def _plan(model, B, max_blocks, nw=256, order="tuned", split=0, opts=None):
+    opts = opts if opts is not None else mk.make_opts(order, attn_split=split)
+    return mk.mk_plan_schedule(_cfg(model, B), B, max_blocks, opts, nw)
 
 
 @pytest.mark.parametrize("model,B,mb", [(W.TINY_MOE, 1, 5), (W.MOE_30B, 1, 529), (W.MOE_30B, 8, 1041),
@@ -203,7 +204,8 @@ def test_signal_counts_match_wait_targets(lib):
 
 
 @pytest.mark.parametrize("order", ["tuned", "interleaved", "attention_first", "partitioned", "tuned-separate-topk",
-                                   "tuned-separate-combine", "partitioned-separate-combine", "tuned-static-moe"])
+                                   "tuned-separate-combine", "partitioned-separate-combine", "tuned-static-moe",
+                                   "tuned-separate-finalize", "tuned-static-attn", "attention_first-static-attn"])
 @pytest.mark.parametrize("case", [
     ("tiny", W.TINY_MOE, 1, 5, [65], [2, 2]),
     ("moe30b", W.MOE_30B, 1, 529, [8193], [8] * 48),
@@ -216,7 +218,10 @@ def test_schedule_is_deadlock_free(lib, order, case):
     flags = mk.MK_SCHED_SEPARATE_TOPK if order.endswith("separate-topk") else 0
     flags |= mk.MK_SCHED_SEPARATE_COMBINE if order.endswith("separate-combine") else 0
     flags |= mk.MK_SCHED_STATIC_MOE if order.endswith("static-moe") else 0
-    base = order.replace("-separate-topk", "").replace("-separate-combine", "").replace("-static-moe", "")
+    if order.endswith("separate-finalize"):
+        flags |= mk.MK_SCHED_SEPARATE_TOPK | mk.MK_SCHED_SEPARATE_FINALIZE
+    flags |= mk.MK_SCHED_STATIC_ATTN if order.endswith("static-attn") else 0
+    base = order.split("-")[0]
     opts = mk.make_opts(base, flags=flags)
     for nw in (256, 64, 7):
         rc, stuck = mk.mk_plan_simulate(_cfg(model, B), B, mb, opts, nw, sl, na)
@@ -229,3 +234,25 @@ def test_simulator_detects_a_blocked_schedule(lib):
     assert rc == mk.MK_E_STATE and stuck == 0
     rc = mk.mk_plan_simulate(_cfg(W.TINY_MOE, 1), 2, 5, mk.make_opts(), 4, [65, 65], [2, 2])[0]
     assert rc == mk.MK_E_INVAL   # batch above the configured maximum
+
+
+def test_static_attention_and_separate_finalize_tasks(lib):
+    """The static-attention schedule emits one ATTN_DECODE per (sequence, group,
+    split) of the longest context and a combine per (sequence, group); the
+    separate-finalize schedule emits ROUTE_FINALIZE after ROUTER_TOPK."""
+    model, B, mb = W.MOE_30B, 2, 100      # 1600 keys at most
+    tasks, _ = _plan(model, B, mb, opts=mk.make_opts(flags=mk.MK_SCHED_STATIC_ATTN))
+    op = {n: i for i, n in enumerate(mk.OPCODES)}
+    dec = [t for t in tasks if t.op == op["ATTN_DECODE"] and t.layer == 0]
+    ns = max(t.split for t in dec) + 1
+    assert len(dec) == B * model.n_kv_heads * ns
+    assert {(t.batch, t.group) for t in dec} == {(b, g) for b in range(B) for g in range(model.n_kv_heads)}
+    comb = [t for t in tasks if t.op == op["ATTN_COMBINE"] and t.layer == 0]
+    assert len(comb) == B * model.n_kv_heads and all(t.wait_target == mk.MK_WAIT_SPLITS for t in comb)
+    assert not any(t.op == op["ATTN_DRAIN"] for t in tasks)
+    fl = mk.MK_SCHED_SEPARATE_TOPK | mk.MK_SCHED_SEPARATE_FINALIZE
+    tasks, _ = _plan(model, B, mb, opts=mk.make_opts(flags=fl))
+    top = [t for t in tasks if t.op == op["ROUTER_TOPK"] and t.layer == 3]
+    fin = [t for t in tasks if t.op == op["ROUTE_FINALIZE"] and t.layer == 3]
+    assert len(top) == 1 and len(fin) == 1 and not top[0].flags & 8
+    assert fin[0].wait_ctr == top[0].signal_ctr == top[0].wait_ctr and fin[0].wait_target == top[0].wait_target + 1

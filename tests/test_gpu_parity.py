@@ -106,7 +106,7 @@ def test_empty_slots_are_skipped():
     rep.check()
 
 
-def test_determinism_and_per_opcode_ablation_agree():
+def test_determinism_same_inputs_same_bits():
     wl = W.Workload("moe30b-shape-det", MOE_SMALL, batch=2, ctx="fixed:100", steps=2, seed=16)
     eng = _engine(wl)
     inp = eng.step_inputs()
@@ -115,19 +115,84 @@ def test_determinism_and_per_opcode_ablation_agree():
     b = eng.decode(inputs=inp).clone()       # same inputs again (rewrites the same KV slot)
     assert eng.status().code == 0
     assert torch.equal(a, b)
-    mk.mk_build_schedule(eng.h, wl.batch, mk.make_opts(launch_mode="per_opcode"))
-    c = eng.decode(inputs=inp).clone()
+
+
+# Every schedule the builder offers, each checked against the oracle
+# (teacher-forced, two steps) and, on its first step, bit for bit against the
+# tuned schedule: the same tiles in other placements, orders, task splits or
+# launches must give the same bits (the split length is the minimum for these
+# contexts in every order, so the attention partials are the same).
+SCHEDULES = [
+    ("tuned", {}),
+    ("interleaved", dict(wave_order="interleaved")),
+    ("attention_first", dict(wave_order="attention_first")),
+    ("partitioned", dict(wave_order="partitioned")),
+    ("per_opcode_launch", dict(launch_mode="per_opcode")),
+    ("separate_topk_finalize_combine", dict(flags=mk.MK_SCHED_SEPARATE_TOPK | mk.MK_SCHED_SEPARATE_FINALIZE
+                                            | mk.MK_SCHED_SEPARATE_COMBINE)),
+    ("static_attention", dict(flags=mk.MK_SCHED_STATIC_ATTN)),
+    ("static_moe", dict(flags=mk.MK_SCHED_STATIC_MOE)),
+]
+_SCHED_WL = W.Workload("moe30b-shape-sched", MOE_SMALL, batch=2, ctx="list:100,77", steps=2, seed=16)
+_sched_state = {}
+
+
+@pytest.mark.parametrize("name,kw", SCHEDULES, ids=[s[0] for s in SCHEDULES])
+def test_schedule_variant_matches_oracle(name, kw):
+    wl = _SCHED_WL
+    if "oracle" not in _sched_state:
+        _sched_state["oracle"] = O.Weights(wl, cache_limit=4 << 30)
+    eng = _engine(wl, opts=mk.make_opts(**kw))
+    first = eng.decode(inputs=eng.step_inputs()).clone()
     assert eng.status().code == 0
-    assert torch.equal(a, c)
-    # the same tiles in other placements and orders give the same bits (the
-    # attention split length is the minimum for this context in every order)
-    for order, flags in (("interleaved", 0), ("attention_first", 0), ("partitioned", 0),
-                         ("tuned", mk.MK_SCHED_SEPARATE_COMBINE | mk.MK_SCHED_SEPARATE_TOPK),
-                         ("tuned", mk.MK_SCHED_STATIC_MOE)):
-        mk.mk_build_schedule(eng.h, wl.batch, mk.make_opts(wave_order=order, flags=flags))
-        d = eng.decode(inputs=inp).clone()
-        assert eng.status().code == 0
-        assert torch.equal(a, d), order
+    if name == "tuned":
+        _sched_state["tuned"] = first
+    elif "tuned" in _sched_state:
+        assert torch.equal(first, _sched_state["tuned"]), name
+    eng.close()
+    eng = _engine(wl, opts=mk.make_opts(**kw))
+    run_teacher_forced(eng, 2, W_oracle=_sched_state["oracle"]).check()
+
+
+def test_moe30b_shape_bs8_long_ragged_contexts():
+    """8 sequences of up to 16,380 cached keys: the block table (B x max_blocks
+    > 2048 entries) is read from memory rather than LDS, and the attention
+    splits sit at their LDS cap (960 keys)."""
+    wl = W.Workload("moe30b-shape-bs8-16k", MOE_SMALL, batch=8,
+                    ctx="list:16380,9000,12001,700,15000,4000,16100,2048", steps=2, seed=21)
+    eng = _engine(wl)
+    assert wl.batch * eng.max_blocks > 2048
+    tasks, _ = mk.mk_plan_schedule(eng.mkcfg, 8, eng.max_blocks, mk.make_opts(flags=mk.MK_SCHED_STATIC_ATTN), 256)
+    ns = max(t.split for t in tasks if t.op == mk.OPCODES.index("ATTN_DECODE")) + 1
+    assert -(-eng.max_blocks * 16 // ns) > 900, ns        # splits of about 960 keys
+    run_teacher_forced(eng, 2, W_oracle=O.Weights(wl, cache_limit=8 << 30)).check()
+
+
+SWA_4L = W.ModelConfig(name="moe30b-swa4096-4l", n_layers=4, d_model=2048, n_q_heads=32, n_kv_heads=4,
+                       head_dim=128, vocab=2048, n_experts=128, top_k=8, expert_inter=768,
+                       swa_window=4096, swa_period=4)
+
+
+def test_sliding_window_4096_at_262k_context():
+    """Layers 0-2 see the 4096 most recent keys, layer 3 all 262,145: RoPE at
+    positions past 262K, hundreds of 960-key splits per KV group feeding the
+    combine, and the block table read from memory."""
+    wl = W.Workload("moe30b-swa-262k", SWA_4L, batch=1, ctx="fixed:262144", steps=2, seed=22)
+    eng = _engine(wl)
+    assert eng.max_blocks > 2048
+    rep = run_teacher_forced(eng, 2, W_oracle=O.Weights(wl, cache_limit=4 << 30))
+    rep.check()
+    assert rep.compared == 2
+
+
+def test_dense1b_full_16_layers_tied_vocab():
+    """The dense Llama-1B-shaped decoder at its real size: 16 sequential
+    pre-norm layers, head dim 64, the tied 128,256-row LM head, 4K context."""
+    wl = W.WORKLOADS["dense1b"]
+    eng = _engine(wl, steps=2)
+    rep = run_teacher_forced(eng, 2, W_oracle=O.Weights(wl, cache_limit=16 << 30))
+    rep.check()
+    assert rep.compared == 2
 
 
 def test_watchdog_reports_timeout_and_recovers():

@@ -145,3 +145,46 @@ def test_oracle_reproduces_golden_greedy_decode():
         assert g["fed_token"] == f[0] and g["argmax"] == r[0].token
         assert g["experts"] == [t.route.ids.tolist() for t in r[0].layers]
         assert np.allclose(g["logits_head"], r[0].logits[:8], rtol=0, atol=1e-12)
+
+
+def _cached_kv_mutant(shift_prefill=0, layer_fixed=None, shift_appended=0):
+    """cached_kv with a planted offset, layer or appended-index mistake."""
+    def fn(wl, seq, layer, p0, p1, keep=True):
+        cfg = wl.model
+        parts_k, parts_v = [], []
+        if p0 < seq.ctx0:
+            q1 = min(p1, seq.ctx0)
+            ly = layer if layer_fixed is None else layer_fixed
+            parts_k.append(O._f64(W.gen_kv(wl.seed, cfg, seq.seq_id, ly, "k", p0 + shift_prefill, q1 + shift_prefill)))
+            parts_v.append(O._f64(W.gen_kv(wl.seed, cfg, seq.seq_id, ly, "v", p0 + shift_prefill, q1 + shift_prefill)))
+        if p1 > seq.ctx0:
+            a0 = max(p0, seq.ctx0) - seq.ctx0 + shift_appended
+            a1 = p1 - seq.ctx0 + shift_appended
+            parts_k.append(np.stack(seq.appended_k[layer][a0:a1]))
+            parts_v.append(np.stack(seq.appended_v[layer][a0:a1]))
+        return np.concatenate(parts_k), np.concatenate(parts_v)
+    return fn
+
+
+@pytest.mark.parametrize("kw", [{"shift_prefill": 1}, {"shift_prefill": -1}, {"layer_fixed": 0},
+                                {"shift_appended": 1}, {"shift_appended": -1}],
+                         ids=["prefill+1", "prefill-1", "layer0", "appended+1", "appended-1"])
+def test_cache_pins_catch_offset_mistakes(monkeypatch, kw):
+    monkeypatch.setattr(O, "cached_kv", _cached_kv_mutant(**kw))
+    caught = 0
+    for pin in (lambda: P.test_cached_kv_prefill_rows_equal_generator_rows(13, 29),
+                lambda: P.test_cached_kv_prefill_rows_equal_generator_rows(1, 40),
+                P.test_cached_kv_straddles_prefill_and_appended_entries):
+        try:
+            pin()
+        except (AssertionError, ValueError, IndexError):
+            caught += 1
+    assert caught > 0, f"no pin caught the cache mutation {kw}"
+
+
+def test_tied_head_pin_catches_untied_stream(monkeypatch):
+    def rows(self, r0, r1):
+        return O._f64(W.gen_tensor(self.seed, "lm_head", (self.cfg.vocab, self.cfg.d_model), rows=slice(r0, r1)))
+    monkeypatch.setattr(O.Weights, "lm_head_rows", rows)
+    with pytest.raises(AssertionError):
+        P.test_tied_lm_head_rows_are_embedding_rows()

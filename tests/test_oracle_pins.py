@@ -7,6 +7,7 @@ in ``oracle/decode.py`` fails at least one of them.
 """
 import itertools
 import math
+from dataclasses import replace
 
 import numpy as np
 import pytest
@@ -363,3 +364,62 @@ def test_batch_rows_equal_single_sequence_runs():
         s1 = O.new_sequence(plan.slots[b][0][1].seq_id, plan.slots[b][0][1].ctx)
         r1 = O.decode_one(wl, Wt, s1, toks[b])
         assert np.array_equal(r1.logits, res[b].logits)
+
+
+# ------------------------------------------------------ cache and tied LM head
+# The oracle reads the pre-filled cache through ``cached_kv`` (a row offset
+# into the KV stream of the sequence and layer) and the tied LM head through
+# the embedding stream.  Both are pinned to whole-tensor draws of the
+# generator, sliced with numpy, so an offset, layer or stream mix-up fails.
+def _kv_rows(wl, seq_id, layer, which, ctx):
+    return W.gen_kv(wl.seed, wl.model, seq_id, layer, which, 0, ctx).float().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("p0,p1", [(0, 40), (13, 29), (39, 40), (0, 1), (17, 18)])
+def test_cached_kv_prefill_rows_equal_generator_rows(p0, p1):
+    wl = W.WORKLOADS["tiny"]
+    seq = O.new_sequence(3, 40)
+    for layer in (0, 1):
+        K, V = O.cached_kv(wl, seq, layer, p0, p1, keep=False)
+        assert np.array_equal(K, _kv_rows(wl, 3, layer, "k", 40)[p0:p1])
+        assert np.array_equal(V, _kv_rows(wl, 3, layer, "v", 40)[p0:p1])
+    # another layer, sequence or operand is another stream
+    K1, _ = O.cached_kv(wl, seq, 1, 0, 40, keep=False)
+    K0, V0 = O.cached_kv(wl, seq, 0, 0, 40, keep=False)
+    assert not np.array_equal(K0, K1) and not np.array_equal(K0, V0)
+    assert not np.array_equal(K0, O.cached_kv(wl, O.new_sequence(4, 40), 0, 0, 40, keep=False)[0])
+
+
+def test_cached_kv_straddles_prefill_and_appended_entries():
+    wl = W.WORKLOADS["tiny"]
+    cfg = wl.model
+    seq = O.new_sequence(5, 40)
+    app_k = [np.full((cfg.n_kv_heads, cfg.head_dim), 100.0 + i) for i in range(3)]
+    app_v = [np.full((cfg.n_kv_heads, cfg.head_dim), -100.0 - i) for i in range(3)]
+    seq.appended_k[1] = list(app_k)
+    seq.appended_v[1] = list(app_v)
+    seq.length = 43
+    gk, gv = _kv_rows(wl, 5, 1, "k", 40), _kv_rows(wl, 5, 1, "v", 40)
+    K, V = O.cached_kv(wl, seq, 1, 35, 43, keep=False)
+    assert np.array_equal(K, np.concatenate([gk[35:40], np.stack(app_k)]))
+    assert np.array_equal(V, np.concatenate([gv[35:40], np.stack(app_v)]))
+    K, V = O.cached_kv(wl, seq, 1, 41, 43, keep=False)
+    assert np.array_equal(K, np.stack(app_k[1:])) and np.array_equal(V, np.stack(app_v[1:]))
+    # the kept slice of one layer is not served to another range
+    K, _ = O.cached_kv(wl, seq, 1, 0, 10)
+    K2, _ = O.cached_kv(wl, seq, 1, 10, 20)
+    assert np.array_equal(K2, gk[10:20])
+
+
+def test_tied_lm_head_rows_are_embedding_rows():
+    cfg = W.ModelConfig(name="pin-tied", n_layers=1, d_model=64, n_q_heads=2, n_kv_heads=1, head_dim=64,
+                        vocab=300, ffn_inter=64, tied_embeddings=True, parallel_block=False)
+    wl = W.Workload("pin-tied", cfg, batch=1, ctx="fixed:4", steps=1, seed=9)
+    Wt = O.Weights(wl)
+    emb = W.gen_tensor(wl.seed, "embed", (cfg.vocab, cfg.d_model)).float().numpy().astype(np.float64)
+    for r0, r1 in ((0, 300), (17, 18), (250, 300)):
+        assert np.array_equal(Wt.lm_head_rows(r0, r1), emb[r0:r1])
+    assert np.array_equal(Wt.embed_row(123), emb[123])
+    # untied: the LM head is its own stream
+    wu = O.Weights(wl.with_(model=replace(cfg, tied_embeddings=False)))
+    assert not np.array_equal(wu.lm_head_rows(0, 300), emb)
