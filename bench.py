@@ -5,9 +5,12 @@ python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload moe30b]
 Times K greedy decode steps (after W untimed ones) of the 30B / 3.3B-active
 parallel-block MoE at batch 1 with an 8K-token pre-filled paged KV cache,
 random-init bf16 weights from the seeded generator.  Each step is one
-mk_decode_step launch (the whole decode step in one persistent kernel) plus
-the caller's greedy argmax and position update, all on one stream with no
-host synchronisation inside the timed region.  Prints one JSON line.
+mk_decode_step_sample launch: the whole decode step in one persistent kernel,
+with the greedy next token picked on the device after LM_HEAD and the slots
+advanced by the kernel, so the timed loop launches nothing else and never
+synchronises with the host.  Prints one JSON line, which also carries the
+batch-8 leg of the metric (the ragged continuous-batching workload) and the
+wave-order / one-launch-per-wave ablation.
 
 Reported next to the throughput:
 * roofline: speed-of-light bytes of every step (active weights read once, KV
@@ -69,6 +72,8 @@ def parse():
     ap.add_argument("--attn-split", type=int, default=0)
     ap.add_argument("--sched-flags", type=int, default=0, help="MK_SCHED_* bits for the schedule")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-bs8", action="store_true", help="skip the batch-8 leg of the metric")
+    ap.add_argument("--no-ablation", action="store_true", help="skip the wave-order / per-opcode ablation")
     ap.add_argument("--verbose", action="store_true")
     ap.add_argument("--trace", default="", help="after timing, trace one step and write a summary here")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -144,6 +149,93 @@ def cpu_baseline(wl, sample_layers: int = 4, lm_frac: int = 16, min_seconds: flo
     }
 
 
+def time_steps(eng, n_warm: int, n_steps: int, route_log_every: bool = True):
+    """Warm up, then time n_steps decode steps enqueued back to back.
+
+    Each step is one mk_decode_step_sample launch with greedy sampling and
+    MK_SAMPLE_ADVANCE: the kernel picks the next token after LM_HEAD and
+    advances the slots' tokens, positions and lengths itself, so the loop
+    runs no other kernel and needs no host synchronisation.  Returns the
+    wall time of the timed steps, the per-launch event times (ms) on the
+    launch stream, the positions before the first timed step and the routed
+    expert ids of every timed step (batch > 1), for the exact byte count.
+    """
+    import torch
+
+    from persistent_moe_amd import mk
+
+    wl, cfg, B = eng.wl, eng.cfg, eng.wl.batch
+    stream = torch.cuda.current_stream()
+    tok, pos, sl = eng.step_inputs()
+    nxt = torch.zeros(B, dtype=torch.int32, device=eng.dev)
+    smp = mk.make_sampling(0.0, advance=True)
+    ids_tap = eng.tap("topk_ids") if cfg.is_moe else None
+    L, K = cfg.n_layers, max(cfg.top_k, 1)
+    route_log = (torch.zeros((n_steps, L * B * K), dtype=torch.int32, device=eng.dev)
+                 if cfg.is_moe and B > 1 and route_log_every else None)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_steps)]
+
+    def launch():
+        mk.mk_decode_step_sample(eng.h, tok.data_ptr(), pos.data_ptr(), eng.block_tables.data_ptr(),
+                                 sl.data_ptr(), eng.logits.data_ptr(), smp, nxt.data_ptr(), stream.cuda_stream)
+
+    for _ in range(n_warm):
+        launch()
+    torch.cuda.synchronize()
+    st = eng.status()
+    if st.code != 0:
+        raise SystemExit(f"device error during warmup: {mk.strerror(st.code)} task {st.task}")
+    pos0 = pos.cpu().numpy().copy()
+    t0 = time.perf_counter()
+    for i in range(n_steps):
+        ev[i][0].record(stream)
+        launch()
+        ev[i][1].record(stream)
+        if route_log is not None:
+            route_log[i].copy_(ids_tap[:L * B * K])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    st = eng.status()
+    if st.code != 0:
+        raise SystemExit(f"device error: {mk.strerror(st.code)} task {st.task} counter {st.counter}")
+    eng.slot_len = [int(v) for v in sl.cpu().numpy() - 1]   # the kernel advanced the slots
+    eng.slot_tok = [int(v) for v in tok.cpu().numpy()]
+    kern = [a.elapsed_time(b) for a, b in ev]
+    return wall, kern, pos0, (route_log.cpu().numpy() if route_log is not None else None)
+
+
+def step_metrics(cfg, B, wall, kern, pos0, rl, n_steps):
+    """tok/s, ms/step and the kernel's roofline from the exact bytes of every
+    timed step (active weights read once + the KV of every visible key)."""
+    from persistent_moe_amd import sol
+
+    L, K = cfg.n_layers, max(cfg.top_k, 1)
+    step_bytes = []
+    for i in range(n_steps):
+        p = (pos0 + i).tolist()
+        if rl is not None:
+            ids = rl[i].reshape(L, B, K)
+            distinct = [len(np.unique(ids[l])) for l in range(L)]
+        else:
+            distinct = [K if cfg.is_moe else 0] * L
+        step_bytes.append(sol.step_bytes(cfg, p, distinct))
+    mean_bytes = float(np.mean(step_bytes))
+    mean_kern_s = float(np.mean(kern)) / 1e3
+    achieved = mean_bytes / mean_kern_s / 1e9
+    sol_tok_s = float(np.mean([sol.sol_tok_s(b, B) for b in step_bytes]))
+    value = B * n_steps / wall
+    return {
+        "value": round(value, 2),
+        "ms_per_step": round(wall / n_steps * 1e3, 4),
+        "kernel_ms": round(mean_kern_s * 1e3, 4),
+        "sol_tok_s": round(sol_tok_s, 1),
+        "sol_fraction": round(value / sol_tok_s, 4),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_step": int(mean_bytes), "kernel": "mk_persistent"},
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -152,14 +244,16 @@ def main():
         sys.exit(2)
     import torch
 
-    from persistent_moe_amd import mk, sol
+    from persistent_moe_amd import mk
     from persistent_moe_amd import workloads as W
     from persistent_moe_amd.runner import DecodeEngine
 
     wl = W.WORKLOADS[args.workload]
     cfg = wl.model
     B = wl.batch
-    total_steps = args.warmup + args.steps
+    abl_steps = 0 if args.no_ablation else 16
+    ablation = [("interleaved", "persistent"), ("attention_first", "persistent"), ("tuned", "per_opcode")]
+    total_steps = args.warmup + args.steps + len(ablation) * (abl_steps + 2)
     log(f"workload {wl.name}: building inputs for {total_steps} steps")
     t0 = time.time()
     opts = mk.make_opts(args.order, args.launch, attn_split=args.attn_split, flags=args.sched_flags)
@@ -167,28 +261,6 @@ def main():
     log(f"inputs ready in {time.time() - t0:.1f}s ({eng.weight_bytes() / 1e9:.1f} GB weights)")
     if wl.swap_every:
         log("note: slot swaps are not applied inside the timed loop")
-    stream = torch.cuda.current_stream()
-    tok, pos, sl = eng.step_inputs()
-    ids_tap = eng.tap("topk_ids") if cfg.is_moe else None
-    L, K = cfg.n_layers, max(cfg.top_k, 1)
-    # distinct experts per layer: top_k at batch 1; logged per step otherwise
-    route_log = (torch.zeros((total_steps, L * B * K), dtype=torch.int32, device="cuda")
-                 if cfg.is_moe and B > 1 else None)
-    pos0 = pos.cpu().numpy().copy()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(total_steps)]
-
-    def one(i):
-        ev[i][0].record(stream)
-        mk.mk_decode_step(eng.h, tok.data_ptr(), pos.data_ptr(), eng.block_tables.data_ptr(), sl.data_ptr(),
-                          eng.logits.data_ptr(), stream.cuda_stream)
-        ev[i][1].record(stream)
-        if route_log is not None:
-            route_log[i].copy_(ids_tap[:L * B * K])
-        torch.argmax(eng.logits, dim=-1, out=argmax_buf)
-        tok.copy_(argmax_buf)
-        pos.add_(1)
-        sl.add_(1)
-
     if args.calib_copy_mib:
         # an elementwise kernel (negation) that reads and writes exactly n bytes
         n = args.calib_copy_mib << 20
@@ -199,49 +271,19 @@ def main():
         torch.cuda.synchronize()
         log(f"calibration kernel: 3 x ({args.calib_copy_mib} MiB read + {args.calib_copy_mib} MiB written)")
         del src, dst
-    argmax_buf = torch.zeros(B, dtype=torch.int64, device="cuda")
-    for i in range(args.warmup):
-        one(i)
-    torch.cuda.synchronize()
-    st = eng.status()
-    if st.code != 0:
-        raise SystemExit(f"device error during warmup: {mk.strerror(st.code)} task {st.task}")
-    t_start = time.perf_counter()
-    for i in range(args.warmup, total_steps):
-        one(i)
-    torch.cuda.synchronize()
-    t_total = time.perf_counter() - t_start
-    st = eng.status()
-    if st.code != 0:
-        raise SystemExit(f"device error: {mk.strerror(st.code)} task {st.task} counter {st.counter}")
-    kern_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(args.warmup, total_steps)]
-    # exact algorithmic bytes of every timed step
-    step_bytes = []
-    rl = route_log.cpu().numpy() if route_log is not None else None
-    for i in range(args.warmup, total_steps):
-        p = (pos0 + i).tolist()
-        if rl is not None:
-            ids = rl[i].reshape(L, B, K)
-            distinct = [len(np.unique(ids[l])) for l in range(L)]
-        else:
-            distinct = [K if cfg.is_moe else 0] * L
-        step_bytes.append(sol.step_bytes(cfg, p, distinct))
-    mean_bytes = float(np.mean(step_bytes))
-    mean_kern_s = float(np.mean(kern_ms)) / 1e3
-    achieved = mean_bytes / mean_kern_s / 1e9
-    ms_per_step = t_total / args.steps * 1e3
-    value = B * args.steps / t_total
-    sol_tok_s = float(np.mean([sol.sol_tok_s(b, B) for b in step_bytes]))
-    log(f"{value:.1f} tok/s, {ms_per_step:.3f} ms/step; kernel {mean_kern_s * 1e3:.3f} ms "
-        f"(min {min(kern_ms):.3f}); {achieved:.0f} GB/s = {achieved / HBM_PEAK_GBS:.1%} of HBM SoL")
+    wall, kern, pos0, rl = time_steps(eng, args.warmup, args.steps)
+    m = step_metrics(cfg, B, wall, kern, pos0, rl, args.steps)
+    m["roofline"]["traffic"] = measured_traffic(wl.name)
+    log(f"{m['value']:.1f} tok/s, {m['ms_per_step']:.3f} ms/step; kernel {m['kernel_ms']:.3f} ms "
+        f"(min {min(kern):.3f}); {m['roofline']['achieved']:.0f} GB/s = {m['roofline']['frac']:.1%} of HBM SoL")
     out = {
         "metric": METRIC,
-        "value": round(value, 2),
+        "value": m["value"],
         "unit": "tok/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step": m["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -250,22 +292,32 @@ def main():
         "config": {"workload": wl.name, "batch": B, "context": W.context_length(wl, 0),
                    "layers": cfg.n_layers, "experts": cfg.n_experts, "top_k": cfg.top_k,
                    "order": args.order, "launch": args.launch, "sched_flags": args.sched_flags,
-                   "attn_split": args.attn_split or "auto"},
-        "sol_fraction": round(value / sol_tok_s, 4),
-        "sol_tok_s": round(sol_tok_s, 1),
-        "kernel_ms": round(mean_kern_s * 1e3, 4),
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(wl.name),
-                     "bytes_per_step": int(mean_bytes), "kernel": "mk_persistent"},
+                   "attn_split": args.attn_split or "auto", "sampling": "greedy, on device, fused after LM_HEAD"},
+        "sol_fraction": m["sol_fraction"],
+        "sol_tok_s": m["sol_tok_s"],
+        "kernel_ms": m["kernel_ms"],
+        "roofline": m["roofline"],
     }
+    if abl_steps:
+        # the pages' scheduling ablation (tuned vs interleaved vs attention-first
+        # wave orders) and one launch per task wave instead of the megakernel,
+        # on the same engine and inputs
+        abl = {"tuned": {"tok_s": m["value"], "kernel_ms": m["kernel_ms"]}}
+        for order, launch in ablation:
+            mk.mk_build_schedule(eng.h, B, mk.make_opts(order, launch))
+            w2, k2, _, _ = time_steps(eng, 2, abl_steps, route_log_every=False)
+            name = order if launch == "persistent" else "per_opcode_launch"
+            abl[name] = {"tok_s": round(B * abl_steps / w2, 2), "kernel_ms": round(float(np.mean(k2)), 4)}
+            log(f"ablation {name}: {abl[name]['tok_s']:.1f} tok/s")
+        mk.mk_build_schedule(eng.h, B, opts)
+        out["ablation"] = abl
     if args.trace:
         from persistent_moe_amd import trace as T
         topt = mk.make_opts(args.order, args.launch, attn_split=args.attn_split,
                             flags=args.sched_flags | mk.MK_SCHED_TRACE)
         eng.opts = topt
         mk.mk_build_schedule(eng.h, B, topt)
-        one(total_steps - 1)
-        torch.cuda.synchronize()
+        time_steps(eng, 0, 1, route_log_every=False)
         tr = T.load(eng)
         summ = T.summarize(tr)
         with open(args.trace, "w") as fh:
@@ -273,6 +325,30 @@ def main():
         T.chrome_trace(tr, os.path.splitext(args.trace)[0] + ".chrome.json")
         log(f"trace: step {summ['step_us']:.1f} us; " +
             ", ".join(f"{k} busy {v['busy_us']:.0f} wait {v['wait_us']:.0f}" for k, v in summ["per_op"].items()))
+    # release this engine before the batch-8 leg (explicit teardown: every
+    # launch has completed before the handle and the buffers go)
+    torch.cuda.synchronize()
+    eng.close()
+    del eng
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    if not args.no_bs8 and args.workload == "moe30b":
+        wl8 = W.WORKLOADS["moe30b_bs8"]
+        log(f"workload {wl8.name}: building inputs")
+        n8 = max(8, args.steps // 2)
+        eng8 = DecodeEngine(wl8, steps=args.warmup + n8 + 1, verbose=args.verbose)
+        w8, k8, p8, r8 = time_steps(eng8, args.warmup, n8)
+        m8 = step_metrics(wl8.model, wl8.batch, w8, k8, p8, r8, n8)
+        m8["steps"] = n8
+        m8["config"] = {"workload": wl8.name, "batch": wl8.batch,
+                        "contexts": [W.context_length(wl8, b) for b in range(wl8.batch)]}
+        out["bs8"] = m8
+        log(f"bs8: {m8['value']:.1f} tok/s, {m8['ms_per_step']:.3f} ms/step, "
+            f"{m8['roofline']['frac']:.1%} of HBM SoL")
+        torch.cuda.synchronize()
+        eng8.close()
+        del eng8
+        torch.cuda.synchronize()
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         try:
@@ -280,7 +356,6 @@ def main():
         except Exception as e:  # the GPU figure stands on its own
             out["cpu_baseline"] = {"error": repr(e)}
     print(json.dumps(out), flush=True)
-    eng.close()
 
 
 if __name__ == "__main__":

@@ -291,6 +291,44 @@ int mk_decode_step(mk_handle* h, const int32_t* token_ids, const int32_t* positi
                    const int32_t* block_tables, const int32_t* seq_lens, float* logits,
                    void* stream);
 
+/* -------------------------------------------------------------- sampling
+ * The pages' engine decodes with greedy or temperature sampling only (page 1,
+ * "Current limitations").  mk_decode_step_sample runs the same step and
+ * then picks each sequence's next token on the device, fused after LM_HEAD:
+ * every LM_HEAD tile reduces its rows to a best (score, id) per sequence and
+ * the last tile to finish reduces the tiles' bests, so no separate argmax
+ * kernel and no host round trip are needed between steps.
+ *   temperature == 0  greedy: the largest logit, ties to the lowest id;
+ *   temperature  > 0  a draw from softmax(logits / temperature) by the
+ *                     Gumbel-max method: the id maximising
+ *                     logits[v] / temperature - ln(-ln u_v), with
+ *                     u_v = (floor(h_v / 2^8) + 1/2) / 2^24 and
+ *                     h_v = fmix32(fmix32(fmix32(fmix32(seed) ^ position)
+ *                                  ^ slot) ^ v)
+ *                     (fmix32: MurmurHash3's 32-bit finaliser; position =
+ *                     positions[slot] of the step, the cache index of the
+ *                     token that was fed).                                 */
+#define MK_SAMPLE_ADVANCE 1   /* after the step, for every live slot b:
+                                 token_ids[b] = next_tokens[b],
+                                 positions[b] += 1, seq_lens[b] += 1 (the
+                                 caller keeps pages for the new positions in
+                                 the block tables), so steps can be enqueued
+                                 back to back with no host work between    */
+typedef struct mk_sampling {
+  float temperature;        /* >= 0, finite                                  */
+  uint32_t seed;            /* stream of the temperature draws               */
+  int32_t flags;            /* MK_SAMPLE_* bits                              */
+} mk_sampling;
+
+/* mk_decode_step plus the next token of every slot, written to
+ * next_tokens[B] (device, int32; -1 for an empty slot).  With
+ * MK_SAMPLE_ADVANCE, token_ids, positions and seq_lens are updated in place
+ * at the end of the step.  Errors as mk_decode_step; INVAL for a bad
+ * sampling argument.                                                      */
+int mk_decode_step_sample(mk_handle* h, int32_t* token_ids, int32_t* positions,
+                          const int32_t* block_tables, int32_t* seq_lens, float* logits,
+                          const mk_sampling* sampling, int32_t* next_tokens, void* stream);
+
 /* Synchronise the handle's last stream, read and clear the device error
  * record.  st may be NULL.  Returns st->code.  A persistent kernel has no
  * kernel boundary at which a failure can surface (page 2, "// Overview":

@@ -366,6 +366,62 @@ def decode_one(wl, W: Weights, seq: Sequence, token: int, keep_cache: bool = Tru
     return StepResult(logits=logits, token=int(np.argmax(logits)), layers=taps)
 
 
+# ---------------------------------------------------------------------------
+# the next token: greedy or temperature sampling after the LM head
+# ---------------------------------------------------------------------------
+_M32 = 0xFFFFFFFF
+
+
+def _fmix32(h: np.ndarray) -> np.ndarray:
+    """MurmurHash3's 32-bit finaliser (Austin Appleby), elementwise on uint64
+    arrays holding 32-bit values: xor-shift 16, multiply 0x85ebca6b, xor-shift
+    13, multiply 0xc2b2ae35, xor-shift 16, all modulo 2**32."""
+    h = np.asarray(h, dtype=np.uint64) & np.uint64(_M32)
+    h ^= h >> np.uint64(16)
+    h = (h * np.uint64(0x85EBCA6B)) & np.uint64(_M32)
+    h ^= h >> np.uint64(13)
+    h = (h * np.uint64(0xC2B2AE35)) & np.uint64(_M32)
+    h ^= h >> np.uint64(16)
+    return h
+
+
+def sampling_uniforms(seed: int, position: int, slot: int, n: int) -> np.ndarray:
+    """One uniform in (0, 1) per vocabulary id for the token sampled at cache
+    position ``position`` of batch slot ``slot``: a counter-based stream,
+    u_v = (floor(h_v / 2**8) + 1/2) / 2**24 (24 bits, so the value is exact
+    in single precision) with
+    h_v = fmix32(fmix32(fmix32(fmix32(seed) ^ position) ^ slot) ^ v)."""
+    k = _fmix32(np.array([seed & _M32]))[0]
+    k = _fmix32(np.array([int(k) ^ (position & _M32)]))[0]
+    k = _fmix32(np.array([int(k) ^ (slot & _M32)]))[0]
+    h = _fmix32(np.arange(n, dtype=np.uint64) ^ np.uint64(k))
+    return ((h >> np.uint64(8)).astype(np.float64) + 0.5) / 16777216.0
+
+
+def sample_token(logits: np.ndarray, temperature: float, seed: int = 0, position: int = 0,
+                 slot: int = 0) -> Tuple[int, float]:
+    """The next token and the margin of the decision.
+
+    temperature == 0: greedy, the largest logit (ties to the lowest id).
+    temperature > 0: a draw from softmax(logits / temperature) by the
+    Gumbel-max method: the id maximising logits_v / T + g_v, with the Gumbel
+    noise g_v = -ln(-ln u_v) of the counter-based uniforms above (ties to the
+    lowest id).  The margin is the gap between the best and the second-best
+    score (a near-tie can go either way under rounding).
+    """
+    z = np.asarray(logits, dtype=np.float64)
+    if temperature > 0:
+        u = sampling_uniforms(seed, position, slot, z.shape[0])
+        z = z / temperature - np.log(-np.log(u))
+    tok = int(np.argmax(z))
+    if z.shape[0] > 1:
+        top2 = np.partition(z, -2)[-2:]
+        gap = float(top2[1] - top2[0])
+    else:
+        gap = math.inf
+    return tok, gap
+
+
 def decode_step(wl, W: Weights, seqs: List[Sequence], tokens: List[int],
                 keep_cache: bool = True) -> List[StepResult]:
     """One decode step of a batch: each sequence independently."""

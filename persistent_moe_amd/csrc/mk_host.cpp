@@ -32,7 +32,7 @@ constexpr int kMaxGemvK = 8192;    // GEMV reduction length: 16 register slots x
 struct Layout {
   size_t off_tasks, off_ranges, off_ctr, off_err, off_layers, off_invf;
   size_t off_x, off_xn, off_xmid, off_xn2, off_qkv, off_attn, off_opart, off_rlog, off_topi, off_topw;
-  size_t off_moe, off_H, off_Y, off_fh, off_fo, off_oout, off_pml, off_po, off_trace;
+  size_t off_moe, off_H, off_Y, off_fh, off_fo, off_oout, off_pml, off_po, off_lmbest, off_trace;
   size_t total;
   int32_t max_tasks, n_ctr, max_splits, bk, moe_stride;
   mk_ctr_layout cl;
@@ -96,6 +96,9 @@ int max_tasks_bound(const mk_config* c) {
   return (c->n_layers + 1) * per_layer + kMaxWorkgroups;
 }
 int max_waves_bound(const mk_config* c) { return (c->n_layers + 1) * 12 + 4; }
+// LM-head tiles: one per workgroup, or more when a tile would exceed the
+// LDS rows of the sampling epilogue (kYsFloats / 8)
+int max_lm_tiles(const mk_config* c) { return kMaxWorkgroups + c->vocab / (kYsFloats / 8) + 1; }
 
 Layout make_layout(const mk_config* c, int32_t max_blocks) {
   Layout L{};
@@ -136,6 +139,7 @@ Layout make_layout(const mk_config* c, int32_t max_blocks) {
   L.off_oout = take((size_t)Lr * B * d * 4);
   L.off_pml = take((size_t)2 * B * c->n_q_heads * L.max_splits * 2 * 4);
   L.off_po = take((size_t)2 * B * c->n_q_heads * L.max_splits * hd * 4);
+  L.off_lmbest = take((size_t)max_lm_tiles(c) * B * 2 * 4);
   L.off_trace = take((size_t)L.max_tasks * 16 * 8);
   L.total = o;
   return L;
@@ -244,7 +248,9 @@ int build_plan(const mk_config* c, int B, int32_t max_blocks, const mk_sched_opt
   const int o_tiles_g = std::max(1, (part ? n_attn_wg : NW) / Hkv);
   const int o_rows = ceil_div(d, o_tiles_g);
   const int n_o_g = ceil_div(d, o_rows);
-  const int lm_rows = ceil_div(c->vocab, NW);
+  // LM-head tiles land in LDS (8 rows per batch slot of kYsFloats) for the
+  // sampling epilogue: at most kYsFloats / 8 rows each
+  const int lm_rows = std::min(ceil_div(c->vocab, NW), kYsFloats / 8);
   const int n_lm = ceil_div(c->vocab, lm_rows);
   if (moe) {
     const int K = c->top_k, I = c->expert_inter;
@@ -525,6 +531,8 @@ int build_plan(const mk_config* c, int B, int32_t max_blocks, const mk_sched_opt
     t.n1 = std::min(c->vocab, t.n0 + lm_rows);
     t.wait_ctr = ctr_of(p.cl, Lr, MK_CTR_NORM);
     t.wait_target = 1;
+    t.aux[0] = n_lm;     // tiles (the last to finish reduces the sampling bests)
+    t.aux[1] = i;        // this tile's slot in lm_best
     push(t);
   }
   p.wave_bounds.push_back((int32_t)T.size());
@@ -842,11 +850,18 @@ int mk_build_schedule(mk_handle* h, int32_t batch_size, const mk_sched_opts* opt
   return MK_OK;
 }
 
-int mk_decode_step(mk_handle* h, const int32_t* token_ids, const int32_t* positions,
-                   const int32_t* block_tables, const int32_t* seq_lens, float* logits, void* stream) {
+namespace {
+int launch_step(mk_handle* h, const int32_t* token_ids, const int32_t* positions, const int32_t* block_tables,
+                const int32_t* seq_lens, float* logits, const mk_sampling* smp, int32_t* next_tokens,
+                void* stream) {
   if (!h) return MK_E_INVAL;
   if (!h->have_plan) return MK_E_STATE;
   if (!token_ids || !positions || !block_tables || !seq_lens || !logits) return MK_E_INVAL;
+  if (smp) {
+    if (!next_tokens || !(smp->temperature >= 0.f) || !std::isfinite(smp->temperature) ||
+        (smp->flags & ~MK_SAMPLE_ADVANCE) != 0)
+      return MK_E_INVAL;
+  }
   const mk_config& c = h->cfg;
   const Layout& L = h->lay;
   mk_kargs a;
@@ -868,6 +883,13 @@ int mk_decode_step(mk_handle* h, const int32_t* token_ids, const int32_t* positi
   a.block_tables = block_tables;
   a.seq_lens = seq_lens;
   a.logits = logits;
+  if (smp) {
+    a.next_tok = next_tokens;
+    a.lm_best = reinterpret_cast<int32_t*>(ws + L.off_lmbest);
+    a.inv_temp = smp->temperature > 0.f ? (float)(1.0 / (double)smp->temperature) : 0.f;
+    a.sample_seed = smp->seed;
+    a.advance = (smp->flags & MK_SAMPLE_ADVANCE) ? 1 : 0;
+  }
   a.L = c.n_layers; a.d = c.d_model; a.Hq = c.n_q_heads; a.Hkv = c.n_kv_heads; a.hd = c.head_dim;
   a.G = c.n_q_heads / c.n_kv_heads; a.E = c.n_experts; a.topk = c.top_k; a.I = c.expert_inter;
   a.F = c.ffn_inter; a.V = c.vocab; a.parallel = c.parallel_block; a.page = c.page_size;
@@ -908,6 +930,19 @@ int mk_decode_step(mk_handle* h, const int32_t* token_ids, const int32_t* positi
   h->last_stream = reinterpret_cast<hipStream_t>(stream);
   a.wg_range = reinterpret_cast<const int32_t*>(ws + L.off_ranges);
   return mk_launch(&a, h->opts.launch_mode, a.wg_range, (int)h->plan.wave_bounds.size() - 1, stream);
+}
+}  // namespace
+
+int mk_decode_step(mk_handle* h, const int32_t* token_ids, const int32_t* positions,
+                   const int32_t* block_tables, const int32_t* seq_lens, float* logits, void* stream) {
+  return launch_step(h, token_ids, positions, block_tables, seq_lens, logits, nullptr, nullptr, stream);
+}
+
+int mk_decode_step_sample(mk_handle* h, int32_t* token_ids, int32_t* positions, const int32_t* block_tables,
+                          int32_t* seq_lens, float* logits, const mk_sampling* sampling, int32_t* next_tokens,
+                          void* stream) {
+  if (!sampling) return MK_E_INVAL;
+  return launch_step(h, token_ids, positions, block_tables, seq_lens, logits, sampling, next_tokens, stream);
 }
 
 int mk_get_status(mk_handle* h, mk_status* st) {

@@ -34,6 +34,7 @@ enum {
 enum {
   MK_CG_DONE = 0,     // workgroups finished with the step
   MK_CG_ABORT = 1,    // set when any wait timed out
+  MK_CG_LM = 2,       // LM_HEAD tiles finished (sampling: the last one reduces)
   MK_CG_COUNT = 4
 };
 enum {
@@ -114,6 +115,12 @@ struct mk_kargs {
   const int32_t* block_tables;
   const int32_t* seq_lens;
   float* logits;
+  // sampling after LM_HEAD (next_tok null: none)
+  int32_t* next_tok;              // [B] sampled token of each slot
+  int32_t* lm_best;               // [n_lm_tiles][B][2]: best score (bits), id per tile
+  float inv_temp;                 // 1 / temperature, 0 for greedy
+  uint32_t sample_seed;
+  int32_t advance;                // MK_SAMPLE_ADVANCE: update tokens, positions, seq_lens
   // shapes
   int32_t L, d, Hq, Hkv, hd, G, E, topk, I, F, V;
   int32_t parallel, page, swa_window, swa_period;

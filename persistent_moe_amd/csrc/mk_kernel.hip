@@ -1054,6 +1054,98 @@ __device__ __forceinline__ void epi_swiglu(Smem& sm, int np, int nb, float* out,
   }
 }
 
+// ------------------------------------------------------------- LM_HEAD
+// The tile's logits (rows [n0, n1) of every slot, in LDS ys[r][b]) go to the
+// caller's buffer.  When the step samples, each slot's candidate of the tile
+// is the row with the largest score -- the logit (greedy), or logit / T plus
+// Gumbel noise -- ties to the lowest id; the tile writes its candidates to
+// lm_best, and the last tile to finish reduces all tiles' candidates into
+// next_tok (one decision per slot, in the same order-free way: largest score,
+// then lowest id).
+__device__ __forceinline__ uint32_t fmix32(uint32_t h) {
+  h ^= h >> 16;
+  h *= 0x85EBCA6Bu;
+  h ^= h >> 13;
+  h *= 0xC2B2AE35u;
+  h ^= h >> 16;
+  return h;
+}
+// the larger of two (score, id) candidates; equal scores go to the lower id
+__device__ __forceinline__ void best_of(float& s, int& id, float s2, int id2) {
+  if (s2 > s || (s2 == s && id2 < id)) { s = s2; id = id2; }
+}
+// wave-wide best candidate, returned uniform
+__device__ __forceinline__ void wave_best(float& s, int& id) {
+  const float m = wave_max(s);
+  id = wave_min(s == m ? id : 0x7FFFFFFF);
+  s = m;
+}
+__device__ __forceinline__ void epi_lm_head(const KA a, Smem& sm, const mk_task& t) {
+  const int nr = t.n1 - t.n0, B = a->B, V = a->V;
+  const int tid = tid_v(), wave = tid >> 6, lane = tid & 63;
+  for (int idx = tid; idx < nr * B; idx += MK_THREADS) {
+    const int b = idx / nr, r = idx - b * nr;
+    stc(a->logits + (long)b * V + t.n0 + r, sm.ys[r * NBMAX + b]);
+  }
+  if (!a->next_tok) return;
+  const float it = a->inv_temp;
+  float* cs = sm.red;                               // [MK_WAVES][NBMAX] scores
+  int* ci = reinterpret_cast<int*>(sm.red) + 64;    // [MK_WAVES][NBMAX] ids
+  for (int b = 0; b < B; ++b) {
+    uint32_t key = 0;
+    if (it > 0.f) {
+      key = fmix32(fmix32(fmix32(a->sample_seed) ^ (uint32_t)position_u(b)) ^ (uint32_t)b);
+    }
+    float bs = -INFINITY;
+    int bi = 0x7FFFFFFF;
+    for (int r = tid; r < nr; r += MK_THREADS) {
+      float sc = sm.ys[r * NBMAX + b];
+      if (it > 0.f) {
+        // u = (h / 2^8 + 1/2) / 2^24 is exact in fp32 and lies in (0, 1)
+        const uint32_t h = fmix32(key ^ (uint32_t)(t.n0 + r));
+        const float u = ((float)(h >> 8) + 0.5f) * 5.9604644775390625e-8f;
+        sc = sc * it - logf(-logf(u));
+      }
+      best_of(bs, bi, sc, t.n0 + r);
+    }
+    wave_best(bs, bi);
+    if (lane == 0) {
+      cs[wave * NBMAX + b] = bs;
+      ci[wave * NBMAX + b] = bi;
+    }
+  }
+  __syncthreads();
+  if (tid < B) {
+    float bs = cs[tid];
+    int bi = ci[tid];
+#pragma unroll
+    for (int w = 1; w < MK_WAVES; ++w) best_of(bs, bi, cs[w * NBMAX + tid], ci[w * NBMAX + tid]);
+    int32_t* slot = a->lm_best + ((long)t.aux[1] * B + tid) * 2;
+    stc(slot, __float_as_int(bs));
+    stc(slot + 1, bi);
+  }
+  stores_done();
+  __syncthreads();
+  if (tid == 0)
+    sm.misc[3] = __hip_atomic_fetch_add(ctrp(a, MK_CG_LM), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                 t.aux[0] - 1;
+  __syncthreads();
+  if (!sm.misc[3]) return;
+  // the last tile: one wave per slot reduces every tile's candidate
+  const int n_tiles = t.aux[0];
+  for (int b = wave; b < B; b += MK_WAVES) {
+    float bs = -INFINITY;
+    int bi = 0x7FFFFFFF;
+    for (int k = lane; k < n_tiles; k += 64) {
+      const int32_t* slot = a->lm_best + ((long)k * B + b) * 2;
+      best_of(bs, bi, __int_as_float(ldc(slot)), ldc(slot + 1));
+    }
+    wave_best(bs, bi);
+    if (lane == 0) stc(a->next_tok + b, seq_len_u(b) > 0 ? bi : -1);
+  }
+  stores_done();
+}
+
 // ---------------------------------------------------------- ROUTER_TOPK
 // Per token: top-k router logits (ties to the lower expert id); gate weights
 // are the softmax probabilities of the selected experts renormalised to sum
@@ -1834,9 +1926,10 @@ extern "C" __global__ void __launch_bounds__(MK_THREADS, 1) mk_persistent(mk_kar
           st.base = a->fh + (long)l * B * a->F; st.ld = a->F; st.K = a->F;
           break;
         case MK_OP_LM_HEAD:
+          // the tile's logits land in LDS for the epilogue (logits out and
+          // the tile's sampling candidates)
           kind = U_GEMV;
           g.base = a->lm_head; g.ldw = a->d; g.K = a->d;
-          g.out = a->logits + t.n0; g.ob = a->V;
           st.base = a->xn + (long)a->L * B * a->d; st.ld = a->d; st.K = a->d;
           break;
         case MK_OP_MOE_UPGATE_ACT_DRAIN: {
@@ -1910,6 +2003,10 @@ extern "C" __global__ void __launch_bounds__(MK_THREADS, 1) mk_persistent(mk_kar
             break;
           case MK_OP_MOE_DOWN_DRAIN:
             break;   // the claimer signals once its queue is drained
+          case MK_OP_LM_HEAD:
+            __syncthreads();
+            epi_lm_head(a, sm, t);
+            break;
           case MK_OP_ROUTER_GEMM:
             if (t.flags & MK_F_FUSE_TOPK) {
               // the last router tile to finish runs top-k and ROUTE_FINALIZE
@@ -2049,6 +2146,15 @@ extern "C" __global__ void __launch_bounds__(MK_THREADS, 1) mk_persistent(mk_kar
   if (sm.misc[2]) {
     if (final_launch) {
       for (int i = tid; i < a->n_ctr; i += MK_THREADS) stc(ctrp(a, i), 0);
+      // every workgroup has read the step inputs by now: advance the slots
+      if (a->next_tok && a->advance && tid < a->B) {
+        const int nt = ldc(a->next_tok + tid);
+        if (sh_seq_lens[tid] > 0 && nt >= 0) {
+          stc(const_cast<int32_t*>(a->tokens) + tid, nt);
+          stc(const_cast<int32_t*>(a->positions) + tid, sh_positions[tid] + 1);
+          stc(const_cast<int32_t*>(a->seq_lens) + tid, sh_seq_lens[tid] + 1);
+        }
+      }
     } else if (tid == 0) {
       stc(ctrp(a, MK_CG_DONE), 0);
     }

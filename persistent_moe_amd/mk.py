@@ -31,8 +31,9 @@ ORDER = {"tuned": 0, "interleaved": 1, "attention_first": 2, "partitioned": 3}
 LAUNCH = {"persistent": 0, "per_opcode": 1}
 TAPS = {"x": 0, "xn": 1, "qkv": 2, "attn": 3, "router_logits": 4, "topk_ids": 5, "topk_weights": 6,
         "ffn_out": 7, "attn_out": 8, "trace": 9}
-EXPORTS = ["mk_workspace_size", "mk_init", "mk_build_schedule", "mk_decode_step", "mk_get_status",
-           "mk_tap_offset", "mk_plan_schedule", "mk_plan_simulate", "mk_destroy", "mk_strerror"]
+EXPORTS = ["mk_workspace_size", "mk_init", "mk_build_schedule", "mk_decode_step", "mk_decode_step_sample",
+           "mk_get_status", "mk_tap_offset", "mk_plan_schedule", "mk_plan_simulate", "mk_destroy", "mk_strerror"]
+MK_SAMPLE_ADVANCE = 1
 
 
 class MkError(RuntimeError):
@@ -68,6 +69,10 @@ class mk_sched_opts(ctypes.Structure):
         "wave_order", "launch_mode", "attn_split", "n_workgroups", "timeout_ms", "flags")]
 
 
+class mk_sampling(ctypes.Structure):
+    _fields_ = [("temperature", ctypes.c_float), ("seed", ctypes.c_uint32), ("flags", ctypes.c_int32)]
+
+
 class mk_status(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in ("code", "task", "counter", "value", "target", "workgroup")]
 
@@ -101,6 +106,7 @@ def load(path: Optional[str] = None):
                           P, ctypes.c_size_t, ctypes.c_int32, ctypes.POINTER(P)]
     L.mk_build_schedule.argtypes = [P, ctypes.c_int32, ctypes.POINTER(mk_sched_opts)]
     L.mk_decode_step.argtypes = [P, P, P, P, P, P, P]
+    L.mk_decode_step_sample.argtypes = [P, P, P, P, P, P, ctypes.POINTER(mk_sampling), P, P]
     L.mk_get_status.argtypes = [P, ctypes.POINTER(mk_status)]
     L.mk_tap_offset.argtypes = [P, ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t),
                                 ctypes.POINTER(ctypes.c_size_t)]
@@ -116,7 +122,8 @@ def load(path: Optional[str] = None):
     L.mk_destroy.restype = None
     L.mk_strerror.argtypes = [ctypes.c_int]
     L.mk_strerror.restype = ctypes.c_char_p
-    for name in ("mk_init", "mk_build_schedule", "mk_decode_step", "mk_get_status", "mk_tap_offset",
+    for name in ("mk_init", "mk_build_schedule", "mk_decode_step", "mk_decode_step_sample", "mk_get_status",
+                 "mk_tap_offset",
                  "mk_plan_schedule", "mk_plan_simulate"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
@@ -183,6 +190,20 @@ def mk_decode_step(h, token_ids: int, positions: int, block_tables: int, seq_len
     _check(load().mk_decode_step(h, ctypes.c_void_p(token_ids), ctypes.c_void_p(positions),
                                  ctypes.c_void_p(block_tables), ctypes.c_void_p(seq_lens),
                                  ctypes.c_void_p(logits), ctypes.c_void_p(stream)), "mk_decode_step")
+
+
+def mk_decode_step_sample(h, token_ids: int, positions: int, block_tables: int, seq_lens: int, logits: int,
+                          sampling: mk_sampling, next_tokens: int, stream: int = 0) -> None:
+    _check(load().mk_decode_step_sample(h, ctypes.c_void_p(token_ids), ctypes.c_void_p(positions),
+                                        ctypes.c_void_p(block_tables), ctypes.c_void_p(seq_lens),
+                                        ctypes.c_void_p(logits), ctypes.byref(sampling),
+                                        ctypes.c_void_p(next_tokens), ctypes.c_void_p(stream)),
+           "mk_decode_step_sample")
+
+
+def make_sampling(temperature: float = 0.0, seed: int = 0, advance: bool = False) -> mk_sampling:
+    return mk_sampling(temperature=temperature, seed=seed & 0xFFFFFFFF,
+                       flags=MK_SAMPLE_ADVANCE if advance else 0)
 
 
 def mk_get_status(h) -> mk_status:

@@ -89,6 +89,8 @@ def test_init_rejects_null_and_small_workspace(lib):
 def test_null_handle_calls_fail_cleanly(lib):
     assert lib.mk_build_schedule(None, 1, None) == mk.MK_E_INVAL
     assert lib.mk_decode_step(None, None, None, None, None, None, None) == mk.MK_E_INVAL
+    smp = mk.make_sampling(0.7, 3, advance=True)
+    assert lib.mk_decode_step_sample(None, None, None, None, None, None, ctypes.byref(smp), None, None) == mk.MK_E_INVAL
     assert lib.mk_get_status(None, None) == mk.MK_E_INVAL
     lib.mk_destroy(None)
 

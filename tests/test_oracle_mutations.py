@@ -188,3 +188,27 @@ def test_tied_head_pin_catches_untied_stream(monkeypatch):
     monkeypatch.setattr(O.Weights, "lm_head_rows", rows)
     with pytest.raises(AssertionError):
         P.test_tied_lm_head_rows_are_embedding_rows()
+
+
+def _sample_mutant(kind):
+    def fn(logits, temperature, seed=0, position=0, slot=0):
+        z = np.asarray(logits, dtype=np.float64)
+        if temperature > 0:
+            u = O.sampling_uniforms(seed, position, slot, z.shape[0])
+            g = -np.log(-np.log(u))
+            z = {"noise_sign": z / temperature - g, "temp_times": z * temperature + g,
+                 "log_noise": z / temperature + np.log(u)}[kind]
+        return int(np.argmax(z)), 0.0
+    return fn
+
+
+@pytest.mark.parametrize("kind", ["noise_sign", "temp_times", "log_noise"])
+def test_sampling_pin_catches_planted_mistake(monkeypatch, kind):
+    monkeypatch.setattr(O, "sample_token", _sample_mutant(kind))
+    caught = 0
+    for T in (0.5, 2.0):
+        try:
+            P.test_temperature_sampling_draws_from_tempered_softmax(T)
+        except AssertionError:
+            caught += 1
+    assert caught > 0, kind

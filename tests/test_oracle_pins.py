@@ -423,3 +423,34 @@ def test_tied_lm_head_rows_are_embedding_rows():
     # untied: the LM head is its own stream
     wu = O.Weights(wl.with_(model=replace(cfg, tied_embeddings=False)))
     assert not np.array_equal(wu.lm_head_rows(0, 300), emb)
+
+
+# ----------------------------------------------------------------- sampling
+def test_greedy_sampling_is_argmax_with_ties_to_lowest_id():
+    z = np.array([0.5, 2.0, -1.0, 2.0, 1.9])
+    assert O.sample_token(z, 0.0) == (1, 0.0)
+    tok, gap = O.sample_token(np.array([0.1, 0.7, 0.3]), 0.0)
+    assert tok == 1 and abs(gap - 0.4) < 1e-15
+
+
+def test_sampling_uniforms_reference_values():
+    # with seed, position and slot 0 the key is fmix32(0) = 0, so u_v is
+    # (fmix32(v) / 2^8 + 1/2) / 2^24; MurmurHash3's fmix32(1) is 0x514E28B7
+    u = O.sampling_uniforms(0, 0, 0, 2)
+    assert u[0] == 0.5 / 2 ** 24 and u[1] == (0x514E28 + 0.5) / 2 ** 24
+    a, b = O.sampling_uniforms(7, 100, 3, 1000), O.sampling_uniforms(7, 101, 3, 1000)
+    assert np.all((a > 0) & (a < 1)) and not np.array_equal(a, b)
+    assert not np.array_equal(a, O.sampling_uniforms(7, 100, 2, 1000))
+    assert abs(a.mean() - 0.5) < 0.03
+
+
+@pytest.mark.parametrize("T", [0.5, 1.0, 2.0])
+def test_temperature_sampling_draws_from_tempered_softmax(T):
+    # the Gumbel-max draw over many positions has the frequencies of
+    # softmax(logits / T): a chi-square test at 6 dof (p = 1e-4 cut)
+    z = np.array([1.0, 0.2, -0.5, 0.9, 0.0, -2.0, 0.4])
+    n = 20000
+    counts = np.bincount([O.sample_token(z, T, seed=11, position=p)[0] for p in range(n)], minlength=7)
+    p = np.exp(z / T) / np.exp(z / T).sum()
+    chi2 = float(np.sum((counts - n * p) ** 2 / (n * p)))
+    assert chi2 < 27.9, (counts, n * p)
