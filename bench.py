@@ -333,22 +333,29 @@ def main():
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     if not args.no_bs8 and args.workload == "moe30b":
-        wl8 = W.WORKLOADS["moe30b_bs8"]
-        log(f"workload {wl8.name}: building inputs")
-        n8 = max(8, args.steps // 2)
-        eng8 = DecodeEngine(wl8, steps=args.warmup + n8 + 1, verbose=args.verbose)
-        w8, k8, p8, r8 = time_steps(eng8, args.warmup, n8)
-        m8 = step_metrics(wl8.model, wl8.batch, w8, k8, p8, r8, n8)
-        m8["steps"] = n8
-        m8["config"] = {"workload": wl8.name, "batch": wl8.batch,
-                        "contexts": [W.context_length(wl8, b) for b in range(wl8.batch)]}
-        out["bs8"] = m8
-        log(f"bs8: {m8['value']:.1f} tok/s, {m8['ms_per_step']:.3f} ms/step, "
-            f"{m8['roofline']['frac']:.1%} of HBM SoL")
-        torch.cuda.synchronize()
-        eng8.close()
-        del eng8
-        torch.cuda.synchronize()
+        # the batch-8 leg of the metric: uniform routing (random router) and
+        # concentrated routing (Zipf router bias), ragged contexts
+        for key, name in (("bs8", "moe30b_bs8"), ("bs8_zipf", "moe30b_bs8_zipf")):
+            wl8 = W.WORKLOADS[name]
+            log(f"workload {wl8.name}: building inputs")
+            n8 = max(8, args.steps // 2)
+            eng8 = DecodeEngine(wl8, steps=args.warmup + n8 + 1, verbose=args.verbose)
+            w8, k8, p8, r8 = time_steps(eng8, args.warmup, n8)
+            m8 = step_metrics(wl8.model, wl8.batch, w8, k8, p8, r8, n8)
+            m8["steps"] = n8
+            m8["distinct_experts_per_layer"] = round(float(np.mean(
+                [len(np.unique(r8[i].reshape(wl8.model.n_layers, -1)[l])) for i in range(n8)
+                 for l in range(wl8.model.n_layers)])), 2)
+            m8["config"] = {"workload": wl8.name, "batch": wl8.batch, "router_zipf": wl8.model.router_zipf,
+                            "contexts": [W.context_length(wl8, b) for b in range(wl8.batch)]}
+            out[key] = m8
+            log(f"{key}: {m8['value']:.1f} tok/s, {m8['ms_per_step']:.3f} ms/step, "
+                f"{m8['roofline']['frac']:.1%} of HBM SoL, {m8['distinct_experts_per_layer']} experts/layer")
+            torch.cuda.synchronize()
+            eng8.close()
+            del eng8
+            torch.cuda.synchronize()
+            torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         try:

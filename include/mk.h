@@ -134,7 +134,16 @@ typedef struct mk_config {
  *   w_o       [d][Hq*hd]
  *   w_router  [E][d]                 (MoE)
  *   w_upgate  [E][2I][d] (MoE) or [2F][d] (dense): gate rows, then up rows
- *   w_down    [E][d][I]  (MoE) or [d][F]  (dense)                        */
+ *   w_down    [E][d][I]  (MoE) or [d][F]  (dense)
+ *   router_bias [E]                  optional (NULL: none), added to the
+ *                                    router logits before the softmax and the
+ *                                    top-k: it moves both the selection and
+ *                                    the gate weights.  Real routing is
+ *                                    concentrated on a few experts, and the
+ *                                    pages report the megakernel's advantage
+ *                                    growing there (page 1, "Benchmark
+ *                                    results"); a bias reproduces that skew
+ *                                    with synthetic weights.             */
 typedef struct mk_layer_weights {
   const void* attn_norm;
   const void* ffn_norm;
@@ -143,6 +152,7 @@ typedef struct mk_layer_weights {
   const void* w_router;
   const void* w_upgate;
   const void* w_down;
+  const void* router_bias;
 } mk_layer_weights;
 
 typedef struct mk_weights {

@@ -222,6 +222,10 @@ class Weights:
             self.seed, "w_down", self.shapes["w_down"], layer=layer, expert=e)))
         return ug, dn
 
+    def router_bias(self, layer: int) -> Optional[np.ndarray]:
+        b = wlmod.router_bias(self.seed, self.cfg, layer)
+        return None if b is None else _f64(b)
+
     def dense_ffn(self, layer: int):
         return self.layer("w_upgate", layer), self.layer("w_down", layer)
 
@@ -342,6 +346,11 @@ def decode_one(wl, W: Weights, seq: Sequence, token: int, keep_cache: bool = Tru
             # x += Attn(RMSNorm(x)) + MoE(RMSNorm(x)) with one shared norm
             if cfg.is_moe:
                 r = W.layer("w_router", l) @ h
+                bias = W.router_bias(l)
+                if bias is not None:
+                    # a router bias is part of the logits: it moves both the
+                    # selection and the softmax gate weights
+                    r = r + bias
                 sel = route(r, cfg.top_k)
                 m = moe(h, sel, lambda e, l=l: W.expert(l, e))
                 t.router_logits, t.route = r, sel

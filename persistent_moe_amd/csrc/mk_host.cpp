@@ -799,6 +799,7 @@ int mk_init(const mk_config* cfg, const mk_weights* w, const mk_kv_pool* kv, voi
     ld.w_router = static_cast<const uint16_t*>(lw.w_router);
     ld.w_upgate = static_cast<const uint16_t*>(lw.w_upgate);
     ld.w_down = static_cast<const uint16_t*>(lw.w_down);
+    ld.router_bias = static_cast<const uint16_t*>(lw.router_bias);
     ld.k = static_cast<uint16_t*>(kv->k[l]);
     ld.v = static_cast<uint16_t*>(kv->v[l]);
   }

@@ -92,6 +92,7 @@ struct mk_layer_dev {
   const uint16_t* w_router;
   const uint16_t* w_upgate;
   const uint16_t* w_down;
+  const uint16_t* router_bias;   // [E] or null
   uint16_t* k;
   uint16_t* v;
 };

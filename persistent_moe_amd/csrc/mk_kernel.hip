@@ -1154,12 +1154,22 @@ __device__ __forceinline__ void epi_lm_head(const KA a, Smem& sm, const mk_task&
 __device__ __forceinline__ void router_topk(const KA a, Smem& sm, int l) {
   const int B = a->B, E = a->E, K = a->topk;
   const int wave = tid_v() >> 6, lane = tid_v() & 63;
+  const uint16_t* bias = LAYER_PTR(l, router_bias);   // optional [E] logit bias
   for (int b = wave; b < B; b += MK_WAVES) {
     float v[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int e = lane + 64 * u;
       v[u] = e < E ? ldc(a->rlog + ((long)l * B + b) * E + e) : -INFINITY;
+    }
+    if (bias) {
+      // the bias is part of the logits (selection and gate weights); the
+      // router-logit tap keeps the projection alone
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int e = lane + 64 * u;
+        if (e < E) v[u] += bf16_to_f(((GLOBAL const uint16_t*)bias)[e]);
+      }
     }
     float top0 = 0.f, wsum = 0.f;
     float myw = 0.f;

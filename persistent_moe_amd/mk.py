@@ -51,7 +51,7 @@ class mk_config(ctypes.Structure):
 
 class mk_layer_weights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
-        "attn_norm", "ffn_norm", "w_qkv", "w_o", "w_router", "w_upgate", "w_down")]
+        "attn_norm", "ffn_norm", "w_qkv", "w_o", "w_router", "w_upgate", "w_down", "router_bias")]
 
 
 class mk_weights(ctypes.Structure):

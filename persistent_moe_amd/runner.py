@@ -107,10 +107,18 @@ class DecodeEngine:
                     lw[name] = t
                 else:
                     lw[name] = gen(name, shp, l)
+            rb = W.router_bias(seed, cfg, l)
+            if rb is not None:
+                lw["router_bias"] = rb.to(dev)
             self.layers.append(lw)
             if self.verbose and (l % 8 == 7 or l == cfg.n_layers - 1):
                 torch.cuda.synchronize()
                 _log(True, "generated layer", l)
+
+    def router_bias_f64(self, layer: int):
+        """Layer ``layer``'s router bias as float64 values (or None)."""
+        lw = self.layers[layer]
+        return lw["router_bias"].float().cpu().numpy().astype(np.float64) if "router_bias" in lw else None
 
     def weight_bytes(self) -> int:
         n = self.embed.numel() + self.final_norm.numel()
@@ -168,6 +176,7 @@ class DecodeEngine:
             arr[l].w_router = lw["w_router"].data_ptr() if "w_router" in lw else None
             arr[l].w_upgate = lw["w_upgate"].data_ptr()
             arr[l].w_down = lw["w_down"].data_ptr()
+            arr[l].router_bias = lw["router_bias"].data_ptr() if "router_bias" in lw else None
         self._layer_arr = arr
         self._w = mk.mk_weights(embed=self.embed.data_ptr(), lm_head=self.lm_head.data_ptr(),
                                 final_norm=self.final_norm.data_ptr(), layers=arr)

@@ -68,6 +68,7 @@ class ModelConfig:
     rms_eps: float = 1.0e-5
     swa_window: int = 0        # 0: every layer attends to the whole context
     swa_period: int = 0        # layer l is global iff l % swa_period == swa_period - 1
+    router_zipf: float = 0.0   # > 0: each layer's router has a bias that skews routing (router_bias)
 
     @property
     def group(self) -> int:
@@ -126,6 +127,7 @@ MOE_30B = ModelConfig(
     tied_embeddings=False, parallel_block=True)
 
 MOE_30B_SWA = replace(MOE_30B, name="moe-30b-a3.3b-swa", swa_window=4096, swa_period=4)
+MOE_30B_ZIPF = replace(MOE_30B, name="moe-30b-a3.3b-zipf", router_zipf=1.2)
 
 WORKLOADS = {
     "tiny": Workload("tiny-moe-bs1-ctx64", TINY_MOE, batch=1, ctx="fixed:64", steps=8, seed=0),
@@ -135,6 +137,10 @@ WORKLOADS = {
                            steps=256, seed=3, swap_every=32),
     "moe30b_256k": Workload("moe30b-bs1-ctx256k-swa", MOE_30B_SWA, batch=1, ctx="fixed:262144",
                             steps=64, seed=4),
+    # concentrated routing: the continuous-batching workload with a router
+    # bias that favours a seeded few experts per layer (Zipf ranks)
+    "moe30b_bs8_zipf": Workload("moe30b-bs8-ragged-zipf", MOE_30B_ZIPF, batch=8, ctx="loguniform:512:16384",
+                                steps=256, seed=5, swap_every=32),
 }
 
 
@@ -471,6 +477,23 @@ def gen_tensor(seed: int, name: str, shape, layer: int = -1, expert: int = -1,
     ncol = int(np.prod(shape[1:]))
     out = torch.empty((r1 - r0,) + tuple(shape[1:]), dtype=torch.bfloat16, device=device)
     return fill_normal_(out, key, mean, std, start=r0 * ncol)
+
+
+def router_bias(seed: int, cfg: ModelConfig, layer: int) -> Optional[torch.Tensor]:
+    """The router bias of one layer as bf16 [E], or None without one.
+
+    Experts get Zipf ranks from a seeded permutation per layer; expert e of
+    rank k (0-based) has bias -s * ln(k + 1), s = cfg.router_zipf, so that
+    with the bias alone routing picks expert ranks with weights proportional
+    to (k + 1)**-s (real traffic concentrates on a few experts).  Rounded to
+    float32 and then bf16, both round-to-nearest-even, like every weight.
+    """
+    if cfg.router_zipf <= 0 or cfg.n_experts == 0:
+        return None
+    rank = np.empty(cfg.n_experts, dtype=np.int64)
+    rank[permutation(seed, "router_rank_layer%d" % layer, cfg.n_experts)] = np.arange(cfg.n_experts)
+    b = -cfg.router_zipf * np.log(rank.astype(np.float64) + 1.0)
+    return torch.from_numpy(b.astype(np.float32)).to(torch.bfloat16)
 
 
 def kv_key(seed: int, seq_id: int, layer: int, which: str) -> int:

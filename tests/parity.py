@@ -82,8 +82,12 @@ def compare_step(eng, res: List["O.StepResult"], logits: torch.Tensor, rep: Repo
             rl = taps["router_logits"][:L * B * cfg.n_experts].reshape(L, B, cfg.n_experts)
             for l in range(L):
                 tap = r.layers[l]
+                # the device tap holds the projection; a router bias is added
+                # where the logits are read for the top-k
+                bias = eng.router_bias_f64(l)
+                want = tap.router_logits - bias if bias is not None else tap.router_logits
                 rep.worst_router_err = max(rep.worst_router_err,
-                                           float(np.max(np.abs(rl[l, b] - tap.router_logits))))
+                                           float(np.max(np.abs(rl[l, b] - want))))
                 if set(ids[l, b].tolist()) != set(tap.route.ids.tolist()):
                     if tap.route.margin < NEAR_TIE:
                         flipped = True

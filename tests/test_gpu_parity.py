@@ -168,6 +168,21 @@ def test_moe30b_shape_bs8_long_ragged_contexts():
     run_teacher_forced(eng, 2, W_oracle=O.Weights(wl, cache_limit=8 << 30)).check()
 
 
+def test_moe30b_shape_bs8_concentrated_routing():
+    """A router bias with Zipf ranks concentrates the routing (about 21
+    distinct experts per layer at bs=8 instead of about 51), as in real
+    traffic; parity holds with the bias in the logits."""
+    from dataclasses import replace
+    wl = W.Workload("moe30b-shape-bs8-zipf", replace(MOE_SMALL, name="moe30b-shape-zipf", router_zipf=1.2),
+                    batch=8, ctx="loguniform:100:900", steps=2, seed=23)
+    eng = _engine(wl)
+    rep = run_teacher_forced(eng, 2, W_oracle=O.Weights(wl, cache_limit=4 << 30))
+    rep.check()
+    ids = eng.tap("topk_ids").cpu().numpy()[:2 * 8 * 8].reshape(2, 8 * 8)
+    distinct = [len(set(ids[l].tolist())) for l in range(2)]
+    assert max(distinct) < 40, distinct
+
+
 SWA_4L = W.ModelConfig(name="moe30b-swa4096-4l", n_layers=4, d_model=2048, n_q_heads=32, n_kv_heads=4,
                        head_dim=128, vocab=2048, n_experts=128, top_k=8, expert_inter=768,
                        swa_window=4096, swa_period=4)

@@ -454,3 +454,34 @@ def test_temperature_sampling_draws_from_tempered_softmax(T):
     p = np.exp(z / T) / np.exp(z / T).sum()
     chi2 = float(np.sum((counts - n * p) ** 2 / (n * p)))
     assert chi2 < 27.9, (counts, n * p)
+
+
+# ------------------------------------------------------------- router bias
+def test_router_bias_values_are_zipf_ranks():
+    cfg = W.MOE_30B_ZIPF
+    b = W.router_bias(5, cfg, 3).float().numpy().astype(np.float64)
+    want = np.sort(O.bf16_round(-cfg.router_zipf * np.log(np.arange(cfg.n_experts) + 1.0)))
+    assert np.array_equal(np.sort(b), want)            # one expert per rank
+    assert not np.array_equal(b, W.router_bias(5, cfg, 4).float().numpy())
+    assert W.router_bias(5, W.MOE_30B, 3) is None
+
+
+def test_router_bias_moves_selection_and_gate_weights():
+    # zero router weights: the logits are the bias alone, so the selected
+    # experts and their gates are the top-k of the bias
+    wl = _tiny_wl()
+    t = _hand_tensors(wl.model)
+    for l in range(wl.model.n_layers):
+        t["w_router"][l] = np.zeros_like(t["w_router"][l])
+    bias = np.array([0.1, 1.5, 0.7])
+
+    class Biased(_HandWeights):
+        def router_bias(self, layer):
+            return bias
+
+    res = O.decode_one(wl, Biased(wl, t), O.new_sequence(0, 3), token=2)
+    for tap in res.layers:
+        assert tap.route.ids.tolist() == [1, 2]
+        w1 = 1.0 / (1.0 + math.exp(0.7 - 1.5))
+        assert np.allclose(tap.route.weights, [w1, 1 - w1], atol=1e-14)
+        assert np.allclose(tap.router_logits, bias)
