@@ -311,10 +311,14 @@ int build_plan(const mk_config* c, int B, int32_t max_blocks, const mk_sched_opt
   p.ncomb = std::max(1, std::min(G, (NW - 1) / std::max(1, B * Hkv) + 1));
   int layer_target_prev = 0;
   for (int l = 0; l <= Lr; ++l) {
-    // ADD_RMSNORM entering layer l (l == Lr: the final norm)
+    // ADD_RMSNORM entering layer l (l == Lr: the final norm), one task per
+    // sequence: each row is an independent reduction, and one workgroup
+    // summing the residual sources of every row in turn would put B memory
+    // round trips on the critical path
     wave();
-    {
+    for (int b = 0; b < B; ++b) {
       mk_task t = blank(MK_OP_ADD_RMSNORM, l);
+      t.batch = b;
       if (l == 0) {
         t.flags |= MK_F_EMBED;
       } else {
@@ -323,7 +327,7 @@ int build_plan(const mk_config* c, int B, int32_t max_blocks, const mk_sched_opt
       }
       if (l == Lr) t.flags |= MK_F_FINAL;
       t.signal_ctr = ctr_of(p.cl, l, MK_CTR_NORM);
-      place(t, onA, 0);
+      place(t, onA, b);
     }
     if (l == Lr) break;
     const int cNORM = ctr_of(p.cl, l, MK_CTR_NORM);
@@ -334,7 +338,7 @@ int build_plan(const mk_config* c, int B, int32_t max_blocks, const mk_sched_opt
         t.n0 = i * qkv_pp;
         t.n1 = std::min(pairs_tot, t.n0 + qkv_pp);
         t.wait_ctr = cNORM;
-        t.wait_target = 1;
+        t.wait_target = B;
         t.signal_ctr = ctr_of(p.cl, l, MK_CTR_QKV);
         if (router_own) push_on(t, n_r + i);
         else push(t);
@@ -416,7 +420,7 @@ int build_plan(const mk_config* c, int B, int32_t max_blocks, const mk_sched_opt
           t.n0 = i * r_rows;
           t.n1 = std::min(c->n_experts, t.n0 + r_rows);
           t.wait_ctr = cNORM;
-          t.wait_target = 1;
+          t.wait_target = B;
           t.signal_ctr = ctr_of(p.cl, l, MK_CTR_ROUTER);
           if (fuse_topk) {
             t.flags |= MK_F_FUSE_TOPK;
@@ -493,9 +497,10 @@ int build_plan(const mk_config* c, int B, int32_t max_blocks, const mk_sched_opt
       const int cFUG = ctr_of(p.cl, l, MK_CTR_FFNUG);
       emit_qkv(); emit_attn(); emit_combine(); emit_oproj(cO);
       wave();
-      {
+      for (int b = 0; b < B; ++b) {
         mk_task t = blank(MK_OP_ADD_RMSNORM, l);
         t.flags |= MK_F_MID;
+        t.batch = b;
         t.wait_ctr = cO;
         t.wait_target = Hkv * n_o_g;
         t.signal_ctr = cN2;
@@ -507,7 +512,7 @@ int build_plan(const mk_config* c, int B, int32_t max_blocks, const mk_sched_opt
         t.n0 = i * ffn_pp;
         t.n1 = std::min(c->ffn_inter, t.n0 + ffn_pp);
         t.wait_ctr = cN2;
-        t.wait_target = 1;
+        t.wait_target = B;
         t.signal_ctr = cFUG;
         push(t);
       }
@@ -530,7 +535,7 @@ int build_plan(const mk_config* c, int B, int32_t max_blocks, const mk_sched_opt
     t.n0 = i * lm_rows;
     t.n1 = std::min(c->vocab, t.n0 + lm_rows);
     t.wait_ctr = ctr_of(p.cl, Lr, MK_CTR_NORM);
-    t.wait_target = 1;
+    t.wait_target = B;
     t.aux[0] = n_lm;     // tiles (the last to finish reduces the sampling bests)
     t.aux[1] = i;        // this tile's slot in lm_best
     push(t);

@@ -477,6 +477,16 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
 }
 
+// D = A B + C on the matrix cores: A 16 x 32 bf16 (lane l: row l mod 16, K
+// elements 8 (l / 16) .. + 7), B 32 x 16 bf16 (lane l: column l mod 16, the
+// same K elements), D 16 x 16 fp32 (lane l: rows 4 (l / 16) .. + 3, column
+// l mod 16).
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                 0, 0, 0);
+}
+
 template <int NB>
 struct GemvTile {
   static constexpr int WB = NB >= 4 ? MK_WB / 2 : MK_WB;
@@ -825,26 +835,147 @@ __device__ __forceinline__ bool gemv_run(const KA a, Smem& sm, const GemvArgs& g
   return true;
 }
 
+// ------------------------------------------------ MFMA GEMV (3 to 8 batch rows)
+// With several batch rows the dot-product form costs 8 instructions per
+// 16-byte weight slot for every row, and two LDS reads of x per row: the
+// multiply becomes VALU- and LDS-bound.  Here the weights are the A operand
+// of v_mfma_f32_16x16x32_bf16 (16 weight rows x 32 K elements per K-step)
+// and the staged rows of x the B operand (32 K x 16 columns: batch row n in
+// column n, zeros in the columns past the batch), so a 16-byte weight slot
+// costs two MFMAs (x = hi + lo, as in the dot-product form) for all the
+// batch rows at once.  Lane l loads 8 consecutive K elements of weight row
+// l mod 16 of the block (each wave load covers 16 rows x 64 bytes).  A group
+// is one 16-row block per compute wave times a 512-element K chunk (16
+// K-steps, 16 KB per wave); blocks go to the compute waves in turn, and a
+// wave walks the K chunks of its block in order, accumulating in registers,
+// before its next block.  Rows past the tile and K past the row read as
+// zeros (out-of-range buffer offsets).
+struct MfmaTile {
+  static constexpr int WS = 16;   // K-steps (16-byte slots per lane) per group
+  u32x4 w[WS];
+
+  // 16-row block and K chunk of group grp for compute wave cw (1..MK_CW)
+  __device__ __forceinline__ static void where(int grp, int cw, int kch, int& blk, int& ch) {
+    const int bt = grp / kch;
+    ch = grp - bt * kch;
+    blk = bt * MK_CW + cw - 1;
+  }
+
+  __device__ __forceinline__ void load(const GemvArgs& g, int grp, int kch, int nblk) {
+    const int wave = __builtin_amdgcn_readfirstlane(tid_v() >> 6), lane = tid_v() & 63;
+    int blk, ch;
+    where(grp, wave, kch, blk, ch);
+    if (blk >= nblk) return;   // wave-uniform: no block for this wave
+    const int r = blk * 16 + (lane & 15);
+    const bool rv = r < g.nrows;
+    // element offset of the lane's weight row from the matrix base
+    const uint32_t roff = rv ? (uint32_t)(gemv_row(g, r) - g.base) : 0u;
+    __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(g.base), (short)0, 0x7FFFFFFF, 0x00020000);
+    const int k0 = ch * 512 + 8 * (lane >> 4);
+#pragma unroll
+    for (int u = 0; u < WS; ++u) {
+      const int k = k0 + 32 * u;
+      const uint32_t off = (rv && k < g.K) ? (roff + (uint32_t)k) * 2u : 0x80000000u;
+      w[u] = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, 2 /* nontemporal */);
+    }
+  }
+
+  // xh / xl: the staged hi / lo bf16 rows (row n at n * g.xstride)
+  __device__ __forceinline__ void compute(const GemvArgs& g, int grp, int kch, int nblk, const uint16_t* xh,
+                                          const uint16_t* xl, f32x4& acc, float* ys) {
+    const int wave = __builtin_amdgcn_readfirstlane(tid_v() >> 6), lane = tid_v() & 63;
+    int blk, ch;
+    where(grp, wave, kch, blk, ch);
+    if (blk >= nblk) return;
+    const int n = lane & 15;
+    const bool nv = n < g.nb;
+    const int xo = n * g.xstride + ch * 512 + 8 * (lane >> 4);
+#pragma unroll
+    for (int u = 0; u < WS; ++u) {
+      const u32x4 bh = nv ? *reinterpret_cast<const u32x4*>(xh + xo + 32 * u) : (u32x4){0u, 0u, 0u, 0u};
+      const u32x4 bl = nv ? *reinterpret_cast<const u32x4*>(xl + xo + 32 * u) : (u32x4){0u, 0u, 0u, 0u};
+      acc = mfma_bf16(w[u], bh, acc);
+      acc = mfma_bf16(w[u], bl, acc);
+    }
+    if (ch == kch - 1) {
+      // lane l holds rows 4 (l / 16) .. + 3 of the block, batch column l mod 16
+      if (nv) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = blk * 16 + 4 * (lane >> 4) + i;
+          if (r < g.nrows) {
+            if (g.out) stc(g.out + (long)n * g.ob + r, acc[i]);
+            else ys[r * NBMAX + n] = acc[i];
+          }
+        }
+      }
+      acc = (f32x4){0.f, 0.f, 0.f, 0.f};
+    }
+  }
+};
+
+__device__ __forceinline__ bool gemv_run_mfma(const KA a, Smem& sm, const GemvArgs& g_in, const StageArgs& s) {
+  MfmaTile T[MK_NT];
+  GemvArgs g = g_in;
+  make_uniform(g);
+  const int kch = (g.K + 511) >> 9;
+  const int kl = kch <= 1 ? 0 : 32 - __builtin_clz(kch - 1);
+  const int nblk = (g.nrows + 15) >> 4;
+  const int ng = ((nblk + MK_CW - 1) / MK_CW) * kch;
+  const bool cw = (tid_v() >> 6) != 0;
+  // the first MK_NT groups are in flight before the dependency resolves
+  if (cw) {
+#pragma unroll
+    for (int u = 0; u < MK_NT; ++u)
+      if (u < ng) T[u].load(g, u, kch, nblk);
+  }
+  const int kp = 512 << kl;   // staged row stride (elements)
+  if (!wait_and_stage(a, sm, s, kp)) return false;
+  const uint16_t* xh = reinterpret_cast<const uint16_t*>(sm.xs);
+  const uint16_t* xl = xh + s.nb * kp;
+  GemvArgs gx = g;
+  gx.xstride = kp;
+  make_uniform(gx);
+  if (a->trace && tid_v() == 64) sm.t_mark[3] = wall_clock64();
+  if (cw) {
+    f32x4 acc = (f32x4){0.f, 0.f, 0.f, 0.f};
+    for (int grp = 0; grp < ng; grp += MK_NT) {
+#pragma unroll
+      for (int u = 0; u < MK_NT; ++u) {
+        if (grp + u < ng) {
+          T[u].compute(gx, grp + u, kch, nblk, xh, xl, acc, sm.ys);
+          if (grp + u + MK_NT < ng) T[u].load(g, grp + u + MK_NT, kch, nblk);
+        }
+      }
+    }
+  }
+  if (a->trace && tid_v() == 64) sm.t_mark[4] = wall_clock64();
+  if (a->trace && tid_v() == 0 && sm.t_mark[1] == 0) sm.t_mark[1] = wall_clock64();
+  return true;
+}
+
 // Runs one GEMV tile: prefetch, wait, stage x, multiply.  false if the step
 // was aborted while waiting.
 __device__ __forceinline__ bool gemv(const KA a, Smem& sm, const GemvArgs& g, const StageArgs& s) {
   if (g.nb <= 1) return gemv_run<1>(a, sm, g, s);
   if (g.nb <= 2) return gemv_run<2>(a, sm, g, s);
-  if (g.nb <= 4) return gemv_run<4>(a, sm, g, s);
-  return gemv_run<8>(a, sm, g, s);
+  return gemv_run_mfma(a, sm, g, s);
 }
 
 // ------------------------------------------------------------- ADD_RMSNORM
 // x_l = x_{l-1} + sum_g O-proj partial_g + sum_j w_j Y_j (parallel block), or
-// the embedding row at layer 0; xn_l = x_l / sqrt(mean(x_l^2) + eps) * gain.
-// Each thread takes up to four 4-element chunks of a batch row (rows in
-// turn); the ~Hkv + k + 1 source loads of all its chunks are issued together,
-// so a row costs one round trip.  x is kept in LDS between the two passes.
+// the embedding row at layer 0; xn_l = x_l / sqrt(mean(x_l^2) + eps) * gain,
+// for the batch row t.batch (one task per sequence).  Each thread takes up to
+// four 4-element chunks of the row; the ~Hkv + k + 1 source loads of all its
+// chunks are issued together, so the row costs one round trip.  x is kept in
+// LDS between the two passes.
 // The MoE combine (the gate-weighted sum of the routed expert outputs, in
 // top-k order) is folded into this task.
 __device__ __forceinline__ bool op_add_rmsnorm(const KA a, Smem& sm, const mk_task& t, int ti) {
   constexpr int NCH = 4;            // 4-element chunks per thread (d <= 4096)
   const int l = t.layer, d = a->d, B = a->B, nv = d >> 2, K = a->topk;
+  const int b0 = t.batch, b1 = t.batch + 1;   // the row of this task
   const int tid = tid_v(), wave = tid >> 6, lane = tid & 63;
   const bool mid = t.flags & MK_F_MID;
   const bool fin = t.flags & MK_F_FINAL;
@@ -868,9 +999,9 @@ __device__ __forceinline__ bool op_add_rmsnorm(const KA a, Smem& sm, const mk_ta
   if (moe_in) {
     if (!wg_wait(a, sm, layer_ctr(a, lp, MK_CTR_ROUTE), 1, ti)) return false;
     const int32_t* slot = a->moe + (long)lp * a->moe_stride + 4;
-    if (tid < B * K) {
-      srow[tid] = ldc(slot + tid);
-      sw[tid] = ldc(a->topw + (long)lp * B * K + tid);
+    if (tid < K) {
+      srow[b0 * K + tid] = ldc(slot + b0 * K + tid);
+      sw[b0 * K + tid] = ldc(a->topw + ((long)lp * B + b0) * K + tid);
     }
   }
   if (!wg_wait(a, sm, t.wait_ctr, t.wait_target, ti)) return false;
@@ -879,7 +1010,7 @@ __device__ __forceinline__ bool op_add_rmsnorm(const KA a, Smem& sm, const mk_ta
   float* red = sm.red;      // [MK_WAVES][NBMAX] partial sums of squares
   float* xv = sm.xs;        // [B][d] the new residual rows
 #pragma unroll 1
-  for (int b = 0; b < B; ++b) {
+  for (int b = b0; b < b1; ++b) {
     const bool live = seq_len_u(b) > 0;
     int tok = 0;
     if (emb && live) {
@@ -967,7 +1098,7 @@ __device__ __forceinline__ bool op_add_rmsnorm(const KA a, Smem& sm, const mk_ta
   }
   __syncthreads();
 #pragma unroll 1
-  for (int b = 0; b < B; ++b) {
+  for (int b = b0; b < b1; ++b) {
     float tot = 0.f;
 #pragma unroll
     for (int w = 0; w < MK_WAVES; ++w) tot += red[w * NBMAX + b];
@@ -1279,11 +1410,7 @@ __device__ __forceinline__ void route_finalize(const KA a, Smem& sm, int l) {
 // fragments of the first tiles are loaded before the wait on the QKV tiles
 // (cached keys are immutable); the key appended this step is re-read with a
 // coherent load after the wait.  q goes through LDS, staged by wave 0.
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-__device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
-                                                 0, 0, 0);
-}
+
 constexpr int ATT_PT = 4;   // K tiles in flight per compute wave
 constexpr int ATT_PV = 6;   // V k-steps (32 keys) in flight per compute wave
 

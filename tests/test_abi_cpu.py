@@ -117,7 +117,8 @@ def test_plan_structure(lib, model, B, mb):
     assert all(0 <= o < 16 for o in ops)
     L = model.n_layers
     norms = [t for t in tasks if t.op == 0]
-    assert len(norms) == L + 1 + (0 if model.parallel_block else L)
+    assert len(norms) == B * (L + 1 + (0 if model.parallel_block else L))   # one per sequence
+    assert sorted({t.batch for t in norms}) == list(range(B))
     assert sum(1 for t in tasks if t.op == mk.OPCODES.index("LM_HEAD")) > 0
     lm = [t for t in tasks if t.op == mk.OPCODES.index("LM_HEAD")]
     assert lm[0].n0 == 0 and lm[-1].n1 == model.vocab
