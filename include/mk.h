@@ -275,6 +275,25 @@ int mk_init(const mk_config* cfg, const mk_weights* w, const mk_kv_pool* kv,
             void* workspace, size_t ws_bytes, int32_t max_blocks_per_seq,
             mk_handle** out);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): mk_init
+ * without a caller workspace.  The handle's workspace is the library's own
+ * file-scope device array of MK_NOALLOC_WS_BYTES, one per device (held from
+ * the library's first use on a device until the process ends), and the
+ * handle itself is the library's per-device one; no device or host memory is
+ * allocated.  The layout leaves out the task-trace region (MK_SCHED_TRACE is
+ * refused) and sizes the task list for at most one workgroup per CU.
+ * A model and max_blocks_per_seq whose workspace does not fit return
+ * MK_E_NOMEM (the 30B MoE at batch 1 and 8K context needs about 30 MB; batch
+ * 8 at 16K does not fit and needs mk_init).  Each call on a device rebinds
+ * and clears that device's array and handle: a handle returned earlier on the
+ * same device then sees the new binding, and steps of two such handles must
+ * not overlap (they would race on the one array).  mk_destroy on this handle
+ * only forgets its schedule.  Other arguments and errors as mk_init.     */
+#define MK_NOALLOC_WS_BYTES (48u << 20)
+int mk_init_noalloc(const mk_config* cfg, const mk_weights* w, const mk_kv_pool* kv,
+                    int32_t max_blocks_per_seq, mk_handle** out);
+
 /* Build the task list for a batch of `batch_size` slots and upload it to the
  * workspace (the host builds named waves per layer and deals task k to
  * workgroup k mod N: page 1 "Scheduling: mostly static, selectively

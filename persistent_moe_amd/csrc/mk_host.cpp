@@ -35,6 +35,8 @@ struct Layout {
   size_t off_moe, off_H, off_Y, off_fh, off_fo, off_oout, off_pml, off_po, off_lmbest, off_trace;
   size_t total;
   int32_t max_tasks, n_ctr, max_splits, bk, moe_stride;
+  int32_t nw_bound;   // schedules may use up to this many workgroups
+  bool has_trace;     // the task-trace region exists
   mk_ctr_layout cl;
 };
 
@@ -91,16 +93,19 @@ int validate_config(const mk_config* c) {
   return MK_OK;
 }
 
-int max_tasks_bound(const mk_config* c) {
-  const int per_layer = 8 * kMaxWorkgroups + 2 * c->max_batch * c->n_kv_heads + 64;
-  return (c->n_layers + 1) * per_layer + kMaxWorkgroups;
+// Task-list capacity for schedules of up to nw workgroups.
+int max_tasks_bound(const mk_config* c, int nw = kMaxWorkgroups) {
+  const int per_layer = 8 * nw + 2 * c->max_batch * c->n_kv_heads + 64;
+  return (c->n_layers + 1) * per_layer + nw;
 }
 int max_waves_bound(const mk_config* c) { return (c->n_layers + 1) * 12 + 4; }
 // LM-head tiles: one per workgroup, or more when a tile would exceed the
 // LDS rows of the sampling epilogue (kYsFloats / 8)
-int max_lm_tiles(const mk_config* c) { return kMaxWorkgroups + c->vocab / (kYsFloats / 8) + 1; }
+int max_lm_tiles(const mk_config* c, int nw = kMaxWorkgroups) { return nw + c->vocab / (kYsFloats / 8) + 1; }
 
-Layout make_layout(const mk_config* c, int32_t max_blocks) {
+// Workspace layout for schedules of up to nw_bound workgroups, with or
+// without the task-trace region.
+Layout make_layout(const mk_config* c, int32_t max_blocks, int nw_bound = kMaxWorkgroups, bool trace = true) {
   Layout L{};
   const int Lr = c->n_layers, B = c->max_batch, d = c->d_model, hd = c->head_dim;
   const int rows = (c->n_q_heads + 2 * c->n_kv_heads) * hd;
@@ -110,13 +115,15 @@ Layout make_layout(const mk_config* c, int32_t max_blocks) {
   L.moe_stride = mk_moe_stride(L.bk);
   L.cl = mk_make_ctr_layout(Lr, c->n_kv_heads, B, E > 0 ? K : 0);
   L.n_ctr = L.cl.total;
-  L.max_tasks = max_tasks_bound(c);
+  L.max_tasks = max_tasks_bound(c, nw_bound);
+  L.nw_bound = nw_bound;
+  L.has_trace = trace;
   const long max_ctx = (long)max_blocks * c->page_size;
   L.max_splits = (int)std::max<long>(1, (max_ctx + MK_MIN_SPLIT - 1) / MK_MIN_SPLIT);
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t r = o; o = align_up(o + bytes, 256); return r; };
   L.off_tasks = take((size_t)L.max_tasks * sizeof(mk_task));
-  L.off_ranges = take((size_t)(1 + max_waves_bound(c)) * kMaxWorkgroups * 2 * 4);
+  L.off_ranges = take((size_t)(1 + max_waves_bound(c)) * nw_bound * 2 * 4);
   L.off_ctr = take((size_t)L.n_ctr * MK_CTR_PAD * 4);
   L.off_err = take(MK_ERR_WORDS * 4);
   L.off_layers = take((size_t)Lr * sizeof(mk_layer_dev));
@@ -139,8 +146,8 @@ Layout make_layout(const mk_config* c, int32_t max_blocks) {
   L.off_oout = take((size_t)Lr * B * d * 4);
   L.off_pml = take((size_t)2 * B * c->n_q_heads * L.max_splits * 2 * 4);
   L.off_po = take((size_t)2 * B * c->n_q_heads * L.max_splits * hd * 4);
-  L.off_lmbest = take((size_t)max_lm_tiles(c) * B * 2 * 4);
-  L.off_trace = take((size_t)L.max_tasks * 16 * 8);
+  L.off_lmbest = take((size_t)max_lm_tiles(c, nw_bound) * B * 2 * 4);
+  L.off_trace = take(trace ? (size_t)L.max_tasks * 16 * 8 : 0);
   L.total = o;
   return L;
 }
@@ -742,7 +749,7 @@ struct mk_handle {
   size_t ws_bytes;
   int32_t max_blocks;
   int32_t num_pages;
-  std::vector<mk_layer_dev> layers;
+  mk_layer_dev layers[128];   // one per layer (n_layers <= 128)
   const uint16_t* embed;
   const uint16_t* lm_head;
   const uint16_t* final_norm;
@@ -753,22 +760,18 @@ struct mk_handle {
   mk_sched_opts opts;
   hipStream_t last_stream;
   int device;
+  bool in_scratch;            // bound to the library's per-device scratch array
 };
 
-extern "C" {
+namespace {
+constexpr int kMaxDevices = 16;
+// handles of mk_init_noalloc: one per device, like the scratch array they use
+mk_handle g_noalloc_handle[kMaxDevices];
 
-size_t mk_workspace_size(const mk_config* cfg, int32_t max_blocks_per_seq) {
-  if (validate_config(cfg) != MK_OK || max_blocks_per_seq < 1) return 0;
-  return make_layout(cfg, max_blocks_per_seq).total;
-}
-
-int mk_init(const mk_config* cfg, const mk_weights* w, const mk_kv_pool* kv, void* workspace,
-            size_t ws_bytes, int32_t max_blocks_per_seq, mk_handle** out) {
-  if (!out) return MK_E_INVAL;
-  *out = nullptr;
+int check_init_args(const mk_config* cfg, const mk_weights* w, const mk_kv_pool* kv, int32_t max_blocks) {
   int rc = validate_config(cfg);
   if (rc != MK_OK) return rc;
-  if (!w || !kv || !workspace || max_blocks_per_seq < 1) return MK_E_INVAL;
+  if (!w || !kv || max_blocks < 1) return MK_E_INVAL;
   if (!w->embed || !w->lm_head || !w->final_norm || !w->layers || !kv->k || !kv->v || kv->num_pages < 1)
     return MK_E_INVAL;
   const bool moe = cfg->n_experts > 0;
@@ -779,21 +782,21 @@ int mk_init(const mk_config* cfg, const mk_weights* w, const mk_kv_pool* kv, voi
     if (moe && !lw.w_router) return MK_E_INVAL;
     if (!moe && !lw.ffn_norm) return MK_E_INVAL;
   }
-  Layout lay = make_layout(cfg, max_blocks_per_seq);
-  if (ws_bytes < lay.total) return MK_E_NOMEM;
-  if (((uintptr_t)workspace) % 256 != 0) return MK_E_INVAL;
-  mk_handle* h = new (std::nothrow) mk_handle();
-  if (!h) return MK_E_INVAL;
+  return MK_OK;
+}
+
+// Fill a handle over the workspace ws (device) and clear / upload it.
+int bind_handle(mk_handle* h, const mk_config* cfg, const mk_weights* w, const mk_kv_pool* kv, char* ws,
+                size_t ws_bytes, int32_t max_blocks, const Layout& lay, int device) {
   h->cfg = *cfg;
   h->lay = lay;
-  h->ws = static_cast<char*>(workspace);
+  h->ws = ws;
   h->ws_bytes = ws_bytes;
-  h->max_blocks = max_blocks_per_seq;
+  h->max_blocks = max_blocks;
   h->num_pages = kv->num_pages;
   h->embed = static_cast<const uint16_t*>(w->embed);
   h->lm_head = static_cast<const uint16_t*>(w->lm_head);
   h->final_norm = static_cast<const uint16_t*>(w->final_norm);
-  h->layers.resize(cfg->n_layers);
   for (int l = 0; l < cfg->n_layers; ++l) {
     const mk_layer_weights& lw = w->layers[l];
     mk_layer_dev& ld = h->layers[l];
@@ -811,17 +814,73 @@ int mk_init(const mk_config* cfg, const mk_weights* w, const mk_kv_pool* kv, voi
   h->have_plan = false;
   h->batch = 0;
   h->last_stream = nullptr;
-  if (hipGetDevice(&h->device) != hipSuccess) { delete h; return MK_E_HIP; }
-  std::vector<double> invf(cfg->head_dim / 2);
+  h->device = device;
+  // RoPE inverse frequencies (head dim <= 128: at most 64 values)
+  double invf[64];
   for (int i = 0; i < cfg->head_dim / 2; ++i)
     invf[i] = std::pow((double)cfg->rope_theta, -2.0 * i / (double)cfg->head_dim);
   if (hipMemset(h->ws, 0, lay.total) != hipSuccess ||
-      hipMemcpy(h->ws + lay.off_layers, h->layers.data(), h->layers.size() * sizeof(mk_layer_dev),
+      hipMemcpy(h->ws + lay.off_layers, h->layers, (size_t)cfg->n_layers * sizeof(mk_layer_dev),
                 hipMemcpyHostToDevice) != hipSuccess ||
-      hipMemcpy(h->ws + lay.off_invf, invf.data(), invf.size() * 8, hipMemcpyHostToDevice) != hipSuccess) {
-    delete h;
+      hipMemcpy(h->ws + lay.off_invf, invf, (size_t)(cfg->head_dim / 2) * 8, hipMemcpyHostToDevice) != hipSuccess)
     return MK_E_HIP;
+  return MK_OK;
+}
+}  // namespace
+
+extern "C" {
+
+size_t mk_workspace_size(const mk_config* cfg, int32_t max_blocks_per_seq) {
+  if (validate_config(cfg) != MK_OK || max_blocks_per_seq < 1) return 0;
+  return make_layout(cfg, max_blocks_per_seq).total;
+}
+
+int mk_init(const mk_config* cfg, const mk_weights* w, const mk_kv_pool* kv, void* workspace,
+            size_t ws_bytes, int32_t max_blocks_per_seq, mk_handle** out) {
+  if (!out) return MK_E_INVAL;
+  *out = nullptr;
+  int rc = check_init_args(cfg, w, kv, max_blocks_per_seq);
+  if (rc != MK_OK) return rc;
+  if (!workspace) return MK_E_INVAL;
+  Layout lay = make_layout(cfg, max_blocks_per_seq);
+  if (ws_bytes < lay.total) return MK_E_NOMEM;
+  if (((uintptr_t)workspace) % 256 != 0) return MK_E_INVAL;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MK_E_HIP;
+  mk_handle* h = new (std::nothrow) mk_handle();
+  if (!h) return MK_E_INVAL;
+  h->in_scratch = false;
+  rc = bind_handle(h, cfg, w, kv, static_cast<char*>(workspace), ws_bytes, max_blocks_per_seq, lay, dev);
+  if (rc != MK_OK) {
+    delete h;
+    return rc;
   }
+  *out = h;
+  return MK_OK;
+}
+
+int mk_init_noalloc(const mk_config* cfg, const mk_weights* w, const mk_kv_pool* kv, int32_t max_blocks_per_seq,
+                    mk_handle** out) {
+  if (!out) return MK_E_INVAL;
+  *out = nullptr;
+  int rc = check_init_args(cfg, w, kv, max_blocks_per_seq);
+  if (rc != MK_OK) return rc;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MK_E_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return MK_E_UNSUPPORTED;
+  rc = device_cu_count(&cus);
+  if (rc != MK_OK) return rc;
+  void* scratch = nullptr;
+  size_t cap = 0;
+  rc = mk_scratch_region(&scratch, &cap);   // this device's array (looked up once per device)
+  if (rc != MK_OK) return rc;
+  // schedules of at most one workgroup per CU, no task trace
+  Layout lay = make_layout(cfg, max_blocks_per_seq, cus, false);
+  if (lay.total > cap) return MK_E_NOMEM;
+  mk_handle* h = &g_noalloc_handle[dev];
+  h->in_scratch = true;
+  rc = bind_handle(h, cfg, w, kv, static_cast<char*>(scratch), cap, max_blocks_per_seq, lay, dev);
+  if (rc != MK_OK) return rc;
   *out = h;
   return MK_OK;
 }
@@ -835,7 +894,8 @@ int mk_build_schedule(mk_handle* h, int32_t batch_size, const mk_sched_opts* opt
     int rc = device_cu_count(&nw);
     if (rc != MK_OK) return rc;
   }
-  if (nw > kMaxWorkgroups) return MK_E_UNSUPPORTED;
+  if (nw > h->lay.nw_bound) return MK_E_UNSUPPORTED;
+  if ((o.flags & MK_SCHED_TRACE) && !h->lay.has_trace) return MK_E_UNSUPPORTED;
   Plan p;
   int rc = build_plan(&h->cfg, batch_size, h->max_blocks, &o, nw, &p);
   if (rc != MK_OK) return rc;
@@ -990,7 +1050,10 @@ int mk_tap_offset(const mk_handle* h, int32_t tap, size_t* offset, size_t* bytes
     case MK_TAP_TOPK_WEIGHTS: *offset = L.off_topw; *bytes = c.n_experts > 0 ? Lr * B * c.top_k * 4 : 0; break;
     case MK_TAP_FFN_OUT: *offset = L.off_fo; *bytes = Lr * B * d * 4; break;
     case MK_TAP_ATTN_OUT: *offset = L.off_oout; *bytes = Lr * B * d * 4; break;
-    case MK_TAP_TRACE: *offset = L.off_trace; *bytes = (size_t)(h->have_plan ? h->plan.tasks.size() : 0) * 128; break;
+    case MK_TAP_TRACE:
+      *offset = L.off_trace;
+      *bytes = L.has_trace ? (size_t)(h->have_plan ? h->plan.tasks.size() : 0) * 128 : 0;
+      break;
     default: return MK_E_INVAL;
   }
   return MK_OK;
@@ -1025,7 +1088,14 @@ int mk_plan_simulate(const mk_config* cfg, int32_t batch_size, int32_t max_block
   return simulate(cfg, batch_size, p, n_workgroups, seq_lens, n_active_experts, stuck_task);
 }
 
-void mk_destroy(mk_handle* h) { delete h; }
+void mk_destroy(mk_handle* h) {
+  if (!h) return;
+  if (h->in_scratch) {   // a per-device handle of mk_init_noalloc: only forget the schedule
+    h->have_plan = false;
+    return;
+  }
+  delete h;
+}
 
 const char* mk_strerror(int code) {
   switch (code) {

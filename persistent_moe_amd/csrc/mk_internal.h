@@ -157,6 +157,10 @@ struct mk_kargs {
   uint64_t* trace; // [n_tasks][4] or null
 };
 
+// The library's per-device scratch array (mk_kernel.hip): its address on
+// the current device (looked up once per device) and its size in bytes.
+extern "C" int mk_scratch_region(void** ptr, size_t* bytes);
+
 // host entry of the device code (mk_kernel.hip)
 // wg_ranges: (1 + n_waves) blocks of [n_wg][2] (block 0: the whole step,
 // block 1 + v: wave v, used by the one-launch-per-wave ablation)

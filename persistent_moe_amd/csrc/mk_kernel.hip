@@ -33,6 +33,7 @@
 // claim queues whose head is an atomic counter (page 1, "Scheduling").
 
 #include <hip/hip_runtime.h>
+#include <mutex>
 #include <type_traits>
 #include <stdint.h>
 
@@ -2296,6 +2297,37 @@ extern "C" __global__ void __launch_bounds__(MK_THREADS, 1) mk_persistent(mk_kar
       stc(ctrp(a, MK_CG_DONE), 0);
     }
   }
+}
+
+// ------------------------------------------------------- per-device scratch
+// The workspace of the handle made by mk_init_noalloc: a file-scope device
+// array, of which every device the library runs on holds its own copy until
+// the process ends.  On the host the array's name stands for a host-side
+// placeholder, not device memory, so host code never passes it: the array's
+// address on each device is looked up once, with that device current, and
+// kept; every later use (kernel arguments, clears, copies) goes through that
+// address.
+static __device__ __align__(256) char scratch[MK_NOALLOC_WS_BYTES];
+
+namespace {
+constexpr int kScratchDevices = 16;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kScratchDevices];
+}  // namespace
+
+extern "C" int mk_scratch_region(void** ptr, size_t* bytes) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MK_E_HIP;
+  if (dev < 0 || dev >= kScratchDevices) return MK_E_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MK_E_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  *bytes = MK_NOALLOC_WS_BYTES;
+  return MK_OK;
 }
 
 // ------------------------------------------------------------------ launch

@@ -31,7 +31,8 @@ ORDER = {"tuned": 0, "interleaved": 1, "attention_first": 2, "partitioned": 3}
 LAUNCH = {"persistent": 0, "per_opcode": 1}
 TAPS = {"x": 0, "xn": 1, "qkv": 2, "attn": 3, "router_logits": 4, "topk_ids": 5, "topk_weights": 6,
         "ffn_out": 7, "attn_out": 8, "trace": 9}
-EXPORTS = ["mk_workspace_size", "mk_init", "mk_build_schedule", "mk_decode_step", "mk_decode_step_sample",
+EXPORTS = ["mk_workspace_size", "mk_init", "mk_init_noalloc", "mk_build_schedule", "mk_decode_step",
+           "mk_decode_step_sample",
            "mk_get_status", "mk_tap_offset", "mk_plan_schedule", "mk_plan_simulate", "mk_destroy", "mk_strerror"]
 MK_SAMPLE_ADVANCE = 1
 
@@ -104,6 +105,8 @@ def load(path: Optional[str] = None):
     L.mk_workspace_size.restype = ctypes.c_size_t
     L.mk_init.argtypes = [ctypes.POINTER(mk_config), ctypes.POINTER(mk_weights), ctypes.POINTER(mk_kv_pool),
                           P, ctypes.c_size_t, ctypes.c_int32, ctypes.POINTER(P)]
+    L.mk_init_noalloc.argtypes = [ctypes.POINTER(mk_config), ctypes.POINTER(mk_weights),
+                                  ctypes.POINTER(mk_kv_pool), ctypes.c_int32, ctypes.POINTER(P)]
     L.mk_build_schedule.argtypes = [P, ctypes.c_int32, ctypes.POINTER(mk_sched_opts)]
     L.mk_decode_step.argtypes = [P, P, P, P, P, P, P]
     L.mk_decode_step_sample.argtypes = [P, P, P, P, P, P, ctypes.POINTER(mk_sampling), P, P]
@@ -122,7 +125,7 @@ def load(path: Optional[str] = None):
     L.mk_destroy.restype = None
     L.mk_strerror.argtypes = [ctypes.c_int]
     L.mk_strerror.restype = ctypes.c_char_p
-    for name in ("mk_init", "mk_build_schedule", "mk_decode_step", "mk_decode_step_sample", "mk_get_status",
+    for name in ("mk_init", "mk_init_noalloc", "mk_build_schedule", "mk_decode_step", "mk_decode_step_sample", "mk_get_status",
                  "mk_tap_offset",
                  "mk_plan_schedule", "mk_plan_simulate"):
         getattr(L, name).restype = ctypes.c_int
@@ -177,6 +180,13 @@ def mk_init(cfg: mk_config, weights: mk_weights, kv: mk_kv_pool, workspace_ptr: 
     _check(load().mk_init(ctypes.byref(cfg), ctypes.byref(weights), ctypes.byref(kv),
                           ctypes.c_void_p(workspace_ptr), ws_bytes, max_blocks_per_seq, ctypes.byref(h)),
            "mk_init")
+    return h
+
+
+def mk_init_noalloc(cfg: mk_config, weights: mk_weights, kv: mk_kv_pool, max_blocks_per_seq: int) -> ctypes.c_void_p:
+    h = ctypes.c_void_p()
+    _check(load().mk_init_noalloc(ctypes.byref(cfg), ctypes.byref(weights), ctypes.byref(kv), max_blocks_per_seq,
+                                  ctypes.byref(h)), "mk_init_noalloc")
     return h
 
 
