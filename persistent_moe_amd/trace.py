@@ -55,7 +55,11 @@ def summarize(tr: dict) -> dict:
         s[0] += 1
         s[1] += (end[i] - ready[i]) * TICK_US
         s[2] += (ready[i] - start[i]) * TICK_US
-        st, cp, so = raw[i, 2], raw[i, 3], raw[i, 4]
+        # staged (mark 0), the compute waves' last row group (mark 4, set by
+        # the first compute wave; mark 1 is the control wave's), stores
+        # acknowledged (mark 2)
+        st, so = raw[i, 2], raw[i, 4]
+        cp = raw[i, 6] if raw[i, 6] >= st and raw[i, 6] else raw[i, 3]
         if st and cp and so:
             ph = phases[name]
             ph[0].append((st - raw[i, 1]) * TICK_US)
@@ -73,6 +77,27 @@ def summarize(tr: dict) -> dict:
         pl = per_layer[t.layer]
         pl[0] = min(pl[0], start[i] * TICK_US)
         pl[1] = max(pl[1], end[i] * TICK_US)
+    # per-layer critical path: when the last task of each kind in layer l
+    # finished (its signal), relative to the end of the norm entering l
+    kinds = {"ADD_RMSNORM": "norm", "QKV_PROJ": "qkv", "ROUTER_GEMM": "routing", "ATTN_DRAIN": "attention+combine",
+             "ATTN_DECODE": "attention", "ATTN_COMBINE": "combine", "MOE_UPGATE_ACT_DRAIN": "moe_upgate",
+             "O_PROJ": "o_proj", "MOE_DOWN_DRAIN": "moe_down", "FFN_UPGATE_ACT": "ffn_upgate", "FFN_DOWN": "ffn_down"}
+    last = defaultdict(dict)
+    for i, t in enumerate(tasks):
+        k = kinds.get(OPCODES[t.op])
+        if k is None:
+            continue
+        e = end[i] * TICK_US
+        last[t.layer][k] = max(last[t.layer].get(k, 0.0), e)
+    crit = defaultdict(list)
+    layers = sorted(l for l in last if "norm" in last[l])
+    for l in layers[1:-1]:
+        n0 = last[l]["norm"]
+        for k, v in last[l].items():
+            if k != "norm":
+                crit[k].append(v - n0)
+        if l + 1 in last and "norm" in last[l + 1]:
+            crit["next_norm"].append(last[l + 1]["norm"] - n0)
     step_us = (end.max()) * TICK_US
     n_wg = int(wg.max()) + 1
     idle_tail = float(np.mean([step_us - end[wg == w].max() * TICK_US for w in range(n_wg)]))
@@ -84,6 +109,8 @@ def summarize(tr: dict) -> dict:
                    for k, v in sorted(per_op.items(), key=lambda kv: -kv[1][1])},
         "per_layer": {int(k): {"first_start_us": round(v[0], 2), "last_end_us": round(v[1], 2)}
                       for k, v in sorted(per_layer.items())},
+        "layer_critical_path_median_us": {k: round(float(np.median(v)), 2)
+                                          for k, v in sorted(crit.items(), key=lambda kv: np.median(kv[1]))},
         "phases_median_us": {k: {"stage": round(float(np.median(v[0])), 2),
                                  "compute": round(float(np.median(v[1])), 2),
                                  "store_ack": round(float(np.median(v[2])), 2),
