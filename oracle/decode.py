@@ -58,6 +58,22 @@ def bf16_round(x: np.ndarray) -> np.ndarray:
     return np.ldexp(np.rint(m * 256.0) / 256.0, e)
 
 
+def e4m3_decode(codes: np.ndarray) -> np.ndarray:
+    """Values of OCP FP8 E4M3 (e4m3fn) codes, from the format's definition.
+
+    Bit 7 is the sign, bits 6-3 the exponent e (bias 7), bits 2-0 the
+    mantissa m: e > 0 gives 2**(e - 7) * (1 + m/8), e = 0 the subnormal
+    2**-6 * m/8; e = 15 with m = 7 is NaN (the format has no infinities).
+    """
+    c = np.asarray(codes, dtype=np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    mag = np.where(e > 0, np.ldexp(1.0 + m / 8.0, e - 7), np.ldexp(m / 8.0, -6))
+    out = sign * mag
+    return np.where((e == 15) & (c & 0x7 == 7), np.nan, out)
+
+
 def rms_norm(x: np.ndarray, gain: np.ndarray, eps: float) -> np.ndarray:
     """x / sqrt(mean(x^2) + eps) * gain  (the ADD_RMSNORM task's normalisation)."""
     return x / np.sqrt(np.mean(x * x) + eps) * gain
@@ -216,10 +232,15 @@ class Weights:
             wlmod.gen_tensor(self.seed, name, shape, layer=layer)))
 
     def expert(self, layer: int, e: int):
-        ug = self._get(("w_upgate", layer, e), lambda: _f64(wlmod.gen_tensor(
-            self.seed, "w_upgate", self.shapes["w_upgate"], layer=layer, expert=e)))
-        dn = self._get(("w_down", layer, e), lambda: _f64(wlmod.gen_tensor(
-            self.seed, "w_down", self.shapes["w_down"], layer=layer, expert=e)))
+        def make(name):
+            w = wlmod.gen_tensor(self.seed, name, self.shapes[name], layer=layer, expert=e)
+            if not self.cfg.expert_fp8:
+                return _f64(w)
+            # FP8 storage: the expert computes with s_r * E4M3(q[r, k])
+            codes, scale = wlmod.quantize_e4m3_rows(w)
+            return e4m3_decode(codes.numpy()) * scale.numpy().astype(np.float64)[:, None]
+        ug = self._get(("w_upgate", layer, e), lambda: make("w_upgate"))
+        dn = self._get(("w_down", layer, e), lambda: make("w_down"))
         return ug, dn
 
     def router_bias(self, layer: int) -> Optional[np.ndarray]:

@@ -69,6 +69,7 @@ class ModelConfig:
     swa_window: int = 0        # 0: every layer attends to the whole context
     swa_period: int = 0        # layer l is global iff l % swa_period == swa_period - 1
     router_zipf: float = 0.0   # > 0: each layer's router has a bias that skews routing (router_bias)
+    expert_fp8: bool = False   # expert weights stored as E4M3 codes with a per-row scale (quantize_e4m3_rows)
 
     @property
     def group(self) -> int:
@@ -128,6 +129,7 @@ MOE_30B = ModelConfig(
 
 MOE_30B_SWA = replace(MOE_30B, name="moe-30b-a3.3b-swa", swa_window=4096, swa_period=4)
 MOE_30B_ZIPF = replace(MOE_30B, name="moe-30b-a3.3b-zipf", router_zipf=1.2)
+MOE_30B_FP8 = replace(MOE_30B, name="moe-30b-a3.3b-fp8-experts", expert_fp8=True)
 
 WORKLOADS = {
     "tiny": Workload("tiny-moe-bs1-ctx64", TINY_MOE, batch=1, ctx="fixed:64", steps=8, seed=0),
@@ -141,6 +143,9 @@ WORKLOADS = {
     # bias that favours a seeded few experts per layer (Zipf ranks)
     "moe30b_bs8_zipf": Workload("moe30b-bs8-ragged-zipf", MOE_30B_ZIPF, batch=8, ctx="loguniform:512:16384",
                                 steps=256, seed=5, swap_every=32),
+    # the bs=1 8K workload (same seed, so the same bf16 draws) with the expert
+    # weights streamed as FP8
+    "moe30b_fp8": Workload("moe30b-bs1-ctx8k-fp8", MOE_30B_FP8, batch=1, ctx="fixed:8192", steps=256, seed=2),
 }
 
 
@@ -494,6 +499,26 @@ def router_bias(seed: int, cfg: ModelConfig, layer: int) -> Optional[torch.Tenso
     rank[permutation(seed, "router_rank_layer%d" % layer, cfg.n_experts)] = np.arange(cfg.n_experts)
     b = -cfg.router_zipf * np.log(rank.astype(np.float64) + 1.0)
     return torch.from_numpy(b.astype(np.float32)).to(torch.bfloat16)
+
+
+E4M3_MAX = 448.0      # the largest finite OCP E4M3 (e4m3fn) value
+
+
+def quantize_e4m3_rows(w: torch.Tensor):
+    """Per-row FP8 storage of a weight matrix [..., rows, K] (bf16 or float).
+
+    Each row r gets the scale s_r = max_k |w[r, k]| / 448 (float32; 1 for an
+    all-zero row) and the codes q[r, k] = E4M3(w[r, k] / s_r), rounded to
+    nearest even (torch's float8_e4m3fn conversion), so that s_r * q[r, k]
+    approximates w[r, k].  Returns (codes as uint8, scales as float32).  The
+    same operations on the CPU and on a GPU give the same bits (IEEE float32
+    division and a correctly rounded conversion).
+    """
+    wf = w.float()
+    amax = wf.abs().amax(dim=-1)
+    scale = torch.where(amax > 0, amax / E4M3_MAX, torch.ones_like(amax))
+    q = (wf / scale.unsqueeze(-1)).to(torch.float8_e4m3fn)
+    return q.view(torch.uint8), scale
 
 
 def kv_key(seed: int, seq_id: int, layer: int, which: str) -> int:

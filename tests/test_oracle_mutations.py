@@ -212,3 +212,32 @@ def test_sampling_pin_catches_planted_mistake(monkeypatch, kind):
         except AssertionError:
             caught += 1
     assert caught > 0, kind
+
+
+def _e4m3_bias8(codes):
+    c = np.asarray(codes, dtype=np.int64)
+    e, m = (c >> 3) & 0xF, (c & 7).astype(np.float64)
+    mag = np.where(e > 0, np.ldexp(1.0 + m / 8.0, e - 8), np.ldexp(m / 8.0, -7))
+    return np.where(c & 0x80, -mag, mag)
+
+
+def _e4m3_no_subnormals(codes):
+    v = _orig_e4m3(codes)
+    e = (np.asarray(codes) >> 3) & 0xF
+    return np.where(e == 0, 0.0, v)
+
+
+_orig_e4m3 = O.e4m3_decode
+
+
+@pytest.mark.parametrize("fn", [_e4m3_bias8, _e4m3_no_subnormals])
+def test_e4m3_pins_catch_planted_mistakes(monkeypatch, fn):
+    monkeypatch.setattr(O, "e4m3_decode", fn)
+    caught = 0
+    for pin in (P.test_e4m3_decode_matches_the_library_conversion_on_every_code,
+                P.test_e4m3_decode_closed_form_values):
+        try:
+            pin()
+        except AssertionError:
+            caught += 1
+    assert caught > 0

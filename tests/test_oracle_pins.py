@@ -485,3 +485,31 @@ def test_router_bias_moves_selection_and_gate_weights():
         w1 = 1.0 / (1.0 + math.exp(0.7 - 1.5))
         assert np.allclose(tap.route.weights, [w1, 1 - w1], atol=1e-14)
         assert np.allclose(tap.router_logits, bias)
+
+
+# ---------------------------------------------------------------- FP8 experts
+def test_e4m3_decode_matches_the_library_conversion_on_every_code():
+    codes = np.arange(256)
+    ours = O.e4m3_decode(codes)
+    ref = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).float().numpy()
+    assert np.array_equal(np.isnan(ours), np.isnan(ref))
+    assert np.array_equal(ours[~np.isnan(ours)], ref[~np.isnan(ref)].astype(np.float64))
+
+
+def test_e4m3_decode_closed_form_values():
+    v = O.e4m3_decode(np.array([0x00, 0x01, 0x07, 0x08, 0x38, 0x3C, 0x7E, 0xB8, 0x7F]))
+    assert v[0] == 0.0 and v[1] == 2.0 ** -9 and v[2] == 7 * 2.0 ** -9 and v[3] == 2.0 ** -6
+    assert v[4] == 1.0 and v[5] == 1.5 and v[6] == 448.0 and v[7] == -1.0 and np.isnan(v[8])
+
+
+def test_fp8_expert_rows_round_trip_within_half_a_code_step():
+    wl = W.WORKLOADS["tiny"].with_(model=replace(W.TINY_MOE, expert_fp8=True))
+    ug_q, dn_q = O.Weights(wl).expert(1, 3)
+    ug = W.gen_tensor(wl.seed, "w_upgate", W.weight_shapes(wl.model)["w_upgate"], layer=1, expert=3).double().numpy()
+    # each row's largest magnitude maps to 448 and is exact; every element is
+    # within half an E4M3 step (2**-4 relative for normal values) of its weight
+    amax = np.abs(ug).max(axis=1, keepdims=True)
+    assert np.allclose(np.abs(ug_q).max(axis=1, keepdims=True), amax, rtol=1e-6)
+    assert np.all(np.abs(ug_q - ug) <= np.maximum(np.abs(ug) * 2.0 ** -4, amax / 448 * 2.0 ** -9) + 1e-12)
+    assert not np.array_equal(ug_q, ug)
+    assert dn_q.shape == W.weight_shapes(wl.model)["w_down"]
