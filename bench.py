@@ -74,6 +74,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bs8", action="store_true", help="skip the batch-8 leg of the metric")
     ap.add_argument("--no-ablation", action="store_true", help="skip the wave-order / per-opcode ablation")
+    ap.add_argument("--no-fp8", action="store_true", help="skip the FP8-expert leg")
     ap.add_argument("--verbose", action="store_true")
     ap.add_argument("--trace", default="", help="after timing, trace one step and write a summary here")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -332,10 +333,17 @@ def main():
     del eng
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
+    legs = []
     if not args.no_bs8 and args.workload == "moe30b":
         # the batch-8 leg of the metric: uniform routing (random router) and
         # concentrated routing (Zipf router bias), ragged contexts
-        for key, name in (("bs8", "moe30b_bs8"), ("bs8_zipf", "moe30b_bs8_zipf")):
+        legs += [("bs8", "moe30b_bs8"), ("bs8_zipf", "moe30b_bs8_zipf")]
+    if not args.no_fp8 and args.workload == "moe30b":
+        # the bs=1 8K workload with the expert weights stored as E4M3 codes
+        # and float32 row scales (the rest bf16)
+        legs.append(("fp8_experts", "moe30b_fp8"))
+    if legs:
+        for key, name in legs:
             wl8 = W.WORKLOADS[name]
             log(f"workload {wl8.name}: building inputs")
             n8 = max(8, args.steps // 2)
@@ -343,11 +351,13 @@ def main():
             w8, k8, p8, r8 = time_steps(eng8, args.warmup, n8)
             m8 = step_metrics(wl8.model, wl8.batch, w8, k8, p8, r8, n8)
             m8["steps"] = n8
-            m8["distinct_experts_per_layer"] = round(float(np.mean(
+            m8["distinct_experts_per_layer"] = wl8.model.top_k if r8 is None else round(float(np.mean(
                 [len(np.unique(r8[i].reshape(wl8.model.n_layers, -1)[l])) for i in range(n8)
                  for l in range(wl8.model.n_layers)])), 2)
             m8["config"] = {"workload": wl8.name, "batch": wl8.batch, "router_zipf": wl8.model.router_zipf,
                             "contexts": [W.context_length(wl8, b) for b in range(wl8.batch)]}
+            if wl8.model.expert_fp8:
+                m8["config"]["experts"] = "e4m3 codes + f32 row scales"
             out[key] = m8
             log(f"{key}: {m8['value']:.1f} tok/s, {m8['ms_per_step']:.3f} ms/step, "
                 f"{m8['roofline']['frac']:.1%} of HBM SoL, {m8['distinct_experts_per_layer']} experts/layer")

@@ -123,6 +123,9 @@ typedef struct mk_config {
   int32_t swa_period;      /* layer l is global iff l % period == period - 1 */
   float rope_theta;        /* RoPE base                                      */
   float rms_eps;           /* RMSNorm epsilon                                */
+  int32_t expert_fp8;      /* 1: expert weights are FP8 (see mk_layer_weights);
+                              MoE only, max_batch 1, d and I <= 2048 and
+                              multiples of 16                               */
 } mk_config;
 
 /* Per-layer weights, all device pointers to bf16, row-major [out][in].
@@ -143,7 +146,16 @@ typedef struct mk_config {
  *                                    pages report the megakernel's advantage
  *                                    growing there (page 1, "Benchmark
  *                                    results"); a bias reproduces that skew
- *                                    with synthetic weights.             */
+ *                                    with synthetic weights.
+ *   upgate_scale [E][2I], down_scale [E][d]   float32, with expert_fp8 only:
+ *                                    w_upgate and w_down then hold OCP FP8
+ *                                    E4M3 (e4m3fn) codes, one byte per weight
+ *                                    in the same [out][in] order, and weight
+ *                                    [r][k] = scale[r] * E4M3(code[r][k]).
+ *                                    FP8 weight streaming is on the pages'
+ *                                    roadmap (page 1, "Current limitations":
+ *                                    no FP8/FP4 yet): it halves the bytes of
+ *                                    the largest stream of a MoE step.    */
 typedef struct mk_layer_weights {
   const void* attn_norm;
   const void* ffn_norm;
@@ -153,6 +165,8 @@ typedef struct mk_layer_weights {
   const void* w_upgate;
   const void* w_down;
   const void* router_bias;
+  const void* upgate_scale;
+  const void* down_scale;
 } mk_layer_weights;
 
 typedef struct mk_weights {

@@ -82,6 +82,14 @@ int validate_config(const mk_config* c) {
   const int gd = c->n_q_heads / c->n_kv_heads * c->head_dim;
   if ((size_t)c->max_batch * gd > (size_t)kXsFloats) return MK_E_UNSUPPORTED;
   if (c->swa_window < 0 || c->swa_period < 0) return MK_E_INVAL;
+  if (c->expert_fp8 != 0 && c->expert_fp8 != 1) return MK_E_INVAL;
+  if (c->expert_fp8) {
+    // FP8 experts run the one-row GEMV with x in registers: batch 1, K up
+    // to two 1024-element chunks, rows of whole 16-byte loads
+    if (!moe || c->max_batch != 1) return MK_E_UNSUPPORTED;
+    if (c->d_model > 2048 || c->expert_inter > 2048) return MK_E_UNSUPPORTED;
+    if (c->d_model % 16 != 0 || c->expert_inter % 16 != 0) return MK_E_UNSUPPORTED;
+  }
   // staged GEMV inputs (hi and lo bf16 rows, padded) must fit the LDS staging area
   {
     const long B = c->max_batch;
@@ -781,6 +789,7 @@ int check_init_args(const mk_config* cfg, const mk_weights* w, const mk_kv_pool*
       return MK_E_INVAL;
     if (moe && !lw.w_router) return MK_E_INVAL;
     if (!moe && !lw.ffn_norm) return MK_E_INVAL;
+    if (cfg->expert_fp8 && (!lw.upgate_scale || !lw.down_scale)) return MK_E_INVAL;
   }
   return MK_OK;
 }
@@ -808,6 +817,8 @@ int bind_handle(mk_handle* h, const mk_config* cfg, const mk_weights* w, const m
     ld.w_upgate = static_cast<const uint16_t*>(lw.w_upgate);
     ld.w_down = static_cast<const uint16_t*>(lw.w_down);
     ld.router_bias = static_cast<const uint16_t*>(lw.router_bias);
+    ld.upgate_scale = cfg->expert_fp8 ? static_cast<const float*>(lw.upgate_scale) : nullptr;
+    ld.down_scale = cfg->expert_fp8 ? static_cast<const float*>(lw.down_scale) : nullptr;
     ld.k = static_cast<uint16_t*>(kv->k[l]);
     ld.v = static_cast<uint16_t*>(kv->v[l]);
   }
@@ -960,6 +971,7 @@ int launch_step(mk_handle* h, const int32_t* token_ids, const int32_t* positions
   a.G = c.n_q_heads / c.n_kv_heads; a.E = c.n_experts; a.topk = c.top_k; a.I = c.expert_inter;
   a.F = c.ffn_inter; a.V = c.vocab; a.parallel = c.parallel_block; a.page = c.page_size;
   a.swa_window = c.swa_window; a.swa_period = c.swa_period;
+  a.expert_fp8 = c.expert_fp8;
   a.B = h->batch; a.max_blocks = h->max_blocks; a.num_pages = h->num_pages;
   a.eps = c.rms_eps;
   a.attn_scale = (float)(1.0 / std::sqrt((double)c.head_dim));

@@ -93,6 +93,8 @@ struct mk_layer_dev {
   const uint16_t* w_upgate;
   const uint16_t* w_down;
   const uint16_t* router_bias;   // [E] or null
+  const float* upgate_scale;     // [E][2I] with FP8 experts, else null
+  const float* down_scale;       // [E][d]  with FP8 experts, else null
   uint16_t* k;
   uint16_t* v;
 };
@@ -125,6 +127,7 @@ struct mk_kargs {
   // shapes
   int32_t L, d, Hq, Hkv, hd, G, E, topk, I, F, V;
   int32_t parallel, page, swa_window, swa_period;
+  int32_t expert_fp8;             // expert weights are E4M3 codes with per-row scales
   int32_t B, max_blocks, num_pages;
   float eps, attn_scale;
   int32_t attn_split, max_splits;

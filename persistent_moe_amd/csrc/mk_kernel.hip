@@ -457,12 +457,14 @@ __device__ __forceinline__ void make_uniform(GemvArgs& g) {
   g.hs = g.mode == ROW_ROPE_PAIRS ? 31 - __builtin_clz(g.half) : 31;
 }
 
-// The element offset of a weight row is a 32 x 32 -> 64-bit scalar multiply
-// (row index and row pitch both fit in 32 bits).
-__device__ __forceinline__ const uint16_t* gemv_row(const GemvArgs& g, int r) {
+// The weight row of tile row r, and its element offset: a 32 x 32 -> 64-bit
+// scalar multiply (row index and row pitch both fit in 32 bits).
+__device__ __forceinline__ uint32_t gemv_row_index(const GemvArgs& g, int r) {
   const int p = g.r0 + (r >> g.pm), upper = r & g.pm;
-  const uint32_t row = (uint32_t)(p + ((p >> g.hs) + upper) * g.half);
-  return g.base + (uint64_t)row * (uint32_t)g.ldw;
+  return (uint32_t)(p + ((p >> g.hs) + upper) * g.half);
+}
+__device__ __forceinline__ const uint16_t* gemv_row(const GemvArgs& g, int r) {
+  return g.base + (uint64_t)gemv_row_index(g, r) * (uint32_t)g.ldw;
 }
 
 // Register tile of one row group: WB 16-byte weight loads per lane of each
@@ -834,6 +836,147 @@ __device__ __forceinline__ bool gemv_run(const KA a, Smem& sm, const GemvArgs& g
   if (a->trace && tid_v() == 64) sm.t_mark[4] = wall_clock64();
   if (a->trace && tid_v() == 0 && sm.t_mark[1] == 0) sm.t_mark[1] = wall_clock64();
   return true;
+}
+
+// ------------------------------------------------- FP8 weights, one batch row
+// Expert matrices stored as E4M3 codes (one byte per weight, [out][in]) with
+// a float32 scale per row: row r computes scale[r] * sum_k E4M3(q[r][k]) x[k].
+// The register tile and its loads are the bf16 tile's, byte for byte (16
+// bytes per lane, 1 KB per wave load), but a slot now holds 16 weights, so a
+// K-chunk is 1024 elements; each 16-byte slot is widened to bf16 pairs with
+// v_cvt_scalef32_pk_bf16_fp8 (exact: every E4M3 value is a bf16 value) and
+// multiplied into the hi and lo parts of x as in the bf16 form (24
+// instructions per slot against 8, for half the bytes).  The row scales
+// travel with the weights: lane j of the wave loads row j's scale just before
+// the tile's weight loads, so the wait for the weights covers it.
+template <int KL>
+struct Fp8Tile {
+  static constexpr int WB = MK_WB;           // 16-byte slots per lane per row group
+  static constexpr int RPW = WB >> KL;       // rows per wave per row group
+  u32x4 w[WB];
+  float scv;                                 // lane j < RPW: the scale of the group's row j
+
+  __device__ __forceinline__ static int row0(int grp, int cw) { return (grp * MK_CW + cw - 1) * RPW; }
+
+  __device__ __forceinline__ void load(const GemvArgs& g, const float* scale, int grp, int voff) {
+    const int wave = __builtin_amdgcn_readfirstlane(tid_v() >> 6), lane = tid_v() & 63;
+    const int r0 = row0(grp, wave);
+    {
+      const int r = r0 + lane;
+      const bool ok = lane < RPW && r < g.nrows;
+      __amdgpu_buffer_rsrc_t rs =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(scale), (short)0, 0x7FFFFFFF, 0x00020000);
+      scv = ok ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, (int)(gemv_row_index(g, r) * 4u), 0, 0))
+               : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < RPW; ++j) {
+      const int r = r0 + j;
+      __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint16_t*>(gemv_row(g, r < g.nrows ? r : 0)), (short)0, r < g.nrows ? g.K : 0, 0x00020000);
+#pragma unroll
+      for (int c = 0; c < (1 << KL); ++c)
+        w[(j << KL) + c] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff + c * 1024, 0, 2 /* nontemporal */);
+    }
+  }
+
+  // xrh / xrl: the lane's 16 elements of x per K-chunk c in [2c], [2c + 1]
+  __device__ __forceinline__ void compute(const GemvArgs& g, int grp, const u32x4* xrh, const u32x4* xrl,
+                                          float* ys) {
+    constexpr int CM = (1 << KL) - 1;
+    const int wave = __builtin_amdgcn_readfirstlane(tid_v() >> 6), lane = tid_v() & 63;
+    const int r0 = row0(grp, wave);
+    if (r0 >= g.nrows) return;   // wave-uniform: no rows in this group
+    float acc[WB];
+#pragma unroll
+    for (int u = 0; u < WB; ++u) {
+      const int c = u & CM;
+      const u32x4 v = w[u];
+      const uint32_t vw[4] = {v.x, v.y, v.z, v.w};
+      const u32x4 h0 = xrh[2 * c], h1 = xrh[2 * c + 1], q0 = xrl[2 * c], q1 = xrl[2 * c + 1];
+      const uint32_t hw[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
+      const uint32_t qw[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+      float s = 0.f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        // weights 4q, 4q + 1 and 4q + 2, 4q + 3 of the slot, as bf16 pairs
+        const uint32_t a0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(vw[q], 1.0f, false));
+        const uint32_t a1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(vw[q], 1.0f, true));
+        s = dot2_bf16(a0, hw[2 * q], s);
+        s = dot2_bf16(a1, hw[2 * q + 1], s);
+        s = dot2_bf16(a0, qw[2 * q], s);
+        s = dot2_bf16(a1, qw[2 * q + 1], s);
+      }
+      acc[u] = s;
+    }
+    // add the K-chunks of each row pairwise
+#pragma unroll
+    for (int step = 1; step < (1 << KL); step <<= 1) {
+#pragma unroll
+      for (int i = 0; i < WB / (2 * step); ++i) acc[i] = acc[2 * i] + acc[2 * i + 1];
+    }
+#pragma unroll
+    for (int j = 0; j < RPW; ++j) {
+      const int r = r0 + j;
+      const float sv = wave_sum(acc[j]) * __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, scv), j));
+      if (lane == 0 && r < g.nrows && g.nb > 0) {
+        if (g.out) stc(g.out + r, sv);
+        else ys[r * NBMAX] = sv;
+      }
+    }
+  }
+};
+
+template <int KL>
+__device__ __forceinline__ bool gemv_fp8_run(const KA a, Smem& sm, const GemvArgs& g_in, const StageArgs& s,
+                                             const float* scale) {
+  Fp8Tile<KL> T[MK_NT];
+  GemvArgs g = g_in;
+  make_uniform(g);
+  scale = uniform_ptr(scale);
+  constexpr int PER = MK_CW * Fp8Tile<KL>::RPW;
+  const int ng = (g.nrows + PER - 1) / PER;
+  const bool cw = (tid_v() >> 6) != 0;
+  const int lane = tid_v() & 63;
+  const int voff = lane * 16;
+  if (cw) {
+#pragma unroll
+    for (int u = 0; u < MK_NT; ++u)
+      if (u < ng) T[u].load(g, scale, u, voff);
+  }
+  constexpr int kp = 1024 << KL;   // staged row stride: whole 1024-element chunks
+  if (!wait_and_stage(a, sm, s, kp)) return false;
+  if (cw) {
+    const uint16_t* xh = reinterpret_cast<const uint16_t*>(sm.xs) + lane * 16;
+    const uint16_t* xl = xh + s.nb * kp;
+    u32x4 xrh[4], xrl[4];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const bool in = c < (1 << KL);
+      xrh[2 * c] = in ? *reinterpret_cast<const u32x4*>(xh + 1024 * c) : (u32x4){0u, 0u, 0u, 0u};
+      xrh[2 * c + 1] = in ? *reinterpret_cast<const u32x4*>(xh + 1024 * c + 8) : (u32x4){0u, 0u, 0u, 0u};
+      xrl[2 * c] = in ? *reinterpret_cast<const u32x4*>(xl + 1024 * c) : (u32x4){0u, 0u, 0u, 0u};
+      xrl[2 * c + 1] = in ? *reinterpret_cast<const u32x4*>(xl + 1024 * c + 8) : (u32x4){0u, 0u, 0u, 0u};
+    }
+    for (int grp = 0; grp < ng; grp += MK_NT) {
+#pragma unroll
+      for (int u = 0; u < MK_NT; ++u) {
+        if (grp + u < ng) {
+          T[u].compute(g, grp + u, xrh, xrl, sm.ys);
+          if (grp + u + MK_NT < ng) T[u].load(g, scale, grp + u + MK_NT, voff);
+        }
+      }
+    }
+  }
+  if (a->trace && tid_v() == 0 && sm.t_mark[1] == 0) sm.t_mark[1] = wall_clock64();
+  return true;
+}
+
+// One FP8-weight GEMV tile (one batch row): K up to two 1024-element chunks.
+__device__ __forceinline__ bool gemv_fp8(const KA a, Smem& sm, const GemvArgs& g, const StageArgs& s,
+                                         const float* scale) {
+  if (g.K <= 1024) return gemv_fp8_run<0>(a, sm, g, s, scale);
+  return gemv_fp8_run<1>(a, sm, g, s, scale);
 }
 
 // ------------------------------------------------ MFMA GEMV (3 to 8 batch rows)
@@ -2025,6 +2168,7 @@ extern "C" __global__ void __launch_bounds__(MK_THREADS, 1) mk_persistent(mk_kar
       StageArgs st;
       int kind = U_NONE;
       int epi_ae = 0, epi_r0 = 0, epi_nr = 0, epi_p0 = 0, epi_np = 0;
+      const float* fp8_scale = nullptr;   // FP8 expert tile: its row scales
       g.mode = ROW_PLAIN; g.half = 0; g.hd = a->hd; g.nb = B; g.out = nullptr; g.ob = 0;
       g.r0 = t.n0; g.nrows = t.n1 - t.n0;
       st.use_tok = false; st.nb = B; st.wait_idx = t.wait_ctr; st.wait_target = t.wait_target;
@@ -2091,7 +2235,15 @@ extern "C" __global__ void __launch_bounds__(MK_THREADS, 1) mk_persistent(mk_kar
           st.tok[7] = __builtin_amdgcn_readfirstlane((int)r2v.w);
           epi_p0 = tt * a->ug_pairs;
           epi_np = min(a->ug_pairs, a->I - epi_p0);
-          g.base = LAYER_PTR(l, w_upgate) + (long)e * 2 * a->I * a->d; g.ldw = a->d; g.r0 = epi_p0;
+          if (a->expert_fp8) {   // one byte per weight: the row pitch in 16-bit units is d / 2
+            g.base = reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(LAYER_PTR(l, w_upgate)) +
+                                                       (long)e * 2 * a->I * a->d);
+            g.ldw = a->d / 2;
+            fp8_scale = LAYER_PTR(l, upgate_scale) + (long)e * 2 * a->I;
+          } else {
+            g.base = LAYER_PTR(l, w_upgate) + (long)e * 2 * a->I * a->d; g.ldw = a->d;
+          }
+          g.r0 = epi_p0;
           g.nrows = 2 * epi_np; g.K = a->d; g.mode = ROW_GATE_UP; g.half = a->I; g.nb = epi_nr;
           st.base = a->xn + (long)l * B * a->d; st.ld = a->d; st.nb = epi_nr;
           st.K = a->d; st.wait_idx = -1;
@@ -2107,7 +2259,15 @@ extern "C" __global__ void __launch_bounds__(MK_THREADS, 1) mk_persistent(mk_kar
           const int r0 = __builtin_amdgcn_readfirstlane((int)r0v.y);
           const int nr = __builtin_amdgcn_readfirstlane((int)r0v.z);
           const int n0 = tt * a->dn_rows;
-          g.base = LAYER_PTR(l, w_down) + (long)e * a->d * a->I; g.ldw = a->I; g.r0 = n0;
+          if (a->expert_fp8) {
+            g.base = reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(LAYER_PTR(l, w_down)) +
+                                                       (long)e * a->d * a->I);
+            g.ldw = a->I / 2;
+            fp8_scale = LAYER_PTR(l, down_scale) + (long)e * a->d;
+          } else {
+            g.base = LAYER_PTR(l, w_down) + (long)e * a->d * a->I; g.ldw = a->I;
+          }
+          g.r0 = n0;
           g.nrows = min(a->dn_rows, a->d - n0); g.K = a->I; g.nb = nr;
           g.out = a->Y + ((long)l * a->bk + r0) * a->d + n0; g.ob = a->d;
           st.base = a->H + ((long)l * a->bk + r0) * a->I; st.ld = a->I; st.nb = nr; st.K = a->I;
@@ -2118,7 +2278,7 @@ extern "C" __global__ void __launch_bounds__(MK_THREADS, 1) mk_persistent(mk_kar
           break;
       }
       if (kind == U_GEMV) {
-        if (!gemv(a, sm, g, st)) {
+        if (!(fp8_scale ? gemv_fp8(a, sm, g, st, fp8_scale) : gemv(a, sm, g, st))) {
           aborted = true;
           goto unit_done;
         }

@@ -47,12 +47,14 @@ class mk_config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "n_layers", "d_model", "n_q_heads", "n_kv_heads", "head_dim", "vocab", "n_experts", "top_k",
         "expert_inter", "ffn_inter", "parallel_block", "page_size", "max_batch", "swa_window",
-        "swa_period")] + [("rope_theta", ctypes.c_float), ("rms_eps", ctypes.c_float)]
+        "swa_period")] + [("rope_theta", ctypes.c_float), ("rms_eps", ctypes.c_float),
+                          ("expert_fp8", ctypes.c_int32)]
 
 
 class mk_layer_weights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
-        "attn_norm", "ffn_norm", "w_qkv", "w_o", "w_router", "w_upgate", "w_down", "router_bias")]
+        "attn_norm", "ffn_norm", "w_qkv", "w_o", "w_router", "w_upgate", "w_down", "router_bias",
+        "upgate_scale", "down_scale")]
 
 
 class mk_weights(ctypes.Structure):
@@ -151,7 +153,7 @@ def make_config(model, max_batch: int) -> mk_config:
         n_experts=model.n_experts, top_k=model.top_k, expert_inter=model.expert_inter,
         ffn_inter=model.ffn_inter, parallel_block=int(model.parallel_block), page_size=model.page_size,
         max_batch=max_batch, swa_window=model.swa_window, swa_period=model.swa_period,
-        rope_theta=model.rope_theta, rms_eps=model.rms_eps)
+        rope_theta=model.rope_theta, rms_eps=model.rms_eps, expert_fp8=int(model.expert_fp8))
 
 
 MK_SCHED_UNREACHABLE_WAIT = 1

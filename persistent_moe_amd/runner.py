@@ -104,7 +104,11 @@ class DecodeEngine:
                     keys = [W.tensor_key(seed, name, l, e) for e in range(cfg.n_experts)]
                     mean, std = W.tensor_dist(name)
                     W.fill_normal_keyed_(t, keys, mean, std)
-                    lw[name] = t
+                    if cfg.expert_fp8:   # E4M3 codes and per-row scales; the bf16 values are dropped
+                        lw[name], lw[name + "_scale"] = W.quantize_e4m3_rows(t)
+                        del t
+                    else:
+                        lw[name] = t
                 else:
                     lw[name] = gen(name, shp, l)
             rb = W.router_bias(seed, cfg, l)
@@ -121,12 +125,10 @@ class DecodeEngine:
         return lw["router_bias"].float().cpu().numpy().astype(np.float64) if "router_bias" in lw else None
 
     def weight_bytes(self) -> int:
-        n = self.embed.numel() + self.final_norm.numel()
-        if not self.cfg.tied_embeddings:
-            n += self.lm_head.numel()
+        ts = [self.embed, self.final_norm] + ([] if self.cfg.tied_embeddings else [self.lm_head])
         for lw in self.layers:
-            n += sum(t.numel() for t in lw.values())
-        return 2 * n
+            ts += list(lw.values())
+        return sum(t.numel() * t.element_size() for t in ts)
 
     def _admit(self, b: int, seq: W.SequenceSlot, first: bool = False):
         """Put ``seq`` into slot b: write its pre-filled KV into its pages."""
@@ -177,6 +179,8 @@ class DecodeEngine:
             arr[l].w_upgate = lw["w_upgate"].data_ptr()
             arr[l].w_down = lw["w_down"].data_ptr()
             arr[l].router_bias = lw["router_bias"].data_ptr() if "router_bias" in lw else None
+            arr[l].upgate_scale = lw["w_upgate_scale"].data_ptr() if "w_upgate_scale" in lw else None
+            arr[l].down_scale = lw["w_down_scale"].data_ptr() if "w_down_scale" in lw else None
         self._layer_arr = arr
         self._w = mk.mk_weights(embed=self.embed.data_ptr(), lm_head=self.lm_head.data_ptr(),
                                 final_norm=self.final_norm.data_ptr(), layers=arr)

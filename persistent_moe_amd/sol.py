@@ -8,7 +8,8 @@ counted from the actual shapes, the routed experts and the live lengths:
 
 * weights: the embedding rows of the fed tokens, every norm gain, QKV and O
   projections, the router, each *distinct* routed expert of the step (gate,
-  up and down), or the dense FFN, and the LM head;
+  up and down: one byte per weight plus a float32 scale per row when they
+  are stored as FP8), or the dense FFN, and the LM head;
 * KV: for every sequence and layer, K and V of every key it attends to,
   including the token being decoded.
 """
@@ -18,6 +19,8 @@ from typing import Iterable, Sequence
 
 HBM_BYTES_PER_S_MI355X = 8.0e12
 BF16 = 2
+FP8 = 1
+F32 = 4
 
 
 def layer_weight_bytes(cfg, distinct_experts: int) -> int:
@@ -27,7 +30,11 @@ def layer_weight_bytes(cfg, distinct_experts: int) -> int:
     b += d * cfg.attn_dim * BF16
     if cfg.is_moe:
         b += cfg.n_experts * d * BF16              # router
-        b += distinct_experts * 3 * cfg.expert_inter * d * BF16
+        if getattr(cfg, "expert_fp8", False):
+            # codes, then one scale per row: 2I gate/up rows and d down rows
+            b += distinct_experts * (3 * cfg.expert_inter * d * FP8 + (2 * cfg.expert_inter + d) * F32)
+        else:
+            b += distinct_experts * 3 * cfg.expert_inter * d * BF16
     else:
         b += d * BF16                              # second norm gain
         b += 3 * cfg.ffn_inter * d * BF16

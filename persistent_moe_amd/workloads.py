@@ -502,23 +502,51 @@ def router_bias(seed: int, cfg: ModelConfig, layer: int) -> Optional[torch.Tenso
 
 
 E4M3_MAX = 448.0      # the largest finite OCP E4M3 (e4m3fn) value
+# 1/448 rounded to float32: the row scale is amax times this (one float32
+# multiply, the same bits on any device)
+INV_E4M3_MAX_F32 = float(np.float32(1.0 / 448.0))
+
+
+def _pow2_f64(n: torch.Tensor) -> torch.Tensor:
+    """2.0 ** n for integer tensors n in [-1022, 1023], built from the bits."""
+    return ((n.to(torch.int64) + 1023) << 52).view(torch.float64)
 
 
 def quantize_e4m3_rows(w: torch.Tensor):
     """Per-row FP8 storage of a weight matrix [..., rows, K] (bf16 or float).
 
-    Each row r gets the scale s_r = max_k |w[r, k]| / 448 (float32; 1 for an
-    all-zero row) and the codes q[r, k] = E4M3(w[r, k] / s_r), rounded to
-    nearest even (torch's float8_e4m3fn conversion), so that s_r * q[r, k]
-    approximates w[r, k].  Returns (codes as uint8, scales as float32).  The
-    same operations on the CPU and on a GPU give the same bits (IEEE float32
-    division and a correctly rounded conversion).
+    Each row r gets the scale s_r = float32(max_k |w[r, k]| * float32(1/448))
+    (1 for an all-zero row) and the codes q[r, k] = E4M3(w[r, k] / s_r): the
+    quotient in float64, rounded to the nearest value of the E4M3 grid, ties
+    to even, saturating at 448.  Returns (codes as uint8, scales as float32).
+
+    Every operation is exact or correctly rounded (a float32 multiply, a
+    float64 divide, frexp, round-half-even after a power-of-two scaling,
+    integer bit assembly), so a CPU and a GPU produce the same bits; torch's
+    own float8 conversion and its divide-by-scalar are not used, since on a
+    GPU they may take hardware or reciprocal paths.
     """
     wf = w.float()
     amax = wf.abs().amax(dim=-1)
-    scale = torch.where(amax > 0, amax / E4M3_MAX, torch.ones_like(amax))
-    q = (wf / scale.unsqueeze(-1)).to(torch.float8_e4m3fn)
-    return q.view(torch.uint8), scale
+    scale = torch.where(amax > 0, amax * INV_E4M3_MAX_F32, torch.ones_like(amax))
+    y = w.double() / scale.double().unsqueeze(-1)
+    a = y.abs()
+    # binade of a (a = m 2^e, m in [0.5, 1)), at least -6: below 2^-6 the
+    # subnormal step 2^-9 applies; three mantissa bits give a step of 2^(eb-3)
+    _, e = torch.frexp(a)
+    eb = torch.clamp(e.to(torch.int64) - 1, min=-6)
+    k = torch.round(a * _pow2_f64(3 - eb)).to(torch.int64)   # a in steps: 8..16 in a binade, 0..8 below
+    up = k == 16                                              # rounded up into the next binade
+    eb = torch.where(up, eb + 1, eb)
+    k = torch.where(up, torch.full_like(k, 8), k)
+    normal = k >= 8
+    ef = torch.where(normal, eb + 7, torch.zeros_like(eb))     # biased exponent field
+    mf = torch.where(normal, k - 8, k)                          # mantissa field
+    sat = (ef > 15) | ((ef == 15) & (mf == 7))                  # beyond 448: saturate
+    ef = torch.where(sat, torch.full_like(ef, 15), ef)
+    mf = torch.where(sat, torch.full_like(mf, 6), mf)
+    code = (torch.signbit(y).to(torch.int64) << 7) | (ef << 3) | mf
+    return code.to(torch.uint8), scale
 
 
 def kv_key(seed: int, seq_id: int, layer: int, which: str) -> int:

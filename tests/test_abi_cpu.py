@@ -104,6 +104,35 @@ def test_unsupported_shapes(lib):
     assert mk.mk_workspace_size(c, 8) == 0
 
 
+def test_fp8_expert_config_rules(lib):
+    assert mk.mk_workspace_size(_cfg(W.MOE_30B_FP8), 529) > 0
+    assert mk.mk_workspace_size(_cfg(W.MOE_30B_FP8, 2), 529) == 0      # one batch row only
+    c = _cfg(W.MOE_30B)
+    c.expert_fp8 = 2
+    assert mk.mk_workspace_size(c, 8) == 0
+    c = _cfg(W.DENSE_1B)
+    c.expert_fp8 = 1                                                 # no experts to store
+    assert mk.mk_workspace_size(c, 8) == 0
+    c = _cfg(W.MOE_30B_FP8)
+    c.expert_inter = 4096                                            # beyond two 1024-element chunks
+    assert mk.mk_workspace_size(c, 8) == 0
+    # FP8 experts without their row scales
+    cfg = _cfg(W.TINY_MOE)
+    cfg.expert_fp8 = 1
+    L = cfg.n_layers
+    arr = (mk.mk_layer_weights * L)()
+    for l in range(L):
+        for f in ("attn_norm", "w_qkv", "w_o", "w_router", "w_upgate", "w_down"):
+            setattr(arr[l], f, 4096)
+    w = mk.mk_weights(embed=4096, lm_head=4096, final_norm=4096, layers=arr)
+    ptrs = (ctypes.c_void_p * L)(*([4096] * L))
+    kv = mk.mk_kv_pool(k=ptrs, v=ptrs, num_pages=4)
+    h = ctypes.c_void_p()
+    rc = lib.mk_init(ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(kv), ctypes.c_void_p(4096), 1 << 30, 8,
+                     ctypes.byref(h))
+    assert rc == mk.MK_E_INVAL
+
+
 def _plan(model, B, max_blocks, nw=256, order="tuned", split=0, opts=None):
     opts = opts if opts is not None else mk.make_opts(order, attn_split=split)
     return mk.mk_plan_schedule(_cfg(model, B), B, max_blocks, opts, nw)

@@ -502,6 +502,29 @@ def test_e4m3_decode_closed_form_values():
     assert v[4] == 1.0 and v[5] == 1.5 and v[6] == 448.0 and v[7] == -1.0 and np.isnan(v[8])
 
 
+def test_e4m3_quantizer_rounds_like_a_correct_float8_conversion():
+    """With a row maximum of 448 the scale is 1 and the codes must be the
+    round-to-nearest-even E4M3 conversion of each float32 weight, which
+    torch's CPU conversion computes in software: checked on log-spaced
+    magnitudes, exact ties (normal and subnormal), zeros and the maximum."""
+    rng = np.random.default_rng(5)
+    mags = np.exp2(rng.uniform(-13, np.log2(448.0), 4000))
+    grid = O.e4m3_decode(np.arange(0x7F))                        # the non-negative finite values, ascending
+    ties = (grid[:-1] + grid[1:]) / 2                             # every midpoint of the grid
+    v = np.concatenate([mags, ties, grid, [0.0, 448.0]]).astype(np.float32)
+    v = np.where(rng.random(v.size) < 0.5, -v, v).astype(np.float32)
+    v = np.concatenate([v, np.float32([-0.0, 448.0])])
+    w = torch.from_numpy(v.reshape(1, -1))
+    codes, scale = W.quantize_e4m3_rows(w)
+    assert scale.item() == 1.0
+    ref = w.to(torch.float8_e4m3fn).view(torch.uint8)
+    assert torch.equal(codes, ref)
+    # with any row maximum, that element maps to the largest code, +-448
+    rows = torch.from_numpy(rng.standard_normal((64, 300)).astype(np.float32) * np.exp2(rng.uniform(-20, 20, (64, 1))))
+    codes, scale = W.quantize_e4m3_rows(rows)
+    assert torch.equal((codes & 0x7F).amax(dim=1), torch.full((64,), 0x7E, dtype=torch.uint8))
+
+
 def test_fp8_expert_rows_round_trip_within_half_a_code_step():
     wl = W.WORKLOADS["tiny"].with_(model=replace(W.TINY_MOE, expert_fp8=True))
     ug_q, dn_q = O.Weights(wl).expert(1, 3)
