@@ -217,6 +217,10 @@ typedef struct mk_sched_opts {
   int32_t n_workgroups;     /* 0: one per CU                                 */
   int32_t timeout_ms;       /* watchdog per wait; 0 = 2000 ms                */
   int32_t flags;            /* MK_SCHED_* bits; 0 in normal use              */
+  int32_t moe_ug_pairs;     /* gate/up row pairs per MoE up-gate item
+                               (1..512); 0 picks one from the shape and batch */
+  int32_t moe_dn_rows;      /* output rows per MoE down item (1..d); 0 picks
+                               one from the shape and batch                   */
 } mk_sched_opts;
 
 /* Test hook: prepend one task that waits on a counter no task signals, so

@@ -269,13 +269,30 @@ int build_plan(const mk_config* c, int B, int32_t max_blocks, const mk_sched_opt
   const int n_lm = ceil_div(c->vocab, lm_rows);
   if (moe) {
     const int K = c->top_k, I = c->expert_inter;
-    p.ug_pairs = std::max(1, ceil_div((long)K * I, NW));
+    if (o.moe_ug_pairs < 0 || o.moe_ug_pairs > kYsFloats / 8 / 2 || o.moe_dn_rows < 0 || o.moe_dn_rows > d)
+      return MK_E_INVAL;
+    // up-gate items: about one per workgroup for the k experts of one row
+    // (bs=1: latency-bound, 24 pairs for the 30B model: 348 tok/s against
+    // 326 for 16 and 347 for 32); with more rows, larger items in proportion
+    // to the distinct experts expected under uniform routing,
+    // E (1 - (1 - k/E)^B), at 1.5 k per multiple, up to 4 (bs=8, about 52
+    // experts: 96 pairs, 838 tok/s against 730 for 24 and 798 for 48; with
+    // concentrated routing, about 21 experts, 1057 against 971)
+    int ug_mult = 1;
+    if (B > 1) {
+      const double ex = c->n_experts * (1.0 - std::pow(1.0 - (double)K / c->n_experts, B));
+      ug_mult = std::min(4, std::max(1, (int)std::lround(ex / (1.5 * K))));
+    }
+    p.ug_pairs = o.moe_ug_pairs > 0 ? o.moe_ug_pairs : std::max(1, ceil_div((long)K * I, NW)) * ug_mult;
     p.ug_pairs = std::min(p.ug_pairs, kYsFloats / 8 / 2);
     p.ug_tiles = ceil_div(I, p.ug_pairs);
     // one down item per two workgroups (128 rows of the 30B model): 350 tok/s
     // at 8K and bs=1 against 341 for one per workgroup (64 rows) and 318 for
     // 256 rows; the up-gate items stay at one per workgroup (32 pairs: 347)
-    p.dn_rows = std::max(1, ceil_div((long)K * d, std::max(1, NW / 2)));
+    p.dn_rows = o.moe_dn_rows > 0 ? o.moe_dn_rows : std::max(1, ceil_div((long)K * d, std::max(1, NW / 2)));
+    // with several rows, 3/4 of that (bs=8: 96 rows, 846 tok/s against 836
+    // for 128 and 816 for 64; concentrated routing 1084 against 1077)
+    if (o.moe_dn_rows <= 0 && B > 1) p.dn_rows = std::max(16, p.dn_rows * 3 / 4 / 16 * 16);
     p.dn_tiles = ceil_div(d, p.dn_rows);
   }
   int ffn_pp = 0, n_fug = 0, ffn_rows = 0, n_fdn = 0;

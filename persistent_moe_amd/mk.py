@@ -69,7 +69,8 @@ class mk_kv_pool(ctypes.Structure):
 
 class mk_sched_opts(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
-        "wave_order", "launch_mode", "attn_split", "n_workgroups", "timeout_ms", "flags")]
+        "wave_order", "launch_mode", "attn_split", "n_workgroups", "timeout_ms", "flags",
+        "moe_ug_pairs", "moe_dn_rows")]
 
 
 class mk_sampling(ctypes.Structure):
@@ -166,10 +167,10 @@ MK_SCHED_STATIC_ATTN = 128
 
 
 def make_opts(wave_order="tuned", launch_mode="persistent", attn_split=0, n_workgroups=0,
-              timeout_ms=0, flags=0) -> mk_sched_opts:
+              timeout_ms=0, flags=0, moe_ug_pairs=0, moe_dn_rows=0) -> mk_sched_opts:
     return mk_sched_opts(wave_order=ORDER[wave_order], launch_mode=LAUNCH[launch_mode],
                          attn_split=attn_split, n_workgroups=n_workgroups, timeout_ms=timeout_ms,
-                         flags=flags)
+                         flags=flags, moe_ug_pairs=moe_ug_pairs, moe_dn_rows=moe_dn_rows)
 
 
 def mk_workspace_size(cfg: mk_config, max_blocks_per_seq: int) -> int:

@@ -83,6 +83,16 @@ def test_few_workgroups(batch, n_wg):
     run_teacher_forced(eng, 2).check()
 
 
+@pytest.mark.parametrize("batch,ug,dn", [(8, 100, 200), (1, 7, 300)])
+def test_moe_tile_size_options(batch, ug, dn):
+    # explicit MoE item sizes with ragged last tiles (768 = 7 x 100 + 68 or
+    # 109 x 7 + 5 pairs; 2048 = 10 x 200 + 48 or 6 x 300 + 248 rows)
+    wl = W.Workload(f"moe30b-shape-b{batch}-tiles", MOE_SMALL, batch=batch, ctx="loguniform:30:400",
+                    steps=2, seed=41 + batch)
+    eng = _engine(wl, opts=mk.make_opts(moe_ug_pairs=ug, moe_dn_rows=dn))
+    run_teacher_forced(eng, 2).check()
+
+
 def test_sliding_window_layers():
     wl = W.Workload("moe30b-swa-ctx300", SWA_SMALL, batch=1, ctx="fixed:300", steps=2, seed=14)
     eng = _engine(wl)
