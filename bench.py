@@ -341,7 +341,7 @@ def main():
     if not args.no_fp8 and args.workload == "moe30b":
         # the bs=1 8K workload with the expert weights stored as E4M3 codes
         # and float32 row scales (the rest bf16)
-        legs.append(("fp8_experts", "moe30b_fp8"))
+        legs += [("fp8_experts", "moe30b_fp8")] + ([] if args.no_bs8 else [("fp8_experts_bs8", "moe30b_bs8_fp8")])
     if legs:
         for key, name in legs:
             wl8 = W.WORKLOADS[name]

@@ -124,8 +124,7 @@ typedef struct mk_config {
   float rope_theta;        /* RoPE base                                      */
   float rms_eps;           /* RMSNorm epsilon                                */
   int32_t expert_fp8;      /* 1: expert weights are FP8 (see mk_layer_weights);
-                              MoE only, max_batch 1, d and I <= 2048 and
-                              multiples of 16                               */
+                              MoE only, d and I <= 2048 and multiples of 16 */
 } mk_config;
 
 /* Per-layer weights, all device pointers to bf16, row-major [out][in].

@@ -84,9 +84,10 @@ int validate_config(const mk_config* c) {
   if (c->swa_window < 0 || c->swa_period < 0) return MK_E_INVAL;
   if (c->expert_fp8 != 0 && c->expert_fp8 != 1) return MK_E_INVAL;
   if (c->expert_fp8) {
-    // FP8 experts run the one-row GEMV with x in registers: batch 1, K up
-    // to two 1024-element chunks, rows of whole 16-byte loads
-    if (!moe || c->max_batch != 1) return MK_E_UNSUPPORTED;
+    // FP8 expert GEMVs: K up to two 1024-element chunks (the staged row of
+    // one batch row is then at most 2048 elements, 8 rows fit the staging
+    // area), rows of whole 16-byte loads
+    if (!moe) return MK_E_UNSUPPORTED;
     if (c->d_model > 2048 || c->expert_inter > 2048) return MK_E_UNSUPPORTED;
     if (c->d_model % 16 != 0 || c->expert_inter % 16 != 0) return MK_E_UNSUPPORTED;
   }
@@ -96,6 +97,10 @@ int validate_config(const mk_config* c) {
     long kmax = std::max<long>(staged_row(c->d_model), staged_row((long)gd));
     if (moe) kmax = std::max(kmax, staged_row(c->expert_inter));
     else kmax = std::max(kmax, staged_row(c->ffn_inter));
+    if (c->expert_fp8) {   // the FP8 GEMVs stage whole 1024-element chunks
+      kmax = std::max(kmax, 2 * staged_row((c->d_model + 1) / 2));
+      kmax = std::max(kmax, 2 * staged_row((c->expert_inter + 1) / 2));
+    }
     if (B * kmax > kXsFloats) return MK_E_UNSUPPORTED;
   }
   return MK_OK;

@@ -146,6 +146,9 @@ WORKLOADS = {
     # the bs=1 8K workload (same seed, so the same bf16 draws) with the expert
     # weights streamed as FP8
     "moe30b_fp8": Workload("moe30b-bs1-ctx8k-fp8", MOE_30B_FP8, batch=1, ctx="fixed:8192", steps=256, seed=2),
+    # and the continuous-batching bs=8 workload (same seed as moe30b_bs8)
+    "moe30b_bs8_fp8": Workload("moe30b-bs8-ragged-fp8", MOE_30B_FP8, batch=8, ctx="loguniform:512:16384",
+                               steps=256, seed=3, swap_every=32),
 }
 
 

@@ -106,7 +106,7 @@ def test_unsupported_shapes(lib):
 
 def test_fp8_expert_config_rules(lib):
     assert mk.mk_workspace_size(_cfg(W.MOE_30B_FP8), 529) > 0
-    assert mk.mk_workspace_size(_cfg(W.MOE_30B_FP8, 2), 529) == 0      # one batch row only
+    assert mk.mk_workspace_size(_cfg(W.MOE_30B_FP8, 8), 529) > 0
     c = _cfg(W.MOE_30B)
     c.expert_fp8 = 2
     assert mk.mk_workspace_size(c, 8) == 0
@@ -115,6 +115,9 @@ def test_fp8_expert_config_rules(lib):
     assert mk.mk_workspace_size(c, 8) == 0
     c = _cfg(W.MOE_30B_FP8)
     c.expert_inter = 4096                                            # beyond two 1024-element chunks
+    assert mk.mk_workspace_size(c, 8) == 0
+    c = _cfg(W.MOE_30B_FP8)
+    c.expert_inter = 760                                             # rows of whole 16-byte loads
     assert mk.mk_workspace_size(c, 8) == 0
     # FP8 experts without their row scales
     cfg = _cfg(W.TINY_MOE)

@@ -71,6 +71,33 @@ def test_fp8_experts_with_few_workgroups():
     run_teacher_forced(eng, 2).check()
 
 
+def test_tiny_moe_fp8_experts_two_rows():
+    """Two batch rows take the MFMA form of the FP8 GEMV (one partial chunk)."""
+    wl = W.Workload("tiny-moe-fp8-bs2", replace(W.TINY_MOE, expert_fp8=True), batch=2, ctx="list:64,37",
+                    steps=4, seed=34)
+    eng = _engine(wl)
+    rep = run_teacher_forced(eng, wl.steps)
+    rep.check()
+    assert rep.rows == 8
+
+
+def test_moe30b_shape_fp8_experts_bs8_ragged_with_swap():
+    wl = W.Workload("moe30b-shape-fp8-bs8", MOE_SMALL_FP8, batch=8, ctx="loguniform:20:700", steps=4, seed=35,
+                    swap_every=2)
+    eng = _engine(wl)
+    rep = run_teacher_forced(eng, 4)
+    rep.check()
+    assert rep.rows == 32
+
+
+@pytest.mark.parametrize("ug,dn", [(0, 0), (100, 200)])
+def test_fp8_experts_bs8_few_workgroups_and_ragged_items(ug, dn):
+    wl = W.Workload(f"moe30b-shape-fp8-bs8-nw40-{ug}", MOE_SMALL_FP8, batch=8, ctx="loguniform:30:500", steps=2,
+                    seed=36 + ug)
+    eng = _engine(wl, opts=mk.make_opts(n_workgroups=40, moe_ug_pairs=ug, moe_dn_rows=dn))
+    run_teacher_forced(eng, 2).check()
+
+
 def test_full_size_moe30b_fp8_first_step():
     """The 48-layer model with FP8 experts at 8K context, step 0, all logits,
     in the launch configuration the benchmark times."""
