@@ -51,6 +51,9 @@
 #ifndef MK_NT
 #define MK_NT 2           // GEMV row groups (register tiles) in flight per compute wave
 #endif
+#ifndef MK_STAGE_N
+#define MK_STAGE_N 8      // 16-byte activation loads per lane in flight while staging
+#endif
 #ifndef MK_NTM
 #define MK_NTM 3          // MFMA GEMV groups in flight per compute wave (bs=8: 854 tok/s against 846 for 2)
 #endif
@@ -705,30 +708,34 @@ __device__ __forceinline__ bool wait_and_stage(const KA a, Smem& sm, const Stage
     if (lane == 0) sm.misc[0] = ok;
     if (ok) {
       const int kv = s.K >> 2, total = s.nb * kv;
-      for (int i0 = 0; i0 < total; i0 += 64 * 8) {
-        u32x4 v[8];
-        int dst[8];
+      for (int i0 = 0; i0 < total; i0 += 64 * MK_STAGE_N) {
+        // every offset first, then every load back to back, then the
+        // conversion: address arithmetic between the loads made the compiler
+        // reuse a register of an outstanding load and wait for all of them,
+        // which left one or two loads in flight (a 64 KB staging took 17 us)
+        int off[MK_STAGE_N], dst[MK_STAGE_N];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
+        for (int u = 0; u < MK_STAGE_N; ++u) {
           const int i = i0 + u * 64 + lane;
-          dst[u] = -1;
-          if (i < total) {
-            const int j = i / kv, c = i - j * kv;
-            int row = j;
-            if (s.use_tok) {
+          const int j = i / kv, c = i - j * kv;
+          int row = j;
+          if (s.use_tok) {
 #pragma unroll
-              for (int q = 0; q < NBMAX; ++q)
-                if (q == j) row = s.tok[q];
-            }
-            v[u] = ldc16(s.base, (int)(((long)row * s.ld + c * 4) * 4));
-            dst[u] = j * kp + c * 4;
+            for (int q = 0; q < NBMAX; ++q)
+              if (q == j) row = s.tok[q];
           }
+          const bool in = i < total;
+          off[u] = in ? (int)(((long)row * s.ld + c * 4) * 4) : 0;   // a piece past the end reads piece 0
+          dst[u] = in ? j * kp + c * 4 : -1;
         }
+        u32x4 v[MK_STAGE_N];
+#pragma unroll
+        for (int u = 0; u < MK_STAGE_N; ++u) v[u] = ldc16(s.base, off[u]);
         // x = hi + lo, both bf16, into two arrays [nb][kp] at the start of xs
         uint16_t* xh = reinterpret_cast<uint16_t*>(sm.xs);
         uint16_t* xl = xh + s.nb * kp;
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
+        for (int u = 0; u < MK_STAGE_N; ++u)
           if (dst[u] >= 0) {
             uint32_t h0, h1, l0, l1;
             split_bf16(__uint_as_float(v[u].x), __uint_as_float(v[u].y), h0, l0);
