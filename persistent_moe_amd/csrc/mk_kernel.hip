@@ -1,7 +1,7 @@
 // mk_kernel.hip - the persistent decode megakernel for gfx950 (MI355X).
 //
 // One launch runs one decode step.  The grid holds one workgroup per CU
-// (256 threads = 4 wave64s, one per SIMD, about 147 KB of LDS so no second
+// (256 threads = 4 wave64s, one per SIMD, 153,800 bytes of LDS so no second
 // workgroup fits).  One wave per SIMD gives each wave the SIMD's whole
 // register file (256 VGPRs + 256 AGPRs), so the compiler spills into AGPRs
 // instead of scratch memory: a scratch reload is a vector-memory load, and
@@ -26,11 +26,13 @@
 // whole L2 of the XCD on every task, which measured 2-30 us per task here.)
 //
 // Weights are immutable during a step, so every GEMV tile issues the loads of
-// its first two row groups (up to 96 KB per CU) into registers *before* it
-// waits on its activation dependency (page 1, third gain of the megakernel:
-// weights stream while the task's input is not ready yet); they are issued
-// when the workgroup reaches the task, not earlier.  Attention splits and MoE expert tiles are pulled from
-// claim queues whose head is an atomic counter (page 1, "Scheduling").
+// its first row groups into registers *before* it waits on its activation
+// dependency (page 1, third gain of the megakernel: weights stream while the
+// task's input is not ready yet): two groups (96 KB per CU) in the one- and
+// two-row form, three (144 KB) in the MFMA form.  They are issued when the
+// workgroup reaches the task, not earlier.  Attention splits and MoE expert
+// tiles are pulled from claim queues whose head is an atomic counter (page 1,
+// "Scheduling").
 
 #include <hip/hip_runtime.h>
 #include <mutex>
