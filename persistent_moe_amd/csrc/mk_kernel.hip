@@ -1278,13 +1278,16 @@ __device__ __forceinline__ bool gemv(const KA a, Smem& sm, const GemvArgs& g, co
 // x_l = x_{l-1} + sum_g O-proj partial_g + sum_j w_j Y_j (parallel block), or
 // the embedding row at layer 0; xn_l = x_l / sqrt(mean(x_l^2) + eps) * gain,
 // for the batch row t.batch (one task per sequence).  Each thread takes up to
-// four 4-element chunks of the row; the ~Hkv + k + 1 source loads of all its
+// NCH 4-element chunks of the row; the ~Hkv + k + 1 source loads of all its
 // chunks are issued together, so the row costs one round trip.  x is kept in
-// LDS between the two passes.
+// LDS between the two passes.  NCH is 2 for d <= 2048 and 4 up to 4096: with
+// arrays for four chunks the compiler cannot keep every source load of the
+// chunks in registers at once and waits for the first chunks' loads before
+// issuing the next ones (two round trips instead of one at d = 2048).
 // The MoE combine (the gate-weighted sum of the routed expert outputs, in
 // top-k order) is folded into this task.
+template <int NCH>   // 4-element chunks per thread (d <= NCH * 4 * 256)
 __device__ __forceinline__ bool op_add_rmsnorm(const KA a, Smem& sm, const mk_task& t, int ti) {
-  constexpr int NCH = 4;            // 4-element chunks per thread (d <= 4096)
   const int l = t.layer, d = a->d, B = a->B, nv = d >> 2, K = a->topk;
   const int b0 = t.batch, b1 = t.batch + 1;   // the row of this task
   const int tid = tid_v(), wave = tid >> 6, lane = tid & 63;
@@ -1346,52 +1349,66 @@ __device__ __forceinline__ bool op_add_rmsnorm(const KA a, Smem& sm, const mk_ta
         acc[q] = (f32x4){bf_lo(e.x), bf_hi(e.x), bf_lo(e.y), bf_hi(e.y)};
       }
     } else if (mid || moe_in) {
+      // Every load of the chunks is issued before any is used, and none sits
+      // in a branch: a load under a runtime condition (g < Hkv, j < k, the
+      // chunk inside the row) got its own basic block, the compiler merged
+      // the matching add into it and waited right after the load.  Slots
+      // past Hkv or k load a duplicate of the last partial or row and are
+      // dropped by a select; lanes past the row load chunk 0.  The expert
+      // rows come from LDS and are read before the first load.
+      const int hkv = a->Hkv;
+      int yrow[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) yrow[j] = moe_in ? __builtin_amdgcn_readfirstlane(srow[b * K + min(j, K - 1)]) : 0;
       u32x4 og[NCH][8], ym[NCH][8], xq[NCH];
 #pragma unroll
       for (int q = 0; q < NCH; ++q) {
-        const int c = tid + q * MK_THREADS, off = c * 16;
-        if (c < nv) {
+        const int c = tid + q * MK_THREADS, off = c < nv ? c * 16 : 0;
 #pragma unroll
-          for (int g = 0; g < 8; ++g)
-            if (g < a->Hkv) og[q][g] = ldc16(a->opart + (((long)lx * a->Hkv + g) * B + b) * d, off);
-          if (moe_in) {
+        for (int g = 0; g < 8; ++g) og[q][g] = ldc16(a->opart + (((long)lx * hkv + min(g, hkv - 1)) * B + b) * d, off);
+        if (moe_in) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
-              if (j < K)
-                ym[q][j] = ldc16(a->Y + ((long)lp * a->bk + __builtin_amdgcn_readfirstlane(srow[b * K + j])) * d, off);
-          }
-          xq[q] = ldc16(a->x + ((long)lx * B + b) * d, off);
+          for (int j = 0; j < 8; ++j) ym[q][j] = ldc16(a->Y + ((long)lp * a->bk + yrow[j]) * d, off);
         }
+        xq[q] = ldc16(a->x + ((long)lx * B + b) * d, off);
       }
 #pragma unroll
       for (int q = 0; q < NCH; ++q) {
         const int c = tid + q * MK_THREADS, off = c * 16;
-        acc[q] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        f32x4 o = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int g = 0; g < 8; ++g) {
+          const f32x4 v = as_f4(og[q][g]);
+          o += g < hkv ? v : (f32x4){0.f, 0.f, 0.f, 0.f};
+        }
+        acc[q] = as_f4(xq[q]) + o;
+        f32x4 m = (f32x4){0.f, 0.f, 0.f, 0.f};
+        if (moe_in) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) m += (j < K ? sw[b * K + j] : 0.f) * as_f4(ym[q][j]);
+          acc[q] += m;
+        }
         if (c < nv) {
-          f32x4 o = (f32x4){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int g = 0; g < 8; ++g)
-            if (g < a->Hkv) o += as_f4(og[q][g]);
           stc16(a->oout + ((long)lx * B + b) * d, off, as_u4(o));
-          acc[q] = as_f4(xq[q]) + o;
-          if (moe_in) {
-            f32x4 m = (f32x4){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-              if (j < K) m += sw[b * K + j] * as_f4(ym[q][j]);
-            stc16(a->fo + ((long)lp * B + b) * d, off, as_u4(m));
-            acc[q] += m;
-          }
+          if (moe_in) stc16(a->fo + ((long)lp * B + b) * d, off, as_u4(m));
+        } else {
+          acc[q] = (f32x4){0.f, 0.f, 0.f, 0.f};
         }
       }
     } else {
-      // sequential block: x_l = x_mid + FFN output
+      // sequential block: x_l = x_mid + FFN output (every load first, none in
+      // a branch, as above)
+      u32x4 xm[NCH], fq[NCH];
 #pragma unroll
       for (int q = 0; q < NCH; ++q) {
-        const int c = tid + q * MK_THREADS, off = c * 16;
-        acc[q] = c < nv ? as_f4(ldc16(a->xmid + ((long)lp * B + b) * d, off)) +
-                              as_f4(ldc16(a->fo + ((long)lp * B + b) * d, off))
-                        : (f32x4){0.f, 0.f, 0.f, 0.f};
+        const int c = tid + q * MK_THREADS, off = c < nv ? c * 16 : 0;
+        xm[q] = ldc16(a->xmid + ((long)lp * B + b) * d, off);
+        fq[q] = ldc16(a->fo + ((long)lp * B + b) * d, off);
+      }
+#pragma unroll
+      for (int q = 0; q < NCH; ++q) {
+        const int c = tid + q * MK_THREADS;
+        acc[q] = c < nv ? as_f4(xm[q]) + as_f4(fq[q]) : (f32x4){0.f, 0.f, 0.f, 0.f};
       }
     }
     float ss = 0.f;
@@ -2503,7 +2520,8 @@ __device__ __forceinline__ void mk_step(mk_kargs a_arg, int final_launch) {
       }
       switch (t.op) {
         case MK_OP_ADD_RMSNORM:
-          if (!op_add_rmsnorm(a, sm, t, ti)) aborted = true;
+          if (!(a->d <= 2 * 4 * MK_THREADS ? op_add_rmsnorm<2>(a, sm, t, ti) : op_add_rmsnorm<4>(a, sm, t, ti)))
+            aborted = true;
           break;
         case MK_OP_ROUTER_TOPK:
           if (wg_wait(a, sm, t.wait_ctr, t.wait_target, ti)) {
