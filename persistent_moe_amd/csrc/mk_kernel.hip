@@ -1615,21 +1615,23 @@ __device__ __forceinline__ void router_topk(const KA a, Smem& sm, int l) {
   const int wave = tid_v() >> 6, lane = tid_v() & 63;
   const uint16_t* bias = LAYER_PTR(l, router_bias);   // optional [E] logit bias
   for (int b = wave; b < B; b += MK_WAVES) {
+    // the logits and the bias are loaded together, unconditionally (a lane
+    // past E reads expert E - 1 and is masked by a select): loads under a
+    // per-lane condition were each followed by a wait
     float v[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int e = lane + 64 * u;
-      v[u] = e < E ? ldc(a->rlog + ((long)l * B + b) * E + e) : -INFINITY;
-    }
+    for (int u = 0; u < 4; ++u) v[u] = ldc(a->rlog + ((long)l * B + b) * E + min(lane + 64 * u, E - 1));
     if (bias) {
       // the bias is part of the logits (selection and gate weights); the
       // router-logit tap keeps the projection alone
+      uint16_t bb[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int e = lane + 64 * u;
-        if (e < E) v[u] += bf16_to_f(((GLOBAL const uint16_t*)bias)[e]);
-      }
+      for (int u = 0; u < 4; ++u) bb[u] = ((GLOBAL const uint16_t*)bias)[min(lane + 64 * u, E - 1)];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] += bf16_to_f(bb[u]);
     }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = lane + 64 * u < E ? v[u] : -INFINITY;
     float top0 = 0.f, wsum = 0.f;
     float myw = 0.f;
     int myid = 0;
@@ -1794,14 +1796,32 @@ __device__ __forceinline__ bool attn_split(const KA a, Smem& sm, int l, int b, i
   u32x4 kf[ATT_PT][KS], vf[ATT_PV][DTW];
   if (a->trace && tid == 64 && sm.t_mark[8] == 0) sm.t_mark[8] = wall_clock64();   // compute wave enters
   if (cw >= 0) {
-    // every page id first (one round trip), then every K and V load
+    // every page id first (one round trip), then every K and V load.  From
+    // memory the ids are loaded unconditionally (a slot past the split reads
+    // the split's last tile, and a select drops it): under per-lane
+    // conditions each load was followed by a wait, ten round trips per split
     int kpg[ATT_PT], vpg[ATT_PV];
+    if (bt_lds) {
 #pragma unroll
-    for (int u = 0; u < ATT_PT; ++u) kpg[u] = u < nti ? (bt_lds ? btl[cw + MK_CW * u] : bt[cw + MK_CW * u]) : 0;
+      for (int u = 0; u < ATT_PT; ++u) kpg[u] = u < nti ? btl[cw + MK_CW * u] : 0;
 #pragma unroll
-    for (int u = 0; u < ATT_PV; ++u) {
-      const int tt = 2 * u + (lane >> 5);
-      vpg[u] = (u < nks && tt < nt) ? (bt_lds ? btl[tt] : bt[tt]) : -1;
+      for (int u = 0; u < ATT_PV; ++u) {
+        const int tt = 2 * u + (lane >> 5);
+        vpg[u] = (u < nks && tt < nt) ? btl[tt] : -1;
+      }
+    } else {
+      int kr[ATT_PT], vr[ATT_PV];
+#pragma unroll
+      for (int u = 0; u < ATT_PT; ++u) kr[u] = bt[min(cw + MK_CW * u, nt - 1)];
+#pragma unroll
+      for (int u = 0; u < ATT_PV; ++u) vr[u] = bt[min(2 * u + (lane >> 5), nt - 1)];
+#pragma unroll
+      for (int u = 0; u < ATT_PT; ++u) kpg[u] = u < nti ? kr[u] : 0;
+#pragma unroll
+      for (int u = 0; u < ATT_PV; ++u) {
+        const int tt = 2 * u + (lane >> 5);
+        vpg[u] = (u < nks && tt < nt) ? vr[u] : -1;
+      }
     }
     if (a->trace && tid == 64 && sm.t_mark[9] == 0) sm.t_mark[9] = kpg[0] + vpg[0] >= -2 ? wall_clock64() : 1;
     // Every load of the K and V windows is issued unconditionally (a slot
@@ -1842,10 +1862,15 @@ __device__ __forceinline__ bool attn_split(const KA a, Smem& sm, int l, int b, i
     // page ids of the split's key tiles (at most 2 per lane for a split of
     // up to 1024 keys + 2 tiles), in flight during the wait
     int pid[2];
+    if (bt_lds) {
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int t = lane + 64 * u;
-      pid[u] = t < nt ? (bt_lds ? btl[t] : bt[t]) : 0;
+      for (int u = 0; u < 2; ++u) pid[u] = lane + 64 * u < nt ? btl[lane + 64 * u] : 0;
+    } else {
+      int r[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) r[u] = bt[min(lane + 64 * u, nt - 1)];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) pid[u] = lane + 64 * u < nt ? r[u] : 0;
     }
     int ok = 1;
     if (lane == 0) {
