@@ -692,74 +692,85 @@ struct StageArgs {
   int task;
 };
 
-// Wave 0 waits (lane 0 spins) and then stages the activation rows into LDS;
-// the other waves only meet it at the barrier.  Wave 0's own weight loads
-// have landed by the time its spin sees the counter, so its staging loads
-// do not queue behind outstanding weight traffic.  Every thread must call it.
 // Rows go to LDS with stride kp (K padded to the GEMV's whole K-chunks),
-// zeros in the padding.
+// zeros in the padding, as two bf16 arrays [nb][kp] (x = hi + lo) at the
+// start of xs.  Thread th of nth takes 16-byte pieces th, th + nth, ...,
+// MK_STAGE_N at a time.
+__device__ __forceinline__ void stage_rows(Smem& sm, const StageArgs& s, int kp, int th, int nth) {
+  const int kv = s.K >> 2, total = s.nb * kv;
+  uint16_t* xh = reinterpret_cast<uint16_t*>(sm.xs);
+  uint16_t* xl = xh + s.nb * kp;
+  for (int i0 = 0; i0 < total; i0 += nth * MK_STAGE_N) {
+    // every offset first, then every load back to back, then the
+    // conversion: address arithmetic between the loads made the compiler
+    // reuse a register of an outstanding load and wait for all of them,
+    // which left one or two loads in flight (a 64 KB staging took 17 us)
+    int off[MK_STAGE_N], dst[MK_STAGE_N];
+#pragma unroll
+    for (int u = 0; u < MK_STAGE_N; ++u) {
+      const int i = i0 + u * nth + th;
+      const int j = i / kv, c = i - j * kv;
+      int row = j;
+      if (s.use_tok) {
+#pragma unroll
+        for (int q = 0; q < NBMAX; ++q)
+          if (q == j) row = s.tok[q];
+      }
+      const bool in = i < total;
+      off[u] = in ? (int)(((long)row * s.ld + c * 4) * 4) : 0;   // a piece past the end reads piece 0
+      dst[u] = in ? j * kp + c * 4 : -1;
+    }
+    u32x4 v[MK_STAGE_N];
+#pragma unroll
+    for (int u = 0; u < MK_STAGE_N; ++u) v[u] = ldc16(s.base, off[u]);
+#pragma unroll
+    for (int u = 0; u < MK_STAGE_N; ++u)
+      if (dst[u] >= 0) {
+        uint32_t h0, h1, l0, l1;
+        split_bf16(__uint_as_float(v[u].x), __uint_as_float(v[u].y), h0, l0);
+        split_bf16(__uint_as_float(v[u].z), __uint_as_float(v[u].w), h1, l1);
+        *reinterpret_cast<uint2*>(xh + dst[u]) = make_uint2(h0, h1);
+        *reinterpret_cast<uint2*>(xl + dst[u]) = make_uint2(l0, l1);
+      }
+  }
+  if (kp > s.K) {
+    const int pw = (kp - s.K) >> 2;   // 4-element pieces of padding per row
+    for (int i = th; i < s.nb * pw; i += nth) {
+      const int j = i / pw, e = s.K + (i - j * pw) * 4;
+      *reinterpret_cast<uint2*>(xh + j * kp + e) = make_uint2(0u, 0u);
+      *reinterpret_cast<uint2*>(xl + j * kp + e) = make_uint2(0u, 0u);
+    }
+  }
+}
+
+// Wave 0 waits (lane 0 spins), then the activation rows are staged into LDS
+// (stage_rows).  Rows that fit one round of wave 0's loads are staged by
+// wave 0 alone: its own weight loads have landed by the time its spin sees
+// the counter, so its staging loads queue behind nothing, and the compute
+// waves only meet it at the barrier.  Larger stagings (several batch rows)
+// are shared by all four waves after a second barrier: a compute wave's
+// staging loads wait behind its weight loads, which it needs next anyway,
+// and eight rows of 2048 take two rounds instead of eight.  Every thread
+// must call it.
 __device__ __forceinline__ bool wait_and_stage(const KA a, Smem& sm, const StageArgs& s, int kp) {
-  if (tid_v() < 64) {
-    const int lane = tid_v();
+  const bool wide = s.nb * (s.K >> 2) > 64 * MK_STAGE_N;   // uniform
+  const int tid = tid_v();
+  if (tid < 64) {
     int ok = 1;
-    if (lane == 0) {
+    if (tid == 0) {
       ok = (s.wait_idx < 0 || s.wait_target <= 0) ? 1 : (int)spin_until(a, s.wait_idx, s.wait_target, s.task);
       if (a->trace && sm.t_ready == 0) sm.t_ready = wall_clock64();
     }
     ok = __builtin_amdgcn_readfirstlane(ok);
-    if (lane == 0) sm.misc[0] = ok;
-    if (ok) {
-      const int kv = s.K >> 2, total = s.nb * kv;
-      for (int i0 = 0; i0 < total; i0 += 64 * MK_STAGE_N) {
-        // every offset first, then every load back to back, then the
-        // conversion: address arithmetic between the loads made the compiler
-        // reuse a register of an outstanding load and wait for all of them,
-        // which left one or two loads in flight (a 64 KB staging took 17 us)
-        int off[MK_STAGE_N], dst[MK_STAGE_N];
-#pragma unroll
-        for (int u = 0; u < MK_STAGE_N; ++u) {
-          const int i = i0 + u * 64 + lane;
-          const int j = i / kv, c = i - j * kv;
-          int row = j;
-          if (s.use_tok) {
-#pragma unroll
-            for (int q = 0; q < NBMAX; ++q)
-              if (q == j) row = s.tok[q];
-          }
-          const bool in = i < total;
-          off[u] = in ? (int)(((long)row * s.ld + c * 4) * 4) : 0;   // a piece past the end reads piece 0
-          dst[u] = in ? j * kp + c * 4 : -1;
-        }
-        u32x4 v[MK_STAGE_N];
-#pragma unroll
-        for (int u = 0; u < MK_STAGE_N; ++u) v[u] = ldc16(s.base, off[u]);
-        // x = hi + lo, both bf16, into two arrays [nb][kp] at the start of xs
-        uint16_t* xh = reinterpret_cast<uint16_t*>(sm.xs);
-        uint16_t* xl = xh + s.nb * kp;
-#pragma unroll
-        for (int u = 0; u < MK_STAGE_N; ++u)
-          if (dst[u] >= 0) {
-            uint32_t h0, h1, l0, l1;
-            split_bf16(__uint_as_float(v[u].x), __uint_as_float(v[u].y), h0, l0);
-            split_bf16(__uint_as_float(v[u].z), __uint_as_float(v[u].w), h1, l1);
-            *reinterpret_cast<uint2*>(xh + dst[u]) = make_uint2(h0, h1);
-            *reinterpret_cast<uint2*>(xl + dst[u]) = make_uint2(l0, l1);
-          }
-      }
-      if (kp > s.K) {
-        uint16_t* xh = reinterpret_cast<uint16_t*>(sm.xs);
-        uint16_t* xl = xh + s.nb * kp;
-        const int pw = (kp - s.K) >> 2;   // 4-element pieces of padding per row
-        for (int i = lane; i < s.nb * pw; i += 64) {
-          const int j = i / pw, e = s.K + (i - j * pw) * 4;
-          *reinterpret_cast<uint2*>(xh + j * kp + e) = make_uint2(0u, 0u);
-          *reinterpret_cast<uint2*>(xl + j * kp + e) = make_uint2(0u, 0u);
-        }
-      }
-    }
+    if (tid == 0) sm.misc[0] = ok;
+    if (ok && !wide) stage_rows(sm, s, kp, tid, 64);
+  }
+  if (wide) {
+    __syncthreads();
+    if (sm.misc[0]) stage_rows(sm, s, kp, tid, MK_THREADS);
   }
   __syncthreads();
-  if (a->trace && tid_v() == 0 && sm.t_mark[0] == 0) sm.t_mark[0] = wall_clock64();
+  if (a->trace && tid == 0 && sm.t_mark[0] == 0) sm.t_mark[0] = wall_clock64();
   return sm.misc[0] != 0;
 }
 
