@@ -251,6 +251,13 @@ typedef struct mk_sched_opts {
  * fewer atomic per workgroup).  By default every MoE item is pulled from its
  * claim queue, so the workgroups that finish attention first take them.   */
 #define MK_SCHED_STATIC_MOE 16
+/* Tuned order only: every workgroup claims attention splits and then drains
+ * the MoE up-gate queue before its O-proj tile.  By default, when a layer's
+ * splits at the longest context fit in half the workgroups, that many
+ * workgroups (spread evenly over the grid) own them and go from attention
+ * straight to their O-proj tile, and only the others drain the up-gate
+ * queue (page 1 "Scheduling: mostly static, selectively dynamic").        */
+#define MK_SCHED_SHARED_ATTN 32
 
 #define MK_MIN_SPLIT 64
 

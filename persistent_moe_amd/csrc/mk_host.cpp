@@ -272,29 +272,76 @@ int build_plan(const mk_config* c, int B, int32_t max_blocks, const mk_sched_opt
   // sampling epilogue: at most kYsFloats / 8 rows each
   const int lm_rows = std::min(ceil_div(c->vocab, NW), kYsFloats / 8);
   const int n_lm = ceil_div(c->vocab, lm_rows);
+  // Attention owners (tuned order): when a layer's attention items, at the
+  // longest context the block tables allow, fit in half the workgroups,
+  // only that many workgroups claim them (spread evenly over the grid) and
+  // then go straight on to their O-proj tile, which is ready when the
+  // attention ends; the other workgroups drain the up-gate queue meanwhile.
+  // Shared, every workgroup would enter the up-gate drain after its split
+  // and reach its O-proj tile only after that drain's round trips.
+  const bool static_attn = (o.flags & MK_SCHED_STATIC_ATTN) != 0;
+  const bool fuse_combine = !(o.flags & MK_SCHED_SEPARATE_COMBINE) && !static_attn;
+  p.ncomb = std::max(1, std::min(G, (NW - 1) / std::max(1, B * Hkv) + 1));
+  const bool owners_ok = moe && o.wave_order == MK_ORDER_TUNED && !part && fuse_combine &&
+                         !(o.flags & MK_SCHED_SHARED_ATTN);
+  auto vis_ctx = [&](int l) -> long {
+    return (c->swa_window > 0 && c->swa_period > 0 && l % c->swa_period != c->swa_period - 1)
+               ? std::min<long>(max_ctx, c->swa_window)
+               : max_ctx;
+  };
+  // number of owners of layer l's attention items, or 0 (shared): at most
+  // half the workgroups, and more than can wait in fused combines at once
+  auto owners_of = [&](int l) -> int {
+    if (!owners_ok) return 0;
+    const long n = (long)B * Hkv * ceil_div(vis_ctx(l), S);
+    if (n > NW / 2 || n <= (long)(p.ncomb - 1) * B * Hkv) return 0;
+    return (int)n;
+  };
+  int owners_max = 0;
+  for (int l = 0; l < Lr; ++l) owners_max = std::max(owners_max, owners_of(l));
   if (moe) {
     const int K = c->top_k, I = c->expert_inter;
     if (o.moe_ug_pairs < 0 || o.moe_ug_pairs > kYsFloats / 8 / 2 || o.moe_dn_rows < 0 || o.moe_dn_rows > d)
       return MK_E_INVAL;
-    // up-gate items: about one per workgroup for the k experts of one row
-    // (bs=1: latency-bound, 24 pairs for the 30B model: 348 tok/s against
-    // 326 for 16 and 347 for 32); with more rows, larger items in proportion
-    // to the distinct experts expected under uniform routing,
+    // Up-gate items: at most one per workgroup that drains the queue (all of
+    // them, or those that do not own attention), the same number for each of
+    // the k experts of one row.  bs=1, 30B model: shared attention, 24 pairs
+    // (348 tok/s against 326 for 16 and 347 for 32); attention owners, 39
+    // pairs for 164 drainers (374.9 against 369.9 for 48, and 361.9 for 32,
+    // whose 192 items need a second round).  With more rows, larger items in
+    // proportion to the distinct experts expected under uniform routing,
     // E (1 - (1 - k/E)^B), at 1.5 k per multiple, up to 4 (bs=8, about 52
     // experts: 96 pairs, 838 tok/s against 730 for 24 and 798 for 48; with
-    // concentrated routing, about 21 experts, 1057 against 971)
+    // concentrated routing, about 21 experts, 1057 against 971).
     int ug_mult = 1;
     if (B > 1) {
       const double ex = c->n_experts * (1.0 - std::pow(1.0 - (double)K / c->n_experts, B));
       ug_mult = std::min(4, std::max(1, (int)std::lround(ex / (1.5 * K))));
     }
-    p.ug_pairs = o.moe_ug_pairs > 0 ? o.moe_ug_pairs : std::max(1, ceil_div((long)K * I, NW)) * ug_mult;
+    const int ug_wg = NW - owners_max;
+    p.ug_pairs = o.moe_ug_pairs > 0 ? o.moe_ug_pairs : ceil_div(I, std::max(1, ug_wg / K)) * ug_mult;
     p.ug_pairs = std::min(p.ug_pairs, kYsFloats / 8 / 2);
     p.ug_tiles = ceil_div(I, p.ug_pairs);
-    // one down item per two workgroups (128 rows of the 30B model): 350 tok/s
-    // at 8K and bs=1 against 341 for one per workgroup (64 rows) and 318 for
-    // 256 rows; the up-gate items stay at one per workgroup (32 pairs: 347)
-    p.dn_rows = o.moe_dn_rows > 0 ? o.moe_dn_rows : std::max(1, ceil_div((long)K * d, std::max(1, NW / 2)));
+    // Down items: with attention owners, about one per workgroup, rounded up
+    // to whole rounds of the GEMV's row groups (three compute waves of 16
+    // weight slots; a row of I weights takes 2^kl slots of 512 bf16 or 1024
+    // FP8 weights): owners and drainers reach the down drain from their
+    // O-proj tiles at about the same time.  30B model: 72 rows (three rounds
+    // of 24), 379.6 tok/s against 375.1 for 64, 372.7 for 96, 368.6 for 48
+    // and 363.0 for 56 (296 items, a second round).  Shared attention: one
+    // per two workgroups (128 rows: 350 against 341 for 64 and 318 for 256).
+    if (owners_max) {
+      const int chunk = c->expert_fp8 ? 1024 : 512;
+      int kl = 0;
+      while ((chunk << kl) < I) ++kl;
+      const int round_rows = std::max(1, 3 * (16 >> kl));
+      const int per_wg = std::max(1, ceil_div((long)K * d, NW));
+      p.dn_rows = ceil_div(per_wg, round_rows) * round_rows;
+    } else {
+      p.dn_rows = std::max(1, ceil_div((long)K * d, std::max(1, NW / 2)));
+    }
+    if (o.moe_dn_rows > 0) p.dn_rows = o.moe_dn_rows;
+    p.dn_rows = std::min(p.dn_rows, d);
     // with several rows, 3/4 of that (bs=8: 96 rows, 846 tok/s against 836
     // for 128 and 816 for 64; concentrated routing 1084 against 1077)
     if (o.moe_dn_rows <= 0 && B > 1) p.dn_rows = std::max(16, p.dn_rows * 3 / 4 / 16 * 16);
@@ -339,13 +386,12 @@ int build_plan(const mk_config* c, int B, int32_t max_blocks, const mk_sched_opt
   };
   const std::vector<int>* onA = part ? &setA : nullptr;
   const std::vector<int>* onM = part ? &setM : nullptr;
-  const bool static_attn = (o.flags & MK_SCHED_STATIC_ATTN) != 0;
-  const bool fuse_combine = !(o.flags & MK_SCHED_SEPARATE_COMBINE) && !static_attn;
   // the fused combine of a (sequence, group) is shared by its last ncomb
-  // splits, one share of the G heads each; all but the last wait for the
-  // rest, so at most (ncomb - 1) * B * Hkv workgroups wait at once, and one
-  // more must stay free to claim the remaining splits
-  p.ncomb = std::max(1, std::min(G, (NW - 1) / std::max(1, B * Hkv) + 1));
+  // splits (p.ncomb above), one share of the G heads each; all but the last
+  // wait for the rest, so at most (ncomb - 1) * B * Hkv workgroups wait at
+  // once, and one more must stay free to claim the remaining splits
+  // owner workgroup i of n: spread evenly over the grid (and so over the XCDs)
+  auto owner_wg = [&](int i, int n) { return (int)((long)i * NW / n); };
   int layer_target_prev = 0;
   for (int l = 0; l <= Lr; ++l) {
     // ADD_RMSNORM entering layer l (l == Lr: the final norm), one task per
@@ -404,7 +450,8 @@ int build_plan(const mk_config* c, int B, int32_t max_blocks, const mk_sched_opt
             }
         return;
       }
-      const int nc = onA ? (int)onA->size() : n_claim;
+      const int own = owners_of(l);
+      const int nc = own ? own : onA ? (int)onA->size() : n_claim;
       for (int i = 0; i < nc; ++i) {
         mk_task t = blank(MK_OP_ATTN_DRAIN, l);
         t.n0 = i;
@@ -413,7 +460,8 @@ int build_plan(const mk_config* c, int B, int32_t max_blocks, const mk_sched_opt
         t.wait_target = n_qkv;
         t.queue = ctr_of(p.cl, l, MK_CTR_QATTN);
         if (fuse_combine) t.flags |= MK_F_FUSE_COMBINE;
-        place(t, onA, i);
+        if (own) push_on(t, owner_wg(i, own));
+        else place(t, onA, i);
       }
     };
     auto emit_combine = [&]() {
@@ -489,14 +537,24 @@ int build_plan(const mk_config* c, int B, int32_t max_blocks, const mk_sched_opt
       const bool dyn_moe = (o.flags & MK_SCHED_STATIC_MOE) == 0;
       auto emit_ug = [&]() {
         wave();
-        for (int i = 0; i < n_moe_claim; ++i) {
+        const int own = owners_of(l);
+        std::vector<int> drainers;   // with attention owners: every other workgroup
+        if (own) {
+          std::vector<char> is_owner(NW, 0);
+          for (int i = 0; i < own; ++i) is_owner[owner_wg(i, own)] = 1;
+          for (int w = 0; w < NW; ++w)
+            if (!is_owner[w]) drainers.push_back(w);
+        }
+        const int n = own ? (int)drainers.size() : n_moe_claim;
+        for (int i = 0; i < n; ++i) {
           mk_task t = blank(MK_OP_MOE_UPGATE_ACT_DRAIN, l);
           t.n0 = dyn_moe ? INT32_MAX : i;
-          t.n1 = dyn_moe ? 0 : n_moe_claim;
+          t.n1 = dyn_moe ? 0 : n;
           t.wait_ctr = cROUTE;
           t.wait_target = 1;
           t.queue = ctr_of(p.cl, l, MK_CTR_QUG);
-          place(t, onM, i);
+          if (own) push_on(t, drainers[i]);
+          else place(t, onM, i);
         }
       };
       auto emit_dn = [&]() {

@@ -162,6 +162,7 @@ MK_SCHED_TRACE = 2
 MK_SCHED_SEPARATE_TOPK = 4
 MK_SCHED_SEPARATE_COMBINE = 8
 MK_SCHED_STATIC_MOE = 16
+MK_SCHED_SHARED_ATTN = 32
 MK_SCHED_SEPARATE_FINALIZE = 64
 MK_SCHED_STATIC_ATTN = 128
 

@@ -240,7 +240,8 @@ def test_signal_counts_match_wait_targets(lib):
 
 @pytest.mark.parametrize("order", ["tuned", "interleaved", "attention_first", "partitioned", "tuned-separate-topk",
                                    "tuned-separate-combine", "partitioned-separate-combine", "tuned-static-moe",
-                                   "tuned-separate-finalize", "tuned-static-attn", "attention_first-static-attn"])
+                                   "tuned-separate-finalize", "tuned-static-attn", "attention_first-static-attn",
+                                   "tuned-shared-attn"])
 @pytest.mark.parametrize("case", [
     ("tiny", W.TINY_MOE, 1, 5, [65], [2, 2]),
     ("moe30b", W.MOE_30B, 1, 529, [8193], [8] * 48),
@@ -256,6 +257,7 @@ def test_schedule_is_deadlock_free(lib, order, case):
     if order.endswith("separate-finalize"):
         flags |= mk.MK_SCHED_SEPARATE_TOPK | mk.MK_SCHED_SEPARATE_FINALIZE
     flags |= mk.MK_SCHED_STATIC_ATTN if order.endswith("static-attn") else 0
+    flags |= mk.MK_SCHED_SHARED_ATTN if order.endswith("shared-attn") else 0
     base = order.split("-")[0]
     opts = mk.make_opts(base, flags=flags)
     for nw in (256, 64, 7):
