@@ -322,20 +322,21 @@ int build_plan(const mk_config* c, int B, int32_t max_blocks, const mk_sched_opt
     p.ug_pairs = o.moe_ug_pairs > 0 ? o.moe_ug_pairs : ceil_div(I, std::max(1, ug_wg / K)) * ug_mult;
     p.ug_pairs = std::min(p.ug_pairs, kYsFloats / 8 / 2);
     p.ug_tiles = ceil_div(I, p.ug_pairs);
-    // Down items: with attention owners, about one per workgroup, rounded up
-    // to whole rounds of the GEMV's row groups (three compute waves of 16
-    // weight slots; a row of I weights takes 2^kl slots of 512 bf16 or 1024
-    // FP8 weights): owners and drainers reach the down drain from their
-    // O-proj tiles at about the same time.  30B model: 72 rows (three rounds
-    // of 24), 379.6 tok/s against 375.1 for 64, 372.7 for 96, 368.6 for 48
-    // and 363.0 for 56 (296 items, a second round).  Shared attention: one
-    // per two workgroups (128 rows: 350 against 341 for 64 and 318 for 256).
+    // Down items: with attention owners, about one per up-gate drainer (the
+    // drainers go from the up-gate drain straight to the down drain; the
+    // owners have their O-proj tiles first), rounded up to whole rounds of
+    // the GEMV's row groups (three compute waves of 16 weight slots; a row
+    // of I weights takes 2^kl slots of 512 bf16 or 1024 FP8 weights).  30B
+    // model: 120 rows (five rounds of 24; 136 items), 393.2 tok/s against
+    // 386.7 for 144, 379.4 for 168, 384.6 for 96, 385.5 for 72 and 387.9 for
+    // 48.  Shared attention: one per two workgroups (128 rows: 350 against
+    // 341 for 64 and 318 for 256).
     if (owners_max) {
       const int chunk = c->expert_fp8 ? 1024 : 512;
       int kl = 0;
       while ((chunk << kl) < I) ++kl;
       const int round_rows = std::max(1, 3 * (16 >> kl));
-      const int per_wg = std::max(1, ceil_div((long)K * d, NW));
+      const int per_wg = std::max(1, ceil_div((long)K * d, ug_wg));
       p.dn_rows = ceil_div(per_wg, round_rows) * round_rows;
     } else {
       p.dn_rows = std::max(1, ceil_div((long)K * d, std::max(1, NW / 2)));
@@ -478,20 +479,27 @@ int build_plan(const mk_config* c, int B, int32_t max_blocks, const mk_sched_opt
           push(t);
         }
     };
+    // O-proj tiles of layer l: with attention owners, one per owner (the
+    // owners reach them as their attention ends, and the up-gate drainers
+    // go on to the down drain without one); else one per workgroup
+    const int own_l = owners_of(l);
+    const int o_rows_l = own_l ? ceil_div(d, std::max(1, own_l / Hkv)) : o_rows;
+    const int n_o_g_l = own_l ? ceil_div(d, o_rows_l) : n_o_g;
     auto emit_oproj = [&](int signal) {
       wave();
       for (int g = 0; g < Hkv; ++g)
-        for (int i = 0; i < n_o_g; ++i) {
+        for (int i = 0; i < n_o_g_l; ++i) {
           mk_task t = blank(MK_OP_O_PROJ, l);
           t.group = g;
-          t.n0 = i * o_rows;
-          t.n1 = std::min(d, t.n0 + o_rows);
+          t.n0 = i * o_rows_l;
+          t.n1 = std::min(d, t.n0 + o_rows_l);
           t.k0 = g * G * hd;
           t.k1 = t.k0 + G * hd;
           t.wait_ctr = ctr_of(p.cl, l, p.cl.comb + g);
           t.wait_target = B * G;   // every head of every sequence
           t.signal_ctr = signal;
-          place(t, onA, g * n_o_g + i);
+          if (own_l) push_on(t, owner_wg(g * n_o_g_l + i, own_l));
+          else place(t, onA, g * n_o_g + i);
         }
     };
     if (moe) {
@@ -585,7 +593,7 @@ int build_plan(const mk_config* c, int B, int32_t max_blocks, const mk_sched_opt
           emit_router(); emit_qkv(); emit_attn(); emit_ug(); emit_combine(); emit_oproj(cLAYER); emit_dn();
           break;
       }
-      layer_target_prev = n_moe_claim + Hkv * n_o_g;
+      layer_target_prev = n_moe_claim + Hkv * n_o_g_l;
     } else {
       const int cO = ctr_of(p.cl, l, MK_CTR_OPROJ);
       const int cN2 = ctr_of(p.cl, l, MK_CTR_NORM2);
