@@ -290,12 +290,14 @@ int build_plan(const mk_config* c, int B, int32_t max_blocks, const mk_sched_opt
                : max_ctx;
   };
   // number of owners of layer l's attention items, or 0 (shared): at most
-  // half the workgroups, and more than can wait in fused combines at once
+  // half the workgroups.  The live items never outnumber the owners, so
+  // owner i runs item i and nothing is pulled from the queue: a fused
+  // combine that waits for the other splits of its group waits for owners
+  // that need nothing from it.
   auto owners_of = [&](int l) -> int {
     if (!owners_ok) return 0;
     const long n = (long)B * Hkv * ceil_div(vis_ctx(l), S);
-    if (n > NW / 2 || n <= (long)(p.ncomb - 1) * B * Hkv) return 0;
-    return (int)n;
+    return n <= NW / 2 ? (int)n : 0;
   };
   int owners_max = 0;
   for (int l = 0; l < Lr; ++l) owners_max = std::max(owners_max, owners_of(l));
@@ -391,8 +393,17 @@ int build_plan(const mk_config* c, int B, int32_t max_blocks, const mk_sched_opt
   // splits (p.ncomb above), one share of the G heads each; all but the last
   // wait for the rest, so at most (ncomb - 1) * B * Hkv workgroups wait at
   // once, and one more must stay free to claim the remaining splits
-  // owner workgroup i of n: spread evenly over the grid (and so over the XCDs)
-  auto owner_wg = [&](int i, int n) { return (int)((long)i * NW / n); };
+  // owner workgroup i of n: owner i goes to XCD i mod 8 (workgroups are
+  // dealt round-robin over the 8 XCDs), and the owners of one XCD are
+  // spread evenly over its workgroups, counted from the end of the grid
+  // (the router tiles sit on the first workgroups and the last ones hold no
+  // QKV tile); with a grid that is not a multiple of 8, evenly over the grid
+  auto owner_wg = [&](int i, int n) {
+    if (NW % 8 != 0 || n > NW / 2) return NW - 1 - (int)((long)i * NW / n);
+    const int x = i % 8, k = i / 8, per_x = NW / 8;
+    const int c_x = (n - x + 7) / 8;   // owners on XCD x
+    return NW - 1 - (x + 8 * (int)((long)k * per_x / c_x));
+  };
   int layer_target_prev = 0;
   for (int l = 0; l <= Lr; ++l) {
     // ADD_RMSNORM entering layer l (l == Lr: the final norm), one task per

@@ -142,6 +142,7 @@ SCHEDULES = [
                                             | mk.MK_SCHED_SEPARATE_COMBINE)),
     ("static_attention", dict(flags=mk.MK_SCHED_STATIC_ATTN)),
     ("static_moe", dict(flags=mk.MK_SCHED_STATIC_MOE)),
+    ("shared_attention", dict(flags=mk.MK_SCHED_SHARED_ATTN)),
 ]
 _SCHED_WL = W.Workload("moe30b-shape-sched", MOE_SMALL, batch=2, ctx="list:100,77", steps=2, seed=16)
 _sched_state = {}
