@@ -56,6 +56,21 @@ def test_moe30b_shape_ragged_context():
     run_teacher_forced(eng, 3).check()
 
 
+def test_moe30b_shape_attention_owners():
+    """2-layer 30B shape at 8,000 cached tokens, one row: the attention splits
+    number between a quarter and half of the grid, so the default schedule
+    gives them to attention owners, puts the O-proj tiles on the owners and
+    sizes the up-gate and down items for the other workgroups."""
+    wl = W.Workload("moe30b-shape-owners-ctx8000", MOE_SMALL, batch=1, ctx="fixed:8000", steps=3, seed=17)
+    eng = _engine(wl)
+    nw = torch.cuda.get_device_properties(0).multi_processor_count
+    tasks, _ = mk.mk_plan_schedule(eng.mkcfg, 1, eng.max_blocks, eng.opts, nw)
+    n_attn = sum(1 for t in tasks if t.layer == 0 and mk.OPCODES[t.op] == "ATTN_DRAIN")
+    say("attention owners", n_attn, "of", nw)
+    assert nw // 4 <= n_attn <= nw // 2
+    run_teacher_forced(eng, 3).check()
+
+
 def test_dense1b_shape_sequential_block():
     wl = W.Workload("dense1b-shape-ctx200", DENSE_SMALL, batch=1, ctx="fixed:200", steps=3, seed=12)
     eng = _engine(wl)
