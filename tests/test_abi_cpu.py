@@ -189,7 +189,9 @@ def test_tuned_order_gives_router_tiles_their_own_workgroups(lib):
 
 
 @pytest.mark.parametrize("model,B,mb,nw", [(W.MOE_30B, 1, 529, 256), (W.MOE_30B, 2, 40, 256),
-                                           (W.MOE_30B_SWA, 1, 16388, 256), (W.TINY_MOE, 1, 5, 7)])
+                                           (W.MOE_30B_SWA, 1, 16388, 256), (W.TINY_MOE, 1, 5, 7),
+                                           (W.MOE_30B, 1, 529, 200), (W.MOE_30B, 1, 529, 250),
+                                           (W.MOE_30B, 1, 529, 128)])
 def test_attention_owners_placement(lib, model, B, mb, nw):
     """Tuned order with a quarter to half of the grid's worth of attention
     splits: one ATTN_DRAIN claimer per split at the longest context, on
@@ -200,17 +202,22 @@ def test_attention_owners_placement(lib, model, B, mb, nw):
     op = {n: i for i, n in enumerate(mk.OPCODES)}
     tasks, _ = _plan(model, B, mb, nw=nw)
     shared, _ = _plan(model, B, mb, nw=nw, opts=mk.make_opts(flags=mk.MK_SCHED_SHARED_ATTN))
-    S = _plan_split(model, B, mb, nw)
-    G = model.n_q_heads // model.n_kv_heads
+    S = _plan_split(model, B, mb, nw, tasks)
+    names = ("ATTN_DRAIN", "MOE_UPGATE_ACT_DRAIN", "O_PROJ", "MOE_DOWN_DRAIN")
+    kinds = {op[n]: n for n in names}
+    by = {}        # (layer, opcode name) -> tasks, in list order
+    for ts, tag in ((tasks, ""), (shared, "shared:")):
+        for t in ts:
+            if t.op in kinds:
+                by.setdefault((t.layer, tag + kinds[t.op]), []).append(t)
     for l in range(model.n_layers):
         vis = mb * 16
         if model.swa_window and model.swa_period and l % model.swa_period != model.swa_period - 1:
             vis = min(vis, model.swa_window)
         n_items = B * model.n_kv_heads * -(-vis // S)
-        by = lambda ts, name: [t for t in ts if t.layer == l and t.op == op[name]]
-        at, ug, oproj, dn = (by(tasks, n) for n in ("ATTN_DRAIN", "MOE_UPGATE_ACT_DRAIN", "O_PROJ", "MOE_DOWN_DRAIN"))
-        assert {t.aux[16] for t in by(shared, "ATTN_DRAIN")} == set(range(nw))
-        assert {t.aux[16] for t in by(shared, "MOE_UPGATE_ACT_DRAIN")} == set(range(nw))
+        at, ug, oproj, dn = (by.get((l, n), []) for n in names)
+        assert {t.aux[16] for t in by[(l, "shared:ATTN_DRAIN")]} == set(range(nw))
+        assert {t.aux[16] for t in by[(l, "shared:MOE_UPGATE_ACT_DRAIN")]} == set(range(nw))
         assert {t.aux[16] for t in dn} == set(range(nw))
         if n_items > nw // 2 or n_items < nw // 4:   # too many or too few splits: shared
             assert len(at) == nw and len(ug) == nw
@@ -226,30 +233,29 @@ def test_attention_owners_placement(lib, model, B, mb, nw):
             assert rows[0][0] == 0 and rows[-1][1] == model.d_model
             assert all(a[1] == b[0] for a, b in zip(rows, rows[1:]))
         # on each owner: attention, then its O-proj tile, then the down drain
-        for w in set(owners):
-            seq = [t.op for t in tasks if t.layer == l and t.aux[16] == w and
-                   t.op in (op["ATTN_DRAIN"], op["O_PROJ"], op["MOE_DOWN_DRAIN"], op["MOE_UPGATE_ACT_DRAIN"])]
-            assert seq[0] == op["ATTN_DRAIN"] and seq[-1] == op["MOE_DOWN_DRAIN"]
-            assert op["MOE_UPGATE_ACT_DRAIN"] not in seq
-        if owners:
-            # spread: every XCD (workgroup mod 8) holds owners when there are at least 8
-            if len(owners) >= 8 and nw % 8 == 0:
-                assert {w % 8 for w in owners} == set(range(8))
-        assert G >= 1
+        # (list order of one workgroup is builder order, aux[17])
+        seq = {}
+        for t in sorted(at + oproj + dn + ug, key=lambda t: t.aux[17]):
+            seq.setdefault(t.aux[16], []).append(t.op)
+        for w in owners:
+            assert seq[w][0] == op["ATTN_DRAIN"] and seq[w][-1] == op["MOE_DOWN_DRAIN"]
+            assert op["MOE_UPGATE_ACT_DRAIN"] not in seq[w]
+        # spread: every XCD (workgroup mod 8) holds owners when there are at least 8
+        if len(owners) >= 8 and nw % 8 == 0:
+            assert {w % 8 for w in owners} == set(range(8))
 
 
-def _plan_split(model, B, mb, nw):
-    """The split length the builder chose: the plan's max_splits fixes it."""
+def _plan_split(model, B, mb, nw, default_tasks):
+    """The split length the builder chose: the explicit length whose plan
+    equals the default one."""
     cfg = _cfg(model, B)
-    opts = mk.make_opts()
+    want = [(t.op, t.aux[16], t.n0, t.n1) for t in default_tasks]
     for S in range(16, 4097, 16):
-        o2 = mk.make_opts(attn_split=S)
         try:
-            a, _ = mk.mk_plan_schedule(cfg, B, mb, o2, nw)
+            a, _ = mk.mk_plan_schedule(cfg, B, mb, mk.make_opts(attn_split=S), nw)
         except Exception:
             continue
-        b, _ = mk.mk_plan_schedule(cfg, B, mb, opts, nw)
-        if [(t.op, t.aux[16], t.n0, t.n1) for t in a] == [(t.op, t.aux[16], t.n0, t.n1) for t in b]:
+        if [(t.op, t.aux[16], t.n0, t.n1) for t in a] == want:
             return S
     raise AssertionError("split length not found")
 
