@@ -7,6 +7,7 @@ about 0.5 GB of KV at 8K context, over 3.35 TB/s.  292 tok/s is 62% of it and
 185 tok/s is 39%.
 """
 import math
+import os
 
 from persistent_moe_amd import sol
 from persistent_moe_amd import workloads as W
@@ -43,3 +44,36 @@ def test_sliding_window_limits_kv():
     assert sol.visible_keys(cfg, 3, 262144) == 262145
     kv = sol.kv_bytes(cfg, [262144])
     assert kv == (12 * 262145 + 36 * 4096) * 2048
+
+
+def test_fp8_expert_bytes_are_codes_plus_row_scales():
+    """FP8 experts: one byte per weight and a float32 scale per output row
+    (2I gate/up rows and d down rows per expert); the rest stays bf16."""
+    from dataclasses import replace
+    bf = W.MOE_30B
+    f8 = replace(bf, expert_fp8=True)
+    d, I, k = bf.d_model, bf.expert_inter, bf.top_k
+    per_expert_bf16 = 3 * I * d * 2
+    per_expert_fp8 = 3 * I * d + (2 * I + d) * 4
+    diff = sol.layer_weight_bytes(bf, k) - sol.layer_weight_bytes(f8, k)
+    assert diff == k * (per_expert_bf16 - per_expert_fp8)
+    # 5.51 GB per bs=1 8K step with FP8 experts
+    assert abs(sol.step_bytes(f8, [8192], [8] * 48) / 5.51e9 - 1) < 0.01
+
+
+def test_bench_reports_traffic_only_for_the_sources_it_was_taken_with(tmp_path, monkeypatch):
+    """The committed HBM-traffic summary carries the sha256 prefix of the
+    kernel sources; with any source changed, bench.py reports no traffic."""
+    import shutil
+    import bench
+    root = tmp_path / "repo"
+    for f in bench.KERNEL_SOURCES + ["profiles/mk_persistent_moe30b_bs1_ctx8k_traffic.txt"]:
+        (root / f).parent.mkdir(parents=True, exist_ok=True)
+        shutil.copy(os.path.join(bench.ROOT, f), root / f)
+    monkeypatch.setattr(bench, "ROOT", str(root))
+    v = bench.measured_traffic("moe30b-bs1-ctx8k")
+    assert v is not None and 7.3e9 < v < 7.5e9
+    assert bench.measured_traffic("moe30b-bs8-ragged") is None
+    with open(root / bench.KERNEL_SOURCES[1], "a") as fh:
+        fh.write("\n")
+    assert bench.measured_traffic("moe30b-bs1-ctx8k") is None
