@@ -45,11 +45,34 @@ def build_gen() -> str:
     return out
 
 
+def build_mk_host_sanitized(out: str) -> str:
+    """libmk.so with AddressSanitizer and UndefinedBehaviorSanitizer on the
+    host code only (the device code is built as usual), for checking the
+    schedule builder, the simulator and the argument validation on the CPU.
+    Load it with ``mk.load(out)`` in a process started with the clang ASan
+    runtime preloaded (``LD_PRELOAD=.../libclang_rt.asan-x86_64.so``,
+    ``ASAN_OPTIONS=detect_leaks=0``)."""
+    os.makedirs(os.path.dirname(os.path.abspath(out)), exist_ok=True)
+    san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+           "-Xarch_host", "-fno-omit-frame-pointer", "-shared-libsan"]
+    cmd = ([HIPCC] + HIP_FLAGS + ["-Xarch_host", "-g"] + san +
+           [os.path.join(CSRC, "mk_kernel.hip"), os.path.join(CSRC, "mk_host.cpp"), "-o", out])
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr)
+        raise RuntimeError("hipcc failed building the sanitized libmk.so")
+    return out
+
+
 def build(verbose: bool = False) -> None:
     build_gen()
     build_mk(verbose)
 
 
 if __name__ == "__main__":
-    build(verbose="-v" in sys.argv)
-    print("built", os.path.join(LIB, "libmk.so"))
+    if "--host-sanitizers" in sys.argv:
+        out = sys.argv[sys.argv.index("--host-sanitizers") + 1]
+        print("built", build_mk_host_sanitized(out))
+    else:
+        build(verbose="-v" in sys.argv)
+        print("built", os.path.join(LIB, "libmk.so"))
